@@ -1,0 +1,147 @@
+"""Parallax attention oracle -- TEST INFRASTRUCTURE ONLY.
+
+A plain double-precision CPU implementation of the Parallax readout (see
+``oracle.c`` for the definition and the passages it follows). Only the tests,
+``__graft_entry__.smoke()`` and the benchmark's ``cpu_baseline`` leg may
+import this package; the GPU library and its Python binding never do, and the
+two share no code. Inputs are numpy arrays of float32, float64 or of
+bf16 bit patterns (uint16); every result is float64.
+
+Parity pins (tests/test_oracle_pins.py) tie this code to what the pages and
+the mathematics fix: r = 0 against torch's float64 scaled_dot_product_attention,
+the correction against numpy's weighted covariance and against the
+cross-covariance matrix route, the plus sign against the intercept of a
+weighted least-squares fit, closed forms for one and two keys, shift and
+linearity invariants, and a 50-digit mpmath evaluation on tiny inputs.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+F32, BF16, F64 = 0, 1, 2
+
+
+def build() -> str:
+    """Compile ``liboracle.so`` (plain C, double, OpenMP; no fast-math)."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-ffp-contract=off",
+           os.path.join(_HERE, "oracle.c"), "-o", _LIB_PATH + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is not built; run __graft_entry__.build()")
+        lib = ctypes.CDLL(_LIB_PATH)
+        vp, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
+        lib.oracle_decode.argtypes = [vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, dbl, dbl,
+                                      i64, vp, vp]
+        lib.oracle_decode.restype = i32
+        lib.oracle_prefill.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, dbl, dbl,
+                                       i64, vp, vp, vp, vp]
+        lib.oracle_prefill.restype = i32
+        _lib = lib
+    return _lib
+
+
+def _dtype_of(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    if a.dtype == np.float64:
+        return F64
+    raise TypeError(f"oracle inputs are float32, float64 or bf16 bits (uint16), got {a.dtype}")
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def decode(q, r, k, v, *, seq_start=None, seq_len=None, Hkv=None, qk_scale=None, rk_scale=1.0,
+           rows=None):
+    """Parallax decode rows.
+
+    q, r: [B, Hq, D] (r may be None: r = 0, plain softmax attention).
+    k, v: [B, L, Hkv, D] dense, or [T, Hkv, D] packed with ``seq_start`` /
+    ``seq_len`` giving each sequence's token range.
+    rows: optional int array [n, 2] of (b, h); default all rows.
+    Returns float64 [B, Hq, D] (or [n, D] when rows is given).
+    """
+    dt = _dtype_of(q)
+    for a in (r, k, v):
+        if a is not None:
+            assert _dtype_of(a) == dt and a.flags.c_contiguous
+    assert q.flags.c_contiguous
+    B, Hq, D = q.shape
+    if k.ndim == 4:
+        Bk, L, Hk, Dk = k.shape
+        assert Bk == B and Dk == D
+        if seq_start is None:
+            seq_start = np.arange(B, dtype=np.int64) * L
+        if seq_len is None:
+            seq_len = np.full(B, L, dtype=np.int64)
+    else:
+        _, Hk, Dk = k.shape
+        assert Dk == D and seq_start is not None and seq_len is not None
+    Hkv = Hk if Hkv is None else Hkv
+    seq_start = np.ascontiguousarray(seq_start, dtype=np.int64)
+    seq_len = np.ascontiguousarray(seq_len, dtype=np.int64)
+    tau = 1.0 / math.sqrt(D) if qk_scale is None else float(qk_scale)
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 2)
+        out = np.empty((rows.shape[0], D), dtype=np.float64)
+        n = rows.shape[0]
+    else:
+        out = np.empty((B, Hq, D), dtype=np.float64)
+        n = B * Hq
+    rc = _load().oracle_decode(_ptr(q), _ptr(r), _ptr(k), _ptr(v), dt, _ptr(seq_start),
+                               _ptr(seq_len), B, Hq, Hkv, D, tau, float(rk_scale), n, _ptr(rows),
+                               _ptr(out))
+    if rc != 0:
+        raise RuntimeError(f"oracle_decode failed ({rc})")
+    return out
+
+
+def prefill(q, r, k, v, *, qk_scale=None, rk_scale=1.0, rows=None, stats=False):
+    """Causal Parallax prefill rows.
+
+    q, r: [B, Hq, L, D] (r may be None); k, v: [B, Hkv, L, D].
+    rows: optional int array [n, 3] of (b, h, i).
+    Returns o float64 [B, Hq, L, D] (or [n, D]); with stats=True also lse and sbar.
+    """
+    dt = _dtype_of(q)
+    for a in (q, r, k, v):
+        if a is not None:
+            assert _dtype_of(a) == dt and a.flags.c_contiguous
+    B, Hq, L, D = q.shape
+    Hkv = k.shape[1]
+    tau = 1.0 / math.sqrt(D) if qk_scale is None else float(qk_scale)
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 3)
+        n = rows.shape[0]
+        out = np.empty((n, D), dtype=np.float64)
+        lse = np.empty(n, dtype=np.float64)
+        sbar = np.empty(n, dtype=np.float64)
+    else:
+        n = B * Hq * L
+        out = np.empty((B, Hq, L, D), dtype=np.float64)
+        lse = np.empty((B, Hq, L), dtype=np.float64)
+        sbar = np.empty((B, Hq, L), dtype=np.float64)
+    rc = _load().oracle_prefill(_ptr(q), _ptr(r), _ptr(k), _ptr(v), dt, B, Hq, Hkv, L, D, tau,
+                                float(rk_scale), n, _ptr(rows), _ptr(out), _ptr(lse), _ptr(sbar))
+    if rc != 0:
+        raise RuntimeError(f"oracle_prefill failed ({rc})")
+    return (out, lse, sbar) if stats else out
