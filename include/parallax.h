@@ -1,0 +1,134 @@
+/*
+ * parallax.h -- C ABI of the MI355X (gfx950) Parallax attention library.
+ *
+ * Parallax ("Parallax: Parameterized Local Linear Attention for Language
+ * Modeling"; PyPI README, "Quickstart"; neuraltrendhub summary, "What the
+ * paper found"; original abstract) keeps the softmax readout of attention
+ * and adds a learned probe r, one per query head, whose scores s = r . k
+ * read out the key-value covariance. For one query row with visible keys J:
+ *
+ *   z_j  = qk_scale * <q, k_j>,   w = softmax(z) over J
+ *   s_j  = rk_scale * <r, k_j>,   sbar = sum_j w_j s_j
+ *   o    = sum_j w_j v_j + sum_j w_j (s_j - sbar) v_j
+ *
+ * r = 0 gives softmax attention exactly (encorp.ai article, FAQ). The pages
+ * print no equation; this is the local-linear intercept of the cere-bro
+ * blog's diagram with the solver's output replaced by the probe, and the
+ * plus sign is that intercept's. The pages leave the scale of s open:
+ * rk_scale = 1 is the plain reading, and the argument keeps the other one
+ * expressible.
+ *
+ * Conventions shared by every entry point:
+ *  - Every tensor pointer is a DEVICE pointer; buffers are dense row-major
+ *    in the layouts stated below. The caller owns every buffer, including
+ *    the decode workspace; the library never allocates or frees memory.
+ *  - dtype: PLX_F32 (float) or PLX_BF16 (bfloat16 bits). q, r, k, v and o
+ *    share it. Arithmetic is fp32 (bf16 inputs are contracted on matrix
+ *    cores with fp32 accumulation); bf16 outputs are rounded to nearest-even.
+ *  - Query head h reads KV head h / (Hq / Hkv) (consecutive groups, as
+ *    torch's repeat_interleave). The pages show only Hq == Hkv.
+ *  - Argument checks are synchronous, host-only, and happen before any
+ *    launch: a failing check returns a status and touches no memory.
+ *    Launch failures return PLX_ERR_HIP. Work is enqueued on `stream`
+ *    (a hipStream_t; NULL is the default stream); nothing synchronises.
+ *  - Results do not depend on timing: no atomics, a fixed split plan, so
+ *    repeated calls return bit-identical outputs.
+ *  - Non-finite inputs propagate; they are not checked.
+ */
+#ifndef PARALLAX_H
+#define PARALLAX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PARALLAX_ABI_VERSION 1
+
+typedef enum {
+    PLX_OK = 0,
+    PLX_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, Hq % Hkv != 0 */
+    PLX_ERR_UNSUPPORTED = 2, /* valid but not implemented (head_dim, dtype) */
+    PLX_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+    PLX_ERR_HIP = 4          /* the HIP runtime reported an error */
+} plx_status;
+
+typedef enum { PLX_F32 = 0, PLX_BF16 = 1 } plx_dtype;
+
+/* PARALLAX_ABI_VERSION of the built library. */
+int parallax_abi_version(void);
+
+/* Static, never-NULL description of a status code. */
+const char *parallax_status_string(int status);
+
+/* ------------------------------------------------------------------------
+ * Decode: one new query token per sequence against its KV cache (PyPI
+ * README, "Decoding (CuTeDSL)": q, r (B, 1, H, D); k, v (B, kv_len, H, D);
+ * qk_scale = 1/sqrt(D)). Every cached key of a sequence is visible.
+ *
+ *   q, r, o : [B, Hq, D]                  (the (B, 1, Hq, D) of the pages)
+ *   k, v    : [B, kv_len, Hkv, D]         when cu_seqlens_k == NULL
+ *             [cu_seqlens_k[B], Hkv, D]   packed, when cu_seqlens_k != NULL
+ *   cu_seqlens_k : NULL, or DEVICE int32 [B + 1], non-decreasing from 0;
+ *             sequence b owns tokens cu[b] .. cu[b+1]-1 and its length
+ *             must not exceed kv_len (kv_len is the maximum length). A
+ *             zero-length sequence yields o = 0. The offsets are not read
+ *             on the host, so they are not validated.
+ *   B, Hq, Hkv, D, kv_len : sizes, all >= 1; Hq % Hkv == 0; D in {64, 128}.
+ *   qk_scale : softmax logit scale (pass 1/sqrt(D) for the pages' default).
+ *   rk_scale : probe score scale (1 is the plain reading).
+ *   num_splits : 0 lets the library choose how many key ranges (splits)
+ *             each sequence is cut into; >= 1 forces that many. With more
+ *             than one split the per-split streaming states are written
+ *             to the workspace and merged by a second kernel.
+ *   workspace, workspace_bytes : device scratch of at least
+ *             parallax_decode_workspace_bytes(...) bytes for the same
+ *             arguments (may be NULL when that size is 0).
+ * Returns PLX_OK or an error status.
+ * ---------------------------------------------------------------------- */
+size_t parallax_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int kv_len, int dtype,
+                                       int num_splits);
+
+int parallax_decode(const void *q, const void *r, const void *k, const void *v, void *o,
+                    const int32_t *cu_seqlens_k, int B, int Hq, int Hkv, int D, int kv_len,
+                    float qk_scale, float rk_scale, int dtype, int num_splits,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* Plain softmax-attention decode on the same kernels and loader with the
+ * probe path compiled out: o = sum_j w_j v_j. The baseline against which the
+ * cost of the Parallax correction is measured; same layouts and rules as
+ * parallax_decode without r and rk_scale. Uses the same workspace size. */
+int softmax_decode(const void *q, const void *k, const void *v, void *o,
+                   const int32_t *cu_seqlens_k, int B, int Hq, int Hkv, int D, int kv_len,
+                   float qk_scale, int dtype, int num_splits, void *workspace,
+                   size_t workspace_bytes, void *stream);
+
+/* The split count parallax_decode / softmax_decode use for these
+ * arguments (num_splits resolved when it is 0), or 0 when they are invalid. */
+int parallax_decode_num_splits(int B, int Hq, int Hkv, int D, int kv_len, int dtype,
+                               int num_splits);
+
+/* ------------------------------------------------------------------------
+ * Causal prefill / training forward (PyPI README, "Training (Triton)":
+ * parallax_func(q, r, k, v) on (B, H, L, D) tensors, causal, returns
+ * (B, H, L, D)). Query row i sees keys 0 .. i.
+ *
+ *   q, r, o : [B, Hq, L, D]
+ *   k, v    : [B, Hkv, L, D]
+ *   lse     : NULL or DEVICE float [B, Hq, L]: m + ln(sum_j exp(z_j - m))
+ *   sbar    : NULL or DEVICE float [B, Hq, L]: sum_j w_j s_j
+ *             (the row statistics a backward pass needs; not on the pages)
+ *   D == 128 and dtype == PLX_BF16 run on bf16 MFMA with fp32 accumulation;
+ *   other D in {64, 128} and PLX_F32 run on a plain fp32 kernel.
+ * ---------------------------------------------------------------------- */
+int parallax_prefill(const void *q, const void *r, const void *k, const void *v, void *o,
+                     float *lse, float *sbar, int B, int Hq, int Hkv, int L, int D,
+                     float qk_scale, float rk_scale, int dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PARALLAX_H */

@@ -1,0 +1,222 @@
+"""Python binding of the MI355X Parallax attention library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libparallax_hip.so`` (built in-tree by
+``python -m parameterized_local_linear_amd.build``). PyTorch provides device
+memory and the current stream; there is no CPU or PyTorch fallback, and a
+missing library raises.
+
+Entry points mirror the C ABI (include/parallax.h):
+  decode(q, r, k, v, ...)          Parallax decode, q/r [B, Hq, D] or [B, 1, Hq, D]
+  softmax_decode(q, k, v, ...)     the same kernels with the probe path compiled out
+  prefill(q, r, k, v, ...)         causal Parallax prefill on [B, H, L, D]
+and the pages' names ``parallax_decode`` and ``parallax_func`` alias decode
+and prefill.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libparallax_hip.so")
+
+PLX_F32, PLX_BF16 = 0, 1
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration",
+          3: "workspace missing or too small", 4: "HIP runtime error"}
+
+_lib = None
+
+
+class ParallaxError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {STATUS.get(status, status)} (status {status})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m parameterized_local_linear_amd.build` (there is no fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        L.parallax_abi_version.argtypes = []
+        L.parallax_abi_version.restype = i32
+        L.parallax_status_string.argtypes = [i32]
+        L.parallax_status_string.restype = ctypes.c_char_p
+        L.parallax_decode_workspace_bytes.argtypes = [i32] * 7
+        L.parallax_decode_workspace_bytes.restype = sz
+        L.parallax_decode_num_splits.argtypes = [i32] * 7
+        L.parallax_decode_num_splits.restype = i32
+        L.parallax_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, f32,
+                                      i32, i32, vp, sz, vp]
+        L.parallax_decode.restype = i32
+        L.softmax_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32,
+                                     vp, sz, vp]
+        L.softmax_decode.restype = i32
+        L.parallax_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
+                                       f32, i32, vp]
+        L.parallax_prefill.restype = i32
+        _lib = L
+    return _lib
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return PLX_F32
+    if t.dtype == torch.bfloat16:
+        return PLX_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(t: torch.Tensor, name: str, dtype, device):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype or t.device != device:
+        raise ValueError(f"{name} must be {dtype} on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def decode_workspace_bytes(B, Hq, Hkv, D, kv_len, dtype_code, num_splits=0) -> int:
+    return int(lib().parallax_decode_workspace_bytes(B, Hq, Hkv, D, kv_len, dtype_code,
+                                                     num_splits))
+
+
+def decode_num_splits(B, Hq, Hkv, D, kv_len, dtype_code, num_splits=0) -> int:
+    return int(lib().parallax_decode_num_splits(B, Hq, Hkv, D, kv_len, dtype_code, num_splits))
+
+
+def _decode_impl(q, r, k, v, qk_scale, rk_scale, cu_seqlens_k, kv_len, num_splits, out,
+                 workspace, parallax):
+    L_ = lib()
+    squeeze = q.dim() == 4
+    if squeeze:                       # the pages' (B, 1, H, D)
+        if q.shape[1] != 1:
+            raise ValueError("decode takes one query token per sequence")
+        q = q[:, 0]
+        if r is not None:
+            r = r[:, 0]
+    B, Hq, D = q.shape
+    dev, dt = q.device, q.dtype
+    _check(q, "q", dt, dev)
+    if parallax:
+        _check(r, "r", dt, dev)
+        if r.shape != q.shape:
+            raise ValueError("r must have q's shape")
+    _check(k, "k", dt, dev)
+    _check(v, "v", dt, dev)
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    if cu_seqlens_k is None:
+        if k.dim() != 4 or k.shape[0] != B or k.shape[3] != D:
+            raise ValueError("dense k/v must be [B, kv_len, Hkv, D]")
+        kv_len = k.shape[1]
+        Hkv = k.shape[2]
+    else:
+        _check(cu_seqlens_k, "cu_seqlens_k", torch.int32, dev)
+        if cu_seqlens_k.shape != (B + 1,):
+            raise ValueError("cu_seqlens_k must be int32 [B + 1]")
+        if k.dim() != 3 or k.shape[2] != D:
+            raise ValueError("packed k/v must be [total_tokens, Hkv, D]")
+        if kv_len is None:
+            raise ValueError("packed decode needs kv_len (the maximum sequence length)")
+        Hkv = k.shape[1]
+    code = _dtype_code(q)
+    if qk_scale is None:
+        qk_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=dt, device=dev)
+    else:
+        _check(out, "out", dt, dev)
+        if out.shape != (B, Hq, D):
+            raise ValueError("out must be [B, Hq, D]")
+    need = decode_workspace_bytes(B, Hq, Hkv, D, int(kv_len), code, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    stream = _stream_handle(dev)
+    if parallax:
+        st = L_.parallax_decode(_ptr(q), _ptr(r), _ptr(k), _ptr(v), _ptr(out), _ptr(cu_seqlens_k),
+                                B, Hq, Hkv, D, int(kv_len), float(qk_scale), float(rk_scale), code,
+                                int(num_splits), _ptr(workspace), ws_bytes, stream)
+        what = "parallax_decode"
+    else:
+        st = L_.softmax_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(cu_seqlens_k), B, Hq, Hkv,
+                               D, int(kv_len), float(qk_scale), code, int(num_splits),
+                               _ptr(workspace), ws_bytes, stream)
+        what = "softmax_decode"
+    if st != 0:
+        raise ParallaxError(st, what)
+    return out[:, None] if squeeze else out
+
+
+def decode(q, r, k, v, qk_scale=None, rk_scale=1.0, *, cu_seqlens_k=None, kv_len=None,
+           num_splits=0, out=None, workspace=None):
+    """Parallax decode. q, r: [B, Hq, D] (or [B, 1, Hq, D]); k, v: [B, kv_len, Hkv, D],
+    or packed [T, Hkv, D] with int32 ``cu_seqlens_k`` [B + 1] and ``kv_len`` = max length."""
+    return _decode_impl(q, r, k, v, qk_scale, rk_scale, cu_seqlens_k, kv_len, num_splits, out,
+                        workspace, True)
+
+
+def softmax_decode(q, k, v, qk_scale=None, *, cu_seqlens_k=None, kv_len=None, num_splits=0,
+                   out=None, workspace=None):
+    """Softmax-attention decode on the same kernels (the Parallax correction compiled out)."""
+    return _decode_impl(q, None, k, v, qk_scale, 1.0, cu_seqlens_k, kv_len, num_splits, out,
+                        workspace, False)
+
+
+def prefill(q, r, k, v, qk_scale=None, rk_scale=1.0, *, out=None, return_stats=False):
+    """Causal Parallax prefill. q, r: [B, Hq, L, D]; k, v: [B, Hkv, L, D] -> o [B, Hq, L, D]
+    (plus fp32 lse and sbar [B, Hq, L] with return_stats=True)."""
+    L_ = lib()
+    B, Hq, L, D = q.shape
+    dev, dt = q.device, q.dtype
+    for t, name in ((q, "q"), (r, "r"), (k, "k"), (v, "v")):
+        _check(t, name, dt, dev)
+    if r.shape != q.shape:
+        raise ValueError("r must have q's shape")
+    if k.shape != v.shape or k.dim() != 4 or k.shape[0] != B or k.shape[2] != L or k.shape[3] != D:
+        raise ValueError("k, v must be [B, Hkv, L, D]")
+    Hkv = k.shape[1]
+    code = _dtype_code(q)
+    if qk_scale is None:
+        qk_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", dt, dev)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    lse = sbar = None
+    if return_stats:
+        lse = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
+        sbar = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
+    st = L_.parallax_prefill(_ptr(q), _ptr(r), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(sbar),
+                             B, Hq, Hkv, L, D, float(qk_scale), float(rk_scale), code,
+                             _stream_handle(dev))
+    if st != 0:
+        raise ParallaxError(st, "parallax_prefill")
+    return (out, lse, sbar) if return_stats else out
+
+
+parallax_decode = decode
+parallax_func = prefill
+
+__all__ = ["decode", "softmax_decode", "prefill", "parallax_decode", "parallax_func",
+           "decode_workspace_bytes", "decode_num_splits", "lib", "ParallaxError", "LIB_PATH"]

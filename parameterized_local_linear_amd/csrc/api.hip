@@ -1,0 +1,178 @@
+// C ABI of the Parallax library: argument checks, the decode split plan,
+// and the launches. See include/parallax.h for the contract of every entry
+// point. Argument checks are host-only and run before any launch.
+#include "../../include/parallax.h"
+#include "plx_internal.h"
+
+#include <math.h>
+
+namespace plx {
+
+namespace {
+
+int g_cu_count[64];  // per-device compute-unit count, filled on first use
+
+int device_cu_count() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (g_cu_count[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        g_cu_count[dev] = n;
+    }
+    return g_cu_count[dev];
+}
+
+}  // namespace
+
+// Decode plan. The MFMA path (bf16, head_dim 128, group size 1/2/4/8) runs
+// one wave per (KV head, split, sequence); the generic path one wave per
+// (query head, split, sequence). Without a forced count, the sequence is cut
+// into enough splits to give about 8 waves per compute unit, with at least
+// 128 keys per split; one split fuses the final normalisation into the
+// streaming kernel and needs no workspace.
+DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int kv_len, int dtype, int num_splits) {
+    DecodePlan p;
+    const int G = Hq / Hkv;
+    const bool mfma = dtype == PLX_BF16 && D == 128 && (G == 1 || G == 2 || G == 4 || G == 8);
+    p.path = mfma ? DecodePath::Mfma : DecodePath::Generic;
+    const long units = (long)B * (mfma ? Hkv : Hq);
+    const int max_splits = (kv_len + 31) / 32;
+    int splits = num_splits;
+    if (splits <= 0) {
+        const long target = 8L * device_cu_count();
+        long s = (target + units - 1) / units;
+        const long by_len = (kv_len + 127) / 128;
+        if (s > by_len) s = by_len;
+        if (s < 1) s = 1;
+        splits = (int)s;
+    }
+    if (splits > max_splits) splits = max_splits;
+    if (splits > 65535) splits = 65535;  // grid.y limit
+    if (splits < 1) splits = 1;
+    int chunk = (kv_len + splits - 1) / splits;
+    chunk = (chunk + 31) / 32 * 32;
+    splits = (kv_len + chunk - 1) / chunk;
+    p.splits = splits;
+    p.chunk = chunk;
+    p.ws_bytes = splits > 1 ? (size_t)B * Hq * splits * partial_floats(D) * sizeof(float) : 0;
+    return p;
+}
+
+}  // namespace plx
+
+using plx::DecodePlan;
+
+static int check_decode_sizes(int B, int Hq, int Hkv, int D, int kv_len, int dtype) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || kv_len < 1) return PLX_ERR_INVALID_ARG;
+    if (Hq % Hkv != 0) return PLX_ERR_INVALID_ARG;
+    if (B > 65535 || Hq > 65535) return PLX_ERR_UNSUPPORTED;
+    if (dtype != PLX_F32 && dtype != PLX_BF16) return PLX_ERR_UNSUPPORTED;
+    if (D != 64 && D != 128) return PLX_ERR_UNSUPPORTED;
+    return PLX_OK;
+}
+
+extern "C" {
+
+int parallax_abi_version(void) { return PARALLAX_ABI_VERSION; }
+
+const char *parallax_status_string(int status) {
+    switch (status) {
+        case PLX_OK: return "ok";
+        case PLX_ERR_INVALID_ARG: return "invalid argument";
+        case PLX_ERR_UNSUPPORTED: return "unsupported configuration";
+        case PLX_ERR_WORKSPACE: return "workspace missing or too small";
+        case PLX_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+size_t parallax_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int kv_len, int dtype,
+                                       int num_splits) {
+    if (check_decode_sizes(B, Hq, Hkv, D, kv_len, dtype) != PLX_OK) return 0;
+    return plx::plan_decode(B, Hq, Hkv, D, kv_len, dtype, num_splits).ws_bytes;
+}
+
+int parallax_decode_num_splits(int B, int Hq, int Hkv, int D, int kv_len, int dtype, int num_splits) {
+    if (check_decode_sizes(B, Hq, Hkv, D, kv_len, dtype) != PLX_OK) return 0;
+    return plx::plan_decode(B, Hq, Hkv, D, kv_len, dtype, num_splits).splits;
+}
+
+static int decode_common(const void *q, const void *r, const void *k, const void *v, void *o,
+                         const int32_t *cu, int B, int Hq, int Hkv, int D, int kv_len,
+                         float qk_scale, float rk_scale, int dtype, int num_splits, void *ws,
+                         size_t ws_bytes, void *stream, bool parallax) {
+    int st = check_decode_sizes(B, Hq, Hkv, D, kv_len, dtype);
+    if (st != PLX_OK) return st;
+    if (!q || !k || !v || !o || (parallax && !r)) return PLX_ERR_INVALID_ARG;
+    if (num_splits < 0) return PLX_ERR_INVALID_ARG;
+    if (!isfinite(qk_scale) || !isfinite(rk_scale)) return PLX_ERR_INVALID_ARG;
+    const DecodePlan p = plx::plan_decode(B, Hq, Hkv, D, kv_len, dtype, num_splits);
+    if (p.ws_bytes > 0 && (!ws || ws_bytes < p.ws_bytes)) return PLX_ERR_WORKSPACE;
+    plx::DecodeArgs a;
+    a.q = q;
+    a.r = r;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.cu = cu;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.D = D;
+    a.kv_len = kv_len;
+    a.zscale = qk_scale * plx::kLog2e;
+    a.rk_scale = rk_scale;
+    a.splits = p.splits;
+    a.chunk = p.chunk;
+    a.ws = reinterpret_cast<float *>(ws);
+    hipError_t err = plx::launch_decode(a, p.path, dtype, parallax, reinterpret_cast<hipStream_t>(stream));
+    return err == hipSuccess ? PLX_OK : PLX_ERR_HIP;
+}
+
+int parallax_decode(const void *q, const void *r, const void *k, const void *v, void *o,
+                    const int32_t *cu_seqlens_k, int B, int Hq, int Hkv, int D, int kv_len,
+                    float qk_scale, float rk_scale, int dtype, int num_splits, void *workspace,
+                    size_t workspace_bytes, void *stream) {
+    return decode_common(q, r, k, v, o, cu_seqlens_k, B, Hq, Hkv, D, kv_len, qk_scale, rk_scale,
+                         dtype, num_splits, workspace, workspace_bytes, stream, true);
+}
+
+int softmax_decode(const void *q, const void *k, const void *v, void *o, const int32_t *cu_seqlens_k,
+                   int B, int Hq, int Hkv, int D, int kv_len, float qk_scale, int dtype, int num_splits,
+                   void *workspace, size_t workspace_bytes, void *stream) {
+    return decode_common(q, nullptr, k, v, o, cu_seqlens_k, B, Hq, Hkv, D, kv_len, qk_scale, 1.0f,
+                         dtype, num_splits, workspace, workspace_bytes, stream, false);
+}
+
+int parallax_prefill(const void *q, const void *r, const void *k, const void *v, void *o, float *lse,
+                     float *sbar, int B, int Hq, int Hkv, int L, int D, float qk_scale, float rk_scale,
+                     int dtype, void *stream) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || L < 1 || D < 1) return PLX_ERR_INVALID_ARG;
+    if (Hq % Hkv != 0) return PLX_ERR_INVALID_ARG;
+    if (!q || !r || !k || !v || !o) return PLX_ERR_INVALID_ARG;
+    if (!isfinite(qk_scale) || !isfinite(rk_scale)) return PLX_ERR_INVALID_ARG;
+    if (dtype != PLX_F32 && dtype != PLX_BF16) return PLX_ERR_UNSUPPORTED;
+    if (!plx::prefill_supported(D, dtype)) return PLX_ERR_UNSUPPORTED;
+    if (B > 65535 || Hq > 65535) return PLX_ERR_UNSUPPORTED;
+    plx::PrefillArgs a;
+    a.q = q;
+    a.r = r;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.sbar = sbar;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.L = L;
+    a.D = D;
+    a.zscale = qk_scale * plx::kLog2e;
+    a.rk_scale = rk_scale;
+    hipError_t err = plx::launch_prefill(a, dtype, reinterpret_cast<hipStream_t>(stream));
+    return err == hipSuccess ? PLX_OK : PLX_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,64 @@
+// Internal declarations shared by the HIP translation units of the Parallax
+// library (kernels, launchers, the C ABI). Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace plx {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// One decode split's streaming state, stored in the workspace as
+// A[D], B[D], m, l, S, pad (2D + 4 floats) for every (b, hq, split).
+//   m : running maximum of the logits, in log2 units (logit * log2 e)
+//   l : sum_j e_j                         e_j = 2^(z_j log2e - m)
+//   S : sum_j e_j (s_j - pi)              pi = the sequence's pivot score
+//   A : sum_j e_j v_j
+//   B : sum_j e_j (s_j - pi) v_j
+__host__ __device__ constexpr int partial_floats(int D) { return 2 * D + 4; }
+
+struct DecodeArgs {
+    const void *q, *r, *k, *v;
+    void *o;
+    const int32_t *cu;  // device [B+1] or nullptr (dense cache)
+    int B, Hq, Hkv, D, kv_len;
+    float zscale;       // qk_scale * log2(e)
+    float rk_scale;
+    int splits;         // >= 1
+    int chunk;          // keys per split, multiple of 32
+    float *ws;          // partial records, used when splits > 1
+};
+
+enum class DecodePath { Mfma, Generic };
+
+// Host-side decode plan shared by the workspace query and the launch.
+struct DecodePlan {
+    DecodePath path;
+    int splits;
+    int chunk;
+    size_t ws_bytes;
+};
+
+DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int kv_len, int dtype, int num_splits);
+
+hipError_t launch_decode(const DecodeArgs &a, DecodePath path, int dtype, bool parallax,
+                         hipStream_t stream);
+
+struct PrefillArgs {
+    const void *q, *r, *k, *v;
+    void *o;
+    float *lse, *sbar;
+    int B, Hq, Hkv, L, D;
+    float zscale;       // qk_scale * log2(e)
+    float rk_scale;
+};
+
+hipError_t launch_prefill(const PrefillArgs &a, int dtype, hipStream_t stream);
+bool prefill_supported(int D, int dtype);
+
+}  // namespace plx

@@ -1,0 +1,96 @@
+"""The C ABI library: it loads, exports every declared symbol, and rejects bad
+arguments on the host before any launch (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import parameterized_local_linear_amd as plx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    names = []
+    inc = os.path.join(ROOT, "include")
+    for fn in os.listdir(inc):
+        if fn.endswith(".h"):
+            text = open(os.path.join(inc, fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^[A-Za-z_][\w\s\*]*?\b(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "defined")))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"parallax_decode", "softmax_decode", "parallax_prefill",
+            "parallax_decode_workspace_bytes", "parallax_abi_version"} <= set(names)
+    lib = ctypes.CDLL(plx.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings():
+    L = plx.lib()
+    assert L.parallax_abi_version() == 1
+    for s in range(5):
+        assert L.parallax_status_string(s).decode() == plx.STATUS[s]
+    assert L.parallax_status_string(99) == b"unknown status"
+
+
+def _decode(**kw):
+    a = dict(q=FAKE, r=FAKE, k=FAKE, v=FAKE, o=FAKE, cu=None, B=1, Hq=4, Hkv=2, D=128, L=64,
+             qk=0.1, rk=1.0, dt=1, ns=0, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return plx.lib().parallax_decode(a["q"], a["r"], a["k"], a["v"], a["o"], a["cu"], a["B"],
+                                     a["Hq"], a["Hkv"], a["D"], a["L"], a["qk"], a["rk"], a["dt"],
+                                     a["ns"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), 1), (dict(Hq=0), 1), (dict(L=0), 1), (dict(Hq=6, Hkv=4), 1),
+    (dict(q=None), 1), (dict(r=None), 1), (dict(k=None), 1), (dict(o=None), 1),
+    (dict(D=96), 2), (dict(D=256), 2), (dict(dt=2), 2), (dict(ns=-1), 1),
+    (dict(qk=float("nan")), 1), (dict(rk=float("inf")), 1),
+    (dict(ns=4), 3), (dict(ns=4, ws=FAKE, wsb=16), 3),
+])
+def test_decode_rejects_on_host(kw, status):
+    assert _decode(**kw) == status
+
+
+def test_softmax_decode_and_prefill_reject_on_host():
+    L = plx.lib()
+    assert L.softmax_decode(FAKE, FAKE, FAKE, FAKE, None, 1, 4, 3, 128, 10, 0.1, 1, 0, None, 0,
+                            None) == 1
+    assert L.softmax_decode(FAKE, FAKE, FAKE, FAKE, None, 1, 4, 2, 80, 10, 0.1, 1, 0, None, 0,
+                            None) == 2
+    args = [FAKE] * 5 + [None, None]
+    assert L.parallax_prefill(*args, 1, 4, 2, 0, 128, 0.1, 1.0, 1, None) == 1
+    assert L.parallax_prefill(*args, 1, 4, 3, 16, 128, 0.1, 1.0, 1, None) == 1
+    assert L.parallax_prefill(*args, 1, 4, 2, 16, 72, 0.1, 1.0, 1, None) == 2
+    assert L.parallax_prefill(*args, 1, 4, 2, 16, 128, 0.1, 1.0, 5, None) == 2
+    assert L.parallax_prefill(None, *args[1:], 1, 4, 2, 16, 128, 0.1, 1.0, 1, None) == 1
+
+
+def test_workspace_plan():
+    ws = plx.decode_workspace_bytes
+    ns = plx.decode_num_splits
+    assert ws(1, 16, 8, 128, 32768, 1, 1) == 0
+    assert ns(1, 16, 8, 128, 32768, 1, 1) == 1
+    # forced split counts: records of 2D + 4 floats per (b, hq, split)
+    assert ns(1, 16, 8, 128, 32768, 1, 64) == 64
+    assert ws(1, 16, 8, 128, 32768, 1, 64) == 16 * 64 * (2 * 128 + 4) * 4
+    # at least 32 keys per split
+    assert ns(2, 4, 2, 128, 100, 1, 1000) == 4
+    # monotone in the length for a fixed request
+    prev = 0
+    for L in (1, 33, 64, 500, 4096, 70000):
+        cur = ws(4, 8, 2, 64, L, 0, 16)
+        assert cur >= prev
+        prev = cur
+    assert ws(0, 16, 8, 128, 64, 1, 0) == 0 and ns(1, 16, 5, 128, 64, 1, 0) == 0
+    # the automatic plan keeps at least 128 keys per split
+    s = ns(1, 16, 8, 128, 32768, 1, 0)
+    assert 1 < s <= 32768 // 128

@@ -1,0 +1,60 @@
+"""GPU parity of parallax_prefill (causal) against the double oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parameterized_local_linear_amd as plx
+import synth
+from gpu_util import assert_parity, from_gpu, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+S128 = 1.0 / math.sqrt(128.0)
+
+
+def inputs(B, Hq, Hkv, L, D, dtype, scale, seed):
+    q = synth.normal(seed, synth.TID_Q, (B, Hq, L, D), scale, dtype)
+    r = synth.normal(seed, synth.TID_R, (B, Hq, L, D), scale, dtype)
+    k = synth.normal(seed, synth.TID_K, (B, Hkv, L, D), scale, dtype)
+    v = synth.normal(seed, synth.TID_V, (B, Hkv, L, D), scale, dtype)
+    return q, r, k, v
+
+
+@pytest.mark.parametrize("dtype,D", [(synth.BF16, 128), (synth.F32, 64), (synth.BF16, 64),
+                                     (synth.F32, 128)])
+@pytest.mark.parametrize("L", [1, 7, 64, 65, 200])
+def test_prefill_small(dtype, D, L):
+    B, Hq, Hkv = 2, 4, 2
+    q, r, k, v = inputs(B, Hq, Hkv, L, D, dtype, 1.0, 40 + L)
+    t = [to_gpu(x, dtype) for x in (q, r, k, v)]
+    o, lse, sbar = plx.prefill(*t, return_stats=True)
+    ref, ref_lse, ref_sbar = oracle.prefill(q, r, k, v, stats=True)
+    assert_parity(from_gpu(o), ref, dtype, f"prefill L={L}")
+    lse = lse.cpu().numpy().astype(np.float64)
+    sbar = sbar.cpu().numpy().astype(np.float64)
+    assert np.abs(lse - ref_lse).max() <= 1e-4 * max(1.0, np.abs(ref_lse).max())
+    tol = 1e-4 if dtype == synth.F32 else 1e-2
+    assert np.abs(sbar - ref_sbar).max() <= tol * max(1.0, np.abs(ref_sbar).max())
+
+
+@pytest.mark.parametrize("scale", [S128, 1.0])
+def test_prefill_gqa_bf16(scale):
+    B, Hq, Hkv, L, D = 1, 8, 2, 300, 128
+    q, r, k, v = inputs(B, Hq, Hkv, L, D, synth.BF16, scale, 77)
+    t = [to_gpu(x, synth.BF16) for x in (q, r, k, v)]
+    assert_parity(from_gpu(plx.prefill(*t)), oracle.prefill(q, r, k, v), synth.BF16, "gqa")
+
+
+def test_prefill_row_matches_decode_on_prefix():
+    B, Hq, Hkv, L, D = 1, 4, 2, 130, 128
+    q, r, k, v = inputs(B, Hq, Hkv, L, D, synth.BF16, S128, 78)
+    t = [to_gpu(x, synth.BF16) for x in (q, r, k, v)]
+    o = from_gpu(plx.prefill(*t))
+    for i in (0, 64, 129):
+        kd = t[2][:, :, : i + 1].transpose(1, 2).contiguous()
+        vd = t[3][:, :, : i + 1].transpose(1, 2).contiguous()
+        od = from_gpu(plx.decode(t[0][:, :, i].contiguous(), t[1][:, :, i].contiguous(), kd, vd))
+        assert np.abs(od - o[:, :, i]).max() <= 1e-2 * np.abs(o[:, :, i]).max()
