@@ -1,0 +1,350 @@
+#!/usr/bin/env python
+"""Benchmark of the Parallax attention hot path on one MI355X.
+
+Default workload: long-context decode, bf16, B=1, Hq=16, Hkv=8, D=128,
+32768 cached keys (contiguous cache), q/r/K/V ~ N(0,1)/sqrt(128), seeded.
+A step is one parallax_decode call over the batch (streaming kernel + split
+merge). Inputs are resident in HBM before timing; the KV cache is replicated
+into enough copies that consecutive steps never find their keys in the
+256 MB Infinity Cache, and steps rotate through the copies. Warmup and
+timed steps are each captured into one HIP graph and replayed, bracketed
+by device synchronisation and HIP events on the launch stream.
+
+Also measured in the same run:
+  * the streaming kernel alone (a graph of parallax_decode_partial calls),
+    against the HBM roofline (8 TB/s), from algorithmic bytes K + V + q + r;
+  * softmax_decode on the same inputs (the cost of the correction branch);
+  * the CPU oracle on the same inputs (cpu_baseline), on the host's cores.
+
+Other workloads (--workload varlen | large | prefill) print their own line.
+Prints one JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Parallax decode µs/step + achieved HBM TB/s vs roofline; prefill TFLOP/s"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="long", choices=["long", "varlen", "large", "prefill"])
+    ap.add_argument("--num-splits", type=int, default=0, help="0: library plan")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target wall time of the CPU oracle sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain copy kernel of known size (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def upload_cache(torch, spec, synth, tid, tokens, chunk=1 << 16):
+    row = spec.Hkv * spec.D
+    out = torch.empty((tokens, spec.Hkv, spec.D), dtype=torch.bfloat16, device="cuda")
+    host = torch.empty((chunk, spec.Hkv, spec.D), dtype=torch.bfloat16, pin_memory=True)
+    hv = host.view(torch.int16).numpy().view(np.uint16)
+    t0 = 0
+    while t0 < tokens:
+        n = min(chunk, tokens - t0)
+        synth.normal(spec.seed, tid, (n, spec.Hkv, spec.D), spec.scale, spec.dtype,
+                     first=t0 * row, out=hv[:n])
+        out[t0:t0 + n].copy_(host[:n])
+        t0 += n
+    torch.cuda.synchronize()
+    return out
+
+
+def graph_time(torch, fn, steps, warmup):
+    """Capture `warmup` and `steps` calls of fn(i) into two graphs; replay the
+    warmup graph, then time the steps graph with events. Returns seconds/step."""
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for i in range(2):  # eager warm calls before capture
+            fn(i)
+    torch.cuda.synchronize()
+    gw = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gw, stream=stream):
+        for i in range(max(warmup, 1)):
+            fn(i)
+    gs = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gs, stream=stream):
+        for i in range(steps):
+            fn(i)
+    torch.cuda.synchronize()
+    if warmup > 0:
+        gw.replay()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        gs.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / steps
+
+
+def cpu_baseline_decode(oracle, q, r, kv_rows, spec, seconds):
+    """Time the oracle on the full step (all heads, all keys), repeated to fill
+    about `seconds` of wall time. Returns (us_per_step, repeats, threads)."""
+    k, v = kv_rows
+    t = time.perf_counter()
+    oracle.decode(q, r, k, v)
+    one = time.perf_counter() - t
+    reps = max(1, int(seconds / max(one, 1e-6)))
+    t = time.perf_counter()
+    for _ in range(reps):
+        oracle.decode(q, r, k, v)
+    per = (time.perf_counter() - t) / reps
+    threads = min(omp_threads(), spec.B * spec.Hq)
+    return per * 1e6, reps + 1, threads
+
+
+def omp_threads():
+    env = os.environ.get("OMP_NUM_THREADS")
+    n = len(os.sched_getaffinity(0))
+    if env and env.isdigit():
+        return min(int(env), n)
+    return n
+
+
+def run_decode_workload(args, torch, plx, synth, oracle):
+    idx = {"long": 2, "varlen": 3, "large": 4}[args.workload]
+    spec = synth.decode_spec(idx)
+    lens = spec.seq_lengths()
+    T = int(lens.sum())
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    q_np, r_np = synth.decode_qr(spec)
+    q = torch.from_numpy(q_np).view(torch.bfloat16).cuda()
+    r = torch.from_numpy(r_np).view(torch.bfloat16).cuda()
+    k0 = upload_cache(torch, spec, synth, synth.TID_K, T)
+    v0 = upload_cache(torch, spec, synth, synth.TID_V, T)
+    kv_bytes = 2 * k0.numel() * 2
+    copies = max(1, min(4, math.ceil(3 * MALL_BYTES / kv_bytes) + 1)) if kv_bytes < 4 * MALL_BYTES \
+        else 1
+    ks = [k0] + [k0.clone() for _ in range(copies - 1)]
+    vs = [v0] + [v0.clone() for _ in range(copies - 1)]
+    varlen = spec.varlen is not None
+    cu_t = torch.from_numpy(cu.astype(np.int32)).cuda() if varlen else None
+    if not varlen:
+        ks = [k.view(spec.B, spec.L, spec.Hkv, spec.D) for k in ks]
+        vs = [v.view(spec.B, spec.L, spec.Hkv, spec.D) for v in vs]
+    code = plx.PLX_BF16
+    ns = args.num_splits
+    splits = plx.decode_num_splits(spec.B, spec.Hq, spec.Hkv, spec.D, spec.L, code, ns)
+    ws_bytes = plx.decode_workspace_bytes(spec.B, spec.Hq, spec.Hkv, spec.D, spec.L, code, ns)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    out = torch.empty((spec.B, spec.Hq, spec.D), dtype=torch.bfloat16, device="cuda")
+    out_s = torch.empty_like(out)
+    recs = torch.empty((spec.B, spec.Hq, splits, 2 * spec.D + 4), dtype=torch.float32,
+                       device="cuda")
+    kw = dict(cu_seqlens_k=cu_t, kv_len=spec.L, num_splits=ns)
+
+    def step(i):
+        c = i % copies
+        plx.decode(q, r, ks[c], vs[c], out=out, workspace=ws, **kw)
+
+    def step_softmax(i):
+        c = i % copies
+        plx.softmax_decode(q, ks[c], vs[c], out=out_s, workspace=ws, **kw)
+
+    def step_stream_only(i):
+        c = i % copies
+        plx.decode_partial(q, r, ks[c], vs[c], records=recs, **kw)
+
+    t_step = graph_time(torch, step, args.steps, args.warmup)
+    t_soft = graph_time(torch, step_softmax, args.steps, args.warmup)
+    t_kern = graph_time(torch, step_stream_only, args.steps, args.warmup)
+
+    # algorithmic bytes: K + V over the visible keys, plus q, r and o
+    qr_bytes = 2 * q.numel() * 2
+    o_bytes = out.numel() * 2
+    step_bytes = kv_bytes + qr_bytes + o_bytes
+    kern_bytes = kv_bytes + qr_bytes
+    flops = 8 * spec.D * spec.Hq * T
+    res = {
+        "metric": METRIC,
+        "value": round(t_step * 1e6, 3),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "B": spec.B, "Hq": spec.Hq, "Hkv": spec.Hkv,
+                   "head_dim": spec.D, "kv_len": spec.L, "total_kv_tokens": T,
+                   "kv_cache_copies": copies, "splits": splits},
+        "hbm_tb_s": round(step_bytes / t_step / 1e12, 4),
+        "hbm_frac_of_8tbs": round(step_bytes / t_step / 1e9 / HBM_PEAK_GBS, 4),
+        "tflops": round(flops / t_step / 1e12, 3),
+        "softmax_decode_us": round(t_soft * 1e6, 3),
+        "parallax_over_softmax": round(t_step / t_soft, 4),
+        "roofline": {"bound": "hbm", "kernel": "decode_mfma_bf16_d128 (streaming, split records)",
+                     "achieved": round(kern_bytes / t_kern / 1e9, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(kern_bytes / t_kern / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": None, "avg_us": round(t_kern * 1e6, 3),
+                     "bytes_per_launch": kern_bytes},
+    }
+    if not args.no_cpu_baseline:
+        if varlen or spec.B > 64:
+            # bounded sample: the first sequences, regenerated from the same streams
+            nb = 4 if spec.B > 64 else 8
+            sub = slice(0, nb)
+            toks = int(cu[nb])
+            k_h = synth.decode_kv_rows(spec, synth.TID_K, 0, toks)
+            v_h = synth.decode_kv_rows(spec, synth.TID_V, 0, toks)
+            qs, rs = np.ascontiguousarray(q_np[sub]), np.ascontiguousarray(r_np[sub])
+            t = time.perf_counter()
+            reps = 0
+            while True:
+                oracle.decode(qs, rs, k_h, v_h, seq_start=cu[:nb], seq_len=lens[:nb])
+                reps += 1
+                if time.perf_counter() - t > args.cpu_seconds:
+                    break
+            per_seq = (time.perf_counter() - t) / reps / nb
+            # scale by tokens: the oracle's cost is linear in the visible keys
+            us = per_seq * nb / toks * T * 1e6
+            sample = f"{nb} of {spec.B} sequences ({toks} of {T} keys), {reps} repeats, " \
+                     "scaled to the full step by key count"
+            threads = min(omp_threads(), nb * spec.Hq)
+        else:
+            k_h = synth.decode_kv_rows(spec, synth.TID_K, 0, T).reshape(spec.B, spec.L, spec.Hkv,
+                                                                         spec.D)
+            v_h = synth.decode_kv_rows(spec, synth.TID_V, 0, T).reshape(spec.B, spec.L, spec.Hkv,
+                                                                         spec.D)
+            us, reps, threads = cpu_baseline_decode(oracle, q_np, r_np, (k_h, v_h), spec,
+                                                    args.cpu_seconds)
+            sample = f"the full step (all {spec.Hq} heads x {T} keys), {reps} repeats"
+        res["cpu_baseline"] = {"value": round(us, 1), "unit": "us/step", "cores": threads,
+                               "kind": "oracle", "sample": sample}
+    # parity of the timed configuration on a few rows (the full check lives in the tests)
+    o_full = out.float().cpu().numpy().astype(np.float64)
+    rows = [(0, 0), (spec.B - 1, spec.Hq - 1), (spec.B // 2, 3)]
+    errs = []
+    for b, h in rows:
+        toks = int(lens[b])
+        k_h = synth.decode_kv_rows(spec, synth.TID_K, int(cu[b]), toks)[None]
+        v_h = synth.decode_kv_rows(spec, synth.TID_V, int(cu[b]), toks)[None]
+        ref = oracle.decode(np.ascontiguousarray(q_np[b:b + 1]), np.ascontiguousarray(r_np[b:b + 1]),
+                            k_h, v_h)[0, h]
+        errs.append(float(np.abs(o_full[b, h] - ref).max() / np.abs(ref).max()))
+    res["sampled_parity_max_norm_err"] = max(errs)
+    return res
+
+
+def run_prefill_workload(args, torch, plx, synth, oracle):
+    spec = synth.prefill_spec(5)
+    B, Hq, Hkv, L, D = spec.B, spec.Hq, spec.Hkv, spec.L, spec.D
+    arrs = {}
+    for name, tid, H in (("q", synth.TID_Q, Hq), ("r", synth.TID_R, Hq), ("k", synth.TID_K, Hkv),
+                         ("v", synth.TID_V, Hkv)):
+        a = synth.normal(spec.seed, tid, (B, H, L, D), spec.scale, spec.dtype)
+        arrs[name] = a
+    t = {n: torch.from_numpy(a).view(torch.bfloat16).cuda() for n, a in arrs.items()}
+    out = torch.empty_like(t["q"])
+
+    def step(i):
+        plx.prefill(t["q"], t["r"], t["k"], t["v"], out=out)
+
+    steps = max(1, min(args.steps, 20))
+    warm = max(1, min(args.warmup, 3))
+    ts = graph_time(torch, step, steps, warm)
+    flops = 8 * D * Hq * B * L * (L + 1) // 2
+    res = {
+        "metric": METRIC, "value": round(flops / ts / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": steps, "warmup": warm, "ms_per_step": round(ts * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "B": B, "Hq": Hq, "Hkv": Hkv, "L": L, "head_dim": D},
+        "roofline": {"bound": "mfma", "kernel": "prefill", "achieved": round(flops / ts / 1e12, 2),
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(flops / ts / 1e12 / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "avg_us": round(ts * 1e6, 1), "flops_per_launch": flops},
+    }
+    rows = np.array([[0, 0, 0], [B - 1, Hq - 1, L - 1], [3, 5, 1000], [7, 8, 2047]])
+    o = out.float().cpu().numpy()
+    ref = oracle.prefill(arrs["q"], arrs["r"], arrs["k"], arrs["v"], rows=rows)
+    got = o[rows[:, 0], rows[:, 1], rows[:, 2]]
+    res["sampled_parity_max_norm_err"] = float(np.abs(got - ref).max() / np.abs(ref).max())
+    if not args.no_cpu_baseline:
+        # bounded sample: rows spread over the causal range, scaled by visible keys
+        g = np.random.default_rng(0)
+        n = 512
+        sample_rows = np.stack([g.integers(0, B, n), g.integers(0, Hq, n),
+                                g.integers(0, L, n)], axis=1)
+        tt = time.perf_counter()
+        reps = 0
+        while True:
+            oracle.prefill(arrs["q"], arrs["r"], arrs["k"], arrs["v"], rows=sample_rows)
+            reps += 1
+            if time.perf_counter() - tt > args.cpu_seconds:
+                break
+        per = (time.perf_counter() - tt) / reps
+        keys_sample = float((sample_rows[:, 2] + 1).sum())
+        keys_full = B * Hq * L * (L + 1) / 2
+        sec_full = per * keys_full / keys_sample
+        res["cpu_baseline"] = {"value": round(flops / sec_full / 1e12, 6), "unit": "TFLOP/s",
+                               "cores": min(omp_threads(), n), "kind": "oracle",
+                               "sample": f"{n} random query rows, {reps} repeats, scaled to the "
+                                         f"full step by visible keys ({sec_full:.0f} s/step)"}
+    return res
+
+
+def calibrate_copy(torch):
+    """A plain copy kernel of known size, for scaling HBM byte counters."""
+    n = 64 << 20  # floats: 256 MiB read + 256 MiB written
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    torch.mul(x, 2.0, out=y)  # one elementwise kernel: reads 4n bytes, writes 4n bytes
+    torch.cuda.synchronize()
+    return 4 * n
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported by this build "
+              "(the decode and prefill paths are single-GPU kernels).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import oracle
+    import parameterized_local_linear_amd as plx
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    plx.lib()
+    if args.calibrate_copy:
+        calibrate_copy(torch)
+    if args.workload == "prefill":
+        res = run_prefill_workload(args, torch, plx, synth, oracle)
+    else:
+        res = run_decode_workload(args, torch, plx, synth, oracle)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

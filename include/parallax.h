@@ -111,6 +111,45 @@ int parallax_decode_num_splits(int B, int Hq, int Hkv, int D, int kv_len, int dt
                                int num_splits);
 
 /* ------------------------------------------------------------------------
+ * Decode in two halves: the streaming kernel that writes one record per
+ * (sequence, query head, split), and the merge of records into o.
+ * parallax_decode is exactly partial + merge (or one fused kernel when the
+ * plan has a single split). Exposed so that records can be produced where
+ * the keys live and merged elsewhere -- e.g. a long sequence whose key
+ * range is cut across devices: each device streams its range, the records
+ * are gathered, one merge produces o -- and so that each half can be timed.
+ *
+ * Record layout: records[B][Hq][num_records], each 2*D + 4 floats:
+ *   A[D] = sum_j e_j v_j,  B[D] = sum_j e_j (s_j - pi) v_j,
+ *   m    = max_j z_j * log2(e)   (z_j = qk_scale q.k_j; -inf: empty record),
+ *   l    = sum_j e_j,  S = sum_j e_j (s_j - pi),  pi,
+ * with e_j = 2^(z_j log2(e) - m) and pi the probe score of the first key of
+ * the range the call saw. Merging re-bases every record onto one pivot
+ * (exact in real arithmetic), so records from different calls combine.
+ * ---------------------------------------------------------------------- */
+
+/* Bytes of a records array for (B, Hq, D, num_records); 0 if invalid. */
+size_t parallax_decode_record_bytes(int B, int Hq, int D, int num_records);
+
+/* Streaming half of parallax_decode: same arguments and layouts, but writes
+ * parallax_decode_num_splits(...) records per (b, h) into `records`
+ * (DEVICE, at least parallax_decode_record_bytes(B, Hq, D, that count)
+ * bytes) instead of o. r == NULL selects the softmax baseline (the probe
+ * terms of the records are then zero). Returns PLX_ERR_WORKSPACE when
+ * `records` is NULL or too small. */
+int parallax_decode_partial(const void *q, const void *r, const void *k, const void *v,
+                            const int32_t *cu_seqlens_k, int B, int Hq, int Hkv, int D, int kv_len,
+                            float qk_scale, float rk_scale, int dtype, int num_splits,
+                            void *records, size_t records_bytes, void *stream);
+
+/* Merge records[B][Hq][num_records] (DEVICE) into o [B, Hq, D] (DEVICE,
+ * dtype): o = (A + B - (S / l) A) / l over the combined state, or A / l
+ * when with_probe == 0. Empty records are skipped; a row with none gets
+ * o = 0. D in {64, 128}. */
+int parallax_decode_merge(const void *records, void *o, int B, int Hq, int D, int num_records,
+                          int dtype, int with_probe, void *stream);
+
+/* ------------------------------------------------------------------------
  * Causal prefill / training forward (PyPI README, "Training (Triton)":
  * parallax_func(q, r, k, v) on (B, H, L, D) tensors, causal, returns
  * (B, H, L, D)). Query row i sees keys 0 .. i.

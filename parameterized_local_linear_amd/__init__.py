@@ -64,6 +64,13 @@ def lib() -> ctypes.CDLL:
         L.parallax_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
                                        f32, i32, vp]
         L.parallax_prefill.restype = i32
+        L.parallax_decode_record_bytes.argtypes = [i32, i32, i32, i32]
+        L.parallax_decode_record_bytes.restype = sz
+        L.parallax_decode_partial.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, f32,
+                                              i32, i32, vp, sz, vp]
+        L.parallax_decode_partial.restype = i32
+        L.parallax_decode_merge.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, vp]
+        L.parallax_decode_merge.restype = i32
         _lib = L
     return _lib
 
@@ -181,6 +188,55 @@ def softmax_decode(q, k, v, qk_scale=None, *, cu_seqlens_k=None, kv_len=None, nu
                         workspace, False)
 
 
+def decode_partial(q, r, k, v, qk_scale=None, rk_scale=1.0, *, cu_seqlens_k=None, kv_len=None,
+                   num_splits=0, records=None):
+    """Streaming half of decode: returns (records, n) with records a float32
+    [B, Hq, n, 2D + 4] tensor (A, B, m, l, S, pi per split). r=None: softmax records."""
+    L_ = lib()
+    B, Hq, D = q.shape
+    dev, dt = q.device, q.dtype
+    _check(q, "q", dt, dev)
+    if r is not None:
+        _check(r, "r", dt, dev)
+    _check(k, "k", dt, dev)
+    _check(v, "v", dt, dev)
+    if cu_seqlens_k is None:
+        kv_len, Hkv = k.shape[1], k.shape[2]
+    else:
+        _check(cu_seqlens_k, "cu_seqlens_k", torch.int32, dev)
+        Hkv = k.shape[1]
+    code = _dtype_code(q)
+    if qk_scale is None:
+        qk_scale = 1.0 / math.sqrt(D)
+    n = decode_num_splits(B, Hq, Hkv, D, int(kv_len), code, num_splits)
+    if n == 0:
+        raise ParallaxError(1, "parallax_decode_partial")
+    if records is None:
+        records = torch.empty((B, Hq, n, 2 * D + 4), dtype=torch.float32, device=dev)
+    st = L_.parallax_decode_partial(_ptr(q), _ptr(r), _ptr(k), _ptr(v), _ptr(cu_seqlens_k), B, Hq,
+                                    Hkv, D, int(kv_len), float(qk_scale), float(rk_scale), code,
+                                    int(num_splits), _ptr(records),
+                                    records.numel() * records.element_size(), _stream_handle(dev))
+    if st != 0:
+        raise ParallaxError(st, "parallax_decode_partial")
+    return records, n
+
+
+def decode_merge(records, dtype=torch.bfloat16, with_probe=True, out=None):
+    """Merge records [B, Hq, n, 2D + 4] (float32) into o [B, Hq, D]."""
+    L_ = lib()
+    B, Hq, n, F = records.shape
+    D = (F - 4) // 2
+    _check(records, "records", torch.float32, records.device)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=dtype, device=records.device)
+    st = L_.parallax_decode_merge(_ptr(records), _ptr(out), B, Hq, D, n, _dtype_code(out),
+                                  1 if with_probe else 0, _stream_handle(records.device))
+    if st != 0:
+        raise ParallaxError(st, "parallax_decode_merge")
+    return out
+
+
 def prefill(q, r, k, v, qk_scale=None, rk_scale=1.0, *, out=None, return_stats=False):
     """Causal Parallax prefill. q, r: [B, Hq, L, D]; k, v: [B, Hkv, L, D] -> o [B, Hq, L, D]
     (plus fp32 lse and sbar [B, Hq, L] with return_stats=True)."""
@@ -218,5 +274,5 @@ def prefill(q, r, k, v, qk_scale=None, rk_scale=1.0, *, out=None, return_stats=F
 parallax_decode = decode
 parallax_func = prefill
 
-__all__ = ["decode", "softmax_decode", "prefill", "parallax_decode", "parallax_func",
+__all__ = ["decode", "softmax_decode", "prefill", "decode_partial", "decode_merge", "parallax_decode", "parallax_func",
            "decode_workspace_bytes", "decode_num_splits", "lib", "ParallaxError", "LIB_PATH"]

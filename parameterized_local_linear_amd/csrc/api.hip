@@ -99,18 +99,16 @@ int parallax_decode_num_splits(int B, int Hq, int Hkv, int D, int kv_len, int dt
     return plx::plan_decode(B, Hq, Hkv, D, kv_len, dtype, num_splits).splits;
 }
 
-static int decode_common(const void *q, const void *r, const void *k, const void *v, void *o,
-                         const int32_t *cu, int B, int Hq, int Hkv, int D, int kv_len,
-                         float qk_scale, float rk_scale, int dtype, int num_splits, void *ws,
-                         size_t ws_bytes, void *stream, bool parallax) {
+static int fill_decode_args(plx::DecodeArgs &a, const void *q, const void *r, const void *k,
+                            const void *v, void *o, const int32_t *cu, int B, int Hq, int Hkv, int D,
+                            int kv_len, float qk_scale, float rk_scale, int dtype, int num_splits,
+                            bool parallax, DecodePlan &p) {
     int st = check_decode_sizes(B, Hq, Hkv, D, kv_len, dtype);
     if (st != PLX_OK) return st;
     if (!q || !k || !v || !o || (parallax && !r)) return PLX_ERR_INVALID_ARG;
     if (num_splits < 0) return PLX_ERR_INVALID_ARG;
     if (!isfinite(qk_scale) || !isfinite(rk_scale)) return PLX_ERR_INVALID_ARG;
-    const DecodePlan p = plx::plan_decode(B, Hq, Hkv, D, kv_len, dtype, num_splits);
-    if (p.ws_bytes > 0 && (!ws || ws_bytes < p.ws_bytes)) return PLX_ERR_WORKSPACE;
-    plx::DecodeArgs a;
+    p = plx::plan_decode(B, Hq, Hkv, D, kv_len, dtype, num_splits);
     a.q = q;
     a.r = r;
     a.k = k;
@@ -126,8 +124,25 @@ static int decode_common(const void *q, const void *r, const void *k, const void
     a.rk_scale = rk_scale;
     a.splits = p.splits;
     a.chunk = p.chunk;
+    a.ws = nullptr;
+    a.fused = p.splits == 1;
+    return PLX_OK;
+}
+
+static int decode_common(const void *q, const void *r, const void *k, const void *v, void *o,
+                         const int32_t *cu, int B, int Hq, int Hkv, int D, int kv_len,
+                         float qk_scale, float rk_scale, int dtype, int num_splits, void *ws,
+                         size_t ws_bytes, void *stream, bool parallax) {
+    plx::DecodeArgs a;
+    DecodePlan p;
+    int st = fill_decode_args(a, q, r, k, v, o, cu, B, Hq, Hkv, D, kv_len, qk_scale, rk_scale, dtype,
+                              num_splits, parallax, p);
+    if (st != PLX_OK) return st;
+    if (p.ws_bytes > 0 && (!ws || ws_bytes < p.ws_bytes)) return PLX_ERR_WORKSPACE;
     a.ws = reinterpret_cast<float *>(ws);
-    hipError_t err = plx::launch_decode(a, p.path, dtype, parallax, reinterpret_cast<hipStream_t>(stream));
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t err = plx::launch_decode_split(a, p.path, dtype, parallax, s);
+    if (err == hipSuccess && !a.fused) err = plx::launch_decode_merge(a, dtype, parallax, s);
     return err == hipSuccess ? PLX_OK : PLX_ERR_HIP;
 }
 
@@ -144,6 +159,49 @@ int softmax_decode(const void *q, const void *k, const void *v, void *o, const i
                    void *workspace, size_t workspace_bytes, void *stream) {
     return decode_common(q, nullptr, k, v, o, cu_seqlens_k, B, Hq, Hkv, D, kv_len, qk_scale, 1.0f,
                          dtype, num_splits, workspace, workspace_bytes, stream, false);
+}
+
+size_t parallax_decode_record_bytes(int B, int Hq, int D, int num_records) {
+    if (B < 1 || Hq < 1 || num_records < 1 || (D != 64 && D != 128)) return 0;
+    return (size_t)B * Hq * num_records * plx::partial_floats(D) * sizeof(float);
+}
+
+int parallax_decode_partial(const void *q, const void *r, const void *k, const void *v,
+                            const int32_t *cu_seqlens_k, int B, int Hq, int Hkv, int D, int kv_len,
+                            float qk_scale, float rk_scale, int dtype, int num_splits,
+                            void *records, size_t records_bytes, void *stream) {
+    plx::DecodeArgs a;
+    DecodePlan p;
+    const bool parallax = r != nullptr;
+    // o is not written in this mode; any non-null value passes the checks
+    int st = fill_decode_args(a, q, r, k, v, records, cu_seqlens_k, B, Hq, Hkv, D, kv_len, qk_scale,
+                              rk_scale, dtype, num_splits, parallax, p);
+    if (st != PLX_OK) return st;
+    if (!records || records_bytes < parallax_decode_record_bytes(B, Hq, D, p.splits))
+        return PLX_ERR_WORKSPACE;
+    a.o = nullptr;
+    a.ws = reinterpret_cast<float *>(records);
+    a.fused = false;
+    hipError_t err = plx::launch_decode_split(a, p.path, dtype, parallax, reinterpret_cast<hipStream_t>(stream));
+    return err == hipSuccess ? PLX_OK : PLX_ERR_HIP;
+}
+
+int parallax_decode_merge(const void *records, void *o, int B, int Hq, int D, int num_records, int dtype,
+                          int with_probe, void *stream) {
+    if (B < 1 || Hq < 1 || num_records < 1 || !records || !o) return PLX_ERR_INVALID_ARG;
+    if (B > 65535 || Hq > 65535) return PLX_ERR_UNSUPPORTED;
+    if (D != 64 && D != 128) return PLX_ERR_UNSUPPORTED;
+    if (dtype != PLX_F32 && dtype != PLX_BF16) return PLX_ERR_UNSUPPORTED;
+    plx::DecodeArgs a = {};
+    a.o = o;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hq;
+    a.D = D;
+    a.splits = num_records;
+    a.ws = const_cast<float *>(reinterpret_cast<const float *>(records));
+    hipError_t err = plx::launch_decode_merge(a, dtype, with_probe != 0, reinterpret_cast<hipStream_t>(stream));
+    return err == hipSuccess ? PLX_OK : PLX_ERR_HIP;
 }
 
 int parallax_prefill(const void *q, const void *r, const void *k, const void *v, void *o, float *lse,

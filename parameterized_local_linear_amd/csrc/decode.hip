@@ -31,7 +31,7 @@
 //       with 128-bit loads, double-buffered in registers.
 //   decode_generic<T, D, PLX>  fp32 or bf16, head_dim 64/128, any group size.
 //       One wave per (query head, split, sequence), fp32 VALU.
-//   decode_reduce<TO, PLX>  merges split states into o.
+//   decode_reduce<TO, D, PLX>  merges split records into o.
 #include "plx_internal.h"
 
 namespace plx {
@@ -140,12 +140,17 @@ __global__ __launch_bounds__(64) void decode_mfma_bf16_d128(DecodeArgs a) {
     const uint16_t *vh = reinterpret_cast<const uint16_t *>(a.v);
 
     if (sr.len <= 0 || start >= sr.len) {
-        // Nothing to stream. With one split the output row is zero (an empty
-        // sequence); with several, the reduce kernel skips this split.
-        if (a.splits == 1 && live && kind == 0) {
-            uint16_t *o = reinterpret_cast<uint16_t *>(a.o) + ((int64_t)b * a.Hq + hq) * D + 32 * g;
-            uint4 z = {0u, 0u, 0u, 0u};
-            for (int c = 0; c < 4; ++c) reinterpret_cast<uint4 *>(o)[c] = z;
+        // Nothing to stream: a fused call writes the zero output of an empty
+        // sequence, otherwise the record is marked empty for the merge.
+        if (live && kind == 0) {
+            if (a.fused) {
+                uint16_t *o = reinterpret_cast<uint16_t *>(a.o) + ((int64_t)b * a.Hq + hq) * D + 32 * g;
+                uint4 z = {0u, 0u, 0u, 0u};
+                for (int c = 0; c < 4; ++c) reinterpret_cast<uint4 *>(o)[c] = z;
+            } else if (g == 0) {
+                float *rec = a.ws + (((int64_t)b * a.Hq + hq) * a.splits + split) * partial_floats(D);
+                reinterpret_cast<float4 *>(rec + 2 * D)[0] = float4{-INFINITY, 0.f, 0.f, 0.f};
+            }
         }
         return;
     }
@@ -287,7 +292,7 @@ __global__ __launch_bounds__(64) void decode_mfma_bf16_d128(DecodeArgs a) {
 
     lsum = xor_sum_rowgroups(lsum);
 
-    if (a.splits > 1) {
+    if (!a.fused) {
         if (!live) return;
         float *rec = a.ws + (((int64_t)b * a.Hq + hq) * a.splits + split) * partial_floats(D);
         float *dst = rec + kind * D + 32 * g;
@@ -301,8 +306,13 @@ __global__ __launch_bounds__(64) void decode_mfma_bf16_d128(DecodeArgs a) {
             if (kind == 0) {
                 rec[2 * D + 0] = m_run;
                 rec[2 * D + 1] = lsum;
+                if (!PLX) {
+                    rec[2 * D + 2] = 0.f;
+                    rec[2 * D + 3] = 0.f;
+                }
             } else {
                 rec[2 * D + 2] = lsum;
+                rec[2 * D + 3] = piv;
             }
         }
         return;
@@ -410,9 +420,14 @@ __global__ __launch_bounds__(64) void decode_generic(DecodeArgs a) {
     const int start = split * a.chunk;
     T *o = reinterpret_cast<T *>(a.o) + ((int64_t)b * a.Hq + hq) * D;
     if (sr.len <= 0 || start >= sr.len) {
-        if (a.splits == 1 && kgrp == 0) {
-            float zero[EPL] = {};
-            Elem<T>::store(o + c * EPL, zero);
+        if (a.fused) {
+            if (kgrp == 0) {
+                float zero[EPL] = {};
+                Elem<T>::store(o + c * EPL, zero);
+            }
+        } else if (lane == 0) {
+            float *rec = a.ws + (((int64_t)b * a.Hq + hq) * a.splits + split) * partial_floats(D);
+            reinterpret_cast<float4 *>(rec + 2 * D)[0] = float4{-INFINITY, 0.f, 0.f, 0.f};
         }
         return;
     }
@@ -491,17 +506,14 @@ __global__ __launch_bounds__(64) void decode_generic(DecodeArgs a) {
         merge_state(st, y);
     }
     if (kgrp != 0) return;
-    if (a.splits > 1) {
+    if (!a.fused) {
         float *rec = a.ws + (((int64_t)b * a.Hq + hq) * a.splits + split) * partial_floats(D);
         for (int e = 0; e < EPL; ++e) {
             rec[c * EPL + e] = st.A[e];
             rec[D + c * EPL + e] = st.B[e];
         }
-        if (c == 0) {
-            rec[2 * D + 0] = st.m;
-            rec[2 * D + 1] = st.l;
-            rec[2 * D + 2] = st.S;
-        }
+        if (c == 0)
+            reinterpret_cast<float4 *>(rec + 2 * D)[0] = float4{st.m, st.l, st.S, piv};
         return;
     }
     const float inv_l = 1.0f / st.l;
@@ -512,8 +524,13 @@ __global__ __launch_bounds__(64) void decode_generic(DecodeArgs a) {
 }
 
 // -------------------------------------------------------------------------
-// Split merge: one workgroup of 256 threads per (query head, sequence).
-// Wave w folds splits w, w+4, ... ; the four wave states meet in LDS.
+// Record merge: one workgroup of 256 threads per (query head, sequence).
+// Wave w folds records w, w+4, ...; the four wave states meet in LDS. Empty
+// records (m = -inf) are skipped; none at all gives o = 0. Records may carry
+// different pivots: each is re-based onto the pivot of record 0 with
+//   S' = S + (pi_i - pi_0) l,   B' = B + (pi_i - pi_0) A
+// (exact algebra; zero change when the pivots agree, as they do when all
+// records come from one call).
 // -------------------------------------------------------------------------
 template <typename TO, int D, bool PLX>
 __global__ __launch_bounds__(256) void decode_reduce(DecodeArgs a) {
@@ -522,10 +539,9 @@ __global__ __launch_bounds__(256) void decode_reduce(DecodeArgs a) {
     const int w = threadIdx.x >> 6;
     const int hq = blockIdx.x;
     const int b = blockIdx.y;
-    const SeqRange sr = seq_range(a, b);
-    int ns = sr.len <= 0 ? 0 : (sr.len + a.chunk - 1) / a.chunk;
-    ns = min(ns, a.splits);
-    const float *base = a.ws + ((int64_t)b * a.Hq + hq) * a.splits * partial_floats(D);
+    const int ns = a.splits;
+    const float *base = a.ws + ((int64_t)b * a.Hq + hq) * ns * partial_floats(D);
+    const float piv0 = PLX ? base[2 * D + 3] : 0.f;
 
     float m = -INFINITY, l = 0.f, S = 0.f, A[DPL], Bv[DPL];
     for (int d = 0; d < DPL; ++d) {
@@ -534,12 +550,16 @@ __global__ __launch_bounds__(256) void decode_reduce(DecodeArgs a) {
     }
     for (int i = w; i < ns; i += 4) {
         const float *rec = base + (int64_t)i * partial_floats(D);
-        const float mi = rec[2 * D], li = rec[2 * D + 1];
-        const float Si = PLX ? rec[2 * D + 2] : 0.f;
+        const float4 tail = reinterpret_cast<const float4 *>(rec + 2 * D)[0];
+        const float mi = tail.x;
+        if (mi == -INFINITY) continue;
+        const float li = tail.y;
+        const float dp = PLX ? tail.w - piv0 : 0.f;
+        const float Si = PLX ? tail.z + dp * li : 0.f;
         float Ai[DPL], Bi[DPL];
         for (int d = 0; d < DPL; ++d) {
             Ai[d] = rec[lane * DPL + d];
-            Bi[d] = PLX ? rec[D + lane * DPL + d] : 0.f;
+            Bi[d] = PLX ? rec[D + lane * DPL + d] + dp * Ai[d] : 0.f;
         }
         const float M = fmaxf(m, mi);
         const float ax = __builtin_amdgcn_exp2f(m - M);
@@ -573,7 +593,7 @@ __global__ __launch_bounds__(256) void decode_reduce(DecodeArgs a) {
     }
     for (int x = 0; x < 4; ++x) {
         const float mi = sm[x][2 * D];
-        if (mi == -INFINITY) continue;  // this wave folded no split
+        if (mi == -INFINITY) continue;  // this wave folded no record
         const float M = fmaxf(m, mi);
         const float ax = __builtin_amdgcn_exp2f(m - M);
         const float ay = __builtin_amdgcn_exp2f(mi - M);
@@ -588,7 +608,7 @@ __global__ __launch_bounds__(256) void decode_reduce(DecodeArgs a) {
     TO *o = reinterpret_cast<TO *>(a.o) + ((int64_t)b * a.Hq + hq) * D + lane * DPL;
     for (int d = 0; d < DPL; ++d) {
         float val = 0.f;
-        if (ns > 0) {
+        if (m != -INFINITY) {
             const float inv_l = 1.0f / l;
             val = PLX ? (A[d] * (1.0f - S * inv_l) + Bv[d]) * inv_l : A[d] * inv_l;
         }
@@ -635,19 +655,18 @@ hipError_t launch_reduce(const DecodeArgs &a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs &a, DecodePath path, int dtype, bool parallax,
-                         hipStream_t stream) {
-    hipError_t err;
-    const bool bf16 = dtype == 1;
+hipError_t launch_decode_split(const DecodeArgs &a, DecodePath path, int dtype, bool parallax,
+                               hipStream_t stream) {
     if (path == DecodePath::Mfma)
-        err = parallax ? launch_mfma<true>(a, stream) : launch_mfma<false>(a, stream);
-    else if (bf16)
-        err = parallax ? launch_generic<uint16_t, true>(a, stream)
-                       : launch_generic<uint16_t, false>(a, stream);
-    else
-        err = parallax ? launch_generic<float, true>(a, stream) : launch_generic<float, false>(a, stream);
-    if (err != hipSuccess || a.splits == 1) return err;
-    if (bf16)
+        return parallax ? launch_mfma<true>(a, stream) : launch_mfma<false>(a, stream);
+    if (dtype == 1)
+        return parallax ? launch_generic<uint16_t, true>(a, stream)
+                        : launch_generic<uint16_t, false>(a, stream);
+    return parallax ? launch_generic<float, true>(a, stream) : launch_generic<float, false>(a, stream);
+}
+
+hipError_t launch_decode_merge(const DecodeArgs &a, int dtype, bool parallax, hipStream_t stream) {
+    if (dtype == 1)
         return parallax ? launch_reduce<uint16_t, true>(a, stream) : launch_reduce<uint16_t, false>(a, stream);
     return parallax ? launch_reduce<float, true>(a, stream) : launch_reduce<float, false>(a, stream);
 }

@@ -13,13 +13,15 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// One decode split's streaming state, stored in the workspace as
-// A[D], B[D], m, l, S, pad (2D + 4 floats) for every (b, hq, split).
-//   m : running maximum of the logits, in log2 units (logit * log2 e)
-//   l : sum_j e_j                         e_j = 2^(z_j log2e - m)
-//   S : sum_j e_j (s_j - pi)              pi = the sequence's pivot score
-//   A : sum_j e_j v_j
-//   B : sum_j e_j (s_j - pi) v_j
+// One decode split's streaming state ("record"), stored in the workspace as
+// A[D], B[D], m, l, S, pi (2D + 4 floats) for every (b, hq, split).
+//   m  : maximum of the logits over the split's keys, in log2 units
+//        (z_j * log2 e); -inf marks an empty record
+//   l  : sum_j e_j                         e_j = 2^(z_j log2e - m)
+//   S  : sum_j e_j (s_j - pi)
+//   A  : sum_j e_j v_j
+//   B  : sum_j e_j (s_j - pi) v_j
+//   pi : the pivot the record's probe scores are taken against
 __host__ __device__ constexpr int partial_floats(int D) { return 2 * D + 4; }
 
 struct DecodeArgs {
@@ -31,7 +33,8 @@ struct DecodeArgs {
     float rk_scale;
     int splits;         // >= 1
     int chunk;          // keys per split, multiple of 32
-    float *ws;          // partial records, used when splits > 1
+    float *ws;          // records [B][Hq][splits], written unless fused
+    bool fused;         // one split and no records: write o directly
 };
 
 enum class DecodePath { Mfma, Generic };
@@ -46,8 +49,11 @@ struct DecodePlan {
 
 DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int kv_len, int dtype, int num_splits);
 
-hipError_t launch_decode(const DecodeArgs &a, DecodePath path, int dtype, bool parallax,
-                         hipStream_t stream);
+// Streaming kernel (records, or o when a.fused).
+hipError_t launch_decode_split(const DecodeArgs &a, DecodePath path, int dtype, bool parallax,
+                               hipStream_t stream);
+// Merge of a.splits records per (b, hq) into o (a.q/k/v/r/cu unused).
+hipError_t launch_decode_merge(const DecodeArgs &a, int dtype, bool parallax, hipStream_t stream);
 
 struct PrefillArgs {
     const void *q, *r, *k, *v;

@@ -214,3 +214,39 @@ def test_large_batch_decode_sampled_sequences():
         assert_parity(o[b:b + 1], ref, spec.dtype, f"large batch b={b}")
         ref0 = oracle_dense(np.ascontiguousarray(q[b:b + 1]), None, kb, vb)
         assert_parity(o0[b:b + 1], ref0, spec.dtype, f"large batch softmax b={b}")
+
+
+# ------------------------------------------------------------------ partial + merge
+@pytest.mark.parametrize("G", [1, 2, 3])
+def test_partial_then_merge_equals_decode(G):
+    B, Hkv, D, L = 2, 2, 128, 1000
+    Hq = G * Hkv
+    q, r, k, v = decode_inputs(B, Hq, Hkv, D, [L] * B, synth.BF16, 1.0, 90 + G)
+    t = [to_gpu(x, synth.BF16) for x in (q, r, k, v)]
+    recs, n = plx.decode_partial(*t, num_splits=6)
+    assert recs.shape == (B, Hq, n, 2 * D + 4) and n == 6
+    o = plx.decode_merge(recs)
+    assert torch.equal(o, plx.decode(*t, num_splits=6))
+    assert_parity(from_gpu(o), oracle_dense(q, r, k, v), synth.BF16, "partial+merge")
+    recs0, _ = plx.decode_partial(t[0], None, t[2], t[3], num_splits=6)
+    o0 = plx.decode_merge(recs0, with_probe=False)
+    assert torch.equal(o0, plx.softmax_decode(t[0], t[2], t[3], num_splits=6))
+
+
+def test_records_from_separate_key_ranges_merge_to_the_full_sequence():
+    """Key range cut in two and streamed by two calls (each with its own pivot):
+    gathering the records and merging them gives the whole-sequence output."""
+    B, Hq, Hkv, D, L, cut = 2, 4, 2, 128, 1500, 613
+    q, r, k, v = decode_inputs(B, Hq, Hkv, D, [L] * B, synth.BF16, 1.0, 95)
+    ks = (synth.bf16_bits_to_f32(k) + 3.0 * synth.key_shift(95, D)).astype(np.float32)
+    k = np.array([synth.bf16_from_double(x) for x in ks.ravel()], dtype=np.uint16).reshape(k.shape)
+    tq, tr, tk, tv = (to_gpu(x, synth.BF16) for x in (q, r, k, v))
+    ra, na = plx.decode_partial(tq, tr, tk[:, :cut].contiguous(), tv[:, :cut].contiguous(),
+                                num_splits=3)
+    rb, nb = plx.decode_partial(tq, tr, tk[:, cut:].contiguous(), tv[:, cut:].contiguous(),
+                                num_splits=2)
+    recs = torch.cat([ra, rb], dim=2).contiguous()
+    pivots = recs[..., -1]
+    assert not torch.equal(pivots[..., 0], pivots[..., na])   # the two calls' pivots differ
+    o = from_gpu(plx.decode_merge(recs))
+    assert_parity(o, oracle_dense(q, r, k, v), synth.BF16, "sharded merge")
