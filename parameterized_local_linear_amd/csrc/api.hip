@@ -27,32 +27,43 @@ int device_cu_count() {
 }  // namespace
 
 // Decode plan. The MFMA path (bf16, head_dim 128, group size 1/2/4/8) runs
-// one wave per (KV head, split, sequence); the generic path one wave per
-// (query head, split, sequence). Without a forced count, the sequence is cut
-// into enough splits to give about 8 waves per compute unit, with at least
-// 128 keys per split; one split fuses the final normalisation into the
-// streaming kernel and needs no workspace.
+// one four-wave workgroup per (KV head, split, sequence) over a multiple of
+// 128 keys; the generic path one wave per (query head, split, sequence) over
+// a multiple of 32 keys. Without a forced count, the sequence is cut into
+// enough splits for about kTargetWavesPerCU resident waves per compute unit,
+// with at least kMinKeysPerWave keys per wave; one split fuses the final
+// normalisation into the streaming kernel and needs no workspace.
+constexpr int kTargetWavesPerCU = 8;
+constexpr int kMinKeysPerWave = 128;
 DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int kv_len, int dtype, int num_splits) {
     DecodePlan p;
     const int G = Hq / Hkv;
     const bool mfma = dtype == PLX_BF16 && D == 128 && (G == 1 || G == 2 || G == 4 || G == 8);
     p.path = mfma ? DecodePath::Mfma : DecodePath::Generic;
+    const int waves = mfma ? 4 : 1;      // waves per workgroup
+    const int quantum = 32 * waves;      // keys per split are a multiple of this
     const long units = (long)B * (mfma ? Hkv : Hq);
-    const int max_splits = (kv_len + 31) / 32;
+    const int max_splits = (kv_len + quantum - 1) / quantum;
     int splits = num_splits;
     if (splits <= 0) {
-        const long target = 8L * device_cu_count();
+        const long target = (long)kTargetWavesPerCU * device_cu_count() / waves;
         long s = (target + units - 1) / units;
-        const long by_len = (kv_len + 127) / 128;
+        const long by_len = (kv_len + (long)kMinKeysPerWave * waves - 1) / ((long)kMinKeysPerWave * waves);
         if (s > by_len) s = by_len;
         if (s < 1) s = 1;
         splits = (int)s;
     }
     if (splits > max_splits) splits = max_splits;
+    // A split's keys (plus the 64 keys its streaming loop reads ahead) must
+    // span less than 2^31 bytes: the kernels address them with 32-bit offsets.
+    const long long tok_bytes = (long long)Hkv * D * (dtype == PLX_BF16 ? 2 : 4);
+    const long long max_keys = (0x7fffffffLL - 1024) / tok_bytes - 96;
+    const long long min_splits = (kv_len + max_keys - 1) / max_keys;
+    if (splits < min_splits) splits = (int)min_splits;
     if (splits > 65535) splits = 65535;  // grid.y limit
     if (splits < 1) splits = 1;
     int chunk = (kv_len + splits - 1) / splits;
-    chunk = (chunk + 31) / 32 * 32;
+    chunk = (chunk + quantum - 1) / quantum * quantum;
     splits = (kv_len + chunk - 1) / chunk;
     p.splits = splits;
     p.chunk = chunk;

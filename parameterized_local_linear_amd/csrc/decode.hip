@@ -19,8 +19,8 @@
 //
 // Kernels:
 //   decode_mfma_bf16_d128<G, PLX>  bf16, head_dim 128, G query heads per KV
-//       head (1, 2, 4, 8). One wave per (KV head, split, sequence). Both
-//       contractions on v_mfma_f32_16x16x32_bf16, no LDS at all:
+//       head (1, 2, 4, 8). One workgroup of four waves per (KV head, split,
+//       sequence). Both contractions on v_mfma_f32_16x16x32_bf16:
 //         scores   S^T[key, vec] = K_tile . [q_0, r_0, q_1, r_1, ...]^T
 //         readout  O^T[dim, row] = V_tile^T . [p_0, p_0 s'_0, p_1, ...]^T
 //       The key order inside each 16-key block is chosen so that the score
@@ -28,7 +28,8 @@
 //       readout MFMA wants for its B operand (see the lane map below), and
 //       V's natural [key][dim] layout becomes the readout's A operand by an
 //       8x8 16-bit transpose inside each lane's registers. K and V stream
-//       with 128-bit loads, double-buffered in registers.
+//       with 128-bit non-temporal buffer loads straight into registers; the
+//       four waves' states meet in LDS only once, at the end of the split.
 //   decode_generic<T, D, PLX>  fp32 or bf16, head_dim 64/128, any group size.
 //       One wave per (query head, split, sequence), fp32 VALU.
 //   decode_reduce<TO, D, PLX>  merges split records into o.
@@ -54,13 +55,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
 
-// row_shr:1 inside each 16-lane row: lane i receives lane i-1 (lane 0 of a row keeps 0).
-__device__ __forceinline__ float dpp_row_shr1(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xf, 0xf, false));
-}
-// row_shl:1 inside each 16-lane row: lane i receives lane i+1.
-__device__ __forceinline__ float dpp_row_shl1(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x101, 0xf, 0xf, false));
+// quad_perm [0,0,2,2]: every lane receives the even lane of its pair.
+__device__ __forceinline__ float dpp_pair_even(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xA0, 0xf, 0xf, false));
 }
 
 __device__ __forceinline__ float xor_max_rowgroups(float x) {  // over lanes n, n+16, n+32, n+48
@@ -76,6 +73,29 @@ __device__ __forceinline__ float xor_sum_rowgroups(float x) {
 
 __device__ __forceinline__ bf16x8 load16(const uint16_t *p) {
     return *reinterpret_cast<const bf16x8 *>(p);
+}
+
+// Waves per workgroup of the MFMA decode kernel; a split's keys are a
+// multiple of 32 * kDecodeWaves.
+constexpr int kDecodeWaves = 4;
+// How far (log2 units) a tile's max may exceed the running reference max
+// before the accumulators are rescaled.
+constexpr float kRescaleSlack = 8.0f;
+
+// Word 3 of a raw buffer resource for gfx9-family (CDNA) untyped loads.
+constexpr int kBufferFlags = 0x00020000;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte load at byte `voffset` of a buffer; past the buffer's range it
+// returns zeros. The KV stream is read once, so it is fetched non-temporal.
+// The loads are marked volatile (bit 31 of the policy operand, a compiler
+// flag) so that they are issued where they are written: otherwise the
+// compiler sinks a prefetch down to its first use and the pipelining is lost.
+constexpr int kStreamPolicy = 2 | (int)(1u << 31);  // nt, volatile
+__device__ __forceinline__ bf16x8 buffer_load16(__amdgpu_buffer_rsrc_t rs, int voffset) {
+    u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rs, voffset, 0, kStreamPolicy);
+    return __builtin_bit_cast(bf16x8, w);
 }
 
 struct SeqRange {
@@ -99,7 +119,12 @@ __device__ __forceinline__ SeqRange seq_range(const DecodeArgs &a, int b) {
 // -------------------------------------------------------------------------
 // MFMA decode, bf16, head_dim 128.
 //
-// Lane map (lane = 16 * g + n, g = 0..3, n = 0..15):
+// Workgroup = kDecodeWaves waves on one (KV head, split, sequence); wave w
+// streams tiles w, w + kDecodeWaves, ... of the split's 32-key tiles, so the
+// workgroup reads neighbouring tiles together, and the wave states merge in
+// LDS into one record (or, with a single split, straight into o).
+//
+// Lane map inside a wave (lane = 16 * g + n, g = 0..3, n = 0..15):
 //   n : column of both MFMAs -- vector / P-row n. With NR = 2 rows per
 //       head (Parallax): n = 2h is head h's softmax row (q_h, then p_h),
 //       n = 2h + 1 its probe row (r_h, then p_h (s_h - pi)). With NR = 1
@@ -115,12 +140,15 @@ __device__ __forceinline__ SeqRange seq_range(const DecodeArgs &a, int b) {
 // dim 32g + 8i + e: lane (g, n) accumulates P-row n over dims 32g .. 32g+31.
 // -------------------------------------------------------------------------
 template <int G, bool PLX>
-__global__ __launch_bounds__(64) void decode_mfma_bf16_d128(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kDecodeWaves)
+void decode_mfma_bf16_d128(DecodeArgs a) {
     constexpr int D = 128;
     constexpr int NR = PLX ? 2 : 1;
     constexpr int NV = NR * G;
+    constexpr int W = kDecodeWaves;
     static_assert(NV <= 16, "at most 16 live columns");
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
     const int n = lane & 15;
     const int g = lane >> 4;
     const int hkv = blockIdx.x;
@@ -133,6 +161,7 @@ __global__ __launch_bounds__(64) void decode_mfma_bf16_d128(DecodeArgs a) {
     const int h = live ? n / NR : 0;  // head within the group
     const int kind = live ? n % NR : 0;
     const int hq = hkv * G + h;
+    const int64_t row0 = (int64_t)b * a.Hq + (int64_t)hkv * G;  // first query row of the group
 
     const uint16_t *qh = reinterpret_cast<const uint16_t *>(a.q);
     const uint16_t *rh = reinterpret_cast<const uint16_t *>(a.r);
@@ -141,20 +170,58 @@ __global__ __launch_bounds__(64) void decode_mfma_bf16_d128(DecodeArgs a) {
 
     if (sr.len <= 0 || start >= sr.len) {
         // Nothing to stream: a fused call writes the zero output of an empty
-        // sequence, otherwise the record is marked empty for the merge.
-        if (live && kind == 0) {
-            if (a.fused) {
-                uint16_t *o = reinterpret_cast<uint16_t *>(a.o) + ((int64_t)b * a.Hq + hq) * D + 32 * g;
-                uint4 z = {0u, 0u, 0u, 0u};
-                for (int c = 0; c < 4; ++c) reinterpret_cast<uint4 *>(o)[c] = z;
-            } else if (g == 0) {
-                float *rec = a.ws + (((int64_t)b * a.Hq + hq) * a.splits + split) * partial_floats(D);
-                reinterpret_cast<float4 *>(rec + 2 * D)[0] = float4{-INFINITY, 0.f, 0.f, 0.f};
-            }
+        // sequence, otherwise the records are marked empty for the merge.
+        if (a.fused) {
+            uint16_t *o = reinterpret_cast<uint16_t *>(a.o) + row0 * D;
+            for (int i = threadIdx.x; i < G * D; i += 64 * W) o[i] = 0;
+        } else if (threadIdx.x < G) {
+            float *rec = a.ws + ((row0 + threadIdx.x) * a.splits + split) * partial_floats(D);
+            reinterpret_cast<float4 *>(rec + 2 * D)[0] = float4{-INFINITY, 0.f, 0.f, 0.f};
         }
         return;
     }
     const int end = min(start + a.chunk, sr.len);
+
+    // K/V of this split through buffer resources whose range ends at the
+    // split's last key: tail lanes past `end` read zeros (their logits are
+    // masked below), all addressing is 32-bit offsets from a scalar base.
+    const int64_t tok_stride = (int64_t)a.Hkv * D;  // elements between consecutive tokens
+    const int ts_bytes = (int)(tok_stride * 2);
+    const int64_t split0 = (sr.tok0 + start) * tok_stride + (int64_t)hkv * D;
+    const uint32_t span = (uint32_t)(((int64_t)(end - start - 1) * tok_stride + D) * 2);
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(kh + split0), 0, span, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t vrs =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(vh + split0), 0, span, kBufferFlags);
+    // Key permutation inside a 16-key block for the score MFMA's A operand.
+    const int kperm = (n >> 2) + 4 * (n & 3);
+    const int koff0 = kperm * ts_bytes + 16 * g;         // block 0, k-step u at +64u bytes
+    const int koff1 = (16 + kperm) * ts_bytes + 16 * g;  // block 1
+    const int voff = g * ts_bytes + 16 * n;              // key g + 4t at + 4t keys
+
+    // The whole offset goes in the VGPR operand: the range check of a raw
+    // buffer access covers the VGPR and immediate offsets, not soffset.
+    auto load_tile = [&](int t0, bf16x8 *kt, bf16x8 *vt) {
+        const int tb = (t0 - start) * ts_bytes;  // wave-uniform
+        const int k0o = tb + koff0, k1o = tb + koff1, vo = tb + voff;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            kt[u] = buffer_load16(krs, k0o + 64 * u);
+            kt[4 + u] = buffer_load16(krs, k1o + 64 * u);
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) vt[t] = buffer_load16(vrs, vo + 4 * t * ts_bytes);
+    };
+
+    // Two tile buffers per wave: while one tile is consumed the next is in
+    // flight. Loads are never predicated: a tile past `end` lies outside the
+    // buffer range and reads zeros without touching memory, so every step
+    // issues the same loads and waits for exactly the tile it consumes.
+    constexpr int kStride = 32 * W;  // keys between a wave's consecutive tiles
+    bf16x8 kA[8], vA[8], kB[8], vB[8];
+    int t0 = start + 32 * wave;
+    load_tile(t0, kA, vA);  // first tiles in flight before anything else is read
+    load_tile(t0 + kStride, kB, vB);
 
     // B operand of the score MFMA: vector n, dims 8(g + 4u) .. +8.
     bf16x8 qr[4];
@@ -169,176 +236,193 @@ __global__ __launch_bounds__(64) void decode_mfma_bf16_d128(DecodeArgs a) {
         }
     }
 
-    const int64_t tok_stride = (int64_t)a.Hkv * D;  // elements between consecutive tokens
-    const uint16_t *kseq = kh + sr.tok0 * tok_stride + (int64_t)hkv * D;
-    const uint16_t *vseq = vh + sr.tok0 * tok_stride + (int64_t)hkv * D;
-
     // Pivot pi = rk_scale * r_h . k_0 on the probe lanes (same for every split).
     float piv = 0.0f;
     if (PLX) {
+        const uint16_t *kfirst = kh + sr.tok0 * tok_stride + (int64_t)hkv * D;
         float part = 0.0f;
         for (int u = 0; u < 4; ++u) {
-            bf16x8 k0 = load16(kseq + 8 * (g + 4 * u));
+            bf16x8 k0 = load16(kfirst + 8 * (g + 4 * u));
             for (int e = 0; e < 8; ++e) part += (float)qr[u][e] * (float)k0[e];
         }
         part = xor_sum_rowgroups(part);
         piv = part * a.rk_scale;
     }
 
-    // Key permutation inside a 16-key block for the score MFMA's A operand.
-    const int kperm = (n >> 2) + 4 * (n & 3);
-
-    float m_run = -INFINITY;  // running max of the column's head (log2 units)
-    float lsum = 0.0f;        // per-lane partial: sum p (n even) or sum p s' (n odd)
+    // Running reference max of the column's head, in log2 units. It is only
+    // raised when a tile's max exceeds it by more than kRescaleSlack (or on
+    // the first tile), so the accumulators are rarely rescaled; terms are
+    // then at most 2^kRescaleSlack, far from fp32 or bf16 overflow.
+    float m_run = -INFINITY;
+    float lsum = 0.0f;  // per-lane partial: sum p (n even) or sum p s' (n odd)
     floatx4 acc[8];
     for (int e = 0; e < 8; ++e) acc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // per-lane factor turning p into the column's P-row: 1 on softmax rows,
+    // (rk_scale * raw - pi) on probe rows -- one FMA, no select
+    const float fa = (PLX && kind) ? a.rk_scale : 0.f;
+    const float fc = (PLX && kind) ? -piv : 1.f;
 
-    bf16x8 kA[8], vA[8], kB[8], vB[8];
-
-    auto load_tile = [&](int t0, bf16x8 *kt, bf16x8 *vt) {
-        const int last = end - 1;
-        for (int kb = 0; kb < 2; ++kb) {
-            int key = min(t0 + 16 * kb + kperm, last);
-            const uint16_t *p = kseq + (int64_t)key * tok_stride + 8 * g;
-            for (int u = 0; u < 4; ++u) kt[4 * kb + u] = load16(p + 32 * u);
-        }
-        for (int t = 0; t < 8; ++t) {
-            int key = min(t0 + g + 4 * t, last);
-            vt[t] = load16(vseq + (int64_t)key * tok_stride + 8 * n);
-        }
-    };
-
-    auto compute_tile = [&](int t0, const bf16x8 *kt, const bf16x8 *vt) {
+    auto step = [&](bool tail, bf16x8 *kt, bf16x8 *vt) {
         // ---- both score sets from one K tile
         floatx4 sc0 = {0.f, 0.f, 0.f, 0.f}, sc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
         for (int u = 0; u < 4; ++u) {
             sc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt[u], qr[u], sc0, 0, 0, 0);
             sc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt[4 + u], qr[u], sc1, 0, 0, 0);
         }
-        float raw[8];
+        float raw[8], zr[8];
+#pragma unroll
         for (int i = 0; i < 4; ++i) {
             raw[i] = sc0[i];
             raw[4 + i] = sc1[i];
         }
-        // logits of the column's head: own value on softmax rows, the left
-        // neighbour's (row 2h) on probe rows
-        float z[8];
-        const int nvalid = end - t0;  // keys g + 4t valid iff g + 4t < nvalid
-        float tmax = -INFINITY;
+        // the column's head logit (unscaled): own value on softmax rows, the
+        // left neighbour's on probe rows (quad_perm [0,0,2,2])
+        const int nvalid = end - t0;  // key g + 4t is valid iff g + 4t < nvalid
+        float rmax = -INFINITY;
+#pragma unroll
         for (int t = 0; t < 8; ++t) {
-            float zr = raw[t];
-            if (PLX) {
-                float left = dpp_row_shr1(zr);
-                zr = kind ? left : zr;
-            }
-            z[t] = (g + 4 * t < nvalid) ? zr * a.zscale : -INFINITY;
-            tmax = fmaxf(tmax, z[t]);
+            zr[t] = PLX ? dpp_pair_even(raw[t]) : raw[t];
+            if (tail && g + 4 * t >= nvalid) zr[t] = -INFINITY;
+            rmax = fmaxf(rmax, zr[t]);
         }
-        tmax = xor_max_rowgroups(tmax);
-        const float m_new = fmaxf(m_run, tmax);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        float pv[8];
+        const float tmax = xor_max_rowgroups(rmax) * a.zscale;
+        // lazy rescale, decided for the whole wave
+        const bool raise = tmax > m_run + kRescaleSlack;
+        if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+            const float m_new = fmaxf(m_run, tmax);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            lsum *= alpha;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] *= alpha;
+        }
+        const float neg_m = -m_run;
         float tsum = 0.0f;
-        for (int t = 0; t < 8; ++t) {
-            float p = __builtin_amdgcn_exp2f(z[t] - m_new);
-            if (PLX && kind) p *= raw[t] * a.rk_scale - piv;
-            p = live ? p : 0.0f;
-            pv[t] = p;
-            tsum += p;
-        }
-        lsum = lsum * alpha + tsum;
         bf16x8 pf;
-        for (int t = 0; t < 8; ++t) pf[t] = (__bf16)pv[t];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            float p = __builtin_amdgcn_exp2f(fmaf(zr[t], a.zscale, neg_m));
+            p *= fmaf(raw[t], fa, fc);
+            tsum += p;
+            pf[t] = (__bf16)p;
+        }
+        lsum += tsum;
 
         // ---- V^T operand: 8x8 16-bit transpose in registers.
         // vt[t] holds dims 8n..8n+7 of key g + 4t; vT[e] holds keys t = 0..7 of dim 8n + e.
-        uint32_t tw[8][4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint4 x = __builtin_bit_cast(uint4, vt[2 * j]);
-            const uint4 y = __builtin_bit_cast(uint4, vt[2 * j + 1]);
-            const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
-            const uint32_t ys[4] = {y.x, y.y, y.z, y.w};
-#pragma unroll
-            for (int d2 = 0; d2 < 4; ++d2) {
-                tw[2 * d2][j] = (xs[d2] & 0xffffu) | (ys[d2] << 16);          // dim 2*d2
-                tw[2 * d2 + 1][j] = (xs[d2] >> 16) | (ys[d2] & 0xffff0000u);  // dim 2*d2+1
-            }
-        }
         bf16x8 vT[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            vT[e] = __builtin_bit_cast(bf16x8, uint4{tw[e][0], tw[e][1], tw[e][2], tw[e][3]});
-        // ---- rescale and accumulate both readouts from one V tile
-        for (int e = 0; e < 8; ++e) {
-            acc[e] *= alpha;
-            acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vT[e], pf, acc[e], 0, 0, 0);
+        for (int d2 = 0; d2 < 4; ++d2) {
+            uint32_t lo[4], hi[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t x = __builtin_bit_cast(uint4, vt[2 * j])[d2];
+                const uint32_t y = __builtin_bit_cast(uint4, vt[2 * j + 1])[d2];
+                lo[j] = __builtin_amdgcn_perm(y, x, 0x05040100u);  // dim 2*d2   of keys 2j, 2j+1
+                hi[j] = __builtin_amdgcn_perm(y, x, 0x07060302u);  // dim 2*d2+1 of keys 2j, 2j+1
+            }
+            vT[2 * d2] = __builtin_bit_cast(bf16x8, uint4{lo[0], lo[1], lo[2], lo[3]});
+            vT[2 * d2 + 1] = __builtin_bit_cast(bf16x8, uint4{hi[0], hi[1], hi[2], hi[3]});
         }
+        // ---- both readouts from one V tile
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vT[e], pf, acc[e], 0, 0, 0);
+        // this buffer takes the tile two steps ahead
+        load_tile(t0 + 2 * kStride, kt, vt);
+        t0 += kStride;
     };
 
-    int t0 = start;
-    load_tile(t0, kA, vA);
     while (true) {
-        if (t0 + 32 < end) load_tile(t0 + 32, kB, vB);
-        compute_tile(t0, kA, vA);
-        t0 += 32;
         if (t0 >= end) break;
-        if (t0 + 32 < end) load_tile(t0 + 32, kA, vA);
-        compute_tile(t0, kB, vB);
-        t0 += 32;
+        if (t0 + 32 <= end) step(false, kA, vA); else step(true, kA, vA);
         if (t0 >= end) break;
+        if (t0 + 32 <= end) step(false, kB, vB); else step(true, kB, vB);
     }
 
     lsum = xor_sum_rowgroups(lsum);
 
-    if (!a.fused) {
-        if (!live) return;
-        float *rec = a.ws + (((int64_t)b * a.Hq + hq) * a.splits + split) * partial_floats(D);
-        float *dst = rec + kind * D + 32 * g;
-        for (int i = 0; i < 4; ++i) {
-            float4 lo = {acc[0][i], acc[1][i], acc[2][i], acc[3][i]};
-            float4 hi = {acc[4][i], acc[5][i], acc[6][i], acc[7][i]};
-            reinterpret_cast<float4 *>(dst + 8 * i)[0] = lo;
-            reinterpret_cast<float4 *>(dst + 8 * i)[1] = hi;
-        }
+    // ---- merge the waves' states in LDS
+    __shared__ float sm_acc[W][NV][D];
+    __shared__ float sm_m[W][NV], sm_l[W][NV], sm_piv[NV];
+    if (live) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sm_acc[wave][n][32 * g + 8 * i + e] = acc[e][i];
         if (g == 0) {
-            if (kind == 0) {
-                rec[2 * D + 0] = m_run;
-                rec[2 * D + 1] = lsum;
+            sm_m[wave][n] = m_run;
+            sm_l[wave][n] = lsum;
+            if (wave == 0) sm_piv[n] = piv;
+        }
+    }
+    __syncthreads();
+
+    if (!a.fused) {
+        // record element (column n, dim d) for every live column
+        for (int idx = threadIdx.x; idx < NV * D; idx += 64 * W) {
+            const int cn = idx / D, d = idx % D;
+            float M = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < W; ++w) M = fmaxf(M, sm_m[w][cn]);
+            float val = 0.f;
+#pragma unroll
+            for (int w = 0; w < W; ++w) {
+                const float mw = sm_m[w][cn];
+                if (mw != -INFINITY) val += __builtin_amdgcn_exp2f(mw - M) * sm_acc[w][cn][d];
+            }
+            float *rec = a.ws + ((row0 + cn / NR) * a.splits + split) * partial_floats(D);
+            rec[(cn % NR) * D + d] = val;
+        }
+        if (threadIdx.x < NV) {
+            const int cn = threadIdx.x;
+            float M = -INFINITY;
+            for (int w = 0; w < W; ++w) M = fmaxf(M, sm_m[w][cn]);
+            float sum = 0.f;
+            for (int w = 0; w < W; ++w) {
+                const float mw = sm_m[w][cn];
+                if (mw != -INFINITY) sum += __builtin_amdgcn_exp2f(mw - M) * sm_l[w][cn];
+            }
+            float *rec = a.ws + ((row0 + cn / NR) * a.splits + split) * partial_floats(D);
+            if (cn % NR == 0) {
+                rec[2 * D + 0] = M;
+                rec[2 * D + 1] = sum;
                 if (!PLX) {
                     rec[2 * D + 2] = 0.f;
                     rec[2 * D + 3] = 0.f;
                 }
             } else {
-                rec[2 * D + 2] = lsum;
-                rec[2 * D + 3] = piv;
+                rec[2 * D + 2] = sum;
+                rec[2 * D + 3] = sm_piv[cn];
             }
         }
         return;
     }
 
-    // One split: finalise here. Probe rows hand B and S to the softmax row on their left.
-    float bsum[32];
-    float s_tot = 0.0f;
-    if (PLX) {
-        for (int e = 0; e < 8; ++e)
-            for (int i = 0; i < 4; ++i) bsum[8 * i + e] = dpp_row_shl1(acc[e][i]);
-        s_tot = dpp_row_shl1(lsum);
-    }
-    if (!live || kind != 0) return;
-    const float inv_l = 1.0f / lsum;
-    const float cA = PLX ? (1.0f - s_tot * inv_l) : 1.0f;
-    uint16_t *o = reinterpret_cast<uint16_t *>(a.o) + ((int64_t)b * a.Hq + hq) * D + 32 * g;
-    for (int i = 0; i < 4; ++i) {
-        float ov[8];
-        for (int e = 0; e < 8; ++e) {
-            float A = acc[e][i];
-            ov[e] = PLX ? (A * cA + bsum[8 * i + e]) * inv_l : A * inv_l;
+    // One split: finalise here, o = (A + B - (S / l) A) / l per (head, dim).
+    for (int idx = threadIdx.x; idx < G * D; idx += 64 * W) {
+        const int hh = idx / D, d = idx % D;
+        const int ca = NR * hh;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < W; ++w) M = fmaxf(M, sm_m[w][ca]);
+        float A = 0.f, Bv = 0.f, l = 0.f, S = 0.f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            const float mw = sm_m[w][ca];
+            if (mw == -INFINITY) continue;
+            const float c = __builtin_amdgcn_exp2f(mw - M);
+            A += c * sm_acc[w][ca][d];
+            l += c * sm_l[w][ca];
+            if (PLX) {
+                Bv += c * sm_acc[w][ca + 1][d];
+                S += c * sm_l[w][ca + 1];
+            }
         }
-        uint4 w = {pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3]), pack_bf16x2(ov[4], ov[5]),
-                   pack_bf16x2(ov[6], ov[7])};
-        reinterpret_cast<uint4 *>(o + 8 * i)[0] = w;
+        const float inv_l = 1.0f / l;
+        const float val = PLX ? (A * (1.0f - S * inv_l) + Bv) * inv_l : A * inv_l;
+        reinterpret_cast<uint16_t *>(a.o)[(row0 + hh) * D + d] = f32_to_bf16(val);
     }
 }
 
@@ -524,110 +608,103 @@ __global__ __launch_bounds__(64) void decode_generic(DecodeArgs a) {
 }
 
 // -------------------------------------------------------------------------
-// Record merge: one workgroup of 256 threads per (query head, sequence).
-// Wave w folds records w, w+4, ...; the four wave states meet in LDS. Empty
-// records (m = -inf) are skipped; none at all gives o = 0. Records may carry
-// different pivots: each is re-based onto the pivot of record 0 with
+// Record merge. One workgroup of 256 threads per (query head, sequence,
+// half of the dims). Wave w owns records w, w+4, w+8, ...; it issues the
+// loads of a whole batch of kBatch records before touching any of them (the
+// merge is latency-bound: a handful of dependent round trips would cost more
+// than the bytes), then folds the batch with the online rescaling. The four
+// wave states meet in LDS.
+// Empty records (m = -inf) are skipped (their A, B are never written); a row
+// with no record gets o = 0. Records may carry different pivots: each is
+// re-based onto record 0's pivot pi_0 with
 //   S' = S + (pi_i - pi_0) l,   B' = B + (pi_i - pi_0) A
-// (exact algebra; zero change when the pivots agree, as they do when all
-// records come from one call).
+// (exact algebra; no change when the pivots agree, as in one call).
 // -------------------------------------------------------------------------
+constexpr int kBatch = 16;
+
 template <typename TO, int D, bool PLX>
 __global__ __launch_bounds__(256) void decode_reduce(DecodeArgs a) {
-    constexpr int DPL = D / 64;  // dims per lane
+    constexpr int DS = D / 2;  // dims per workgroup
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
     const int hq = blockIdx.x;
     const int b = blockIdx.y;
+    const int d = blockIdx.z * DS + (lane < DS ? lane : 0);
     const int ns = a.splits;
     const float *base = a.ws + ((int64_t)b * a.Hq + hq) * ns * partial_floats(D);
     const float piv0 = PLX ? base[2 * D + 3] : 0.f;
 
-    float m = -INFINITY, l = 0.f, S = 0.f, A[DPL], Bv[DPL];
-    for (int d = 0; d < DPL; ++d) {
-        A[d] = 0.f;
-        Bv[d] = 0.f;
-    }
-    for (int i = w; i < ns; i += 4) {
-        const float *rec = base + (int64_t)i * partial_floats(D);
-        const float4 tail = reinterpret_cast<const float4 *>(rec + 2 * D)[0];
-        const float mi = tail.x;
-        if (mi == -INFINITY) continue;
-        const float li = tail.y;
-        const float dp = PLX ? tail.w - piv0 : 0.f;
-        const float Si = PLX ? tail.z + dp * li : 0.f;
-        float Ai[DPL], Bi[DPL];
-        for (int d = 0; d < DPL; ++d) {
-            Ai[d] = rec[lane * DPL + d];
-            Bi[d] = PLX ? rec[D + lane * DPL + d] + dp * Ai[d] : 0.f;
+    float m = -INFINITY, l = 0.f, S = 0.f, A = 0.f, Bv = 0.f;
+    for (int i0 = w; i0 < ns; i0 += 4 * kBatch) {
+        float4 tail[kBatch];
+        float Ai[kBatch], Bi[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const int i = min(i0 + 4 * j, ns - 1);
+            const float *rec = base + (int64_t)i * partial_floats(D);
+            tail[j] = reinterpret_cast<const float4 *>(rec + 2 * D)[0];
+            Ai[j] = rec[d];
+            Bi[j] = PLX ? rec[D + d] : 0.f;
         }
-        const float M = fmaxf(m, mi);
-        const float ax = __builtin_amdgcn_exp2f(m - M);
-        const float ay = __builtin_amdgcn_exp2f(mi - M);
-        m = M;
-        l = l * ax + li * ay;
-        S = S * ax + Si * ay;
-        for (int d = 0; d < DPL; ++d) {
-            A[d] = A[d] * ax + Ai[d] * ay;
-            Bv[d] = Bv[d] * ax + Bi[d] * ay;
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const float mi = tail[j].x;
+            if (i0 + 4 * j >= ns || mi == -INFINITY) continue;
+            const float dp = PLX ? tail[j].w - piv0 : 0.f;
+            const float M = fmaxf(m, mi);
+            const float ax = __builtin_amdgcn_exp2f(m - M);
+            const float ay = __builtin_amdgcn_exp2f(mi - M);
+            m = M;
+            l = l * ax + tail[j].y * ay;
+            A = A * ax + Ai[j] * ay;
+            if (PLX) {
+                S = S * ax + (tail[j].z + dp * tail[j].y) * ay;
+                Bv = Bv * ax + (Bi[j] + dp * Ai[j]) * ay;
+            }
         }
     }
-    __shared__ float sm[4][2 * D + 4];
-    for (int d = 0; d < DPL; ++d) {
-        sm[w][lane * DPL + d] = A[d];
-        sm[w][D + lane * DPL + d] = Bv[d];
-    }
-    if (lane == 0) {
-        sm[w][2 * D] = m;
-        sm[w][2 * D + 1] = l;
-        sm[w][2 * D + 2] = S;
-    }
+    __shared__ float part[4][5][64];
+    part[w][0][lane] = m;
+    part[w][1][lane] = l;
+    part[w][2][lane] = S;
+    part[w][3][lane] = A;
+    part[w][4][lane] = Bv;
     __syncthreads();
-    if (w != 0) return;
-    m = -INFINITY;
-    l = 0.f;
-    S = 0.f;
-    for (int d = 0; d < DPL; ++d) {
-        A[d] = 0.f;
-        Bv[d] = 0.f;
-    }
-    for (int x = 0; x < 4; ++x) {
-        const float mi = sm[x][2 * D];
-        if (mi == -INFINITY) continue;  // this wave folded no record
-        const float M = fmaxf(m, mi);
-        const float ax = __builtin_amdgcn_exp2f(m - M);
-        const float ay = __builtin_amdgcn_exp2f(mi - M);
-        m = M;
-        l = l * ax + sm[x][2 * D + 1] * ay;
-        S = S * ax + sm[x][2 * D + 2] * ay;
-        for (int d = 0; d < DPL; ++d) {
-            A[d] = A[d] * ax + sm[x][lane * DPL + d] * ay;
-            Bv[d] = Bv[d] * ax + sm[x][D + lane * DPL + d] * ay;
+    if (w != 0 || lane >= DS) return;
+    float M = -INFINITY;
+    for (int x = 0; x < 4; ++x) M = fmaxf(M, part[x][0][lane]);
+    float val = 0.f;
+    if (M != -INFINITY) {
+        l = S = A = Bv = 0.f;
+        for (int x = 0; x < 4; ++x) {
+            const float mx = part[x][0][lane];
+            if (mx == -INFINITY) continue;
+            const float c = __builtin_amdgcn_exp2f(mx - M);
+            l += part[x][1][lane] * c;
+            S += part[x][2][lane] * c;
+            A += part[x][3][lane] * c;
+            Bv += part[x][4][lane] * c;
         }
+        const float inv_l = 1.0f / l;
+        val = PLX ? (A * (1.0f - S * inv_l) + Bv) * inv_l : A * inv_l;
     }
-    TO *o = reinterpret_cast<TO *>(a.o) + ((int64_t)b * a.Hq + hq) * D + lane * DPL;
-    for (int d = 0; d < DPL; ++d) {
-        float val = 0.f;
-        if (m != -INFINITY) {
-            const float inv_l = 1.0f / l;
-            val = PLX ? (A[d] * (1.0f - S * inv_l) + Bv[d]) * inv_l : A[d] * inv_l;
-        }
-        if constexpr (sizeof(TO) == 4)
-            o[d] = val;
-        else
-            o[d] = f32_to_bf16(val);
-    }
+    TO *o = reinterpret_cast<TO *>(a.o) + ((int64_t)b * a.Hq + hq) * D + d;
+    if constexpr (sizeof(TO) == 4)
+        *o = val;
+    else
+        *o = f32_to_bf16(val);
 }
 
 template <bool PLX>
 hipError_t launch_mfma(const DecodeArgs &a, hipStream_t stream) {
     dim3 grid(a.Hkv, a.splits, a.B);
+    dim3 block(64 * kDecodeWaves);
     const int G = a.Hq / a.Hkv;
     switch (G) {
-        case 1: hipLaunchKernelGGL((decode_mfma_bf16_d128<1, PLX>), grid, dim3(64), 0, stream, a); break;
-        case 2: hipLaunchKernelGGL((decode_mfma_bf16_d128<2, PLX>), grid, dim3(64), 0, stream, a); break;
-        case 4: hipLaunchKernelGGL((decode_mfma_bf16_d128<4, PLX>), grid, dim3(64), 0, stream, a); break;
-        case 8: hipLaunchKernelGGL((decode_mfma_bf16_d128<8, PLX>), grid, dim3(64), 0, stream, a); break;
+        case 1: hipLaunchKernelGGL((decode_mfma_bf16_d128<1, PLX>), grid, block, 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((decode_mfma_bf16_d128<2, PLX>), grid, block, 0, stream, a); break;
+        case 4: hipLaunchKernelGGL((decode_mfma_bf16_d128<4, PLX>), grid, block, 0, stream, a); break;
+        case 8: hipLaunchKernelGGL((decode_mfma_bf16_d128<8, PLX>), grid, block, 0, stream, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -645,7 +722,7 @@ hipError_t launch_generic(const DecodeArgs &a, hipStream_t stream) {
 
 template <typename TO, bool PLX>
 hipError_t launch_reduce(const DecodeArgs &a, hipStream_t stream) {
-    dim3 grid(a.Hq, a.B);
+    dim3 grid(a.Hq, a.B, 2);
     if (a.D == 64)
         hipLaunchKernelGGL((decode_reduce<TO, 64, PLX>), grid, dim3(256), 0, stream, a);
     else

@@ -54,9 +54,11 @@ def _decode(**kw):
     (dict(q=None), 1), (dict(r=None), 1), (dict(k=None), 1), (dict(o=None), 1),
     (dict(D=96), 2), (dict(D=256), 2), (dict(dt=2), 2), (dict(ns=-1), 1),
     (dict(qk=float("nan")), 1), (dict(rk=float("inf")), 1),
-    (dict(ns=4), 3), (dict(ns=4, ws=FAKE, wsb=16), 3),
+    (dict(ns=4, L=4096), 3), (dict(ns=4, L=4096, ws=FAKE, wsb=16), 3),
 ])
 def test_decode_rejects_on_host(kw, status):
+    # every case must fail validation: FAKE pointers may never reach a launch
+    assert status != 0
     assert _decode(**kw) == status
 
 
@@ -82,8 +84,10 @@ def test_workspace_plan():
     # forced split counts: records of 2D + 4 floats per (b, hq, split)
     assert ns(1, 16, 8, 128, 32768, 1, 64) == 64
     assert ws(1, 16, 8, 128, 32768, 1, 64) == 16 * 64 * (2 * 128 + 4) * 4
-    # at least 32 keys per split
-    assert ns(2, 4, 2, 128, 100, 1, 1000) == 4
+    # at least 32 keys per split on the generic path (fp32), 128 on the MFMA path (bf16, D=128)
+    assert ns(2, 4, 2, 128, 100, 0, 1000) == 4
+    assert ns(2, 4, 2, 128, 100, 1, 1000) == 1
+    assert ns(2, 4, 2, 128, 1000, 1, 1000) == 8
     # monotone in the length for a fixed request
     prev = 0
     for L in (1, 33, 64, 500, 4096, 70000):
@@ -91,6 +95,8 @@ def test_workspace_plan():
         assert cur >= prev
         prev = cur
     assert ws(0, 16, 8, 128, 64, 1, 0) == 0 and ns(1, 16, 5, 128, 64, 1, 0) == 0
-    # the automatic plan keeps at least 128 keys per split
+    # the automatic plan keeps at least 128 keys per wave (4 waves per split on the MFMA path)
     s = ns(1, 16, 8, 128, 32768, 1, 0)
+    assert 1 < s <= 32768 // 512
+    s = ns(1, 16, 8, 64, 32768, 1, 0)
     assert 1 < s <= 32768 // 128
