@@ -1,0 +1,69 @@
+// Device helpers shared by the decode and prefill kernels (gfx950).
+#pragma once
+
+#include "plx_internal.h"
+
+namespace plx {
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(((uint32_t)b) << 16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+    __bf16 h = (__bf16)x;  // v_cvt_pk_bf16_f32: round to nearest even
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// quad_perm [0,0,2,2]: every lane receives the even lane of its pair.
+__device__ __forceinline__ float dpp_pair_even(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xA0, 0xf, 0xf, false));
+}
+
+__device__ __forceinline__ float xor_max_rowgroups(float x) {  // over lanes n, n+16, n+32, n+48
+    x = fmaxf(x, __shfl_xor(x, 16));
+    x = fmaxf(x, __shfl_xor(x, 32));
+    return x;
+}
+__device__ __forceinline__ float xor_sum_rowgroups(float x) {
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    return x;
+}
+
+__device__ __forceinline__ bf16x8 load16(const uint16_t *p) {
+    return *reinterpret_cast<const bf16x8 *>(p);
+}
+
+// How far (log2 units) a tile's max may exceed the running reference max
+// before the accumulators are rescaled.
+constexpr float kRescaleSlack = 8.0f;
+
+// Word 3 of a raw buffer resource for gfx9-family (CDNA) untyped loads.
+constexpr int kBufferFlags = 0x00020000;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte load at byte `voffset` of a buffer; past the buffer's range it
+// returns zeros. The KV stream is read once, so it is fetched non-temporal.
+// The loads are marked volatile (bit 31 of the policy operand, a compiler
+// flag) so that they are issued where they are written: otherwise the
+// compiler sinks a prefetch down to its first use and the pipelining is lost.
+constexpr int kStreamPolicy = 2 | (int)(1u << 31);  // nt, volatile
+__device__ __forceinline__ bf16x8 buffer_load16(__amdgpu_buffer_rsrc_t rs, int voffset) {
+    u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rs, voffset, 0, kStreamPolicy);
+    return __builtin_bit_cast(bf16x8, w);
+}
+// Same, cached normally (data that other workgroups read again).
+constexpr int kReusePolicy = (int)(1u << 31);  // volatile only
+__device__ __forceinline__ u32x4 buffer_load16_cached(__amdgpu_buffer_rsrc_t rs, int voffset) {
+    return __builtin_amdgcn_raw_buffer_load_b128(rs, voffset, 0, kReusePolicy);
+}
+
+}  // namespace plx

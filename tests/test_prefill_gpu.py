@@ -58,3 +58,37 @@ def test_prefill_row_matches_decode_on_prefix():
         vd = t[3][:, :, : i + 1].transpose(1, 2).contiguous()
         od = from_gpu(plx.decode(t[0][:, :, i].contiguous(), t[1][:, :, i].contiguous(), kd, vd))
         assert np.abs(od - o[:, :, i]).max() <= 1e-2 * np.abs(o[:, :, i]).max()
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 2), (2, 2), (8, 2), (6, 2), (3, 1)])
+@pytest.mark.parametrize("L", [1, 31, 64, 100, 257])
+def test_prefill_mfma_shapes(Hq, Hkv, L):
+    """bf16, head_dim 128: the MFMA kernel (group sizes 1 and even) across q-tile,
+    KV-tile and diagonal boundaries; other group sizes take the generic kernel."""
+    B, D = 2, 128
+    q, r, k, v = inputs(B, Hq, Hkv, L, D, synth.BF16, 1.0, 300 + L + Hq)
+    t = [to_gpu(x, synth.BF16) for x in (q, r, k, v)]
+    o, lse, sbar = plx.prefill(*t, return_stats=True)
+    ref, ref_lse, ref_sbar = oracle.prefill(q, r, k, v, stats=True)
+    assert_parity(from_gpu(o), ref, synth.BF16, f"Hq={Hq} Hkv={Hkv} L={L}")
+    lse = lse.cpu().numpy().astype(np.float64)
+    assert np.abs(lse - ref_lse).max() <= 1e-3 * max(1.0, np.abs(ref_lse).max())
+    sbar = sbar.cpu().numpy().astype(np.float64)
+    assert np.abs(sbar - ref_sbar).max() <= 1e-2 * max(1.0, np.abs(ref_sbar).max())
+
+
+def test_prefill_workload_sampled_rows():
+    """B=8, L=4096, Hq=16, Hkv=8, D=128, bf16, N(0,1)/sqrt(128): sampled rows
+    across the causal range (every row's oracle cost is its prefix)."""
+    spec = synth.prefill_spec(5)
+    B, Hq, Hkv, L, D = spec.B, spec.Hq, spec.Hkv, spec.L, spec.D
+    q, r, k, v = inputs(B, Hq, Hkv, L, D, spec.dtype, spec.scale, spec.seed)
+    t = [to_gpu(x, spec.dtype) for x in (q, r, k, v)]
+    o = plx.prefill(*t)
+    g = np.random.default_rng(5)
+    rows = np.stack([g.integers(0, B, 96), g.integers(0, Hq, 96), g.integers(0, L, 96)], axis=1)
+    rows = np.concatenate([rows, [[0, 0, 0], [B - 1, Hq - 1, L - 1], [3, 7, 63], [3, 7, 64],
+                                  [5, 2, 127], [5, 2, 128]]])
+    ref = oracle.prefill(q, r, k, v, rows=rows)
+    got = from_gpu(o[rows[:, 0], rows[:, 1], rows[:, 2]])
+    assert_parity(got, ref, spec.dtype, "prefill workload rows")
