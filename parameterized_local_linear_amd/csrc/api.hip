@@ -33,7 +33,7 @@ int device_cu_count() {
 // enough splits for about kTargetWavesPerCU resident waves per compute unit,
 // with at least kMinKeysPerWave keys per wave; one split fuses the final
 // normalisation into the streaming kernel and needs no workspace.
-constexpr int kTargetWavesPerCU = 8;
+constexpr int kTargetWavesPerCU = 4;
 constexpr int kMinKeysPerWave = 128;
 DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int kv_len, int dtype, int num_splits) {
     DecodePlan p;

@@ -26,15 +26,21 @@ __device__ __forceinline__ float dpp_pair_even(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xA0, 0xf, 0xf, false));
 }
 
-__device__ __forceinline__ float xor_max_rowgroups(float x) {  // over lanes n, n+16, n+32, n+48
-    x = fmaxf(x, __shfl_xor(x, 16));
-    x = fmaxf(x, __shfl_xor(x, 32));
-    return x;
+// Reductions over the four lanes n, n+16, n+32, n+48 (the four 16-lane rows
+// of a wave), with gfx950's v_permlane32_swap / v_permlane16_swap: swapping a
+// value with itself leaves each lane holding its own and its partner's value
+// (partner = lane ^ 32, then lane ^ 16), all in VALU, no LDS round trip.
+__device__ __forceinline__ float xor_max_rowgroups(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float xor_sum_rowgroups(float x) {
-    x += __shfl_xor(x, 16);
-    x += __shfl_xor(x, 32);
-    return x;
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ __forceinline__ bf16x8 load16(const uint16_t *p) {

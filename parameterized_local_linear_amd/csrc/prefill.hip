@@ -16,6 +16,11 @@
 #include "plx_internal.h"
 #include "plx_device.h"
 
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <type_traits>
+
 namespace plx {
 
 namespace {
@@ -151,10 +156,10 @@ __global__ __launch_bounds__(64) void prefill_generic(PrefillArgs a) {
 // -------------------------------------------------------------------------
 // MFMA prefill, bf16, head_dim 128.
 //
-// Workgroup: four waves over one (sequence, KV head, group of HPW query
-// heads, q-tile of 128 / HPW rows per head); each wave owns 32 query rows
-// of one head as two 16-row blocks. Every query head of the workgroup reads
-// the same KV head, so one K/V tile in LDS feeds all four waves.
+// Workgroup: NW waves over one (sequence, KV head, group of HPW query heads,
+// q-tile of 16 * QB * NW / HPW rows per head); each wave owns QB blocks of
+// 16 query rows of one head. Every query head of the workgroup reads the
+// same KV head, so one K/V tile in LDS feeds all the waves.
 //
 // K/V tiles of 64 keys are copied global -> registers -> LDS, double
 // buffered: the next tile's global loads are issued before the current tile
@@ -170,7 +175,7 @@ __global__ __launch_bounds__(64) void prefill_generic(PrefillArgs a) {
 // scores of query n for exactly the keys g + 4t it feeds the readout MFMA
 // (P never leaves registers), and V^T built by an in-register 8x8 transpose
 // of rows read from LDS. The K and V operands are read once per sub-tile and
-// shared by both query blocks and both score/readout pairs.
+// shared by the wave's query blocks and by both score/readout pairs.
 //
 // Causality: keys j <= i. Sub-tiles entirely above a wave's rows are
 // skipped, sub-tiles crossing the diagonal are masked. Work items run
@@ -180,12 +185,16 @@ __global__ __launch_bounds__(64) void prefill_generic(PrefillArgs a) {
 // -------------------------------------------------------------------------
 constexpr int kPrefillKeys = 64;  // keys per LDS tile
 
-template <int HPW>
-__global__ __launch_bounds__(256) void prefill_mfma_bf16_d128(PrefillArgs a) {
+template <int HPW, int QB, int NW>
+__global__ __launch_bounds__(64 * NW) void prefill_mfma_bf16_d128(PrefillArgs a) {
     constexpr int D = 128;
-    constexpr int WPH = 4 / HPW;       // waves per head
-    constexpr int RPH = 32 * WPH;      // rows per head per work item
+    constexpr int WPH = NW / HPW;       // waves per head
+    constexpr int RW = 16 * QB;         // rows per wave
+    constexpr int RPH = RW * WPH;       // rows per head per work item
     constexpr int TK = kPrefillKeys;
+    constexpr int NT = 64 * NW;         // threads
+    constexpr int LOADS = TK * 16 / NT; // 16-byte chunks of K (and of V) per thread per tile
+    static_assert(NW % HPW == 0 && LOADS >= 1, "bad workgroup shape");
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int n = lane & 15;
@@ -203,7 +212,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_bf16_d128(PrefillArgs a) {
     const int hkv = (grp / hgroups) % a.Hkv;
     const int hsub = grp % hgroups;
     const int hq = hkv * G + hsub * HPW + wave / WPH;
-    const int q0 = qt * RPH + (wave % WPH) * 32;    // this wave's first row
+    const int q0 = qt * RPH + (wave % WPH) * RW;    // this wave's first row
     const int kend = min(a.L, (qt + 1) * RPH);      // keys the workgroup needs
     const int ntiles = (kend + TK - 1) / TK;
 
@@ -219,13 +228,13 @@ __global__ __launch_bounds__(256) void prefill_mfma_bf16_d128(PrefillArgs a) {
     // ---- LDS: two K/V tiles
     __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][TK * D];
     __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][TK * D];
-    // loader: thread handles (key tk, chunk tc) and (key tk + 16 * j) for j < 4
+    // loader: thread handles chunk tc of keys tk + (NT / 16) * j
     const int tk = threadIdx.x >> 4, tc = threadIdx.x & 15;
-    u32x4 stage_k[TK / 16], stage_v[TK / 16];
+    u32x4 stage_k[LOADS], stage_v[LOADS];
     auto global_tile = [&](int tile) {
 #pragma unroll
-        for (int j = 0; j < TK / 16; ++j) {
-            const int key = tile * TK + tk + 16 * j;
+        for (int j = 0; j < LOADS; ++j) {
+            const int key = tile * TK + tk + (NT / 16) * j;
             const int off = (key * D + tc * 8) * 2;
             stage_k[j] = buffer_load16_cached(krs, off);
             stage_v[j] = buffer_load16_cached(vrs, off);
@@ -233,8 +242,8 @@ __global__ __launch_bounds__(256) void prefill_mfma_bf16_d128(PrefillArgs a) {
     };
     auto lds_store = [&](int buf) {
 #pragma unroll
-        for (int j = 0; j < TK / 16; ++j) {
-            const int key = tk + 16 * j;
+        for (int j = 0; j < LOADS; ++j) {
+            const int key = tk + (NT / 16) * j;
             const int slot = key * D + ((tc ^ (key & 15)) * 8);
             *reinterpret_cast<u32x4 *>(&lds_k[buf][slot]) = stage_k[j];
             *reinterpret_cast<u32x4 *>(&lds_v[buf][slot]) = stage_v[j];
@@ -242,13 +251,13 @@ __global__ __launch_bounds__(256) void prefill_mfma_bf16_d128(PrefillArgs a) {
     };
     global_tile(0);
 
-    // ---- per-wave query operands: block qb, vector (q or r) w, k-step u
-    bf16x8 qop[2][4], rop[2][4];
-    float piv[2];
+    // ---- per-wave query operands: block qb, k-step u
+    bf16x8 qop[QB][4], rop[QB][4];
+    float piv[QB];
     {
         const int64_t rowbase = ((int64_t)b * a.Hq + hq) * a.L;
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < QB; ++qb) {
             const int row = min(q0 + 16 * qb + n, a.L - 1);
             const uint16_t *qp = qh + (rowbase + row) * D;
             const uint16_t *rp = rh + (rowbase + row) * D;
@@ -260,32 +269,37 @@ __global__ __launch_bounds__(256) void prefill_mfma_bf16_d128(PrefillArgs a) {
         }
         // pivot: probe score of key 0 for each query row
         const uint16_t *k0 = reinterpret_cast<const uint16_t *>(a.k) + kvbase;
-        float part[2] = {0.f, 0.f};
+        float part[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) part[qb] = 0.f;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const bf16x8 kk = load16(k0 + 8 * (g + 4 * u));
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
+            for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) part[qb] += (float)rop[qb][u][e] * (float)kk[e];
         }
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) piv[qb] = xor_sum_rowgroups(part[qb]) * a.rk_scale;
+        for (int qb = 0; qb < QB; ++qb) piv[qb] = xor_sum_rowgroups(part[qb]) * a.rk_scale;
     }
 
-    float m_run[2] = {-INFINITY, -INFINITY};
-    float lsA[2] = {0.f, 0.f}, lsS[2] = {0.f, 0.f};
-    floatx4 accA[2][8], accB[2][8];
+    float m_run[QB], lsA[QB], lsS[QB];
+    floatx4 accA[QB][8], accB[QB][8];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < QB; ++qb) {
+        m_run[qb] = -INFINITY;
+        lsA[qb] = 0.f;
+        lsS[qb] = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             accA[qb][e] = floatx4{0.f, 0.f, 0.f, 0.f};
             accB[qb][e] = floatx4{0.f, 0.f, 0.f, 0.f};
         }
+    }
 
     const int kperm = (n >> 2) + 4 * (n & 3);
-    const int q_last = q0 + 31;
+    const int q_last = q0 + RW - 1;
 
     // One 32-key sub-tile at key k0 from LDS buffer `buf` (local key offset kl).
     auto subtile = [&](int buf, int kl, int k0, bool diag) {
@@ -301,29 +315,31 @@ __global__ __launch_bounds__(256) void prefill_mfma_bf16_d128(PrefillArgs a) {
             }
         }
         // V^T operand: rows key kl + g + 4t, chunk n, transposed in registers
-        bf16x8 vrow[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const int key = kl + g + 4 * t;
-            const int slot = key * D + ((n ^ (key & 15)) * 8);
-            vrow[t] = *reinterpret_cast<const bf16x8 *>(&lds_v[buf][slot]);
-        }
         bf16x8 vT[8];
+        {
+            bf16x8 vrow[8];
 #pragma unroll
-        for (int d2 = 0; d2 < 4; ++d2) {
-            uint32_t lo[4], hi[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t x = __builtin_bit_cast(uint4, vrow[2 * j])[d2];
-                const uint32_t y = __builtin_bit_cast(uint4, vrow[2 * j + 1])[d2];
-                lo[j] = __builtin_amdgcn_perm(y, x, 0x05040100u);
-                hi[j] = __builtin_amdgcn_perm(y, x, 0x07060302u);
+            for (int t = 0; t < 8; ++t) {
+                const int key = kl + g + 4 * t;
+                const int slot = key * D + ((n ^ (key & 15)) * 8);
+                vrow[t] = *reinterpret_cast<const bf16x8 *>(&lds_v[buf][slot]);
             }
-            vT[2 * d2] = __builtin_bit_cast(bf16x8, uint4{lo[0], lo[1], lo[2], lo[3]});
-            vT[2 * d2 + 1] = __builtin_bit_cast(bf16x8, uint4{hi[0], hi[1], hi[2], hi[3]});
+#pragma unroll
+            for (int d2 = 0; d2 < 4; ++d2) {
+                uint32_t lo[4], hi[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t x = __builtin_bit_cast(uint4, vrow[2 * j])[d2];
+                    const uint32_t y = __builtin_bit_cast(uint4, vrow[2 * j + 1])[d2];
+                    lo[j] = __builtin_amdgcn_perm(y, x, 0x05040100u);
+                    hi[j] = __builtin_amdgcn_perm(y, x, 0x07060302u);
+                }
+                vT[2 * d2] = __builtin_bit_cast(bf16x8, uint4{lo[0], lo[1], lo[2], lo[3]});
+                vT[2 * d2 + 1] = __builtin_bit_cast(bf16x8, uint4{hi[0], hi[1], hi[2], hi[3]});
+            }
         }
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < QB; ++qb) {
             floatx4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = z0, s0 = z0, s1 = z0;
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
@@ -383,28 +399,35 @@ __global__ __launch_bounds__(256) void prefill_mfma_bf16_d128(PrefillArgs a) {
         }
     };
 
-    lds_store(0);
-    __syncthreads();
-    for (int tile = 0; tile < ntiles; ++tile) {
-        const int buf = tile & 1;
+    // One 64-key tile from LDS buffer BUF (compile-time, so every LDS
+    // address is a per-lane constant plus an immediate offset).
+    auto tile_step = [&](auto bufc, int tile) {
+        constexpr int BUF = decltype(bufc)::value;
         if (tile + 1 < ntiles) global_tile(tile + 1);
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             const int k0 = tile * TK + 32 * half;
             if (k0 <= q_last) {  // wave-uniform: sub-tiles above the wave's rows are skipped
                 if (k0 + 31 <= q0)
-                    subtile(buf, 32 * half, k0, false);
+                    subtile(BUF, 32 * half, k0, false);
                 else
-                    subtile(buf, 32 * half, k0, true);
+                    subtile(BUF, 32 * half, k0, true);
             }
         }
-        if (tile + 1 < ntiles) lds_store(buf ^ 1);
+        if (tile + 1 < ntiles) lds_store(BUF ^ 1);
         __syncthreads();
+    };
+
+    lds_store(0);
+    __syncthreads();
+    for (int tile = 0; tile < ntiles; tile += 2) {
+        tile_step(std::integral_constant<int, 0>{}, tile);
+        if (tile + 1 < ntiles) tile_step(std::integral_constant<int, 1>{}, tile + 1);
     }
 
     // ---- epilogue: o = (A + B - (S / l) A) / l per row
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
         const float l = xor_sum_rowgroups(lsA[qb]);
         const float S = xor_sum_rowgroups(lsS[qb]);
         const int row = q0 + 16 * qb + n;
@@ -433,18 +456,42 @@ __global__ __launch_bounds__(256) void prefill_mfma_bf16_d128(PrefillArgs a) {
 
 bool prefill_supported(int D, int dtype) { return (D == 64 || D == 128) && (dtype == 0 || dtype == 1); }
 
+// Workgroup shape of the MFMA prefill: QB query blocks of 16 rows per wave,
+// NW waves; selectable for measurement through PARALLAX_PREFILL_SHAPE
+// ("QB,NW"), default below.
+static int prefill_shape_qb = 0, prefill_shape_nw = 0;
+
 hipError_t launch_prefill(const PrefillArgs &a, int dtype, hipStream_t stream) {
     const int G = a.Hq / a.Hkv;
+    if (prefill_shape_qb == 0) {
+        prefill_shape_qb = 1;
+        prefill_shape_nw = 8;
+        if (const char *env = getenv("PARALLAX_PREFILL_SHAPE")) {
+            int qb = 0, nw = 0;
+            if (sscanf(env, "%d,%d", &qb, &nw) == 2 && ((qb == 2 && nw == 4) || (qb == 1 && nw == 8))) {
+                prefill_shape_qb = qb;
+                prefill_shape_nw = nw;
+            }
+        }
+    }
     if (dtype == 1 && a.D == 128 && (G % 2 == 0 || G == 1)) {
         const int hpw = (G % 2 == 0) ? 2 : 1;
-        const int rph = 128 / hpw;
+        const int rph = 16 * prefill_shape_qb * prefill_shape_nw / hpw;
         const long items = (long)a.B * a.Hkv * (G / hpw) * ((a.L + rph - 1) / rph);
         if (items <= 0x7fffffffL) {
             dim3 grid((unsigned)items);
-            if (hpw == 2)
-                hipLaunchKernelGGL((prefill_mfma_bf16_d128<2>), grid, dim3(256), 0, stream, a);
-            else
-                hipLaunchKernelGGL((prefill_mfma_bf16_d128<1>), grid, dim3(256), 0, stream, a);
+            const bool wide = prefill_shape_qb == 2;
+            if (hpw == 2) {
+                if (wide)
+                    hipLaunchKernelGGL((prefill_mfma_bf16_d128<2, 2, 4>), grid, dim3(256), 0, stream, a);
+                else
+                    hipLaunchKernelGGL((prefill_mfma_bf16_d128<2, 1, 8>), grid, dim3(512), 0, stream, a);
+            } else {
+                if (wide)
+                    hipLaunchKernelGGL((prefill_mfma_bf16_d128<1, 2, 4>), grid, dim3(256), 0, stream, a);
+                else
+                    hipLaunchKernelGGL((prefill_mfma_bf16_d128<1, 1, 8>), grid, dim3(512), 0, stream, a);
+            }
             return hipGetLastError();
         }
     }
