@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the CPU oracle sample")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch steps one by one instead of replaying a HIP graph (for profilers)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain copy kernel of known size (HBM counter calibration)")
     return ap.parse_args()
@@ -71,10 +73,27 @@ def upload_cache(torch, spec, synth, tid, tokens, chunk=1 << 16):
     return out
 
 
+EAGER = False
+
+
 def graph_time(torch, fn, steps, warmup):
     """Capture `warmup` and `steps` calls of fn(i) into two graphs; replay the
-    warmup graph, then time the steps graph with events. Returns seconds/step."""
+    warmup graph, then time the steps graph with events. Returns seconds/step.
+    With --eager the same calls are launched one by one instead."""
     stream = torch.cuda.Stream()
+    if EAGER:
+        with torch.cuda.stream(stream):
+            for i in range(warmup):
+                fn(i)
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(steps):
+                fn(i)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / steps
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
         for i in range(2):  # eager warm calls before capture
@@ -325,6 +344,8 @@ def calibrate_copy(torch):
 
 def main():
     args = parse()
+    global EAGER
+    EAGER = args.eager
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported by this build "
               "(the decode and prefill paths are single-GPU kernels).", file=sys.stderr)

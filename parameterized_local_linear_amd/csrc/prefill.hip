@@ -16,10 +16,6 @@
 #include "plx_internal.h"
 #include "plx_device.h"
 
-#include <stdio.h>
-#include <stdlib.h>
-
-#include <type_traits>
 
 namespace plx {
 
@@ -156,45 +152,50 @@ __global__ __launch_bounds__(64) void prefill_generic(PrefillArgs a) {
 // -------------------------------------------------------------------------
 // MFMA prefill, bf16, head_dim 128.
 //
-// Workgroup: NW waves over one (sequence, KV head, group of HPW query heads,
-// q-tile of 16 * QB * NW / HPW rows per head); each wave owns QB blocks of
-// 16 query rows of one head. Every query head of the workgroup reads the
-// same KV head, so one K/V tile in LDS feeds all the waves.
+// Workgroup: eight waves over one (sequence, KV head, group of HPW query
+// heads, q-tile of 128 / HPW rows per head); each wave owns 16 query rows of
+// one head. Every query head of the workgroup reads the same KV head, so one
+// K/V tile in LDS feeds all eight waves.
 //
-// K/V tiles of 64 keys are copied global -> registers -> LDS, double
-// buffered: the next tile's global loads are issued before the current tile
-// is consumed. LDS rows are 256 bytes, with 16-byte chunk c of key k stored
-// at chunk slot c ^ (k & 15), which keeps every operand read below free of
-// bank conflicts.
+// K/V tiles of kPrefillKeys keys are copied by the buffer unit straight into
+// LDS (buffer_load ... lds), double buffered in two separate LDS arrays: the
+// next tile's copy is issued before the current tile is consumed and only
+// waited for at the end of the tile. LDS rows are 256 bytes, with 16-byte
+// chunk c of key k stored at chunk slot c ^ swz(k & 15),
+// swz(x) = 4 (x & 3) + (x >> 2): every group of eight lanes of an operand
+// read touches eight distinct 16-byte bank groups.
 //
-// Per 32-key sub-tile and 16-query block the wave computes, as in the decode
-// kernel but with query columns instead of head/probe columns:
+// Per 32-key sub-tile the wave computes, as in the decode kernel but with
+// query columns instead of head/probe columns:
 //   scores  Z^T[key, q] = K . Q^T,  S^T[key, q] = K . R^T   (16 MFMAs)
 //   readout A^T[d, q] += V^T . P^T, B^T[d, q] += V^T . (P o S')^T (16 MFMAs)
 // with the score MFMA's key order permuted so that lane (g, n) receives the
 // scores of query n for exactly the keys g + 4t it feeds the readout MFMA
-// (P never leaves registers), and V^T built by an in-register 8x8 transpose
-// of rows read from LDS. The K and V operands are read once per sub-tile and
-// shared by the wave's query blocks and by both score/readout pairs.
+// (P never leaves registers), and the V^T operand read from the row-major
+// LDS tile with gfx950's transposing LDS read (ds_read_b64_tr_b16).
 //
-// Causality: keys j <= i. Sub-tiles entirely above a wave's rows are
-// skipped, sub-tiles crossing the diagonal are masked. Work items run
-// heaviest-first (last q-tile first), and the group index varies fastest so
-// that all q-tiles of one (sequence, KV head) land on one XCD when the
-// number of groups is a multiple of 8 (its L2 then holds that head's K/V).
+// Causality: keys j <= i. Tiles entirely above a wave's rows are skipped,
+// tiles crossing its diagonal are masked. Work items run heaviest-first
+// (last q-tile first), and the group index varies fastest so that all
+// q-tiles of one (sequence, KV head) land on one XCD when the number of
+// groups is a multiple of 8 (its L2 then holds that head's K/V).
 // -------------------------------------------------------------------------
-constexpr int kPrefillKeys = 64;  // keys per LDS tile
+constexpr int kPrefillKeys = 128;  // keys per LDS tile
+constexpr int kPrefillWaves = 8;
 
-template <int HPW, int QB, int NW>
-__global__ __launch_bounds__(64 * NW) void prefill_mfma_bf16_d128(PrefillArgs a) {
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+template <int HPW>
+__global__ __launch_bounds__(64 * kPrefillWaves) void prefill_mfma_bf16_d128(PrefillArgs a) {
     constexpr int D = 128;
+    constexpr int NW = kPrefillWaves;
     constexpr int WPH = NW / HPW;       // waves per head
-    constexpr int RW = 16 * QB;         // rows per wave
-    constexpr int RPH = RW * WPH;       // rows per head per work item
+    constexpr int RPH = 16 * WPH;       // rows per head per work item
     constexpr int TK = kPrefillKeys;
-    constexpr int NT = 64 * NW;         // threads
-    constexpr int LOADS = TK * 16 / NT; // 16-byte chunks of K (and of V) per thread per tile
-    static_assert(NW % HPW == 0 && LOADS >= 1, "bad workgroup shape");
+    constexpr int NSUB = TK / 32;       // sub-tiles per tile
+    constexpr int DMA = TK / (4 * NW);  // 1 KB copies (4 keys) of K, and of V, per wave per tile
+    static_assert(NW % HPW == 0 && DMA >= 1, "bad workgroup shape");
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int n = lane & 15;
@@ -212,7 +213,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_mfma_bf16_d128(PrefillArgs a)
     const int hkv = (grp / hgroups) % a.Hkv;
     const int hsub = grp % hgroups;
     const int hq = hkv * G + hsub * HPW + wave / WPH;
-    const int q0 = qt * RPH + (wave % WPH) * RW;    // this wave's first row
+    const int q0 = qt * RPH + (wave % WPH) * 16;    // this wave's first row
     const int kend = min(a.L, (qt + 1) * RPH);      // keys the workgroup needs
     const int ntiles = (kend + TK - 1) / TK;
 
@@ -225,229 +226,222 @@ __global__ __launch_bounds__(64 * NW) void prefill_mfma_bf16_d128(PrefillArgs a)
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(reinterpret_cast<const uint16_t *>(a.v) + kvbase), 0, kvbytes, kBufferFlags);
 
-    // ---- LDS: two K/V tiles
-    __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][TK * D];
-    __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][TK * D];
-    // loader: thread handles chunk tc of keys tk + (NT / 16) * j
-    const int tk = threadIdx.x >> 4, tc = threadIdx.x & 15;
-    u32x4 stage_k[LOADS], stage_v[LOADS];
-    auto global_tile = [&](int tile) {
+    // ---- LDS: two K/V tiles in separate arrays (so that the compiler waits
+    // for a tile's copy only where that tile is read)
+    __shared__ __attribute__((aligned(16))) uint16_t lds_k0[TK * D], lds_v0[TK * D];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_k1[TK * D], lds_v1[TK * D];
+    auto swz = [](int key) { return ((key & 3) << 2) | ((key >> 2) & 3); };
+    // copy j of this wave: keys 4 (wave * DMA + j) + lane / 16; lane writes LDS
+    // slot lane % 16 of its key, i.e. fetches chunk (lane % 16) ^ swz(key)
+    auto dma_tile = [&](int tile, uint16_t *lk, uint16_t *lv) __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < LOADS; ++j) {
-            const int key = tile * TK + tk + (NT / 16) * j;
-            const int off = (key * D + tc * 8) * 2;
-            stage_k[j] = buffer_load16_cached(krs, off);
-            stage_v[j] = buffer_load16_cached(vrs, off);
+        for (int j = 0; j < DMA; ++j) {
+            const int kloc = 4 * (wave * DMA + j);
+            const int key = kloc + (lane >> 4);
+            const int chunk = (lane & 15) ^ swz(key);
+            const int off = ((tile * TK + key) * D + chunk * 8) * 2;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void *)(lk + kloc * D), 16, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void *)(lv + kloc * D), 16, off, 0, 0, 0);
         }
     };
-    auto lds_store = [&](int buf) {
-#pragma unroll
-        for (int j = 0; j < LOADS; ++j) {
-            const int key = tk + (NT / 16) * j;
-            const int slot = key * D + ((tc ^ (key & 15)) * 8);
-            *reinterpret_cast<u32x4 *>(&lds_k[buf][slot]) = stage_k[j];
-            *reinterpret_cast<u32x4 *>(&lds_v[buf][slot]) = stage_v[j];
-        }
-    };
-    global_tile(0);
+    dma_tile(0, lds_k0, lds_v0);
 
-    // ---- per-wave query operands: block qb, k-step u
-    bf16x8 qop[QB][4], rop[QB][4];
-    float piv[QB];
+    // ---- per-wave query operands (k-step u) and the row's pivot
+    bf16x8 qop[4], rop[4];
+    float piv;
     {
         const int64_t rowbase = ((int64_t)b * a.Hq + hq) * a.L;
+        const int row = min(q0 + n, a.L - 1);
+        const uint16_t *qp = qh + (rowbase + row) * D;
+        const uint16_t *rp = rh + (rowbase + row) * D;
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            const int row = min(q0 + 16 * qb + n, a.L - 1);
-            const uint16_t *qp = qh + (rowbase + row) * D;
-            const uint16_t *rp = rh + (rowbase + row) * D;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                qop[qb][u] = load16(qp + 8 * (g + 4 * u));
-                rop[qb][u] = load16(rp + 8 * (g + 4 * u));
-            }
+        for (int u = 0; u < 4; ++u) {
+            qop[u] = load16(qp + 8 * (g + 4 * u));
+            rop[u] = load16(rp + 8 * (g + 4 * u));
         }
         // pivot: probe score of key 0 for each query row
         const uint16_t *k0 = reinterpret_cast<const uint16_t *>(a.k) + kvbase;
-        float part[QB];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) part[qb] = 0.f;
+        float part = 0.f;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const bf16x8 kk = load16(k0 + 8 * (g + 4 * u));
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) part[qb] += (float)rop[qb][u][e] * (float)kk[e];
+            for (int e = 0; e < 8; ++e) part += (float)rop[u][e] * (float)kk[e];
         }
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) piv[qb] = xor_sum_rowgroups(part[qb]) * a.rk_scale;
+        piv = xor_sum_rowgroups(part) * a.rk_scale;
     }
 
-    float m_run[QB], lsA[QB], lsS[QB];
-    floatx4 accA[QB][8], accB[QB][8];
+    float m_run = -INFINITY, lsA = 0.f, lsS = 0.f;
+    floatx4 accA[8], accB[8];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        m_run[qb] = -INFINITY;
-        lsA[qb] = 0.f;
-        lsS[qb] = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            accA[qb][e] = floatx4{0.f, 0.f, 0.f, 0.f};
-            accB[qb][e] = floatx4{0.f, 0.f, 0.f, 0.f};
-        }
+    for (int e = 0; e < 8; ++e) {
+        accA[e] = floatx4{0.f, 0.f, 0.f, 0.f};
+        accB[e] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
-
     const int kperm = (n >> 2) + 4 * (n & 3);
-    const int q_last = q0 + RW - 1;
+    const int row = q0 + n;
+    const int q_last = q0 + 15;
 
-    // One 32-key sub-tile at key k0 from LDS buffer `buf` (local key offset kl).
-    auto subtile = [&](int buf, int kl, int k0, bool diag) {
-        // K operand: block kb, k-step u -> key kl + 16kb + kperm, chunk g + 4u
-        bf16x8 kop[2][4];
+    struct Scores {
+        floatx4 z0, z1, s0, s1;
+    };
+    struct Probs {
+        bf16x8 pa, ps;
+    };
+    struct KOp {
+        bf16x8 k[2][4];
+    };
+    struct VOp {
+        bf16x8 v[8];
+    };
+    // K operand of the 32-key sub-tile at local key kl: block kb, k-step u ->
+    // key kl + 16kb + kperm, chunk g + 4u
+    auto load_k = [&](const uint16_t *lk, int kl) __attribute__((always_inline)) {
+        KOp op;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             const int key = kl + 16 * kb + kperm;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int slot = key * D + (((g + 4 * u) ^ (key & 15)) * 8);
-                kop[kb][u] = *reinterpret_cast<const bf16x8 *>(&lds_k[buf][slot]);
-            }
+            for (int u = 0; u < 4; ++u)
+                op.k[kb][u] = *reinterpret_cast<const bf16x8 *>(&lk[key * D + (((g + 4 * u) ^ swz(key)) * 8)]);
         }
-        // V^T operand: rows key kl + g + 4t, chunk n, transposed in registers
-        bf16x8 vT[8];
-        {
-            bf16x8 vrow[8];
+        return op;
+    };
+    // V^T operand of readout block b (dims 16b .. 16b + 15), from LDS with the
+    // transposing 64-bit read: within each 16-lane row, lane j points at
+    // 4 dims of one key and lane i receives dim 16b + i of four keys. Lane
+    // (g, n) gets keys g + 4t (t = 0..7, two reads), the keys it feeds as
+    // element t of P in the score layout.
+    auto load_vT = [&](const uint16_t *lv, int kl) __attribute__((always_inline)) {
+        VOp op;
+        const int q4 = n >> 2, dq = n & 3;  // this lane points at key g + 4 (q4 + 4h), dims 4 dq ..
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const int key = kl + g + 4 * t;
-                const int slot = key * D + ((n ^ (key & 15)) * 8);
-                vrow[t] = *reinterpret_cast<const bf16x8 *>(&lds_v[buf][slot]);
+        for (int b = 0; b < 8; ++b) {
+            const int dim = 16 * b + 4 * dq;
+            v4i16 part[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int key = kl + g + 4 * (q4 + 4 * h);
+                const int addr = key * D + (((dim >> 3) ^ swz(key)) * 8) + (dim & 7);
+                part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) v4i16 *)(lv + addr));
             }
-#pragma unroll
-            for (int d2 = 0; d2 < 4; ++d2) {
-                uint32_t lo[4], hi[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t x = __builtin_bit_cast(uint4, vrow[2 * j])[d2];
-                    const uint32_t y = __builtin_bit_cast(uint4, vrow[2 * j + 1])[d2];
-                    lo[j] = __builtin_amdgcn_perm(y, x, 0x05040100u);
-                    hi[j] = __builtin_amdgcn_perm(y, x, 0x07060302u);
-                }
-                vT[2 * d2] = __builtin_bit_cast(bf16x8, uint4{lo[0], lo[1], lo[2], lo[3]});
-                vT[2 * d2 + 1] = __builtin_bit_cast(bf16x8, uint4{hi[0], hi[1], hi[2], hi[3]});
-            }
+            op.v[b] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
         }
+        return op;
+    };
+    auto scores = [&](const KOp &op) __attribute__((always_inline)) {
+        Scores sc;
+        sc.z0 = sc.z1 = sc.s0 = sc.s1 = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            floatx4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = z0, s0 = z0, s1 = z0;
+        for (int u = 0; u < 4; ++u) {
+            sc.z0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.k[0][u], qop[u], sc.z0, 0, 0, 0);
+            sc.z1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.k[1][u], qop[u], sc.z1, 0, 0, 0);
+            sc.s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.k[0][u], rop[u], sc.s0, 0, 0, 0);
+            sc.s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.k[1][u], rop[u], sc.s1, 0, 0, 0);
+        }
+        return sc;
+    };
+    auto pv = [&](const Probs &p, const VOp &vo) __attribute__((always_inline)) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                z0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[0][u], qop[qb][u], z0, 0, 0, 0);
-                z1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[1][u], qop[qb][u], z1, 0, 0, 0);
-                s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[0][u], rop[qb][u], s0, 0, 0, 0);
-                s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[1][u], rop[qb][u], s1, 0, 0, 0);
-            }
-            float zr[8], sr[8];
+        for (int e = 0; e < 8; ++e) {
+            accA[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vo.v[e], p.pa, accA[e], 0, 0, 0);
+            accB[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vo.v[e], p.ps, accB[e], 0, 0, 0);
+        }
+    };
+    // softmax update of the sub-tile at key k0: rescales the accumulators when
+    // the reference max is raised, returns the bf16 P and P o S' operands
+    auto softmax = [&](Scores sc, int k0, bool diag) __attribute__((always_inline)) {
+        float zr[8], sr[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                zr[i] = z0[i];
-                zr[4 + i] = z1[i];
-                sr[i] = s0[i];
-                sr[4 + i] = s1[i];
-            }
-            const int row = q0 + 16 * qb + n;
-            float rmax = -INFINITY;
+        for (int i = 0; i < 4; ++i) {
+            zr[i] = sc.z0[i];
+            zr[4 + i] = sc.z1[i];
+            sr[i] = sc.s0[i];
+            sr[4 + i] = sc.s1[i];
+        }
+        float rmax = -INFINITY;
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                if (diag && k0 + g + 4 * t > row) zr[t] = -INFINITY;
-                rmax = fmaxf(rmax, zr[t]);
-            }
-            const float tmax = xor_max_rowgroups(rmax) * a.zscale;
-            const bool raise = tmax > m_run[qb] + kRescaleSlack;
-            if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-                const float m_new = fmaxf(m_run[qb], tmax);
-                const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
-                m_run[qb] = m_new;
-                lsA[qb] *= alpha;
-                lsS[qb] *= alpha;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    accA[qb][e] *= alpha;
-                    accB[qb][e] *= alpha;
-                }
-            }
-            const float neg_m = -m_run[qb];
-            bf16x8 pa, ps;
-            float suma = 0.f, sums = 0.f;
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(zr[t], a.zscale, neg_m));
-                const float q = p * fmaf(sr[t], a.rk_scale, -piv[qb]);
-                suma += p;
-                sums += q;
-                pa[t] = (__bf16)p;
-                ps[t] = (__bf16)q;
-            }
-            lsA[qb] += suma;
-            lsS[qb] += sums;
+        for (int t = 0; t < 8; ++t) {
+            if (diag && k0 + g + 4 * t > row) zr[t] = -INFINITY;
+            rmax = fmaxf(rmax, zr[t]);
+        }
+        const float tmax = xor_max_rowgroups(rmax) * a.zscale;
+        const bool raise = tmax > m_run + kRescaleSlack;
+        if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+            const float m_new = fmaxf(m_run, tmax);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            lsA *= alpha;
+            lsS *= alpha;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                accA[qb][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vT[e], pa, accA[qb][e], 0, 0, 0);
-                accB[qb][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vT[e], ps, accB[qb][e], 0, 0, 0);
+                accA[e] *= alpha;
+                accB[e] *= alpha;
             }
         }
-    };
-
-    // One 64-key tile from LDS buffer BUF (compile-time, so every LDS
-    // address is a per-lane constant plus an immediate offset).
-    auto tile_step = [&](auto bufc, int tile) {
-        constexpr int BUF = decltype(bufc)::value;
-        if (tile + 1 < ntiles) global_tile(tile + 1);
+        const float neg_m = -m_run;
+        Probs pr;
+        float suma = 0.f, sums = 0.f;
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int k0 = tile * TK + 32 * half;
-            if (k0 <= q_last) {  // wave-uniform: sub-tiles above the wave's rows are skipped
-                if (k0 + 31 <= q0)
-                    subtile(BUF, 32 * half, k0, false);
-                else
-                    subtile(BUF, 32 * half, k0, true);
-            }
+        for (int t = 0; t < 8; ++t) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(zr[t], a.zscale, neg_m));
+            const float q = p * fmaf(sr[t], a.rk_scale, -piv);
+            suma += p;
+            sums += q;
+            pr.pa[t] = (__bf16)p;
+            pr.ps[t] = (__bf16)q;
         }
-        if (tile + 1 < ntiles) lds_store(BUF ^ 1);
-        __syncthreads();
+        lsA += suma;
+        lsS += sums;
+        return pr;
+    };
+    // one tile: its sub-tiles in order
+    auto tile_body = [&](const uint16_t *lk, const uint16_t *lv, int tile, bool diag) __attribute__((always_inline)) {
+        const int t0 = tile * TK;
+#pragma unroll
+        for (int j = 0; j < NSUB; ++j) {
+            const Probs p = softmax(scores(load_k(lk, 32 * j)), t0 + 32 * j, diag);
+            pv(p, load_vT(lv, 32 * j));
+        }
+    };
+    auto tile_step = [&](int tile, uint16_t *lk, uint16_t *lv, uint16_t *nk, uint16_t *nv) __attribute__((always_inline)) {
+        if (tile + 1 < ntiles) dma_tile(tile + 1, nk, nv);
+        const int t0 = tile * TK;
+        if (t0 <= q_last) {  // wave-uniform: tiles above the wave's rows are skipped
+            if (t0 + TK - 1 <= q0)
+                tile_body(lk, lv, tile, false);
+            else
+                tile_body(lk, lv, tile, true);
+        }
+        __syncthreads();  // waits for the next tile's copy, releases this buffer
     };
 
-    lds_store(0);
     __syncthreads();
     for (int tile = 0; tile < ntiles; tile += 2) {
-        tile_step(std::integral_constant<int, 0>{}, tile);
-        if (tile + 1 < ntiles) tile_step(std::integral_constant<int, 1>{}, tile + 1);
+        tile_step(tile, lds_k0, lds_v0, lds_k1, lds_v1);
+        if (tile + 1 < ntiles) tile_step(tile + 1, lds_k1, lds_v1, lds_k0, lds_v0);
     }
 
     // ---- epilogue: o = (A + B - (S / l) A) / l per row
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const float l = xor_sum_rowgroups(lsA[qb]);
-        const float S = xor_sum_rowgroups(lsS[qb]);
-        const int row = q0 + 16 * qb + n;
-        if (row >= a.L) continue;
+    const float l = xor_sum_rowgroups(lsA);
+    const float S = xor_sum_rowgroups(lsS);
+    if (row < a.L) {
         const float inv_l = 1.0f / l;
         const float cA = 1.0f - S * inv_l;
         const int64_t ro = ((int64_t)b * a.Hq + hq) * a.L + row;
-        uint16_t *o = reinterpret_cast<uint16_t *>(a.o) + ro * D + 32 * g;
+        // readout block b, accumulator element i holds dim 16b + 4g + i
+        uint16_t *o = reinterpret_cast<uint16_t *>(a.o) + ro * D + 4 * g;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float ov[8];
+        for (int b = 0; b < 8; ++b) {
+            float ov[4];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) ov[e] = (accA[qb][e][i] * cA + accB[qb][e][i]) * inv_l;
-            *reinterpret_cast<uint4 *>(o + 8 * i) =
-                uint4{pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3]), pack_bf16x2(ov[4], ov[5]),
-                      pack_bf16x2(ov[6], ov[7])};
+            for (int i = 0; i < 4; ++i) ov[i] = (accA[b][i] * cA + accB[b][i]) * inv_l;
+            *reinterpret_cast<uint2 *>(o + 16 * b) = uint2{pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3])};
         }
         if (g == 0) {
-            if (a.lse) a.lse[ro] = m_run[qb] * 0.6931471805599453f + logf(l);
-            if (a.sbar) a.sbar[ro] = S * inv_l + piv[qb];
+            if (a.lse) a.lse[ro] = m_run * 0.6931471805599453f + logf(l);
+            if (a.sbar) a.sbar[ro] = S * inv_l + piv;
         }
     }
 }
@@ -456,42 +450,18 @@ __global__ __launch_bounds__(64 * NW) void prefill_mfma_bf16_d128(PrefillArgs a)
 
 bool prefill_supported(int D, int dtype) { return (D == 64 || D == 128) && (dtype == 0 || dtype == 1); }
 
-// Workgroup shape of the MFMA prefill: QB query blocks of 16 rows per wave,
-// NW waves; selectable for measurement through PARALLAX_PREFILL_SHAPE
-// ("QB,NW"), default below.
-static int prefill_shape_qb = 0, prefill_shape_nw = 0;
-
 hipError_t launch_prefill(const PrefillArgs &a, int dtype, hipStream_t stream) {
     const int G = a.Hq / a.Hkv;
-    if (prefill_shape_qb == 0) {
-        prefill_shape_qb = 1;
-        prefill_shape_nw = 8;
-        if (const char *env = getenv("PARALLAX_PREFILL_SHAPE")) {
-            int qb = 0, nw = 0;
-            if (sscanf(env, "%d,%d", &qb, &nw) == 2 && ((qb == 2 && nw == 4) || (qb == 1 && nw == 8))) {
-                prefill_shape_qb = qb;
-                prefill_shape_nw = nw;
-            }
-        }
-    }
     if (dtype == 1 && a.D == 128 && (G % 2 == 0 || G == 1)) {
         const int hpw = (G % 2 == 0) ? 2 : 1;
-        const int rph = 16 * prefill_shape_qb * prefill_shape_nw / hpw;
+        const int rph = 16 * kPrefillWaves / hpw;
         const long items = (long)a.B * a.Hkv * (G / hpw) * ((a.L + rph - 1) / rph);
         if (items <= 0x7fffffffL) {
-            dim3 grid((unsigned)items);
-            const bool wide = prefill_shape_qb == 2;
-            if (hpw == 2) {
-                if (wide)
-                    hipLaunchKernelGGL((prefill_mfma_bf16_d128<2, 2, 4>), grid, dim3(256), 0, stream, a);
-                else
-                    hipLaunchKernelGGL((prefill_mfma_bf16_d128<2, 1, 8>), grid, dim3(512), 0, stream, a);
-            } else {
-                if (wide)
-                    hipLaunchKernelGGL((prefill_mfma_bf16_d128<1, 2, 4>), grid, dim3(256), 0, stream, a);
-                else
-                    hipLaunchKernelGGL((prefill_mfma_bf16_d128<1, 1, 8>), grid, dim3(512), 0, stream, a);
-            }
+            dim3 grid((unsigned)items), block(64 * kPrefillWaves);
+            if (hpw == 2)
+                hipLaunchKernelGGL((prefill_mfma_bf16_d128<2>), grid, block, 0, stream, a);
+            else
+                hipLaunchKernelGGL((prefill_mfma_bf16_d128<1>), grid, block, 0, stream, a);
             return hipGetLastError();
         }
     }
