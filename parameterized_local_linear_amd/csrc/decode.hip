@@ -232,10 +232,11 @@ void decode_mfma_bf16_d128(DecodeArgs a) {
             if (tail && g + 4 * t >= nvalid) zr[t] = -INFINITY;
             rmax = fmaxf(rmax, zr[t]);
         }
-        const float tmax = xor_max_rowgroups(rmax) * a.zscale;
-        // lazy rescale, decided for the whole wave
-        const bool raise = tmax > m_run + kRescaleSlack;
+        // lazy rescale, decided for the whole wave from the lane-local max;
+        // the column max across the four rows is only taken when it is raised
+        const bool raise = rmax * a.zscale > m_run + kRescaleSlack;
         if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+            const float tmax = xor_max_rowgroups(rmax) * a.zscale;
             const float m_new = fmaxf(m_run, tmax);
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
             m_run = m_new;

@@ -366,9 +366,12 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_mfma_bf16_d128(Pre
             if (diag && k0 + g + 4 * t > row) zr[t] = -INFINITY;
             rmax = fmaxf(rmax, zr[t]);
         }
-        const float tmax = xor_max_rowgroups(rmax) * a.zscale;
-        const bool raise = tmax > m_run + kRescaleSlack;
+        // Lazy rescale: the lane-local max decides whether any logit of the
+        // column exceeds the reference by more than the slack; only then is
+        // the column max taken across the four rows.
+        const bool raise = rmax * a.zscale > m_run + kRescaleSlack;
         if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+            const float tmax = xor_max_rowgroups(rmax) * a.zscale;
             const float m_new = fmaxf(m_run, tmax);
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
             m_run = m_new;
