@@ -121,6 +121,26 @@ def graph_time(torch, fn, steps, warmup):
     return e0.elapsed_time(e1) * 1e-3 / steps
 
 
+def measured_traffic(workload_name, splits):
+    """HBM bytes per launch of the streaming kernel from the committed counter
+    summary, or None when the kernel sources changed since it was taken (or
+    it covers another workload / split plan)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "decode_long_bf16_hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if not rec["workload"].startswith(workload_name) or not rec["workload"].endswith(
+            f"{splits} splits"):
+        return None
+    h = hashlib.sha256()
+    for src in rec["sources"]:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["source_sha256"] else None
+
+
 def cpu_baseline_decode(oracle, q, r, kv_rows, spec, seconds):
     """Time the oracle on the full step (all heads, all keys), repeated to fill
     about `seconds` of wall time. Returns (us_per_step, repeats, threads)."""
@@ -223,7 +243,8 @@ def run_decode_workload(args, torch, plx, synth, oracle):
         "roofline": {"bound": "hbm", "kernel": "decode_mfma_bf16_d128 (streaming, split records)",
                      "achieved": round(kern_bytes / t_kern / 1e9, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(kern_bytes / t_kern / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": None, "avg_us": round(t_kern * 1e6, 3),
+                     "traffic": measured_traffic(spec.name, splits),
+                     "avg_us": round(t_kern * 1e6, 3),
                      "bytes_per_launch": kern_bytes},
     }
     if not args.no_cpu_baseline:
