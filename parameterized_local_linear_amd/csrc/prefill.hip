@@ -333,6 +333,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_mfma_bf16_d128(Pre
     auto scores = [&](const KOp &op) __attribute__((always_inline)) {
         Scores sc;
         sc.z0 = sc.z1 = sc.s0 = sc.s1 = floatx4{0.f, 0.f, 0.f, 0.f};
+        __builtin_amdgcn_s_setprio(1);  // matrix-core bursts go first; the other wave's VALU fills in
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             sc.z0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.k[0][u], qop[u], sc.z0, 0, 0, 0);
@@ -340,14 +341,17 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_mfma_bf16_d128(Pre
             sc.s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.k[0][u], rop[u], sc.s0, 0, 0, 0);
             sc.s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.k[1][u], rop[u], sc.s1, 0, 0, 0);
         }
+        __builtin_amdgcn_s_setprio(0);
         return sc;
     };
     auto pv = [&](const Probs &p, const VOp &vo) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             accA[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vo.v[e], p.pa, accA[e], 0, 0, 0);
             accB[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vo.v[e], p.ps, accB[e], 0, 0, 0);
         }
+        __builtin_amdgcn_s_setprio(0);
     };
     // softmax update of the sub-tile at key k0: rescales the accumulators when
     // the reference max is raised, returns the bf16 P and P o S' operands
