@@ -39,21 +39,48 @@ def build() -> str:
     return _LIB_PATH
 
 
+def _bind(path: str):
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
+    lib.oracle_decode.argtypes = [vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, dbl, dbl,
+                                  i64, vp, vp]
+    lib.oracle_decode.restype = i32
+    lib.oracle_prefill.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, dbl, dbl,
+                                   i64, vp, vp, vp, vp]
+    lib.oracle_prefill.restype = i32
+    return lib
+
+
 def _load():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB_PATH):
             raise RuntimeError(f"{_LIB_PATH} is not built; run __graft_entry__.build()")
-        lib = ctypes.CDLL(_LIB_PATH)
-        vp, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
-        lib.oracle_decode.argtypes = [vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, dbl, dbl,
-                                      i64, vp, vp]
-        lib.oracle_decode.restype = i32
-        lib.oracle_prefill.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, dbl, dbl,
-                                       i64, vp, vp, vp, vp]
-        lib.oracle_prefill.restype = i32
-        _lib = lib
+        _lib = _bind(_LIB_PATH)
     return _lib
+
+
+class _Using:
+    """Temporarily route decode()/prefill() through another build of oracle.c
+    (the mutation tests compile deliberately broken copies)."""
+
+    def __init__(self, path):
+        self.lib = _bind(path)
+
+    def __enter__(self):
+        global _lib
+        self.saved = _lib
+        _lib = self.lib
+        return self
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.saved
+        return False
+
+
+def using_library(path: str) -> _Using:
+    return _Using(path)
 
 
 def _dtype_of(a: np.ndarray) -> int:

@@ -1,0 +1,106 @@
+"""The pins must catch plausible mistakes in the oracle.
+
+Each case compiles a copy of oracle/oracle.c with one deliberate mistake (on
+the CPU, in a temporary directory), routes the oracle through it, and checks
+that at least one independent check rejects it. The checks are the ones the
+pins use: torch's float64 SDPA (r = 0, GQA, causal), numpy's weighted
+covariance, and the local-linear least-squares intercept.
+"""
+import math
+import os
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import softmax
+
+import oracle
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle",
+                   "oracle.c")
+
+MUTANTS = {
+    "dropped correction": ("o[d] += wj * vd + cj * vd;", "o[d] += wj * vd;"),
+    "wrong sign": ("o[d] += wj * vd + cj * vd;", "o[d] += wj * vd - cj * vd;"),
+    "not centred": ("double cj = z[j] * (s[j] - sb);", "double cj = z[j] * s[j];"),
+    "gqa index": ("int64_t hk = h / g;\n                size_t qo = ((size_t)b",
+                  "int64_t hk = h % Hkv;\n                size_t qo = ((size_t)b"),
+    "prefill gqa index": ("int64_t hk = h / g;\n                size_t qo = (((size_t)b",
+                          "int64_t hk = h % Hkv;\n                size_t qo = (((size_t)b"),
+    "causal off by one": ("i + 1, D, dtype", "i, D, dtype"),
+    "logit scale dropped": ("z[j] = tau * zq;", "z[j] = zq;"),
+    "keys and values swapped": ("double kd = elem(k, dtype, kb + d);",
+                                "double kd = elem(v, dtype, kb + d);"),
+    "sample covariance": ("z[j] /= l;", "z[j] /= (l - z[j] / l * 0.5);"),
+}
+
+
+def build_mutant(name, tmp):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, name
+    path = os.path.join(tmp, "oracle_mutant.c")
+    with open(path, "w") as f:
+        f.write(src.replace(old, new))
+    so = os.path.join(tmp, "liboracle_mutant.so")
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", path, "-o", so,
+                    "-lm"], check=True)
+    return so
+
+
+def independent_checks_pass():
+    """True if every independent check accepts the current oracle."""
+    g = np.random.default_rng(123)
+    ok = True
+    # r = 0 against SDPA, GQA 4:2 (decode)
+    B, Hq, Hkv, L, D = 2, 4, 2, 23, 8
+    q, k, v = g.standard_normal((B, Hq, D)), g.standard_normal((B, L, Hkv, D)), \
+        g.standard_normal((B, L, Hkv, D))
+    tau = 1 / math.sqrt(D)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[:, :, None], torch.from_numpy(np.ascontiguousarray(
+            k.transpose(0, 2, 1, 3))), torch.from_numpy(np.ascontiguousarray(
+                v.transpose(0, 2, 1, 3))), scale=tau, enable_gqa=True)[:, :, 0].numpy()
+    ok &= np.abs(oracle.decode(q, None, k, v, qk_scale=tau) - ref).max() < 1e-12
+    # causal prefill r = 0 against SDPA with GQA
+    Q, K, V = g.standard_normal((1, 4, 19, D)), g.standard_normal((1, 2, 19, D)), \
+        g.standard_normal((1, 2, 19, D))
+    refp = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(Q), torch.from_numpy(K), torch.from_numpy(V), is_causal=True,
+        enable_gqa=True).numpy()
+    ok &= np.abs(oracle.prefill(Q, np.zeros_like(Q), K, V) - refp).max() < 1e-12
+    # correction = weighted covariance
+    L, D = 30, 5
+    q1, r1 = g.standard_normal((1, 1, D)), g.standard_normal((1, 1, D))
+    k1, v1 = g.standard_normal((1, L, 1, D)), g.standard_normal((1, L, 1, D))
+    w = softmax((k1[0, :, 0] @ q1[0, 0]) / math.sqrt(D))
+    s = k1[0, :, 0] @ r1[0, 0]
+    cov = np.array([np.cov(s, v1[0, :, 0, d], aweights=w, bias=True)[0, 1] for d in range(D)])
+    o = oracle.decode(q1, r1, k1, v1)[0, 0]
+    ok &= np.abs(o - (w @ v1[0, :, 0] + cov)).max() < 1e-12
+    # local-linear intercept
+    L, D = 50, 3
+    q2, k2 = g.standard_normal((1, 1, D)), g.standard_normal((1, L, 1, D))
+    v2 = g.standard_normal((1, L, 1, D)) + k2 @ g.standard_normal((D, D))
+    K2, V2 = k2[0, :, 0], v2[0, :, 0]
+    w2 = softmax(0.5 * (K2 @ q2[0, 0]))
+    rv = np.linalg.solve(np.cov(K2.T, aweights=w2, bias=True), q2[0, 0] - w2 @ K2)
+    X = np.concatenate([np.ones((L, 1)), K2 - q2[0, 0]], axis=1)
+    coef, *_ = np.linalg.lstsq(np.sqrt(w2)[:, None] * X, np.sqrt(w2)[:, None] * V2, rcond=None)
+    ok &= np.abs(oracle.decode(q2, rv[None, None], k2, v2, qk_scale=0.5)[0, 0] - coef[0]).max() \
+        < 1e-10
+    return bool(ok)
+
+
+def test_unmutated_oracle_passes_the_checks():
+    assert independent_checks_pass()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    with tempfile.TemporaryDirectory() as tmp:
+        so = build_mutant(name, tmp)
+        with oracle.using_library(so):
+            assert not independent_checks_pass(), f"mutant '{name}' passed every check"
