@@ -12,7 +12,11 @@ the mathematics fix: r = 0 against torch's float64 scaled_dot_product_attention,
 the correction against numpy's weighted covariance and against the
 cross-covariance matrix route, the plus sign against the intercept of a
 weighted least-squares fit, closed forms for one and two keys, shift and
-linearity invariants, and a 50-digit mpmath evaluation on tiny inputs.
+linearity invariants, and a 50-digit mpmath evaluation on tiny inputs. The
+gradients (tests/test_oracle_backward_pins.py) are pinned by central finite
+differences of the pinned forward, torch's float64 autograd through
+scaled_dot_product_attention at r = 0, and exact identities of the forward
+(key-shift invariance, linearity in v, the probe-scale derivative).
 """
 from __future__ import annotations
 
@@ -48,6 +52,9 @@ def _bind(path: str):
     lib.oracle_prefill.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, dbl, dbl,
                                    i64, vp, vp, vp, vp]
     lib.oracle_prefill.restype = i32
+    lib.oracle_prefill_backward.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                            dbl, dbl, i64, vp, vp, vp, vp, vp]
+    lib.oracle_prefill_backward.restype = i32
     return lib
 
 
@@ -172,3 +179,40 @@ def prefill(q, r, k, v, *, qk_scale=None, rk_scale=1.0, rows=None, stats=False):
     if rc != 0:
         raise RuntimeError(f"oracle_prefill failed ({rc})")
     return (out, lse, sbar) if stats else out
+
+
+def prefill_backward(q, r, k, v, do, *, qk_scale=None, rk_scale=1.0, units=None):
+    """Gradients of the causal Parallax prefill for the upstream gradient ``do``.
+
+    q, r, do: [B, Hq, L, D] (r may be None: r = 0); k, v: [B, Hkv, L, D].
+    units: optional int array [n, 2] of (b, hkv): only the query heads reading
+    those KV heads (and those KV heads' keys) are differentiated.
+    Returns float64 (dq, dr, dk, dv): [B, Hq, L, D] and [B, Hkv, L, D], or with
+    ``units`` [n, g, L, D] and [n, L, D].
+    """
+    dt = _dtype_of(q)
+    for a in (q, r, k, v, do):
+        if a is not None:
+            assert _dtype_of(a) == dt and a.flags.c_contiguous
+    B, Hq, L, D = q.shape
+    Hkv = k.shape[1]
+    g = Hq // Hkv
+    tau = 1.0 / math.sqrt(D) if qk_scale is None else float(qk_scale)
+    if units is not None:
+        units = np.ascontiguousarray(units, dtype=np.int64).reshape(-1, 2)
+        n = units.shape[0]
+    else:
+        n = B * Hkv
+    dq = np.empty((n, g, L, D), dtype=np.float64)
+    dr = np.empty((n, g, L, D), dtype=np.float64)
+    dk = np.empty((n, L, D), dtype=np.float64)
+    dv = np.empty((n, L, D), dtype=np.float64)
+    rc = _load().oracle_prefill_backward(_ptr(q), _ptr(r), _ptr(k), _ptr(v), _ptr(do), dt, B, Hq,
+                                         Hkv, L, D, tau, float(rk_scale), n, _ptr(units),
+                                         _ptr(dq), _ptr(dr), _ptr(dk), _ptr(dv))
+    if rc != 0:
+        raise RuntimeError(f"oracle_prefill_backward failed ({rc})")
+    if units is None:
+        return (dq.reshape(B, Hq, L, D), dr.reshape(B, Hq, L, D), dk.reshape(B, Hkv, L, D),
+                dv.reshape(B, Hkv, L, D))
+    return dq, dr, dk, dv

@@ -32,6 +32,7 @@
  * gives o = 0, lse = -inf, sbar = 0.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -205,6 +206,156 @@ int oracle_prefill(const void *q, const void *r, const void *k, const void *v, i
         }
         free(z);
         free(s);
+    }
+    return bad ? 2 : 0;
+}
+
+/*
+ * Gradients of the causal prefill (PyPI README of parallax-kernel, "Training
+ * (Triton)": o = parallax_func(q, r, k, v) is differentiated by autograd;
+ * the "Helion" section holds the four gradients to the same 1e-2 tolerance
+ * as the output). Given go = dLoss/do, returns dLoss/dq, dr, dk, dv.
+ *
+ * Plain reverse-mode differentiation of one_row's steps, taken in reverse
+ * order for every row: the readout o = sum w (1 + s - sbar) v, the mean
+ * sbar = sum w s, the probe scores s = rho r.k, the softmax w = softmax(z),
+ * the logits z = tau q.k. Each adjoint is the transpose of its own step;
+ * no identity beyond the softmax Jacobian w_j (delta_jl - w_l) is used.
+ *
+ * Work unit: one (b, KV head); it owns every query row of the g query heads
+ * that read that KV head, so its dk / dv sums are complete within the unit.
+ * units: n_units (b, hkv) pairs, or NULL for all B * Hkv units in order.
+ * Outputs: dq, dr [n_units, g, L, D]; dk, dv [n_units, L, D]. r may be NULL
+ * (r = 0); dr is still the gradient at r = 0.
+ */
+static void row_backward(const void *q, const void *r, const void *k, const void *v,
+                         const void *go, size_t q_off, size_t kv_off, int64_t n, int D, int dtype,
+                         double tau, double rho, double *dq, double *dr, double *dk, double *dv,
+                         double *w, double *s, double *aw, double *as)
+{
+    /* forward steps: logits, probe scores, softmax, probe mean */
+    for (int64_t j = 0; j < n; ++j) {
+        size_t kb = kv_off + (size_t)j * D;
+        double zq = 0.0, sr = 0.0;
+        for (int d = 0; d < D; ++d) {
+            double kd = elem(k, dtype, kb + d);
+            zq += elem(q, dtype, q_off + d) * kd;
+            if (r)
+                sr += elem(r, dtype, q_off + d) * kd;
+        }
+        w[j] = tau * zq;
+        s[j] = r ? rho * sr : 0.0;
+    }
+    double m = w[0];
+    for (int64_t j = 1; j < n; ++j)
+        if (w[j] > m)
+            m = w[j];
+    double l = 0.0;
+    for (int64_t j = 0; j < n; ++j) {
+        w[j] = exp(w[j] - m);
+        l += w[j];
+    }
+    for (int64_t j = 0; j < n; ++j)
+        w[j] /= l;
+    double sb = 0.0;
+    for (int64_t j = 0; j < n; ++j)
+        sb += w[j] * s[j];
+
+    /* reverse of o = sum_j w_j v_j + sum_j w_j (s_j - sbar) v_j */
+    double a_sb = 0.0;
+    for (int64_t j = 0; j < n; ++j) {
+        size_t vb = kv_off + (size_t)j * D;
+        double t = 0.0;
+        for (int d = 0; d < D; ++d)
+            t += elem(go, dtype, q_off + d) * elem(v, dtype, vb + d);
+        aw[j] = (1.0 + s[j] - sb) * t;
+        as[j] = w[j] * t;
+        a_sb -= w[j] * t;
+        double cv = w[j] * (1.0 + s[j] - sb);
+        for (int d = 0; d < D; ++d)
+            dv[(size_t)j * D + d] += cv * elem(go, dtype, q_off + d);
+    }
+    /* reverse of sbar = sum_j w_j s_j */
+    for (int64_t j = 0; j < n; ++j) {
+        aw[j] += a_sb * s[j];
+        as[j] += a_sb * w[j];
+    }
+    /* reverse of w = softmax(z): a_z = w (a_w - <w, a_w>) (stored into aw) */
+    double waw = 0.0;
+    for (int64_t j = 0; j < n; ++j)
+        waw += w[j] * aw[j];
+    for (int64_t j = 0; j < n; ++j)
+        aw[j] = w[j] * (aw[j] - waw);
+    /* reverse of s_j = rho r.k_j and z_j = tau q.k_j */
+    for (int64_t j = 0; j < n; ++j) {
+        size_t kb = kv_off + (size_t)j * D;
+        double cz = tau * aw[j], cs = rho * as[j];
+        for (int d = 0; d < D; ++d) {
+            double kd = elem(k, dtype, kb + d);
+            dq[d] += cz * kd;
+            dr[d] += cs * kd;
+            dk[(size_t)j * D + d] += cz * elem(q, dtype, q_off + d) +
+                                     (r ? cs * elem(r, dtype, q_off + d) : 0.0);
+        }
+    }
+}
+
+int oracle_prefill_backward(const void *q, const void *r, const void *k, const void *v,
+                            const void *go, int dtype, int B, int Hq, int Hkv, int L, int D,
+                            double tau, double rho, int64_t n_units, const int64_t *units,
+                            double *dq, double *dr, double *dk, double *dv)
+{
+    if (Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || B <= 0 || L <= 0)
+        return 1;
+    int g = Hq / Hkv;
+    int64_t total = units ? n_units : (int64_t)B * Hkv;
+    size_t LD = (size_t)L * D;
+    int bad = 0;
+    for (int64_t u = 0; u < total && !bad; ++u) {
+        int64_t b = units ? units[2 * u] : u / Hkv;
+        int64_t hk = units ? units[2 * u + 1] : u % Hkv;
+        size_t kvo = ((size_t)b * Hkv + (size_t)hk) * LD;
+        double *dk_u = dk + (size_t)u * LD, *dv_u = dv + (size_t)u * LD;
+        memset(dk_u, 0, sizeof(double) * LD);
+        memset(dv_u, 0, sizeof(double) * LD);
+        int64_t nrows = (int64_t)g * L;
+#pragma omp parallel
+        {
+            /* per-thread key-gradient sums, added into the unit in thread order */
+            double *dk_t = (double *)calloc(LD, sizeof(double));
+            double *dv_t = (double *)calloc(LD, sizeof(double));
+            double *scr = (double *)malloc(sizeof(double) * 4 * (size_t)L);
+            if (!dk_t || !dv_t || !scr) {
+#pragma omp atomic write
+                bad = 1;
+            } else {
+#pragma omp for schedule(static, 1) /* fixed row-to-thread map: deterministic sums */
+                for (int64_t t = 0; t < nrows; ++t) {
+                    int64_t hs = t / L, i = L - 1 - t % L; /* longest rows first */
+                    int64_t h = hk * g + hs;
+                    size_t qo = (((size_t)b * Hq + (size_t)h) * L + (size_t)i) * D;
+                    size_t ro = (((size_t)u * g + (size_t)hs) * L + (size_t)i) * D;
+                    for (int d = 0; d < D; ++d) {
+                        dq[ro + d] = 0.0;
+                        dr[ro + d] = 0.0;
+                    }
+                    row_backward(q, r, k, v, go, qo, kvo, i + 1, D, dtype, tau, rho, dq + ro,
+                                 dr + ro, dk_t, dv_t, scr, scr + L, scr + 2 * (size_t)L,
+                                 scr + 3 * (size_t)L);
+                }
+#pragma omp for ordered schedule(static, 1)
+                for (int th = 0; th < omp_get_num_threads(); ++th) {
+#pragma omp ordered
+                    for (size_t e = 0; e < LD; ++e) {
+                        dk_u[e] += dk_t[e];
+                        dv_u[e] += dv_t[e];
+                    }
+                }
+            }
+            free(dk_t);
+            free(dv_t);
+            free(scr);
+        }
     }
     return bad ? 2 : 0;
 }

@@ -29,16 +29,29 @@ MUTANTS = {
                   "int64_t hk = h % Hkv;\n                size_t qo = ((size_t)b"),
     "prefill gqa index": ("int64_t hk = h / g;\n                size_t qo = (((size_t)b",
                           "int64_t hk = h % Hkv;\n                size_t qo = (((size_t)b"),
-    "causal off by one": ("i + 1, D, dtype", "i, D, dtype"),
+    "causal off by one": ("(size_t)D, i + 1, D, dtype", "(size_t)D, i, D, dtype"),
     "logit scale dropped": ("z[j] = tau * zq;", "z[j] = zq;"),
-    "keys and values swapped": ("double kd = elem(k, dtype, kb + d);",
-                                "double kd = elem(v, dtype, kb + d);"),
+    "keys and values swapped": (
+        "double kd = elem(k, dtype, kb + d);\n            zq += elem(q, dtype, q_off + d) * kd;"
+        "\n            if (r)\n                sr += elem(r, dtype, r_off",
+        "double kd = elem(v, dtype, kb + d);\n            zq += elem(q, dtype, q_off + d) * kd;"
+        "\n            if (r)\n                sr += elem(r, dtype, r_off"),
     "sample covariance": ("z[j] /= l;", "z[j] /= (l - z[j] / l * 0.5);"),
+}
+
+# mistakes in the reverse pass (the forward code is untouched)
+BACKWARD_MUTANTS = {
+    "bwd sbar adjoint dropped": ("a_sb -= w[j] * t;", "a_sb -= 0.0 * t;"),
+    "bwd softmax jacobian sign": ("aw[j] = w[j] * (aw[j] - waw);", "aw[j] = w[j] * (aw[j] + waw);"),
+    "bwd causal off by one": ("kvo, i + 1, D, dtype, tau", "kvo, i, D, dtype, tau"),
+    "bwd probe adjoint uses q": ("cs * elem(r, dtype, q_off + d)", "cs * elem(q, dtype, q_off + d)"),
+    "bwd dv without correction": ("double cv = w[j] * (1.0 + s[j] - sb);", "double cv = w[j];"),
+    "bwd dq misses tau": ("double cz = tau * aw[j], cs", "double cz = aw[j], cs"),
 }
 
 
 def build_mutant(name, tmp):
-    old, new = MUTANTS[name]
+    old, new = {**MUTANTS, **BACKWARD_MUTANTS}[name]
     src = open(SRC).read()
     assert src.count(old) == 1, name
     path = os.path.join(tmp, "oracle_mutant.c")
@@ -104,3 +117,47 @@ def test_mutant_is_caught(name):
         so = build_mutant(name, tmp)
         with oracle.using_library(so):
             assert not independent_checks_pass(), f"mutant '{name}' passed every check"
+
+
+def backward_checks_pass():
+    """True if the oracle's gradients pass finite differences of its forward
+    (tiny GQA case) and torch's float64 autograd of causal SDPA at r = 0."""
+    g = np.random.default_rng(321)
+    Hq, Hkv, L, D = 2, 1, 5, 3
+    q, r, do = (g.standard_normal((1, Hq, L, D)) for _ in range(3))
+    k, v = (g.standard_normal((1, Hkv, L, D)) for _ in range(2))
+    grads = dict(zip("qrkv", oracle.prefill_backward(q, r, k, v, do, rk_scale=1.2)))
+    args = dict(q=q, r=r, k=k, v=v)
+    h = 1e-6
+    for name in "qrkv":
+        x = args[name]
+        for idx in np.ndindex(x.shape):
+            a = dict(args)
+            xp = x.copy(); xp[idx] += h
+            xm = x.copy(); xm[idx] -= h
+            a[name] = xp
+            lp = (oracle.prefill(a["q"], a["r"], a["k"], a["v"], rk_scale=1.2) * do).sum()
+            a[name] = xm
+            lm = (oracle.prefill(a["q"], a["r"], a["k"], a["v"], rk_scale=1.2) * do).sum()
+            if abs((lp - lm) / (2 * h) - grads[name][idx]) > 1e-6:
+                return False
+    tq, tk, tv = (torch.from_numpy(x.copy()).requires_grad_(True) for x in (q, k, v))
+    torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True,
+                                                     enable_gqa=True).backward(
+        torch.from_numpy(do))
+    dq, _, dk, dv = oracle.prefill_backward(q, np.zeros_like(q), k, v, do)
+    return bool(np.abs(dq - tq.grad.numpy()).max() < 1e-12
+                and np.abs(dk - tk.grad.numpy()).max() < 1e-12
+                and np.abs(dv - tv.grad.numpy()).max() < 1e-12)
+
+
+def test_unmutated_oracle_passes_the_backward_checks():
+    assert backward_checks_pass()
+
+
+@pytest.mark.parametrize("name", sorted(BACKWARD_MUTANTS))
+def test_backward_mutant_is_caught(name):
+    with tempfile.TemporaryDirectory() as tmp:
+        so = build_mutant(name, tmp)
+        with oracle.using_library(so):
+            assert not backward_checks_pass(), f"mutant '{name}' passed every check"
