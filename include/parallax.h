@@ -160,11 +160,40 @@ int parallax_decode_merge(const void *records, void *o, int B, int Hq, int D, in
  *   sbar    : NULL or DEVICE float [B, Hq, L]: sum_j w_j s_j
  *             (the row statistics a backward pass needs; not on the pages)
  *   D == 128 and dtype == PLX_BF16 run on bf16 MFMA with fp32 accumulation;
- *   other D in {64, 128} and PLX_F32 run on a plain fp32 kernel.
+ *   other D in {64, 128} and PLX_F32 run on a plain fp32 kernel. L <= 2^22.
  * ---------------------------------------------------------------------- */
 int parallax_prefill(const void *q, const void *r, const void *k, const void *v, void *o,
                      float *lse, float *sbar, int B, int Hq, int Hkv, int L, int D,
                      float qk_scale, float rk_scale, int dtype, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Backward of the causal prefill (PyPI README, "Training (Triton)": the
+ * output of parallax_func is differentiated with autograd; its "Helion"
+ * section holds the four gradients to the same tolerance as the output).
+ * Given d_o = dLoss/do, writes dq, dr, dk, dv for the forward
+ *   o_i = sum_{j<=i} w_ij (1 + s_ij - sbar_i) v_j,
+ *   w_i = softmax_j(qk_scale q_i.k_j), s_ij = rk_scale r_i.k_j.
+ * The attention weights are recomputed from the forward's lse; nothing of
+ * size L x L is stored.
+ *
+ *   q, r, o, d_o, dq, dr : [B, Hq, L, D]
+ *   k, v, dk, dv         : [B, Hkv, L, D]     (dk, dv sum over the Hq / Hkv
+ *                                              query heads of each KV head)
+ *   lse, sbar : DEVICE float [B, Hq, L], as written by parallax_prefill for
+ *               the same q, r, k, v, scales and dtype; o likewise.
+ *   workspace, workspace_bytes : DEVICE scratch of at least
+ *               parallax_prefill_backward_workspace_bytes(B, Hq, L) bytes
+ *               (16 bytes per query row).
+ *   Sizes, dtype and kernel choice as parallax_prefill (bf16 with D == 128
+ *   on MFMA); L <= 2^22. Gradients are written in dtype, computed in fp32.
+ * ---------------------------------------------------------------------- */
+size_t parallax_prefill_backward_workspace_bytes(int B, int Hq, int L);
+
+int parallax_prefill_backward(const void *q, const void *r, const void *k, const void *v,
+                              const void *o, const void *d_o, const float *lse,
+                              const float *sbar, void *dq, void *dr, void *dk, void *dv, int B,
+                              int Hq, int Hkv, int L, int D, float qk_scale, float rk_scale,
+                              int dtype, void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -10,8 +10,10 @@ Entry points mirror the C ABI (include/parallax.h):
   decode(q, r, k, v, ...)          Parallax decode, q/r [B, Hq, D] or [B, 1, Hq, D]
   softmax_decode(q, k, v, ...)     the same kernels with the probe path compiled out
   prefill(q, r, k, v, ...)         causal Parallax prefill on [B, H, L, D]
-and the pages' names ``parallax_decode`` and ``parallax_func`` alias decode
-and prefill.
+  prefill_backward(...)            its gradients dq, dr, dk, dv
+The pages' names: ``parallax_decode`` aliases decode, and ``parallax_func``
+is the prefill as a differentiable torch function (forward and backward on
+these kernels).
 """
 from __future__ import annotations
 
@@ -71,6 +73,10 @@ def lib() -> ctypes.CDLL:
         L.parallax_decode_partial.restype = i32
         L.parallax_decode_merge.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, vp]
         L.parallax_decode_merge.restype = i32
+        L.parallax_prefill_backward_workspace_bytes.argtypes = [i32, i32, i32]
+        L.parallax_prefill_backward_workspace_bytes.restype = sz
+        L.parallax_prefill_backward.argtypes = [vp] * 12 + [i32] * 5 + [f32, f32, i32, vp, sz, vp]
+        L.parallax_prefill_backward.restype = i32
         _lib = L
     return _lib
 
@@ -271,8 +277,67 @@ def prefill(q, r, k, v, qk_scale=None, rk_scale=1.0, *, out=None, return_stats=F
     return (out, lse, sbar) if return_stats else out
 
 
-parallax_decode = decode
-parallax_func = prefill
+def prefill_backward(q, r, k, v, o, d_o, lse, sbar, qk_scale=None, rk_scale=1.0, *,
+                     workspace=None):
+    """Gradients of the causal prefill: (dq, dr, dk, dv) for the upstream
+    gradient ``d_o``, from the forward's o, lse and sbar (prefill with
+    return_stats=True on the same inputs and scales)."""
+    L_ = lib()
+    B, Hq, L, D = q.shape
+    dev, dt = q.device, q.dtype
+    for t, name in ((q, "q"), (r, "r"), (k, "k"), (v, "v"), (o, "o"), (d_o, "d_o")):
+        _check(t, name, dt, dev)
+    for t, name in ((lse, "lse"), (sbar, "sbar")):
+        _check(t, name, torch.float32, dev)
+        if t.shape != (B, Hq, L):
+            raise ValueError(f"{name} must be float32 [B, Hq, L]")
+    if r.shape != q.shape or o.shape != q.shape or d_o.shape != q.shape:
+        raise ValueError("r, o and d_o must have q's shape")
+    if k.shape != v.shape or k.dim() != 4 or k.shape[0] != B or k.shape[2] != L or k.shape[3] != D:
+        raise ValueError("k, v must be [B, Hkv, L, D]")
+    Hkv = k.shape[1]
+    if qk_scale is None:
+        qk_scale = 1.0 / math.sqrt(D)
+    need = int(L_.parallax_prefill_backward_workspace_bytes(B, Hq, L))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    dq, dr = torch.empty_like(q), torch.empty_like(r)
+    dk, dv = torch.empty_like(k), torch.empty_like(v)
+    st = L_.parallax_prefill_backward(
+        _ptr(q), _ptr(r), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse), _ptr(sbar), _ptr(dq),
+        _ptr(dr), _ptr(dk), _ptr(dv), B, Hq, Hkv, L, D, float(qk_scale), float(rk_scale),
+        _dtype_code(q), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream_handle(dev))
+    if st != 0:
+        raise ParallaxError(st, "parallax_prefill_backward")
+    return dq, dr, dk, dv
 
-__all__ = ["decode", "softmax_decode", "prefill", "decode_partial", "decode_merge", "parallax_decode", "parallax_func",
-           "decode_workspace_bytes", "decode_num_splits", "lib", "ParallaxError", "LIB_PATH"]
+
+class _ParallaxFunction(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, r, k, v, qk_scale, rk_scale):
+        o, lse, sbar = prefill(q, r, k, v, qk_scale, rk_scale, return_stats=True)
+        ctx.save_for_backward(q, r, k, v, o, lse, sbar)
+        ctx.scales = (qk_scale, rk_scale)
+        return o
+
+    @staticmethod
+    def backward(ctx, d_o):
+        q, r, k, v, o, lse, sbar = ctx.saved_tensors
+        grads = prefill_backward(q, r, k, v, o, d_o.contiguous(), lse, sbar, *ctx.scales)
+        return (*grads, None, None)
+
+
+def parallax_func(q, r, k, v, qk_scale=None, rk_scale=1.0):
+    """Causal Parallax attention on [B, H, L, D] tensors, differentiable in
+    q, r, k and v (the pages' training entry point)."""
+    if torch.is_grad_enabled() and any(t.requires_grad for t in (q, r, k, v)):
+        return _ParallaxFunction.apply(q, r, k, v, qk_scale, rk_scale)
+    return prefill(q, r, k, v, qk_scale, rk_scale)
+
+
+parallax_decode = decode
+
+__all__ = ["decode", "softmax_decode", "prefill", "prefill_backward", "decode_partial",
+           "decode_merge", "parallax_decode", "parallax_func", "decode_workspace_bytes",
+           "decode_num_splits", "lib", "ParallaxError", "LIB_PATH"]

@@ -11,7 +11,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["api.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["api.hip", "decode.hip", "prefill.hip", "backward.hip"]
 LIB = os.path.join(HERE, "libparallax_hip.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

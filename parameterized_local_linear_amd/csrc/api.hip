@@ -75,6 +75,10 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int kv_len, int dtype, int
 
 using plx::DecodePlan;
 
+// Longest prefill sequence: the kernels address one head's [L, D] tensor
+// with 32-bit byte offsets.
+constexpr int kMaxPrefillLen = 1 << 22;
+
 static int check_decode_sizes(int B, int Hq, int Hkv, int D, int kv_len, int dtype) {
     if (B < 1 || Hq < 1 || Hkv < 1 || kv_len < 1) return PLX_ERR_INVALID_ARG;
     if (Hq % Hkv != 0) return PLX_ERR_INVALID_ARG;
@@ -224,7 +228,7 @@ int parallax_prefill(const void *q, const void *r, const void *k, const void *v,
     if (!isfinite(qk_scale) || !isfinite(rk_scale)) return PLX_ERR_INVALID_ARG;
     if (dtype != PLX_F32 && dtype != PLX_BF16) return PLX_ERR_UNSUPPORTED;
     if (!plx::prefill_supported(D, dtype)) return PLX_ERR_UNSUPPORTED;
-    if (B > 65535 || Hq > 65535) return PLX_ERR_UNSUPPORTED;
+    if (B > 65535 || Hq > 65535 || L > kMaxPrefillLen) return PLX_ERR_UNSUPPORTED;
     plx::PrefillArgs a;
     a.q = q;
     a.r = r;
@@ -241,6 +245,52 @@ int parallax_prefill(const void *q, const void *r, const void *k, const void *v,
     a.zscale = qk_scale * plx::kLog2e;
     a.rk_scale = rk_scale;
     hipError_t err = plx::launch_prefill(a, dtype, reinterpret_cast<hipStream_t>(stream));
+    return err == hipSuccess ? PLX_OK : PLX_ERR_HIP;
+}
+
+size_t parallax_prefill_backward_workspace_bytes(int B, int Hq, int L) {
+    if (B < 1 || Hq < 1 || L < 1) return 0;
+    return (size_t)B * Hq * L * sizeof(plx::RowStat);
+}
+
+int parallax_prefill_backward(const void *q, const void *r, const void *k, const void *v, const void *o,
+                              const void *d_o, const float *lse, const float *sbar, void *dq, void *dr,
+                              void *dk, void *dv, int B, int Hq, int Hkv, int L, int D, float qk_scale,
+                              float rk_scale, int dtype, void *workspace, size_t workspace_bytes,
+                              void *stream) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || L < 1 || D < 1) return PLX_ERR_INVALID_ARG;
+    if (Hq % Hkv != 0) return PLX_ERR_INVALID_ARG;
+    if (!q || !r || !k || !v || !o || !d_o || !lse || !sbar || !dq || !dr || !dk || !dv)
+        return PLX_ERR_INVALID_ARG;
+    if (!isfinite(qk_scale) || !isfinite(rk_scale)) return PLX_ERR_INVALID_ARG;
+    if (dtype != PLX_F32 && dtype != PLX_BF16) return PLX_ERR_UNSUPPORTED;
+    if (!plx::prefill_supported(D, dtype)) return PLX_ERR_UNSUPPORTED;
+    if (B > 65535 || Hq > 65535 || L > kMaxPrefillLen) return PLX_ERR_UNSUPPORTED;
+    if (!workspace || workspace_bytes < parallax_prefill_backward_workspace_bytes(B, Hq, L))
+        return PLX_ERR_WORKSPACE;
+    plx::BackwardArgs a;
+    a.q = q;
+    a.r = r;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.go = d_o;
+    a.lse = lse;
+    a.sbar = sbar;
+    a.dq = dq;
+    a.dr = dr;
+    a.dk = dk;
+    a.dv = dv;
+    a.rowstat = reinterpret_cast<plx::RowStat *>(workspace);
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.L = L;
+    a.D = D;
+    a.zscale = qk_scale * plx::kLog2e;
+    a.qk_scale = qk_scale;
+    a.rk_scale = rk_scale;
+    hipError_t err = plx::launch_prefill_backward(a, dtype, reinterpret_cast<hipStream_t>(stream));
     return err == hipSuccess ? PLX_OK : PLX_ERR_HIP;
 }
 

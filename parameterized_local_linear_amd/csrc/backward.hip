@@ -1,0 +1,670 @@
+// Parallax causal prefill backward (training) kernels for gfx950.
+//
+// The pages train through parallax_func with autograd (PyPI README of
+// parallax-kernel, "Training (Triton)"; its "Helion" section holds the output
+// and the four gradients to one tolerance) and print no gradient formula.
+// Differentiating the forward of one row (visible keys j <= i)
+//   w = softmax(z), z_j = qk_scale q.k_j, s_j = rk_scale r.k_j,
+//   sbar = sum_j w_j s_j, o = sum_j w_j c_j v_j with c_j = 1 + s_j - sbar,
+// for an upstream gradient g = dLoss/do gives, with u_j = g.v_j,
+// ubar = sum_j w_j u_j and delta = o.g (both per row):
+//   dv_j += w_j c_j g
+//   ds_j  = w_j (u_j - ubar)                          (adjoint of s_j)
+//   dz_j  = w_j (c_j u_j - ubar (s_j - sbar) - delta)  (adjoint of z_j)
+//   dq    = qk_scale sum_j dz_j k_j,   dr = rk_scale sum_j ds_j k_j
+//   dk_j += qk_scale dz_j q + rk_scale ds_j r
+// w_j is recomputed from the forward's lse: w_j = exp(z_j - lse).
+//
+// Two kernels, no atomics (results are bit-identical from call to call):
+//  - row pass, one query row per output row: a first sweep over the row's
+//    keys gives ubar, a second accumulates dq and dr; it also stores the
+//    row's {lse log2 e, sbar, delta, ubar} for the key pass.
+//  - key pass, one key per output row: sweeps every query row that sees the
+//    key, over all query heads of its KV head, and accumulates dk and dv.
+#include "plx_internal.h"
+#include "plx_device.h"
+
+namespace plx {
+
+namespace {
+
+template <typename T>
+struct Frag;
+template <>
+struct Frag<float> {
+    static constexpr int n = 4;
+    __device__ static void load(const float *p, float *out) {
+        float4 x = *reinterpret_cast<const float4 *>(p);
+        out[0] = x.x; out[1] = x.y; out[2] = x.z; out[3] = x.w;
+    }
+    __device__ static void store(float *p, const float *in) {
+        *reinterpret_cast<float4 *>(p) = float4{in[0], in[1], in[2], in[3]};
+    }
+};
+template <>
+struct Frag<uint16_t> {
+    static constexpr int n = 8;
+    __device__ static void load(const uint16_t *p, float *out) {
+        uint4 x = *reinterpret_cast<const uint4 *>(p);
+        const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+        for (int i = 0; i < 4; ++i) {
+            out[2 * i] = bf16_lo(w[i]);
+            out[2 * i + 1] = bf16_hi(w[i]);
+        }
+    }
+    __device__ static void store(uint16_t *p, const float *in) {
+        *reinterpret_cast<uint4 *>(p) = uint4{pack_bf16x2(in[0], in[1]), pack_bf16x2(in[2], in[3]),
+                                              pack_bf16x2(in[4], in[5]), pack_bf16x2(in[6], in[7])};
+    }
+};
+
+// Sum over the LPR lanes that share one row of a wave.
+template <int LPR>
+__device__ __forceinline__ float row_sum(float x) {
+    for (int off = 1; off < LPR; off <<= 1) x += __shfl_xor(x, off, LPR);
+    return x;
+}
+// Sum over the 64 / LPR rows of a wave (lanes c, c + LPR, ...).
+template <int LPR>
+__device__ __forceinline__ float across_rows(float x) {
+    for (int off = LPR; off < 64; off <<= 1) x += __shfl_xor(x, off);
+    return x;
+}
+
+// -------------------------------------------------------------------------
+// Generic kernels (any dtype, head_dim 64 or 128): one wave per output row;
+// each group of LPR lanes holds one key (row pass) or one query row (key
+// pass), 16 bytes of it per lane.
+// -------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(64) void bwd_rows_generic(BackwardArgs a) {
+    constexpr int EPL = Frag<T>::n;
+    constexpr int LPR = D / EPL;
+    constexpr int KPI = 64 / LPR;
+    const int lane = threadIdx.x;
+    const int kgrp = lane / LPR;
+    const int c = lane % LPR;
+    const int i = blockIdx.x;
+    const int hq = blockIdx.y;
+    const int b = blockIdx.z;
+    const int hkv = hq / (a.Hq / a.Hkv);
+    const int64_t row = ((int64_t)b * a.Hq + hq) * a.L + i;
+    const int64_t kvoff = ((int64_t)b * a.Hkv + hkv) * a.L * D + c * EPL;
+    const T *kb = reinterpret_cast<const T *>(a.k) + kvoff;
+    const T *vb = reinterpret_cast<const T *>(a.v) + kvoff;
+
+    float qv[EPL], rv[EPL], gv[EPL], ov[EPL];
+    Frag<T>::load(reinterpret_cast<const T *>(a.q) + row * D + c * EPL, qv);
+    Frag<T>::load(reinterpret_cast<const T *>(a.r) + row * D + c * EPL, rv);
+    Frag<T>::load(reinterpret_cast<const T *>(a.go) + row * D + c * EPL, gv);
+    Frag<T>::load(reinterpret_cast<const T *>(a.o) + row * D + c * EPL, ov);
+    float part = 0.f;
+    for (int e = 0; e < EPL; ++e) part += ov[e] * gv[e];
+    const float delta = row_sum<LPR>(part);
+    const float lse2 = a.lse[row] * kLog2e;
+    const float sb = a.sbar[row];
+    const int end = i + 1;
+
+    // sweep 1: ubar = sum_j w_j g.v_j
+    float ub = 0.f;
+    for (int j0 = 0; j0 < end; j0 += KPI) {
+        const int j = j0 + kgrp;
+        const int jj = j < end ? j : end - 1;
+        float kv[EPL], vv[EPL];
+        Frag<T>::load(kb + (int64_t)jj * D, kv);
+        Frag<T>::load(vb + (int64_t)jj * D, vv);
+        float zp = 0.f, up = 0.f;
+        for (int e = 0; e < EPL; ++e) {
+            zp += qv[e] * kv[e];
+            up += gv[e] * vv[e];
+        }
+        zp = row_sum<LPR>(zp);
+        up = row_sum<LPR>(up);
+        if (j < end) ub += __builtin_amdgcn_exp2f(fmaf(zp, a.zscale, -lse2)) * up;
+    }
+    ub = across_rows<LPR>(ub);
+
+    // sweep 2: dq, dr
+    float dqa[EPL], dra[EPL];
+    for (int e = 0; e < EPL; ++e) dqa[e] = dra[e] = 0.f;
+    for (int j0 = 0; j0 < end; j0 += KPI) {
+        const int j = j0 + kgrp;
+        const int jj = j < end ? j : end - 1;
+        float kv[EPL], vv[EPL];
+        Frag<T>::load(kb + (int64_t)jj * D, kv);
+        Frag<T>::load(vb + (int64_t)jj * D, vv);
+        float zp = 0.f, sp = 0.f, up = 0.f;
+        for (int e = 0; e < EPL; ++e) {
+            zp += qv[e] * kv[e];
+            sp += rv[e] * kv[e];
+            up += gv[e] * vv[e];
+        }
+        zp = row_sum<LPR>(zp);
+        sp = row_sum<LPR>(sp);
+        up = row_sum<LPR>(up);
+        const float w = j < end ? __builtin_amdgcn_exp2f(fmaf(zp, a.zscale, -lse2)) : 0.f;
+        const float sc = fmaf(sp, a.rk_scale, -sb);  // s_j - sbar
+        const float ds = w * (up - ub);
+        const float dz = w * (fmaf(sc, up, up) - fmaf(ub, sc, delta));
+        for (int e = 0; e < EPL; ++e) {
+            dqa[e] = fmaf(dz, kv[e], dqa[e]);
+            dra[e] = fmaf(ds, kv[e], dra[e]);
+        }
+    }
+    for (int e = 0; e < EPL; ++e) {
+        dqa[e] = across_rows<LPR>(dqa[e]) * a.qk_scale;
+        dra[e] = across_rows<LPR>(dra[e]) * a.rk_scale;
+    }
+    if (kgrp == 0) {
+        Frag<T>::store(reinterpret_cast<T *>(a.dq) + row * D + c * EPL, dqa);
+        Frag<T>::store(reinterpret_cast<T *>(a.dr) + row * D + c * EPL, dra);
+        if (c == 0) a.rowstat[row] = RowStat{lse2, sb, delta, ub};
+    }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(64) void bwd_keys_generic(BackwardArgs a) {
+    constexpr int EPL = Frag<T>::n;
+    constexpr int LPR = D / EPL;
+    constexpr int RPI = 64 / LPR;
+    const int lane = threadIdx.x;
+    const int rgrp = lane / LPR;
+    const int c = lane % LPR;
+    const int j = blockIdx.x;
+    const int hkv = blockIdx.y;
+    const int b = blockIdx.z;
+    const int G = a.Hq / a.Hkv;
+    const int64_t kvrow = ((int64_t)b * a.Hkv + hkv) * a.L + j;
+    float kv[EPL], vv[EPL], dka[EPL], dva[EPL];
+    Frag<T>::load(reinterpret_cast<const T *>(a.k) + kvrow * D + c * EPL, kv);
+    Frag<T>::load(reinterpret_cast<const T *>(a.v) + kvrow * D + c * EPL, vv);
+    for (int e = 0; e < EPL; ++e) dka[e] = dva[e] = 0.f;
+    for (int hs = 0; hs < G; ++hs) {
+        const int64_t rbase = ((int64_t)b * a.Hq + hkv * G + hs) * a.L;
+        for (int i0 = j; i0 < a.L; i0 += RPI) {
+            const int i = i0 + rgrp;
+            const int ii = i < a.L ? i : a.L - 1;
+            const int64_t row = rbase + ii;
+            float qv[EPL], rv[EPL], gv[EPL];
+            Frag<T>::load(reinterpret_cast<const T *>(a.q) + row * D + c * EPL, qv);
+            Frag<T>::load(reinterpret_cast<const T *>(a.r) + row * D + c * EPL, rv);
+            Frag<T>::load(reinterpret_cast<const T *>(a.go) + row * D + c * EPL, gv);
+            const RowStat st = a.rowstat[row];
+            float zp = 0.f, sp = 0.f, up = 0.f;
+            for (int e = 0; e < EPL; ++e) {
+                zp += qv[e] * kv[e];
+                sp += rv[e] * kv[e];
+                up += gv[e] * vv[e];
+            }
+            zp = row_sum<LPR>(zp);
+            sp = row_sum<LPR>(sp);
+            up = row_sum<LPR>(up);
+            const float w = i < a.L ? __builtin_amdgcn_exp2f(fmaf(zp, a.zscale, -st.lse2)) : 0.f;
+            const float sc = fmaf(sp, a.rk_scale, -st.sbar);
+            const float pv = w * (1.0f + sc);
+            const float ds = w * (up - st.ubar) * a.rk_scale;
+            const float dz = w * (fmaf(sc, up, up) - fmaf(st.ubar, sc, st.delta)) * a.qk_scale;
+            for (int e = 0; e < EPL; ++e) {
+                dva[e] = fmaf(pv, gv[e], dva[e]);
+                dka[e] = fmaf(dz, qv[e], fmaf(ds, rv[e], dka[e]));
+            }
+        }
+    }
+    for (int e = 0; e < EPL; ++e) {
+        dka[e] = across_rows<LPR>(dka[e]);
+        dva[e] = across_rows<LPR>(dva[e]);
+    }
+    if (rgrp == 0) {
+        Frag<T>::store(reinterpret_cast<T *>(a.dk) + kvrow * D + c * EPL, dka);
+        Frag<T>::store(reinterpret_cast<T *>(a.dv) + kvrow * D + c * EPL, dva);
+    }
+}
+
+// -------------------------------------------------------------------------
+// MFMA kernels, bf16, head_dim 128 (v_mfma_f32_16x16x32_bf16, fp32
+// accumulation). Operand layout of that instruction: lane l = 16 g + n holds
+// row n of A and column n of B, each with k = 8 g .. 8 g + 7 of the 32-wide
+// k step; the result lane holds column n, rows 4 g .. 4 g + 3.
+//
+// Tiles in LDS are row-major 256-byte rows (one key or one query row of 128
+// bf16) with 16-byte chunk c of row x stored at slot c ^ swz(x & 15),
+// swz(x) = 4 (x & 3) + (x >> 2), filled by the buffer unit directly
+// (buffer_load ... lds). Plain 16-byte reads of a row chunk and the
+// transposing 64-bit reads (ds_read_b64_tr_b16) both hit distinct banks.
+//
+// Permuted score rows: the score MFMA's A row m is loaded from tile row
+// (m >> 2) + 4 (m & 3) (+16 for the second 16-row block), so the result lane
+// (g, n) holds, as element t = 0..7 of the two blocks, tile rows g + 4 t:
+// exactly the k elements it supplies as the B operand of the next
+// contraction, whose A operand is read transposed at the same rows.
+// -------------------------------------------------------------------------
+constexpr int kBwdWaves = 8;
+constexpr int kBwdKeysPerTile = 128;  // row pass: keys per LDS tile
+constexpr int kBwdRowsPerTile = 64;   // key pass: query rows per LDS tile
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int tile_swz(int x) { return ((x & 3) << 2) | ((x >> 2) & 3); }
+
+// 16-byte chunk `chunk` of tile row x.
+__device__ __forceinline__ bf16x8 lds_chunk(const uint16_t *t, int x, int chunk) {
+    return *reinterpret_cast<const bf16x8 *>(&t[x * 128 + ((chunk ^ tile_swz(x)) * 8)]);
+}
+
+// Transposed operand of block `blk` (columns 16 blk .. 16 blk + 15 of the
+// tile) over tile rows x0 + g + 4 t, t = 0..7: lane (g, n) receives column
+// 16 blk + n of those eight rows. Within each 16-lane row of the wave, lane
+// j points at four columns 16 blk + 4 (j & 3) of row x0 + g + 4 ((j >> 2) + 4 h).
+__device__ __forceinline__ bf16x8 lds_transposed(const uint16_t *t, int x0, int blk, int g, int n) {
+    const int q4 = n >> 2, dq = n & 3;
+    const int col = 16 * blk + 4 * dq;
+    v4i16 part[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int x = x0 + g + 4 * (q4 + 4 * h);
+        const int addr = x * 128 + (((col >> 3) ^ tile_swz(x)) * 8) + (col & 7);
+        part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)(t + addr));
+    }
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Copy `nrows` rows (a multiple of 4 * kBwdWaves) starting at row `row0` of
+// the buffer behind `rs` into LDS tile `t`. Rows past the buffer's range
+// read as zeros.
+template <int NROWS>
+__device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t rs, int row0, uint16_t *t, int wave, int lane) {
+    constexpr int PER_WAVE = NROWS / (4 * kBwdWaves);
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+        const int xloc = 4 * (wave * PER_WAVE + j);
+        const int x = xloc + (lane >> 4);
+        const int chunk = (lane & 15) ^ tile_swz(x);
+        const int off = ((row0 + x) * 128 + chunk * 8) * 2;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(t + xloc * 128), 16, off, 0, 0, 0);
+    }
+}
+
+// ---- row pass: dq, dr and the row statistics --------------------------
+//
+// Workgroup: eight waves over one (sequence, KV head, group of HPW query
+// heads, q-tile); each wave owns 16 query rows of one head, as in the
+// forward kernel. K/V tiles of 128 keys are double buffered in LDS and swept
+// twice: first for ubar, then for dq and dr. Per 32-key sub-tile a wave runs
+//   sweep 1: Z^T = K Q^T, U^T = V G^T                        (16 MFMAs)
+//   sweep 2: Z^T, S^T = K R^T, U^T, then dQ^T += K^T dZ^T,
+//            dR^T += K^T dS^T with K^T read transposed       (40 MFMAs)
+template <int HPW>
+__global__ __launch_bounds__(64 * kBwdWaves) void bwd_rows_mfma_bf16_d128(BackwardArgs a) {
+    constexpr int D = 128;
+    constexpr int NW = kBwdWaves;
+    constexpr int WPH = NW / HPW;
+    constexpr int RPH = 16 * WPH;
+    constexpr int TK = kBwdKeysPerTile;
+    constexpr int NSUB = TK / 32;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int n = lane & 15;
+    const int g = lane >> 4;
+
+    const int G = a.Hq / a.Hkv;
+    const int hgroups = G / HPW;
+    const int NG = a.B * a.Hkv * hgroups;
+    const int QT = (a.L + RPH - 1) / RPH;
+    const int item = blockIdx.x;
+    const int grp = item % NG;
+    const int qt = QT - 1 - item / NG;
+    const int b = grp / (a.Hkv * hgroups);
+    const int hkv = (grp / hgroups) % a.Hkv;
+    const int hsub = grp % hgroups;
+    const int hq = hkv * G + hsub * HPW + wave / WPH;
+    const int q0 = qt * RPH + (wave % WPH) * 16;
+    const int kend = min(a.L, (qt + 1) * RPH);
+    const int ntiles = (kend + TK - 1) / TK;
+
+    const int64_t kvbase = ((int64_t)b * a.Hkv + hkv) * a.L * D;
+    const uint32_t kvbytes = (uint32_t)((int64_t)a.L * D * 2);
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(reinterpret_cast<const uint16_t *>(a.k) + kvbase), 0, kvbytes, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(reinterpret_cast<const uint16_t *>(a.v) + kvbase), 0, kvbytes, kBufferFlags);
+
+    __shared__ __attribute__((aligned(16))) uint16_t lds_k0[TK * D], lds_v0[TK * D];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_k1[TK * D], lds_v1[TK * D];
+    auto dma_tile = [&](int tile, uint16_t *lk, uint16_t *lv) __attribute__((always_inline)) {
+        dma_rows<TK>(krs, tile * TK, lk, wave, lane);
+        dma_rows<TK>(vrs, tile * TK, lv, wave, lane);
+    };
+    dma_tile(0, lds_k0, lds_v0);
+
+    // per-wave B operands (query row n, k step u -> chunk g + 4u) and row scalars
+    const int64_t rowbase = ((int64_t)b * a.Hq + hq) * a.L;
+    const int row = q0 + n;
+    const int rowc = min(row, a.L - 1);
+    bf16x8 qop[4], rop[4], gop[4];
+    float delta;
+    {
+        const uint16_t *qp = reinterpret_cast<const uint16_t *>(a.q) + (rowbase + rowc) * D;
+        const uint16_t *rp = reinterpret_cast<const uint16_t *>(a.r) + (rowbase + rowc) * D;
+        const uint16_t *gp = reinterpret_cast<const uint16_t *>(a.go) + (rowbase + rowc) * D;
+        const uint16_t *op = reinterpret_cast<const uint16_t *>(a.o) + (rowbase + rowc) * D;
+        float part = 0.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            qop[u] = load16(qp + 8 * (g + 4 * u));
+            rop[u] = load16(rp + 8 * (g + 4 * u));
+            gop[u] = load16(gp + 8 * (g + 4 * u));
+            const bf16x8 ov = load16(op + 8 * (g + 4 * u));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) part += (float)ov[e] * (float)gop[u][e];
+        }
+        delta = xor_sum_rowgroups(part);
+    }
+    const float lse2 = a.lse[rowbase + rowc] * kLog2e;
+    const float sb = a.sbar[rowbase + rowc];
+    const int kperm = (n >> 2) + 4 * (n & 3);
+    const int q_last = q0 + 15;
+
+    struct Frags {
+        bf16x8 x[2][4];
+    };
+    // A operand rows of a 32-key sub-tile at tile row kl: block kb, k step u
+    auto load_rows = [&](const uint16_t *t, int kl) __attribute__((always_inline)) {
+        Frags f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) f.x[kb][u] = lds_chunk(t, kl + 16 * kb + kperm, g + 4 * u);
+        return f;
+    };
+    auto contract = [&](const Frags &f, const bf16x8 *bop, floatx4 &c0, floatx4 &c1) __attribute__((always_inline)) {
+        c0 = c1 = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.x[0][u], bop[u], c0, 0, 0, 0);
+            c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.x[1][u], bop[u], c1, 0, 0, 0);
+        }
+    };
+    // the sweep over this wave's key tiles; body(lk, lv, kl, key0, diag)
+    auto sweep = [&](auto &&body) __attribute__((always_inline)) {
+        auto step = [&](int tile, uint16_t *lk, uint16_t *lv, uint16_t *nk, uint16_t *nv) __attribute__((always_inline)) {
+            if (tile + 1 < ntiles) dma_tile(tile + 1, nk, nv);
+            const int t0 = tile * TK;
+            if (t0 <= q_last) {
+                const bool diag = t0 + TK - 1 > q0;
+#pragma unroll
+                for (int j = 0; j < NSUB; ++j) body(lk, lv, 32 * j, t0 + 32 * j, diag);
+            }
+            __syncthreads();
+        };
+        __syncthreads();
+        for (int tile = 0; tile < ntiles; tile += 2) {
+            step(tile, lds_k0, lds_v0, lds_k1, lds_v1);
+            if (tile + 1 < ntiles) step(tile + 1, lds_k1, lds_v1, lds_k0, lds_v0);
+        }
+    };
+
+    // ---- sweep 1: ubar
+    float ub_part = 0.f;
+    sweep([&](const uint16_t *lk, const uint16_t *lv, int kl, int key0, bool diag) __attribute__((always_inline)) {
+        floatx4 z0, z1, u0, u1;
+        contract(load_rows(lk, kl), qop, z0, z1);
+        contract(load_rows(lv, kl), gop, u0, u1);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const float z = t < 4 ? z0[t] : z1[t - 4];
+            const float u = t < 4 ? u0[t] : u1[t - 4];
+            float w = __builtin_amdgcn_exp2f(fmaf(z, a.zscale, -lse2));
+            if (diag && key0 + g + 4 * t > row) w = 0.f;
+            ub_part = fmaf(w, u, ub_part);
+        }
+    });
+    const float ubar = xor_sum_rowgroups(ub_part);
+
+    // ---- sweep 2: dq, dr
+    floatx4 accQ[8], accR[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) accQ[e] = accR[e] = floatx4{0.f, 0.f, 0.f, 0.f};
+    dma_tile(0, lds_k0, lds_v0);
+    sweep([&](const uint16_t *lk, const uint16_t *lv, int kl, int key0, bool diag) __attribute__((always_inline)) {
+        floatx4 z0, z1, s0, s1, u0, u1;
+        {
+            const Frags kf = load_rows(lk, kl);
+            __builtin_amdgcn_s_setprio(1);
+            contract(kf, qop, z0, z1);
+            contract(kf, rop, s0, s1);
+            __builtin_amdgcn_s_setprio(0);
+        }
+        contract(load_rows(lv, kl), gop, u0, u1);
+        bf16x8 pz, ps;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const float z = t < 4 ? z0[t] : z1[t - 4];
+            const float s = t < 4 ? s0[t] : s1[t - 4];
+            const float u = t < 4 ? u0[t] : u1[t - 4];
+            float w = __builtin_amdgcn_exp2f(fmaf(z, a.zscale, -lse2));
+            if (diag && key0 + g + 4 * t > row) w = 0.f;
+            const float sc = fmaf(s, a.rk_scale, -sb);
+            pz[t] = (__bf16)(w * (fmaf(sc, u, u) - fmaf(ubar, sc, delta)));
+            ps[t] = (__bf16)(w * (u - ubar));
+        }
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const bf16x8 kt = lds_transposed(lk, kl, e, g, n);
+            accQ[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt, pz, accQ[e], 0, 0, 0);
+            accR[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt, ps, accR[e], 0, 0, 0);
+        }
+        __builtin_amdgcn_s_setprio(0);
+    });
+
+    if (row < a.L) {
+        // block e, accumulator element i holds dim 16 e + 4 g + i
+        uint16_t *dq = reinterpret_cast<uint16_t *>(a.dq) + (rowbase + row) * D + 4 * g;
+        uint16_t *dr = reinterpret_cast<uint16_t *>(a.dr) + (rowbase + row) * D + 4 * g;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const floatx4 x = accQ[e] * a.qk_scale;
+            const floatx4 y = accR[e] * a.rk_scale;
+            *reinterpret_cast<uint2 *>(dq + 16 * e) = uint2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+            *reinterpret_cast<uint2 *>(dr + 16 * e) = uint2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+        }
+        if (g == 0) a.rowstat[rowbase + row] = RowStat{lse2, sb, delta, ubar};
+    }
+}
+
+// ---- key pass: dk, dv ---------------------------------------------------
+//
+// Workgroup: eight waves over one (sequence, KV head, block of 128 keys);
+// wave w owns keys 16 w .. 16 w + 15 of the block, whose K and V stay in
+// registers as B operands. The query rows that see the block (rows >= its
+// first key) of every query head of the KV head stream through LDS in tiles
+// of 64 rows of Q, R and dLoss/do plus their row statistics, double
+// buffered. Per 32-row sub-tile a wave runs
+//   Z = Q K^T, S = R K^T, U = G V^T                      (24 MFMAs)
+//   dV^T += G^T P1, dK^T += Q^T dZ + R^T dS               (24 MFMAs)
+// with P1 = w c, dZ = qk_scale dz, dS = rk_scale ds in bf16 and the
+// transposed A operands read with ds_read_b64_tr_b16. Blocks run first key
+// block first (the longest), with the (sequence, KV head) index fastest so
+// that all blocks of one head share an XCD and its L2.
+__global__ __launch_bounds__(64 * kBwdWaves) void bwd_keys_mfma_bf16_d128(BackwardArgs a) {
+    constexpr int D = 128;
+    constexpr int NW = kBwdWaves;
+    constexpr int TR = kBwdRowsPerTile;
+    constexpr int KB = 16 * NW;  // keys per workgroup
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int n = lane & 15;
+    const int g = lane >> 4;
+
+    const int G = a.Hq / a.Hkv;
+    const int NG = a.B * a.Hkv;
+    const int grp = blockIdx.x % NG;
+    const int kblk = blockIdx.x / NG;
+    const int b = grp / a.Hkv;
+    const int hkv = grp % a.Hkv;
+    const int k0 = kblk * KB;
+    const int kw = k0 + 16 * wave;  // this wave's first key
+    const int key = kw + n;
+    const int nrt = (a.L - k0 + TR - 1) / TR;  // row tiles per query head
+    const int ntiles = G * nrt;
+
+    const int64_t kvbase = ((int64_t)b * a.Hkv + hkv) * a.L * D;
+    bf16x8 kop[4], vop[4];
+    {
+        const int kc = min(key, a.L - 1);
+        const uint16_t *kp = reinterpret_cast<const uint16_t *>(a.k) + kvbase + (int64_t)kc * D;
+        const uint16_t *vp = reinterpret_cast<const uint16_t *>(a.v) + kvbase + (int64_t)kc * D;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            kop[u] = load16(kp + 8 * (g + 4 * u));
+            vop[u] = load16(vp + 8 * (g + 4 * u));
+        }
+    }
+
+    __shared__ __attribute__((aligned(16))) uint16_t lq0[TR * D], lr0[TR * D], lg0[TR * D];
+    __shared__ __attribute__((aligned(16))) uint16_t lq1[TR * D], lr1[TR * D], lg1[TR * D];
+    __shared__ __attribute__((aligned(16))) RowStat ls0[TR], ls1[TR];
+    const uint32_t hbytes = (uint32_t)((int64_t)a.L * D * 2);
+    auto dma_tile = [&](int tile, uint16_t *tq, uint16_t *tr, uint16_t *tg, RowStat *ts) __attribute__((always_inline)) {
+        const int hq = hkv * G + tile / nrt;
+        const int r0 = k0 + (tile % nrt) * TR;
+        const int64_t rowbase = ((int64_t)b * a.Hq + hq) * a.L;
+        const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(reinterpret_cast<const uint16_t *>(a.q) + rowbase * D), 0, hbytes, kBufferFlags);
+        const __amdgpu_buffer_rsrc_t rrs = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(reinterpret_cast<const uint16_t *>(a.r) + rowbase * D), 0, hbytes, kBufferFlags);
+        const __amdgpu_buffer_rsrc_t grs = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(reinterpret_cast<const uint16_t *>(a.go) + rowbase * D), 0, hbytes, kBufferFlags);
+        dma_rows<TR>(qrs, r0, tq, wave, lane);
+        dma_rows<TR>(rrs, r0, tr, wave, lane);
+        dma_rows<TR>(grs, r0, tg, wave, lane);
+        if (wave == 0) {  // 64 rows x 16 bytes: one copy by one wave
+            const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(a.rowstat + rowbase), 0, (uint32_t)((int64_t)a.L * sizeof(RowStat)), kBufferFlags);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (lds_void *)ts, 16, (r0 + lane) * 16, 0, 0, 0);
+        }
+    };
+    dma_tile(0, lq0, lr0, lg0, ls0);
+
+    floatx4 accK[8], accV[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) accK[e] = accV[e] = floatx4{0.f, 0.f, 0.f, 0.f};
+    const int rperm = (n >> 2) + 4 * (n & 3);
+
+    // one 32-row sub-tile at tile row xl (global row rs)
+    auto sub_tile = [&](const uint16_t *tq, const uint16_t *tr, const uint16_t *tg, const RowStat *ts,
+                        int xl, int rs, bool mask) __attribute__((always_inline)) {
+        floatx4 z[2], s[2], uu[2];
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+            z[tb] = s[tb] = uu[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
+            const int x = xl + 16 * tb + rperm;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                z[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_chunk(tq, x, g + 4 * u), kop[u], z[tb], 0, 0, 0);
+                s[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_chunk(tr, x, g + 4 * u), kop[u], s[tb], 0, 0, 0);
+                uu[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_chunk(tg, x, g + 4 * u), vop[u], uu[tb], 0, 0, 0);
+            }
+        }
+        __builtin_amdgcn_s_setprio(0);
+        bf16x8 p1, pz, ps;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const RowStat st = ts[xl + g + 4 * t];
+            const float zz = z[t >> 2][t & 3], ss = s[t >> 2][t & 3], u = uu[t >> 2][t & 3];
+            float w = __builtin_amdgcn_exp2f(fmaf(zz, a.zscale, -st.lse2));
+            if (mask) {
+                const int rw = rs + g + 4 * t;
+                if (rw < key || rw >= a.L) w = 0.f;
+            }
+            const float sc = fmaf(ss, a.rk_scale, -st.sbar);
+            p1[t] = (__bf16)(w * (1.0f + sc));
+            pz[t] = (__bf16)(w * (fmaf(sc, u, u) - fmaf(st.ubar, sc, st.delta)) * a.qk_scale);
+            ps[t] = (__bf16)(w * (u - st.ubar) * a.rk_scale);
+        }
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            accV[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_transposed(tg, xl, e, g, n), p1, accV[e], 0, 0, 0);
+            accK[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_transposed(tq, xl, e, g, n), pz, accK[e], 0, 0, 0);
+            accK[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_transposed(tr, xl, e, g, n), ps, accK[e], 0, 0, 0);
+        }
+        __builtin_amdgcn_s_setprio(0);
+    };
+    auto step = [&](int tile, uint16_t *tq, uint16_t *tr, uint16_t *tg, RowStat *ts, uint16_t *nq,
+                    uint16_t *nr, uint16_t *ng, RowStat *ns) __attribute__((always_inline)) {
+        if (tile + 1 < ntiles) dma_tile(tile + 1, nq, nr, ng, ns);
+        const int r0 = k0 + (tile % nrt) * TR;
+#pragma unroll
+        for (int j = 0; j < TR / 32; ++j) {
+            const int rs = r0 + 32 * j;
+            if (rs + 31 >= kw) {  // wave-uniform: sub-tiles wholly above the wave's keys are skipped
+                const bool mask = rs < kw + 15 || rs + 31 >= a.L;
+                if (mask)
+                    sub_tile(tq, tr, tg, ts, 32 * j, rs, true);
+                else
+                    sub_tile(tq, tr, tg, ts, 32 * j, rs, false);
+            }
+        }
+        __syncthreads();
+    };
+    __syncthreads();
+    for (int tile = 0; tile < ntiles; tile += 2) {
+        step(tile, lq0, lr0, lg0, ls0, lq1, lr1, lg1, ls1);
+        if (tile + 1 < ntiles) step(tile + 1, lq1, lr1, lg1, ls1, lq0, lr0, lg0, ls0);
+    }
+
+    if (key < a.L) {
+        // block e, accumulator element i holds dim 16 e + 4 g + i of key n
+        uint16_t *dk = reinterpret_cast<uint16_t *>(a.dk) + kvbase + (int64_t)key * D + 4 * g;
+        uint16_t *dv = reinterpret_cast<uint16_t *>(a.dv) + kvbase + (int64_t)key * D + 4 * g;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            *reinterpret_cast<uint2 *>(dk + 16 * e) =
+                uint2{pack_bf16x2(accK[e][0], accK[e][1]), pack_bf16x2(accK[e][2], accK[e][3])};
+            *reinterpret_cast<uint2 *>(dv + 16 * e) =
+                uint2{pack_bf16x2(accV[e][0], accV[e][1]), pack_bf16x2(accV[e][2], accV[e][3])};
+        }
+    }
+}
+
+template <typename T, int D>
+hipError_t launch_generic(const BackwardArgs &a, hipStream_t stream) {
+    hipLaunchKernelGGL((bwd_rows_generic<T, D>), dim3(a.L, a.Hq, a.B), dim3(64), 0, stream, a);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((bwd_keys_generic<T, D>), dim3(a.L, a.Hkv, a.B), dim3(64), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill_backward(const BackwardArgs &a, int dtype, hipStream_t stream) {
+    const int G = a.Hq / a.Hkv;
+    if (dtype == 1 && a.D == 128 && (G % 2 == 0 || G == 1)) {
+        const int hpw = (G % 2 == 0) ? 2 : 1;
+        const int rph = 16 * kBwdWaves / hpw;
+        const long row_items = (long)a.B * a.Hkv * (G / hpw) * ((a.L + rph - 1) / rph);
+        const long key_items = (long)a.B * a.Hkv * ((a.L + 16 * kBwdWaves - 1) / (16 * kBwdWaves));
+        if (row_items <= 0x7fffffffL && key_items <= 0x7fffffffL) {
+            if (hpw == 2)
+                hipLaunchKernelGGL((bwd_rows_mfma_bf16_d128<2>), dim3((unsigned)row_items),
+                                   dim3(64 * kBwdWaves), 0, stream, a);
+            else
+                hipLaunchKernelGGL((bwd_rows_mfma_bf16_d128<1>), dim3((unsigned)row_items),
+                                   dim3(64 * kBwdWaves), 0, stream, a);
+            hipError_t err = hipGetLastError();
+            if (err != hipSuccess) return err;
+            hipLaunchKernelGGL(bwd_keys_mfma_bf16_d128, dim3((unsigned)key_items), dim3(64 * kBwdWaves), 0,
+                               stream, a);
+            return hipGetLastError();
+        }
+    }
+    if (dtype == 1)
+        return a.D == 64 ? launch_generic<uint16_t, 64>(a, stream) : launch_generic<uint16_t, 128>(a, stream);
+    return a.D == 64 ? launch_generic<float, 64>(a, stream) : launch_generic<float, 128>(a, stream);
+}
+
+}  // namespace plx

@@ -67,4 +67,22 @@ struct PrefillArgs {
 hipError_t launch_prefill(const PrefillArgs &a, int dtype, hipStream_t stream);
 bool prefill_supported(int D, int dtype);
 
+// Per-row statistics the backward's key pass reads, written by its row pass:
+// {lse * log2 e, sbar, delta = o . dLoss/do, ubar = sum_j w_j dLoss/do . v_j}.
+struct RowStat {
+    float lse2, sbar, delta, ubar;
+};
+
+struct BackwardArgs {
+    const void *q, *r, *k, *v, *o, *go;  // go: dLoss/do, layout of o
+    const float *lse, *sbar;             // the forward's row statistics
+    void *dq, *dr, *dk, *dv;
+    RowStat *rowstat;                    // workspace [B, Hq, L]
+    int B, Hq, Hkv, L, D;
+    float zscale;                        // qk_scale * log2(e)
+    float qk_scale, rk_scale;
+};
+
+hipError_t launch_prefill_backward(const BackwardArgs &a, int dtype, hipStream_t stream);
+
 }  // namespace plx

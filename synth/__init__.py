@@ -29,6 +29,7 @@ BF16 = 1
 BASE_SEED = 20261203
 # tensor ids inside one seed: one independent stream each
 TID_Q, TID_R, TID_K, TID_V, TID_SHIFT, TID_LENGTHS = 0, 1, 2, 3, 4, 5
+TID_DO = 6  # upstream gradient dLoss/do of the training backward
 
 
 def build() -> str:

@@ -100,3 +100,32 @@ def test_workspace_plan():
     assert 1 < s <= 32768 // 512
     s = ns(1, 16, 8, 64, 32768, 1, 0)
     assert 1 < s <= 32768 // 128
+
+
+def _backward(**kw):
+    a = dict(q=FAKE, r=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, sbar=FAKE, dq=FAKE,
+             dr=FAKE, dk=FAKE, dv=FAKE, B=1, Hq=4, Hkv=2, L=64, D=128, qk=0.1, rk=1.0, dt=1,
+             ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return plx.lib().parallax_prefill_backward(
+        a["q"], a["r"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["sbar"], a["dq"], a["dr"],
+        a["dk"], a["dv"], a["B"], a["Hq"], a["Hkv"], a["L"], a["D"], a["qk"], a["rk"], a["dt"],
+        a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), 1), (dict(L=0), 1), (dict(Hq=6, Hkv=4), 1), (dict(q=None), 1),
+    (dict(do=None), 1), (dict(lse=None), 1), (dict(sbar=None), 1), (dict(dk=None), 1),
+    (dict(D=96), 2), (dict(dt=3), 2), (dict(L=(1 << 22) + 1), 2), (dict(rk=float("nan")), 1),
+    (dict(), 3), (dict(ws=FAKE, wsb=4 * 64 * 16 - 1), 3),
+])
+def test_prefill_backward_rejects_on_host(kw, status):
+    # every case must fail validation: FAKE pointers may never reach a launch
+    assert status != 0
+    assert _backward(**kw) == status
+
+
+def test_prefill_backward_workspace_size():
+    f = plx.lib().parallax_prefill_backward_workspace_bytes
+    assert f(2, 16, 4096) == 2 * 16 * 4096 * 16
+    assert f(0, 16, 4096) == 0 and f(1, 1, 0) == 0
