@@ -16,7 +16,9 @@ Also measured in the same run:
   * softmax_decode on the same inputs (the cost of the correction branch);
   * the CPU oracle on the same inputs (cpu_baseline), on the host's cores.
 
-Other workloads (--workload varlen | large | prefill) print their own line.
+Other workloads (--workload varlen | large | prefill | backward) print their
+own line; backward times parallax_prefill_backward (row pass + key pass) on
+the causal-prefill shapes.
 Prints one JSON line on stdout.
 """
 from __future__ import annotations
@@ -45,7 +47,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="long", choices=["long", "varlen", "large", "prefill"])
+    ap.add_argument("--workload", default="long",
+                    choices=["long", "varlen", "large", "prefill", "backward"])
     ap.add_argument("--num-splits", type=int, default=0, help="0: library plan")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -353,6 +356,72 @@ def run_prefill_workload(args, torch, plx, synth, oracle):
     return res
 
 
+def run_backward_workload(args, torch, plx, synth, oracle):
+    spec = synth.prefill_spec(5)
+    B, Hq, Hkv, L, D = spec.B, spec.Hq, spec.Hkv, spec.L, spec.D
+    arrs = {}
+    for name, tid, H, sc in (("q", synth.TID_Q, Hq, spec.scale), ("r", synth.TID_R, Hq, spec.scale),
+                             ("k", synth.TID_K, Hkv, spec.scale), ("v", synth.TID_V, Hkv, spec.scale),
+                             ("do", synth.TID_DO, Hq, 1.0)):
+        arrs[name] = synth.normal(spec.seed, tid, (B, H, L, D), sc, spec.dtype)
+    t = {n: torch.from_numpy(a).view(torch.bfloat16).cuda() for n, a in arrs.items()}
+    o, lse, sbar = plx.prefill(t["q"], t["r"], t["k"], t["v"], return_stats=True)
+    grads = (torch.empty_like(t["q"]), torch.empty_like(t["r"]), torch.empty_like(t["k"]),
+             torch.empty_like(t["v"]))
+    ws = torch.empty(int(plx.lib().parallax_prefill_backward_workspace_bytes(B, Hq, L)),
+                     dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        plx.prefill_backward(t["q"], t["r"], t["k"], t["v"], o, t["do"], lse, sbar,
+                             workspace=ws, out=grads)
+
+    steps = max(1, min(args.steps, 10))
+    warm = max(1, min(args.warmup, 2))
+    ts = graph_time(torch, step, steps, warm)
+    # algorithmic: 8 contractions of 2D flops per visible (query, key) pair and query head --
+    # recompute Z, S, U; dV; dQ, dR; dK from dZ and dS
+    flops = 16 * D * Hq * B * L * (L + 1) // 2
+    res = {
+        "metric": METRIC, "value": round(flops / ts / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": steps, "warmup": warm, "ms_per_step": round(ts * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "causal-prefill-backward-bf16 B8 L4096 Hq16 Hkv8 D128", "B": B,
+                   "Hq": Hq, "Hkv": Hkv, "L": L, "head_dim": D},
+        "roofline": {"bound": "mfma", "kernel": "prefill_backward (row pass + key pass)",
+                     "achieved": round(flops / ts / 1e12, 2), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(flops / ts / 1e12 / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "avg_us": round(ts * 1e6, 1), "flops_per_launch": flops,
+                     "executed_flops_per_launch": flops * 13 // 8},
+    }
+    # parity and CPU baseline: the oracle's complete gradients of one (sequence, KV head) unit
+    units = np.array([[0, 0]])
+    G = Hq // Hkv
+    tt = time.perf_counter()
+    reps = 0
+    while True:
+        ref = oracle.prefill_backward(arrs["q"], arrs["r"], arrs["k"], arrs["v"], arrs["do"],
+                                      units=units)
+        reps += 1
+        if args.no_cpu_baseline or time.perf_counter() - tt > args.cpu_seconds:
+            break
+    per = (time.perf_counter() - tt) / reps
+    got = [grads[0][0, :G], grads[1][0, :G], grads[2][0, 0], grads[3][0, 0]]
+    errs = {}
+    for name, a, b in zip(("dq", "dr", "dk", "dv"), got, ref):
+        a = a.float().cpu().numpy()
+        errs[name] = float(np.abs(a - b[0]).max() / np.abs(b[0]).max())
+    res["sampled_parity_max_norm_err"] = errs
+    if not args.no_cpu_baseline:
+        sec_full = per * B * Hkv
+        res["cpu_baseline"] = {"value": round(flops / sec_full / 1e12, 6), "unit": "TFLOP/s",
+                               "cores": omp_threads(), "kind": "oracle",
+                               "sample": f"complete gradients of 1 of {B * Hkv} (sequence, KV "
+                                         f"head) units, {reps} repeats, scaled by {B * Hkv} "
+                                         f"({sec_full:.0f} s/step)"}
+    return res
+
+
 def calibrate_copy(torch):
     """A plain copy kernel of known size, for scaling HBM byte counters."""
     n = 64 << 20  # floats: 256 MiB read + 256 MiB written
@@ -384,6 +453,8 @@ def main():
         calibrate_copy(torch)
     if args.workload == "prefill":
         res = run_prefill_workload(args, torch, plx, synth, oracle)
+    elif args.workload == "backward":
+        res = run_backward_workload(args, torch, plx, synth, oracle)
     else:
         res = run_decode_workload(args, torch, plx, synth, oracle)
     print(json.dumps(res), flush=True)

@@ -278,10 +278,11 @@ def prefill(q, r, k, v, qk_scale=None, rk_scale=1.0, *, out=None, return_stats=F
 
 
 def prefill_backward(q, r, k, v, o, d_o, lse, sbar, qk_scale=None, rk_scale=1.0, *,
-                     workspace=None):
+                     workspace=None, out=None):
     """Gradients of the causal prefill: (dq, dr, dk, dv) for the upstream
     gradient ``d_o``, from the forward's o, lse and sbar (prefill with
-    return_stats=True on the same inputs and scales)."""
+    return_stats=True on the same inputs and scales). ``out``: optional
+    preallocated (dq, dr, dk, dv)."""
     L_ = lib()
     B, Hq, L, D = q.shape
     dev, dt = q.device, q.dtype
@@ -301,8 +302,13 @@ def prefill_backward(q, r, k, v, o, d_o, lse, sbar, qk_scale=None, rk_scale=1.0,
     need = int(L_.parallax_prefill_backward_workspace_bytes(B, Hq, L))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    dq, dr = torch.empty_like(q), torch.empty_like(r)
-    dk, dv = torch.empty_like(k), torch.empty_like(v)
+    if out is None:
+        out = (torch.empty_like(q), torch.empty_like(r), torch.empty_like(k), torch.empty_like(v))
+    dq, dr, dk, dv = out
+    for t, ref, name in ((dq, q, "dq"), (dr, q, "dr"), (dk, k, "dk"), (dv, k, "dv")):
+        _check(t, name, dt, dev)
+        if t.shape != ref.shape:
+            raise ValueError(f"{name} must have shape {tuple(ref.shape)}")
     st = L_.parallax_prefill_backward(
         _ptr(q), _ptr(r), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse), _ptr(sbar), _ptr(dq),
         _ptr(dr), _ptr(dk), _ptr(dv), B, Hq, Hkv, L, D, float(qk_scale), float(rk_scale),
