@@ -269,12 +269,13 @@ __device__ __forceinline__ bf16x8 lds_transposed(const uint16_t *t, int x0, int 
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// Copy `nrows` rows (a multiple of 4 * kBwdWaves) starting at row `row0` of
-// the buffer behind `rs` into LDS tile `t`. Rows past the buffer's range
-// read as zeros.
-template <int NROWS>
+// Copy NROWS rows (a multiple of 4 * NW) starting at row `row0` of the
+// buffer behind `rs` into LDS tile `t`, shared by NW waves. Rows past the
+// buffer's range read as zeros.
+template <int NROWS, int NW>
 __device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t rs, int row0, uint16_t *t, int wave, int lane) {
-    constexpr int PER_WAVE = NROWS / (4 * kBwdWaves);
+    constexpr int PER_WAVE = NROWS / (4 * NW);
+    static_assert(PER_WAVE * 4 * NW == NROWS, "rows must split evenly over the waves");
 #pragma unroll
     for (int j = 0; j < PER_WAVE; ++j) {
         const int xloc = 4 * (wave * PER_WAVE + j);
@@ -332,8 +333,8 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_rows_mfma_bf16_d128(Backwa
     __shared__ __attribute__((aligned(16))) uint16_t lds_k0[TK * D], lds_v0[TK * D];
     __shared__ __attribute__((aligned(16))) uint16_t lds_k1[TK * D], lds_v1[TK * D];
     auto dma_tile = [&](int tile, uint16_t *lk, uint16_t *lv) __attribute__((always_inline)) {
-        dma_rows<TK>(krs, tile * TK, lk, wave, lane);
-        dma_rows<TK>(vrs, tile * TK, lv, wave, lane);
+        dma_rows<TK, NW>(krs, tile * TK, lk, wave, lane);
+        dma_rows<TK, NW>(vrs, tile * TK, lv, wave, lane);
     };
     dma_tile(0, lds_k0, lds_v0);
 
@@ -475,23 +476,29 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_rows_mfma_bf16_d128(Backwa
 
 // ---- key pass: dk, dv ---------------------------------------------------
 //
-// Workgroup: eight waves over one (sequence, KV head, block of 128 keys);
-// wave w owns keys 16 w .. 16 w + 15 of the block, whose K and V stay in
-// registers as B operands. The query rows that see the block (rows >= its
-// first key) of every query head of the KV head stream through LDS in tiles
-// of 64 rows of Q, R and dLoss/do plus their row statistics, double
-// buffered. Per 32-row sub-tile a wave runs
-//   Z = Q K^T, S = R K^T, U = G V^T                      (24 MFMAs)
-//   dV^T += G^T P1, dK^T += Q^T dZ + R^T dS               (24 MFMAs)
+// Workgroup: four waves over one (sequence, KV head, block of 128 keys);
+// wave w owns keys 32 w .. 32 w + 31 of the block (two 16-key column
+// blocks), whose K and V stay in registers as B operands. The query rows
+// that see the block (rows >= its first key) of every query head of the KV
+// head stream through LDS in tiles of 64 rows of Q, R and dLoss/do plus
+// their row statistics, double buffered. Per 32-row sub-tile a wave runs
+//   Z = Q K^T, S = R K^T, U = G V^T                      (48 MFMAs)
+//   dV^T += G^T P1, dK^T += Q^T dZ + R^T dS               (48 MFMAs)
 // with P1 = w c, dZ = qk_scale dz, dS = rk_scale ds in bf16 and the
-// transposed A operands read with ds_read_b64_tr_b16. Blocks run first key
-// block first (the longest), with the (sequence, KV head) index fastest so
-// that all blocks of one head share an XCD and its L2.
-__global__ __launch_bounds__(64 * kBwdWaves) void bwd_keys_mfma_bf16_d128(BackwardArgs a) {
+// transposed A operands read with ds_read_b64_tr_b16. Every A fragment read
+// from LDS feeds both column blocks, which halves the LDS traffic per MFMA
+// against 16-key waves; one wave per SIMD holds the 32-key accumulators.
+// Blocks run first key block first (the longest), with the (sequence, KV
+// head) index fastest so that all blocks of one head share an XCD and its L2.
+constexpr int kKeyWaves = 4;
+constexpr int kKeyBlocksPerWave = 2;  // 16-key column blocks per wave
+
+__global__ __launch_bounds__(64 * kKeyWaves) void bwd_keys_mfma_bf16_d128(BackwardArgs a) {
     constexpr int D = 128;
-    constexpr int NW = kBwdWaves;
+    constexpr int NW = kKeyWaves;
+    constexpr int KBW = kKeyBlocksPerWave;
     constexpr int TR = kBwdRowsPerTile;
-    constexpr int KB = 16 * NW;  // keys per workgroup
+    constexpr int KB = 16 * KBW * NW;  // keys per workgroup
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int n = lane & 15;
@@ -504,21 +511,21 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_keys_mfma_bf16_d128(Backwa
     const int b = grp / a.Hkv;
     const int hkv = grp % a.Hkv;
     const int k0 = kblk * KB;
-    const int kw = k0 + 16 * wave;  // this wave's first key
-    const int key = kw + n;
+    const int kw = k0 + 16 * KBW * wave;  // this wave's first key
     const int nrt = (a.L - k0 + TR - 1) / TR;  // row tiles per query head
     const int ntiles = G * nrt;
 
     const int64_t kvbase = ((int64_t)b * a.Hkv + hkv) * a.L * D;
-    bf16x8 kop[4], vop[4];
-    {
-        const int kc = min(key, a.L - 1);
+    bf16x8 kop[KBW][4], vop[KBW][4];
+#pragma unroll
+    for (int c = 0; c < KBW; ++c) {
+        const int kc = min(kw + 16 * c + n, a.L - 1);
         const uint16_t *kp = reinterpret_cast<const uint16_t *>(a.k) + kvbase + (int64_t)kc * D;
         const uint16_t *vp = reinterpret_cast<const uint16_t *>(a.v) + kvbase + (int64_t)kc * D;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            kop[u] = load16(kp + 8 * (g + 4 * u));
-            vop[u] = load16(vp + 8 * (g + 4 * u));
+            kop[c][u] = load16(kp + 8 * (g + 4 * u));
+            vop[c][u] = load16(vp + 8 * (g + 4 * u));
         }
     }
 
@@ -536,9 +543,9 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_keys_mfma_bf16_d128(Backwa
             (void *)(reinterpret_cast<const uint16_t *>(a.r) + rowbase * D), 0, hbytes, kBufferFlags);
         const __amdgpu_buffer_rsrc_t grs = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(reinterpret_cast<const uint16_t *>(a.go) + rowbase * D), 0, hbytes, kBufferFlags);
-        dma_rows<TR>(qrs, r0, tq, wave, lane);
-        dma_rows<TR>(rrs, r0, tr, wave, lane);
-        dma_rows<TR>(grs, r0, tg, wave, lane);
+        dma_rows<TR, NW>(qrs, r0, tq, wave, lane);
+        dma_rows<TR, NW>(rrs, r0, tr, wave, lane);
+        dma_rows<TR, NW>(grs, r0, tg, wave, lane);
         if (wave == 0) {  // 64 rows x 16 bytes: one copy by one wave
             const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
                 (void *)(a.rowstat + rowbase), 0, (uint32_t)((int64_t)a.L * sizeof(RowStat)), kBufferFlags);
@@ -547,51 +554,65 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_keys_mfma_bf16_d128(Backwa
     };
     dma_tile(0, lq0, lr0, lg0, ls0);
 
-    floatx4 accK[8], accV[8];
+    floatx4 accK[KBW][8], accV[KBW][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) accK[e] = accV[e] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < KBW; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) accK[c][e] = accV[c][e] = floatx4{0.f, 0.f, 0.f, 0.f};
     const int rperm = (n >> 2) + 4 * (n & 3);
 
     // one 32-row sub-tile at tile row xl (global row rs)
     auto sub_tile = [&](const uint16_t *tq, const uint16_t *tr, const uint16_t *tg, const RowStat *ts,
                         int xl, int rs, bool mask) __attribute__((always_inline)) {
-        floatx4 z[2], s[2], uu[2];
-        __builtin_amdgcn_s_setprio(1);
+        floatx4 z[KBW][2], s[KBW][2], uu[KBW][2];
+#pragma unroll
+        for (int c = 0; c < KBW; ++c)
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) z[c][tb] = s[c][tb] = uu[c][tb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
-            z[tb] = s[tb] = uu[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
             const int x = xl + 16 * tb + rperm;
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                z[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_chunk(tq, x, g + 4 * u), kop[u], z[tb], 0, 0, 0);
-                s[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_chunk(tr, x, g + 4 * u), kop[u], s[tb], 0, 0, 0);
-                uu[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_chunk(tg, x, g + 4 * u), vop[u], uu[tb], 0, 0, 0);
+                const bf16x8 fq = lds_chunk(tq, x, g + 4 * u);
+                const bf16x8 fr = lds_chunk(tr, x, g + 4 * u);
+                const bf16x8 fg = lds_chunk(tg, x, g + 4 * u);
+#pragma unroll
+                for (int c = 0; c < KBW; ++c) {
+                    z[c][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fq, kop[c][u], z[c][tb], 0, 0, 0);
+                    s[c][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr, kop[c][u], s[c][tb], 0, 0, 0);
+                    uu[c][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fg, vop[c][u], uu[c][tb], 0, 0, 0);
+                }
             }
         }
-        __builtin_amdgcn_s_setprio(0);
-        bf16x8 p1, pz, ps;
+        bf16x8 p1[KBW], pz[KBW], ps[KBW];
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             const RowStat st = ts[xl + g + 4 * t];
-            const float zz = z[t >> 2][t & 3], ss = s[t >> 2][t & 3], u = uu[t >> 2][t & 3];
-            float w = __builtin_amdgcn_exp2f(fmaf(zz, a.zscale, -st.lse2));
-            if (mask) {
-                const int rw = rs + g + 4 * t;
-                if (rw < key || rw >= a.L) w = 0.f;
+            const int rw = rs + g + 4 * t;
+#pragma unroll
+            for (int c = 0; c < KBW; ++c) {
+                const float zz = z[c][t >> 2][t & 3], ss = s[c][t >> 2][t & 3], u = uu[c][t >> 2][t & 3];
+                float w = __builtin_amdgcn_exp2f(fmaf(zz, a.zscale, -st.lse2));
+                if (mask && (rw < kw + 16 * c + n || rw >= a.L)) w = 0.f;
+                const float sc = fmaf(ss, a.rk_scale, -st.sbar);
+                p1[c][t] = (__bf16)(w * (1.0f + sc));
+                pz[c][t] = (__bf16)(w * (fmaf(sc, u, u) - fmaf(st.ubar, sc, st.delta)) * a.qk_scale);
+                ps[c][t] = (__bf16)(w * (u - st.ubar) * a.rk_scale);
             }
-            const float sc = fmaf(ss, a.rk_scale, -st.sbar);
-            p1[t] = (__bf16)(w * (1.0f + sc));
-            pz[t] = (__bf16)(w * (fmaf(sc, u, u) - fmaf(st.ubar, sc, st.delta)) * a.qk_scale);
-            ps[t] = (__bf16)(w * (u - st.ubar) * a.rk_scale);
         }
-        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            accV[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_transposed(tg, xl, e, g, n), p1, accV[e], 0, 0, 0);
-            accK[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_transposed(tq, xl, e, g, n), pz, accK[e], 0, 0, 0);
-            accK[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_transposed(tr, xl, e, g, n), ps, accK[e], 0, 0, 0);
+            const bf16x8 gt = lds_transposed(tg, xl, e, g, n);
+            const bf16x8 qt = lds_transposed(tq, xl, e, g, n);
+            const bf16x8 rt = lds_transposed(tr, xl, e, g, n);
+#pragma unroll
+            for (int c = 0; c < KBW; ++c) {
+                accV[c][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gt, p1[c], accV[c][e], 0, 0, 0);
+                accK[c][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qt, pz[c], accK[c][e], 0, 0, 0);
+                accK[c][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rt, ps[c], accK[c][e], 0, 0, 0);
+            }
         }
-        __builtin_amdgcn_s_setprio(0);
     };
     auto step = [&](int tile, uint16_t *tq, uint16_t *tr, uint16_t *tg, RowStat *ts, uint16_t *nq,
                     uint16_t *nr, uint16_t *ng, RowStat *ns) __attribute__((always_inline)) {
@@ -601,7 +622,7 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_keys_mfma_bf16_d128(Backwa
         for (int j = 0; j < TR / 32; ++j) {
             const int rs = r0 + 32 * j;
             if (rs + 31 >= kw) {  // wave-uniform: sub-tiles wholly above the wave's keys are skipped
-                const bool mask = rs < kw + 15 || rs + 31 >= a.L;
+                const bool mask = rs < kw + 16 * KBW - 1 || rs + 31 >= a.L;
                 if (mask)
                     sub_tile(tq, tr, tg, ts, 32 * j, rs, true);
                 else
@@ -616,16 +637,20 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_keys_mfma_bf16_d128(Backwa
         if (tile + 1 < ntiles) step(tile + 1, lq1, lr1, lg1, ls1, lq0, lr0, lg0, ls0);
     }
 
-    if (key < a.L) {
-        // block e, accumulator element i holds dim 16 e + 4 g + i of key n
-        uint16_t *dk = reinterpret_cast<uint16_t *>(a.dk) + kvbase + (int64_t)key * D + 4 * g;
-        uint16_t *dv = reinterpret_cast<uint16_t *>(a.dv) + kvbase + (int64_t)key * D + 4 * g;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            *reinterpret_cast<uint2 *>(dk + 16 * e) =
-                uint2{pack_bf16x2(accK[e][0], accK[e][1]), pack_bf16x2(accK[e][2], accK[e][3])};
-            *reinterpret_cast<uint2 *>(dv + 16 * e) =
-                uint2{pack_bf16x2(accV[e][0], accV[e][1]), pack_bf16x2(accV[e][2], accV[e][3])};
+    for (int c = 0; c < KBW; ++c) {
+        const int key = kw + 16 * c + n;
+        if (key < a.L) {
+            // block e, accumulator element i holds dim 16 e + 4 g + i of the key
+            uint16_t *dk = reinterpret_cast<uint16_t *>(a.dk) + kvbase + (int64_t)key * D + 4 * g;
+            uint16_t *dv = reinterpret_cast<uint16_t *>(a.dv) + kvbase + (int64_t)key * D + 4 * g;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                *reinterpret_cast<uint2 *>(dk + 16 * e) =
+                    uint2{pack_bf16x2(accK[c][e][0], accK[c][e][1]), pack_bf16x2(accK[c][e][2], accK[c][e][3])};
+                *reinterpret_cast<uint2 *>(dv + 16 * e) =
+                    uint2{pack_bf16x2(accV[c][e][0], accV[c][e][1]), pack_bf16x2(accV[c][e][2], accV[c][e][3])};
+            }
         }
     }
 }
@@ -647,7 +672,8 @@ hipError_t launch_prefill_backward(const BackwardArgs &a, int dtype, hipStream_t
         const int hpw = (G % 2 == 0) ? 2 : 1;
         const int rph = 16 * kBwdWaves / hpw;
         const long row_items = (long)a.B * a.Hkv * (G / hpw) * ((a.L + rph - 1) / rph);
-        const long key_items = (long)a.B * a.Hkv * ((a.L + 16 * kBwdWaves - 1) / (16 * kBwdWaves));
+        constexpr int kb = 16 * kKeyBlocksPerWave * kKeyWaves;
+        const long key_items = (long)a.B * a.Hkv * ((a.L + kb - 1) / kb);
         if (row_items <= 0x7fffffffL && key_items <= 0x7fffffffL) {
             if (hpw == 2)
                 hipLaunchKernelGGL((bwd_rows_mfma_bf16_d128<2>), dim3((unsigned)row_items),
@@ -657,7 +683,7 @@ hipError_t launch_prefill_backward(const BackwardArgs &a, int dtype, hipStream_t
                                    dim3(64 * kBwdWaves), 0, stream, a);
             hipError_t err = hipGetLastError();
             if (err != hipSuccess) return err;
-            hipLaunchKernelGGL(bwd_keys_mfma_bf16_d128, dim3((unsigned)key_items), dim3(64 * kBwdWaves), 0,
+            hipLaunchKernelGGL(bwd_keys_mfma_bf16_d128, dim3((unsigned)key_items), dim3(64 * kKeyWaves), 0,
                                stream, a);
             return hipGetLastError();
         }
