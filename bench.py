@@ -16,9 +16,10 @@ Also measured in the same run:
   * softmax_decode on the same inputs (the cost of the correction branch);
   * the CPU oracle on the same inputs (cpu_baseline), on the host's cores.
 
-Other workloads (--workload varlen | large | prefill | backward) print their
-own line; backward times parallax_prefill_backward (row pass + key pass) on
-the causal-prefill shapes.
+Other workloads (--workload varlen | large | prefill | backward | grid) print
+their own line; backward times parallax_prefill_backward (row pass + key
+pass) on the causal-prefill shapes; grid runs the pages' own decode shapes
+(multi-head H = 8, B in {1, 32}, L in {512 .. 16384}) and reports a table.
 Prints one JSON line on stdout.
 """
 from __future__ import annotations
@@ -48,7 +49,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="long",
-                    choices=["long", "varlen", "large", "prefill", "backward"])
+                    choices=["long", "varlen", "large", "prefill", "backward", "grid"])
     ap.add_argument("--num-splits", type=int, default=0, help="0: library plan")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -422,6 +423,85 @@ def run_backward_workload(args, torch, plx, synth, oracle):
     return res
 
 
+# The pages' H200 Parallax decode latencies for the same shapes (PyPI README of
+# parallax-kernel, small- and large-batch decode tables; q50, CUDA-graph replay).
+# Context only: another machine's numbers, not a target of this build.
+PAGES_H200_PARALLAX_US = {(1, 512): 5.79, (1, 1024): 6.48, (1, 4096): 8.61, (1, 16384): 21.53,
+                          (32, 512): 24.02, (32, 1024): 39.55, (32, 4096): 279.96,
+                          (32, 16384): 1094.37}
+
+
+def graph_trials(torch, fn, iters, trials, warmup):
+    """Per-step seconds of `trials` replays of one graph of `iters` calls (after
+    `warmup` eager calls): the pages' q05 / q50 / q95 replay sweep."""
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            fn(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(iters):
+            fn(i)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    out = []
+    with torch.cuda.stream(stream):
+        for _ in range(trials):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            e1.synchronize()
+            out.append(e0.elapsed_time(e1) * 1e-3 / iters)
+    return np.quantile(np.array(out), [0.05, 0.5, 0.95])
+
+
+def run_grid_workload(args, torch, plx, synth, oracle):
+    rows = []
+    for spec in synth.pages_decode_grid():
+        shp = (spec.B, spec.L, spec.Hkv, spec.D)
+        q_np, r_np = synth.decode_qr(spec)
+        k_np = synth.normal(spec.seed, synth.TID_K, shp, spec.scale, spec.dtype)
+        v_np = synth.normal(spec.seed, synth.TID_V, shp, spec.scale, spec.dtype)
+        q, r, k, v = (torch.from_numpy(a).view(torch.bfloat16).cuda()
+                      for a in (q_np, r_np, k_np, v_np))
+        ws = torch.empty(max(1, plx.decode_workspace_bytes(spec.B, spec.Hq, spec.Hkv, spec.D,
+                                                           spec.L, plx.PLX_BF16)),
+                         dtype=torch.uint8, device="cuda")
+        out = torch.empty((spec.B, spec.Hq, spec.D), dtype=torch.bfloat16, device="cuda")
+        out_s = torch.empty_like(out)
+        trials = max(3, min(args.steps, 20))
+        tq = graph_trials(torch, lambda i: plx.decode(q, r, k, v, out=out, workspace=ws), 50,
+                          trials, max(1, min(args.warmup, 100)))
+        ts = graph_trials(torch, lambda i: plx.softmax_decode(q, k, v, out=out_s, workspace=ws),
+                          50, trials, max(1, min(args.warmup, 100)))
+        ref = oracle.decode(q_np, r_np, k_np, v_np)
+        got = out.float().cpu().numpy().astype(np.float64)
+        kv_bytes = 2 * k.numel() * 2
+        rows.append({"B": spec.B, "L": spec.L, "us_q05": round(tq[0] * 1e6, 2),
+                     "us_q50": round(tq[1] * 1e6, 2), "us_q95": round(tq[2] * 1e6, 2),
+                     "kv_gb_s": round(kv_bytes / tq[1] / 1e9, 1),
+                     "softmax_decode_us_q50": round(ts[1] * 1e6, 2),
+                     "max_norm_err": float(np.abs(got - ref).max() / np.abs(ref).max()),
+                     "splits": plx.decode_num_splits(spec.B, spec.Hq, spec.Hkv, spec.D, spec.L,
+                                                     plx.PLX_BF16),
+                     "pages_h200_parallax_us": PAGES_H200_PARALLAX_US[(spec.B, spec.L)]})
+    big = rows[-1]
+    return {
+        "metric": METRIC, "value": big["us_q50"], "unit": "us/step", "n_gpus": 1,
+        "steps": 50, "warmup": max(1, min(args.warmup, 100)), "ms_per_step": big["us_q50"] / 1e3,
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "pages-grid-decode-bf16 H8 D128 B{1,32} L{512..16384}",
+                   "value_row": "B32 L16384", "timing": "q50 of graph replays of 50 steps, "
+                   "inputs not rotated (the pages' replay sweep)"},
+        "table": rows,
+    }
+
+
 def calibrate_copy(torch):
     """A plain copy kernel of known size, for scaling HBM byte counters."""
     n = 64 << 20  # floats: 256 MiB read + 256 MiB written
@@ -455,6 +535,8 @@ def main():
         res = run_prefill_workload(args, torch, plx, synth, oracle)
     elif args.workload == "backward":
         res = run_backward_workload(args, torch, plx, synth, oracle)
+    elif args.workload == "grid":
+        res = run_grid_workload(args, torch, plx, synth, oracle)
     else:
         res = run_decode_workload(args, torch, plx, synth, oracle)
     print(json.dumps(res), flush=True)

@@ -158,6 +158,18 @@ def decode_spec(idx: int) -> DecodeSpec:
     raise ValueError(idx)
 
 
+def pages_decode_grid() -> list:
+    """The decode shapes of the pages' benchmark tables (PyPI README of
+    parallax-kernel, small- and large-batch decode tables): multi-head
+    (Hq = Hkv = 8), D = 128, bf16, B in {1, 32}, L in {512, 1024, 4096, 16384}."""
+    s = 1.0 / np.sqrt(128.0)
+    out = []
+    for i, (B, L) in enumerate((B, L) for B in (1, 32) for L in (512, 1024, 4096, 16384)):
+        out.append(DecodeSpec(f"pages-grid-decode-bf16 B{B} H8 D128 L{L}", B, 8, 8, 128, L, BF16,
+                              s, BASE_SEED + 100 + i))
+    return out
+
+
 def prefill_spec(idx: int = 5) -> PrefillSpec:
     assert idx == 5
     return PrefillSpec("causal-prefill-bf16 B8 L4096 Hq16 Hkv8 D128", 8, 16, 8, 4096, 128, BF16,

@@ -251,3 +251,17 @@ def test_records_from_separate_key_ranges_merge_to_the_full_sequence():
     assert not torch.equal(pivots[..., 0], pivots[..., na])   # the two calls' pivots differ
     o = from_gpu(plx.decode_merge(recs))
     assert_parity(o, oracle_dense(q, r, k, v), synth.BF16, "sharded merge")
+
+
+@pytest.mark.parametrize("spec", synth.pages_decode_grid(), ids=lambda s: f"B{s.B}-L{s.L}")
+def test_pages_decode_grid_full_output(spec):
+    """The pages' own decode shapes (multi-head, H = 8, D = 128, bf16): complete output of
+    decode and softmax_decode against the oracle."""
+    shp = (spec.B, spec.L, spec.Hkv, spec.D)
+    q, r = synth.decode_qr(spec)
+    k = synth.normal(spec.seed, synth.TID_K, shp, spec.scale, spec.dtype)
+    v = synth.normal(spec.seed, synth.TID_V, shp, spec.scale, spec.dtype)
+    t = [to_gpu(x, spec.dtype) for x in (q, r, k, v)]
+    assert_parity(from_gpu(plx.decode(*t)), oracle.decode(q, r, k, v), spec.dtype, spec.name)
+    assert_parity(from_gpu(plx.softmax_decode(t[0], t[2], t[3])), oracle.decode(q, None, k, v),
+                  spec.dtype, spec.name + " softmax")
