@@ -47,13 +47,13 @@ def _bind(path: str):
     lib = ctypes.CDLL(path)
     vp, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
     lib.oracle_decode.argtypes = [vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, dbl, dbl,
-                                  i64, vp, vp]
+                                  i64, i64, vp, vp]
     lib.oracle_decode.restype = i32
     lib.oracle_prefill.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, dbl, dbl,
-                                   i64, vp, vp, vp, vp]
+                                   i64, i64, vp, vp, vp, vp]
     lib.oracle_prefill.restype = i32
     lib.oracle_prefill_backward.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
-                                            dbl, dbl, i64, vp, vp, vp, vp, vp]
+                                            dbl, dbl, i64, i64, vp, vp, vp, vp, vp]
     lib.oracle_prefill_backward.restype = i32
     return lib
 
@@ -105,13 +105,14 @@ def _ptr(a):
 
 
 def decode(q, r, k, v, *, seq_start=None, seq_len=None, Hkv=None, qk_scale=None, rk_scale=1.0,
-           rows=None):
+           rows=None, window=0):
     """Parallax decode rows.
 
     q, r: [B, Hq, D] (r may be None: r = 0, plain softmax attention).
     k, v: [B, L, Hkv, D] dense, or [T, Hkv, D] packed with ``seq_start`` /
     ``seq_len`` giving each sequence's token range.
     rows: optional int array [n, 2] of (b, h); default all rows.
+    window: W > 0 keeps each sequence's last W keys (0: all).
     Returns float64 [B, Hq, D] (or [n, D] when rows is given).
     """
     dt = _dtype_of(q)
@@ -142,18 +143,19 @@ def decode(q, r, k, v, *, seq_start=None, seq_len=None, Hkv=None, qk_scale=None,
         out = np.empty((B, Hq, D), dtype=np.float64)
         n = B * Hq
     rc = _load().oracle_decode(_ptr(q), _ptr(r), _ptr(k), _ptr(v), dt, _ptr(seq_start),
-                               _ptr(seq_len), B, Hq, Hkv, D, tau, float(rk_scale), n, _ptr(rows),
-                               _ptr(out))
+                               _ptr(seq_len), B, Hq, Hkv, D, tau, float(rk_scale), int(window), n,
+                               _ptr(rows), _ptr(out))
     if rc != 0:
         raise RuntimeError(f"oracle_decode failed ({rc})")
     return out
 
 
-def prefill(q, r, k, v, *, qk_scale=None, rk_scale=1.0, rows=None, stats=False):
+def prefill(q, r, k, v, *, qk_scale=None, rk_scale=1.0, rows=None, stats=False, window=0):
     """Causal Parallax prefill rows.
 
     q, r: [B, Hq, L, D] (r may be None); k, v: [B, Hkv, L, D].
     rows: optional int array [n, 3] of (b, h, i).
+    window: W > 0 limits query i to keys i - W + 1 .. i (0: causal only).
     Returns o float64 [B, Hq, L, D] (or [n, D]); with stats=True also lse and sbar.
     """
     dt = _dtype_of(q)
@@ -175,13 +177,14 @@ def prefill(q, r, k, v, *, qk_scale=None, rk_scale=1.0, rows=None, stats=False):
         lse = np.empty((B, Hq, L), dtype=np.float64)
         sbar = np.empty((B, Hq, L), dtype=np.float64)
     rc = _load().oracle_prefill(_ptr(q), _ptr(r), _ptr(k), _ptr(v), dt, B, Hq, Hkv, L, D, tau,
-                                float(rk_scale), n, _ptr(rows), _ptr(out), _ptr(lse), _ptr(sbar))
+                                float(rk_scale), int(window), n, _ptr(rows), _ptr(out), _ptr(lse),
+                                _ptr(sbar))
     if rc != 0:
         raise RuntimeError(f"oracle_prefill failed ({rc})")
     return (out, lse, sbar) if stats else out
 
 
-def prefill_backward(q, r, k, v, do, *, qk_scale=None, rk_scale=1.0, units=None):
+def prefill_backward(q, r, k, v, do, *, qk_scale=None, rk_scale=1.0, units=None, window=0):
     """Gradients of the causal Parallax prefill for the upstream gradient ``do``.
 
     q, r, do: [B, Hq, L, D] (r may be None: r = 0); k, v: [B, Hkv, L, D].
@@ -208,8 +211,8 @@ def prefill_backward(q, r, k, v, do, *, qk_scale=None, rk_scale=1.0, units=None)
     dk = np.empty((n, L, D), dtype=np.float64)
     dv = np.empty((n, L, D), dtype=np.float64)
     rc = _load().oracle_prefill_backward(_ptr(q), _ptr(r), _ptr(k), _ptr(v), _ptr(do), dt, B, Hq,
-                                         Hkv, L, D, tau, float(rk_scale), n, _ptr(units),
-                                         _ptr(dq), _ptr(dr), _ptr(dk), _ptr(dv))
+                                         Hkv, L, D, tau, float(rk_scale), int(window), n,
+                                         _ptr(units), _ptr(dq), _ptr(dr), _ptr(dk), _ptr(dv))
     if rc != 0:
         raise RuntimeError(f"oracle_prefill_backward failed ({rc})")
     if units is None:

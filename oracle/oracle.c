@@ -30,6 +30,12 @@
  * head h / (Hq / Hkv); prefill is causal with key j visible to query i iff
  * j <= i; decode sees every cached key of its sequence; an empty key set
  * gives o = 0, lse = -inf, sbar = 0.
+ *
+ * Sliding window (the PyPI README's overview calls sliding windows
+ * structurally compatible with Parallax and defines none): with window W > 0
+ * a prefill query i sees keys max(0, i - W + 1) .. i (itself and the W - 1
+ * before it), and a decode query of a sequence of n cached keys sees its last
+ * min(n, W) keys. W = 0 means no window.
  */
 #include <math.h>
 #include <omp.h>
@@ -127,7 +133,8 @@ static void one_row(const void *q, size_t q_off, const void *r, size_t r_off,
  */
 int oracle_decode(const void *q, const void *r, const void *k, const void *v, int dtype,
                   const int64_t *seq_start, const int64_t *seq_len, int B, int Hq, int Hkv, int D,
-                  double tau, double rho, int64_t n_rows, const int64_t *rows, double *o)
+                  double tau, double rho, int64_t window, int64_t n_rows, const int64_t *rows,
+                  double *o)
 {
     if (Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || B <= 0)
         return 1;
@@ -152,8 +159,13 @@ int oracle_decode(const void *q, const void *r, const void *k, const void *v, in
                 int64_t h = rows ? rows[2 * t + 1] : t % Hq;
                 int64_t hk = h / g;
                 size_t qo = ((size_t)b * Hq + (size_t)h) * (size_t)D;
-                size_t kvo = ((size_t)seq_start[b] * Hkv + (size_t)hk) * (size_t)D;
-                one_row(q, qo, r, qo, k, v, kvo, (size_t)Hkv * D, seq_len[b], D, dtype, tau, rho,
+                int64_t n = seq_len[b], first = 0; /* visible keys: the last min(n, W) */
+                if (window > 0 && n > window) {
+                    first = n - window;
+                    n = window;
+                }
+                size_t kvo = ((size_t)(seq_start[b] + first) * Hkv + (size_t)hk) * (size_t)D;
+                one_row(q, qo, r, qo, k, v, kvo, (size_t)Hkv * D, n, D, dtype, tau, rho,
                         o + (size_t)t * D, NULL, NULL, z, s);
             }
         }
@@ -169,8 +181,8 @@ int oracle_decode(const void *q, const void *r, const void *k, const void *v, in
  * o: [n_rows, D]; lse, sbar: [n_rows] or NULL.
  */
 int oracle_prefill(const void *q, const void *r, const void *k, const void *v, int dtype, int B,
-                   int Hq, int Hkv, int L, int D, double tau, double rho, int64_t n_rows,
-                   const int64_t *rows, double *o, double *lse, double *sbar)
+                   int Hq, int Hkv, int L, int D, double tau, double rho, int64_t window,
+                   int64_t n_rows, const int64_t *rows, double *o, double *lse, double *sbar)
 {
     if (Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || B <= 0 || L <= 0)
         return 1;
@@ -199,8 +211,10 @@ int oracle_prefill(const void *q, const void *r, const void *k, const void *v, i
                 }
                 int64_t hk = h / g;
                 size_t qo = (((size_t)b * Hq + (size_t)h) * (size_t)L + (size_t)i) * (size_t)D;
-                size_t kvo = ((size_t)b * Hkv + (size_t)hk) * (size_t)L * (size_t)D;
-                one_row(q, qo, r, qo, k, v, kvo, (size_t)D, i + 1, D, dtype, tau, rho,
+                int64_t first = (window > 0 && i + 1 > window) ? i + 1 - window : 0;
+                size_t kvo = (((size_t)b * Hkv + (size_t)hk) * (size_t)L + (size_t)first) *
+                             (size_t)D;
+                one_row(q, qo, r, qo, k, v, kvo, (size_t)D, i + 1 - first, D, dtype, tau, rho,
                         o + (size_t)t * D, lse ? lse + t : NULL, sbar ? sbar + t : NULL, z, s);
             }
         }
@@ -302,8 +316,8 @@ static void row_backward(const void *q, const void *r, const void *k, const void
 
 int oracle_prefill_backward(const void *q, const void *r, const void *k, const void *v,
                             const void *go, int dtype, int B, int Hq, int Hkv, int L, int D,
-                            double tau, double rho, int64_t n_units, const int64_t *units,
-                            double *dq, double *dr, double *dk, double *dv)
+                            double tau, double rho, int64_t window, int64_t n_units,
+                            const int64_t *units, double *dq, double *dr, double *dk, double *dv)
 {
     if (Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || B <= 0 || L <= 0)
         return 1;
@@ -339,9 +353,11 @@ int oracle_prefill_backward(const void *q, const void *r, const void *k, const v
                         dq[ro + d] = 0.0;
                         dr[ro + d] = 0.0;
                     }
-                    row_backward(q, r, k, v, go, qo, kvo, i + 1, D, dtype, tau, rho, dq + ro,
-                                 dr + ro, dk_t, dv_t, scr, scr + L, scr + 2 * (size_t)L,
-                                 scr + 3 * (size_t)L);
+                    int64_t first = (window > 0 && i + 1 > window) ? i + 1 - window : 0;
+                    size_t fo = (size_t)first * D;
+                    row_backward(q, r, k, v, go, qo, kvo + fo, i + 1 - first, D, dtype, tau, rho,
+                                 dq + ro, dr + ro, dk_t + fo, dv_t + fo, scr, scr + L,
+                                 scr + 2 * (size_t)L, scr + 3 * (size_t)L);
                 }
 #pragma omp for ordered schedule(static, 1)
                 for (int th = 0; th < omp_get_num_threads(); ++th) {

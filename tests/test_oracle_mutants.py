@@ -29,7 +29,7 @@ MUTANTS = {
                   "int64_t hk = h % Hkv;\n                size_t qo = ((size_t)b"),
     "prefill gqa index": ("int64_t hk = h / g;\n                size_t qo = (((size_t)b",
                           "int64_t hk = h % Hkv;\n                size_t qo = (((size_t)b"),
-    "causal off by one": ("(size_t)D, i + 1, D, dtype", "(size_t)D, i, D, dtype"),
+    "causal off by one": ("(size_t)D, i + 1 - first, D, dtype", "(size_t)D, i - first, D, dtype"),
     "logit scale dropped": ("z[j] = tau * zq;", "z[j] = zq;"),
     "keys and values swapped": (
         "double kd = elem(k, dtype, kb + d);\n            zq += elem(q, dtype, q_off + d) * kd;"
@@ -37,13 +37,17 @@ MUTANTS = {
         "double kd = elem(v, dtype, kb + d);\n            zq += elem(q, dtype, q_off + d) * kd;"
         "\n            if (r)\n                sr += elem(r, dtype, r_off"),
     "sample covariance": ("z[j] /= l;", "z[j] /= (l - z[j] / l * 0.5);"),
+    "prefill window off by one": (
+        "int64_t first = (window > 0 && i + 1 > window) ? i + 1 - window : 0;\n                size_t kvo",
+        "int64_t first = (window > 0 && i + 1 > window) ? i - window : 0;\n                size_t kvo"),
+    "decode window keeps the first keys": ("first = n - window;", "first = 0;"),
 }
 
 # mistakes in the reverse pass (the forward code is untouched)
 BACKWARD_MUTANTS = {
     "bwd sbar adjoint dropped": ("a_sb -= w[j] * t;", "a_sb -= 0.0 * t;"),
     "bwd softmax jacobian sign": ("aw[j] = w[j] * (aw[j] - waw);", "aw[j] = w[j] * (aw[j] + waw);"),
-    "bwd causal off by one": ("kvo, i + 1, D, dtype, tau", "kvo, i, D, dtype, tau"),
+    "bwd causal off by one": ("kvo + fo, i + 1 - first, D", "kvo + fo, i - first, D"),
     "bwd probe adjoint uses q": ("cs * elem(r, dtype, q_off + d)", "cs * elem(q, dtype, q_off + d)"),
     "bwd dv without correction": ("double cv = w[j] * (1.0 + s[j] - sb);", "double cv = w[j];"),
     "bwd dq misses tau": ("double cz = tau * aw[j], cs", "double cz = aw[j], cs"),
@@ -84,6 +88,17 @@ def independent_checks_pass():
         torch.from_numpy(Q), torch.from_numpy(K), torch.from_numpy(V), is_causal=True,
         enable_gqa=True).numpy()
     ok &= np.abs(oracle.prefill(Q, np.zeros_like(Q), K, V) - refp).max() < 1e-12
+    # sliding window (prefill and decode) against SDPA with a band mask
+    i, j = np.arange(19)[:, None], np.arange(19)[None, :]
+    band = torch.from_numpy((j <= i) & (j > i - 4))
+    refw = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(Q), torch.from_numpy(K), torch.from_numpy(V), attn_mask=band,
+        enable_gqa=True).numpy()
+    ok &= np.abs(oracle.prefill(Q, None, K, V, window=4) - refw).max() < 1e-12
+    kd = np.ascontiguousarray(K.transpose(0, 2, 1, 3))
+    vd = np.ascontiguousarray(V.transpose(0, 2, 1, 3))
+    ok &= np.abs(oracle.decode(np.ascontiguousarray(Q[:, :, 18]), None, kd, vd, window=4)
+                 - refw[:, :, 18]).max() < 1e-12
     # correction = weighted covariance
     L, D = 30, 5
     q1, r1 = g.standard_normal((1, 1, D)), g.standard_normal((1, 1, D))
