@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--workload", default="long",
                     choices=["long", "varlen", "large", "prefill", "backward", "grid"])
     ap.add_argument("--num-splits", type=int, default=0, help="0: library plan")
+    ap.add_argument("--window", type=int, default=0,
+                    help="sliding window (keys a query sees); 0: none")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the CPU oracle sample")
@@ -78,6 +80,13 @@ def upload_cache(torch, spec, synth, tid, tokens, chunk=1 << 16):
 
 
 EAGER = False
+
+
+def visible_pairs(L, W):
+    """(query, key) pairs a causal prefill of length L sees with window W (0: none)."""
+    if W <= 0 or W >= L:
+        return L * (L + 1) // 2
+    return W * (W + 1) // 2 + (L - W) * W
 
 
 def graph_time(torch, fn, steps, warmup):
@@ -145,17 +154,17 @@ def measured_traffic(workload_name, splits):
     return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["source_sha256"] else None
 
 
-def cpu_baseline_decode(oracle, q, r, kv_rows, spec, seconds):
+def cpu_baseline_decode(oracle, q, r, kv_rows, spec, seconds, window=0):
     """Time the oracle on the full step (all heads, all keys), repeated to fill
     about `seconds` of wall time. Returns (us_per_step, repeats, threads)."""
     k, v = kv_rows
     t = time.perf_counter()
-    oracle.decode(q, r, k, v)
+    oracle.decode(q, r, k, v, window=window)
     one = time.perf_counter() - t
     reps = max(1, int(seconds / max(one, 1e-6)))
     t = time.perf_counter()
     for _ in range(reps):
-        oracle.decode(q, r, k, v)
+        oracle.decode(q, r, k, v, window=window)
     per = (time.perf_counter() - t) / reps
     threads = min(omp_threads(), spec.B * spec.Hq)
     return per * 1e6, reps + 1, threads
@@ -192,14 +201,15 @@ def run_decode_workload(args, torch, plx, synth, oracle):
         vs = [v.view(spec.B, spec.L, spec.Hkv, spec.D) for v in vs]
     code = plx.PLX_BF16
     ns = args.num_splits
-    splits = plx.decode_num_splits(spec.B, spec.Hq, spec.Hkv, spec.D, spec.L, code, ns)
-    ws_bytes = plx.decode_workspace_bytes(spec.B, spec.Hq, spec.Hkv, spec.D, spec.L, code, ns)
+    W = args.window
+    splits = plx.decode_num_splits(spec.B, spec.Hq, spec.Hkv, spec.D, spec.L, code, ns, W)
+    ws_bytes = plx.decode_workspace_bytes(spec.B, spec.Hq, spec.Hkv, spec.D, spec.L, code, ns, W)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
     out = torch.empty((spec.B, spec.Hq, spec.D), dtype=torch.bfloat16, device="cuda")
     out_s = torch.empty_like(out)
     recs = torch.empty((spec.B, spec.Hq, splits, 2 * spec.D + 4), dtype=torch.float32,
                        device="cuda")
-    kw = dict(cu_seqlens_k=cu_t, kv_len=spec.L, num_splits=ns)
+    kw = dict(cu_seqlens_k=cu_t, kv_len=spec.L, num_splits=ns, window=W)
 
     def step(i):
         c = i % copies
@@ -218,11 +228,13 @@ def run_decode_workload(args, torch, plx, synth, oracle):
     t_kern = graph_time(torch, step_stream_only, args.steps, args.warmup)
 
     # algorithmic bytes: K + V over the visible keys, plus q, r and o
+    T_vis = int(np.minimum(lens, W).sum()) if W > 0 else T
+    kv_vis = kv_bytes * T_vis // T
     qr_bytes = 2 * q.numel() * 2
     o_bytes = out.numel() * 2
-    step_bytes = kv_bytes + qr_bytes + o_bytes
-    kern_bytes = kv_bytes + qr_bytes
-    flops = 8 * spec.D * spec.Hq * T
+    step_bytes = kv_vis + qr_bytes + o_bytes
+    kern_bytes = kv_vis + qr_bytes
+    flops = 8 * spec.D * spec.Hq * T_vis
     res = {
         "metric": METRIC,
         "value": round(t_step * 1e6, 3),
@@ -236,8 +248,9 @@ def run_decode_workload(args, torch, plx, synth, oracle):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": spec.name, "B": spec.B, "Hq": spec.Hq, "Hkv": spec.Hkv,
-                   "head_dim": spec.D, "kv_len": spec.L, "total_kv_tokens": T,
+        "config": {"workload": spec.name + (f" window{W}" if W > 0 else ""), "B": spec.B,
+                   "Hq": spec.Hq, "Hkv": spec.Hkv, "head_dim": spec.D, "kv_len": spec.L,
+                   "total_kv_tokens": T, "visible_kv_tokens": T_vis, "window": W,
                    "kv_cache_copies": copies, "splits": splits},
         "hbm_tb_s": round(step_bytes / t_step / 1e12, 4),
         "hbm_frac_of_8tbs": round(step_bytes / t_step / 1e9 / HBM_PEAK_GBS, 4),
@@ -247,7 +260,7 @@ def run_decode_workload(args, torch, plx, synth, oracle):
         "roofline": {"bound": "hbm", "kernel": "decode_mfma_bf16_d128 (streaming, split records)",
                      "achieved": round(kern_bytes / t_kern / 1e9, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(kern_bytes / t_kern / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(spec.name, splits),
+                     "traffic": measured_traffic(spec.name, splits) if W == 0 else None,
                      "avg_us": round(t_kern * 1e6, 3),
                      "bytes_per_launch": kern_bytes},
     }
@@ -263,15 +276,16 @@ def run_decode_workload(args, torch, plx, synth, oracle):
             t = time.perf_counter()
             reps = 0
             while True:
-                oracle.decode(qs, rs, k_h, v_h, seq_start=cu[:nb], seq_len=lens[:nb])
+                oracle.decode(qs, rs, k_h, v_h, seq_start=cu[:nb], seq_len=lens[:nb], window=W)
                 reps += 1
                 if time.perf_counter() - t > args.cpu_seconds:
                     break
             per_seq = (time.perf_counter() - t) / reps / nb
             # scale by tokens: the oracle's cost is linear in the visible keys
-            us = per_seq * nb / toks * T * 1e6
-            sample = f"{nb} of {spec.B} sequences ({toks} of {T} keys), {reps} repeats, " \
-                     "scaled to the full step by key count"
+            toks_vis = int(np.minimum(lens[:nb], W).sum()) if W > 0 else toks
+            us = per_seq * nb / toks_vis * T_vis * 1e6
+            sample = f"{nb} of {spec.B} sequences ({toks_vis} of {T_vis} visible keys), " \
+                     f"{reps} repeats, scaled to the full step by key count"
             threads = min(omp_threads(), nb * spec.Hq)
         else:
             k_h = synth.decode_kv_rows(spec, synth.TID_K, 0, T).reshape(spec.B, spec.L, spec.Hkv,
@@ -279,8 +293,8 @@ def run_decode_workload(args, torch, plx, synth, oracle):
             v_h = synth.decode_kv_rows(spec, synth.TID_V, 0, T).reshape(spec.B, spec.L, spec.Hkv,
                                                                          spec.D)
             us, reps, threads = cpu_baseline_decode(oracle, q_np, r_np, (k_h, v_h), spec,
-                                                    args.cpu_seconds)
-            sample = f"the full step (all {spec.Hq} heads x {T} keys), {reps} repeats"
+                                                    args.cpu_seconds, W)
+            sample = f"the full step (all {spec.Hq} heads x {T_vis} keys), {reps} repeats"
         res["cpu_baseline"] = {"value": round(us, 1), "unit": "us/step", "cores": threads,
                                "kind": "oracle", "sample": sample}
     # parity of the timed configuration on a few rows (the full check lives in the tests)
@@ -292,7 +306,7 @@ def run_decode_workload(args, torch, plx, synth, oracle):
         k_h = synth.decode_kv_rows(spec, synth.TID_K, int(cu[b]), toks)[None]
         v_h = synth.decode_kv_rows(spec, synth.TID_V, int(cu[b]), toks)[None]
         ref = oracle.decode(np.ascontiguousarray(q_np[b:b + 1]), np.ascontiguousarray(r_np[b:b + 1]),
-                            k_h, v_h)[0, h]
+                            k_h, v_h, window=W)[0, h]
         errs.append(float(np.abs(o_full[b, h] - ref).max() / np.abs(ref).max()))
     res["sampled_parity_max_norm_err"] = max(errs)
     return res
@@ -309,19 +323,22 @@ def run_prefill_workload(args, torch, plx, synth, oracle):
     t = {n: torch.from_numpy(a).view(torch.bfloat16).cuda() for n, a in arrs.items()}
     out = torch.empty_like(t["q"])
 
+    W = args.window
+
     def step(i):
-        plx.prefill(t["q"], t["r"], t["k"], t["v"], out=out)
+        plx.prefill(t["q"], t["r"], t["k"], t["v"], out=out, window=W)
 
     steps = max(1, min(args.steps, 20))
     warm = max(1, min(args.warmup, 3))
     ts = graph_time(torch, step, steps, warm)
-    flops = 8 * D * Hq * B * L * (L + 1) // 2
+    flops = 8 * D * Hq * B * visible_pairs(L, W)
     res = {
         "metric": METRIC, "value": round(flops / ts / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": steps, "warmup": warm, "ms_per_step": round(ts * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": spec.name, "B": B, "Hq": Hq, "Hkv": Hkv, "L": L, "head_dim": D},
+        "config": {"workload": spec.name + (f" window{W}" if W > 0 else ""), "B": B, "Hq": Hq,
+                   "Hkv": Hkv, "L": L, "head_dim": D, "window": W},
         "roofline": {"bound": "mfma", "kernel": "prefill", "achieved": round(flops / ts / 1e12, 2),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(flops / ts / 1e12 / BF16_PEAK_TFLOPS, 4), "traffic": None,
@@ -329,7 +346,7 @@ def run_prefill_workload(args, torch, plx, synth, oracle):
     }
     rows = np.array([[0, 0, 0], [B - 1, Hq - 1, L - 1], [3, 5, 1000], [7, 8, 2047]])
     o = out.float().cpu().numpy()
-    ref = oracle.prefill(arrs["q"], arrs["r"], arrs["k"], arrs["v"], rows=rows)
+    ref = oracle.prefill(arrs["q"], arrs["r"], arrs["k"], arrs["v"], rows=rows, window=W)
     got = o[rows[:, 0], rows[:, 1], rows[:, 2]]
     res["sampled_parity_max_norm_err"] = float(
         (np.abs(got - ref).max(axis=1) / np.abs(ref).max(axis=1)).max())  # worst row
@@ -342,13 +359,14 @@ def run_prefill_workload(args, torch, plx, synth, oracle):
         tt = time.perf_counter()
         reps = 0
         while True:
-            oracle.prefill(arrs["q"], arrs["r"], arrs["k"], arrs["v"], rows=sample_rows)
+            oracle.prefill(arrs["q"], arrs["r"], arrs["k"], arrs["v"], rows=sample_rows, window=W)
             reps += 1
             if time.perf_counter() - tt > args.cpu_seconds:
                 break
         per = (time.perf_counter() - tt) / reps
-        keys_sample = float((sample_rows[:, 2] + 1).sum())
-        keys_full = B * Hq * L * (L + 1) / 2
+        vis = sample_rows[:, 2] + 1
+        keys_sample = float((np.minimum(vis, W) if W > 0 else vis).sum())
+        keys_full = B * Hq * visible_pairs(L, W)
         sec_full = per * keys_full / keys_sample
         res["cpu_baseline"] = {"value": round(flops / sec_full / 1e12, 6), "unit": "TFLOP/s",
                                "cores": min(omp_threads(), n), "kind": "oracle",
@@ -366,7 +384,8 @@ def run_backward_workload(args, torch, plx, synth, oracle):
                              ("do", synth.TID_DO, Hq, 1.0)):
         arrs[name] = synth.normal(spec.seed, tid, (B, H, L, D), sc, spec.dtype)
     t = {n: torch.from_numpy(a).view(torch.bfloat16).cuda() for n, a in arrs.items()}
-    o, lse, sbar = plx.prefill(t["q"], t["r"], t["k"], t["v"], return_stats=True)
+    W = args.window
+    o, lse, sbar = plx.prefill(t["q"], t["r"], t["k"], t["v"], return_stats=True, window=W)
     grads = (torch.empty_like(t["q"]), torch.empty_like(t["r"]), torch.empty_like(t["k"]),
              torch.empty_like(t["v"]))
     ws = torch.empty(int(plx.lib().parallax_prefill_backward_workspace_bytes(B, Hq, L)),
@@ -374,21 +393,22 @@ def run_backward_workload(args, torch, plx, synth, oracle):
 
     def step(i):
         plx.prefill_backward(t["q"], t["r"], t["k"], t["v"], o, t["do"], lse, sbar,
-                             workspace=ws, out=grads)
+                             workspace=ws, out=grads, window=W)
 
     steps = max(1, min(args.steps, 10))
     warm = max(1, min(args.warmup, 2))
     ts = graph_time(torch, step, steps, warm)
     # algorithmic: 8 contractions of 2D flops per visible (query, key) pair and query head --
     # recompute Z, S, U; dV; dQ, dR; dK from dZ and dS
-    flops = 16 * D * Hq * B * L * (L + 1) // 2
+    flops = 16 * D * Hq * B * visible_pairs(L, W)
     res = {
         "metric": METRIC, "value": round(flops / ts / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": steps, "warmup": warm, "ms_per_step": round(ts * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "causal-prefill-backward-bf16 B8 L4096 Hq16 Hkv8 D128", "B": B,
-                   "Hq": Hq, "Hkv": Hkv, "L": L, "head_dim": D},
+        "config": {"workload": "causal-prefill-backward-bf16 B8 L4096 Hq16 Hkv8 D128"
+                               + (f" window{W}" if W > 0 else ""), "B": B, "Hq": Hq, "Hkv": Hkv,
+                   "L": L, "head_dim": D, "window": W},
         "roofline": {"bound": "mfma", "kernel": "prefill_backward (row pass + key pass)",
                      "achieved": round(flops / ts / 1e12, 2), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(flops / ts / 1e12 / BF16_PEAK_TFLOPS, 4),
@@ -402,7 +422,7 @@ def run_backward_workload(args, torch, plx, synth, oracle):
     reps = 0
     while True:
         ref = oracle.prefill_backward(arrs["q"], arrs["r"], arrs["k"], arrs["v"], arrs["do"],
-                                      units=units)
+                                      units=units, window=W)
         reps += 1
         if args.no_cpu_baseline or time.perf_counter() - tt > args.cpu_seconds:
             break

@@ -34,6 +34,12 @@
  *  - Results do not depend on timing: no atomics, a fixed split plan, so
  *    repeated calls return bit-identical outputs.
  *  - Non-finite inputs propagate; they are not checked.
+ *  - qk_scale must be finite and > 0, rk_scale finite (else INVALID_ARG).
+ *  - window (sliding-window attention; the PyPI README's overview calls it
+ *    structurally compatible with Parallax and defines none): 0 = none; W > 0
+ *    lets a prefill query i see keys max(0, i - W + 1) .. i, and a decode
+ *    query see the last min(n, W) of its sequence's n cached keys. < 0 is
+ *    INVALID_ARG.
  */
 #ifndef PARALLAX_H
 #define PARALLAX_H
@@ -45,7 +51,7 @@
 extern "C" {
 #endif
 
-#define PARALLAX_ABI_VERSION 1
+#define PARALLAX_ABI_VERSION 2
 
 typedef enum {
     PLX_OK = 0,
@@ -88,12 +94,12 @@ const char *parallax_status_string(int status);
  *             arguments (may be NULL when that size is 0).
  * Returns PLX_OK or an error status.
  * ---------------------------------------------------------------------- */
-size_t parallax_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int kv_len, int dtype,
-                                       int num_splits);
+size_t parallax_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int kv_len, int window,
+                                       int dtype, int num_splits);
 
 int parallax_decode(const void *q, const void *r, const void *k, const void *v, void *o,
                     const int32_t *cu_seqlens_k, int B, int Hq, int Hkv, int D, int kv_len,
-                    float qk_scale, float rk_scale, int dtype, int num_splits,
+                    int window, float qk_scale, float rk_scale, int dtype, int num_splits,
                     void *workspace, size_t workspace_bytes, void *stream);
 
 /* Plain softmax-attention decode on the same kernels and loader with the
@@ -102,12 +108,12 @@ int parallax_decode(const void *q, const void *r, const void *k, const void *v, 
  * parallax_decode without r and rk_scale. Uses the same workspace size. */
 int softmax_decode(const void *q, const void *k, const void *v, void *o,
                    const int32_t *cu_seqlens_k, int B, int Hq, int Hkv, int D, int kv_len,
-                   float qk_scale, int dtype, int num_splits, void *workspace,
+                   int window, float qk_scale, int dtype, int num_splits, void *workspace,
                    size_t workspace_bytes, void *stream);
 
 /* The split count parallax_decode / softmax_decode use for these
  * arguments (num_splits resolved when it is 0), or 0 when they are invalid. */
-int parallax_decode_num_splits(int B, int Hq, int Hkv, int D, int kv_len, int dtype,
+int parallax_decode_num_splits(int B, int Hq, int Hkv, int D, int kv_len, int window, int dtype,
                                int num_splits);
 
 /* ------------------------------------------------------------------------
@@ -139,7 +145,7 @@ size_t parallax_decode_record_bytes(int B, int Hq, int D, int num_records);
  * `records` is NULL or too small. */
 int parallax_decode_partial(const void *q, const void *r, const void *k, const void *v,
                             const int32_t *cu_seqlens_k, int B, int Hq, int Hkv, int D, int kv_len,
-                            float qk_scale, float rk_scale, int dtype, int num_splits,
+                            int window, float qk_scale, float rk_scale, int dtype, int num_splits,
                             void *records, size_t records_bytes, void *stream);
 
 /* Merge records[B][Hq][num_records] (DEVICE) into o [B, Hq, D] (DEVICE,
@@ -163,7 +169,7 @@ int parallax_decode_merge(const void *records, void *o, int B, int Hq, int D, in
  *   other D in {64, 128} and PLX_F32 run on a plain fp32 kernel. L <= 2^22.
  * ---------------------------------------------------------------------- */
 int parallax_prefill(const void *q, const void *r, const void *k, const void *v, void *o,
-                     float *lse, float *sbar, int B, int Hq, int Hkv, int L, int D,
+                     float *lse, float *sbar, int B, int Hq, int Hkv, int L, int D, int window,
                      float qk_scale, float rk_scale, int dtype, void *stream);
 
 /* ------------------------------------------------------------------------
@@ -180,7 +186,7 @@ int parallax_prefill(const void *q, const void *r, const void *k, const void *v,
  *   k, v, dk, dv         : [B, Hkv, L, D]     (dk, dv sum over the Hq / Hkv
  *                                              query heads of each KV head)
  *   lse, sbar : DEVICE float [B, Hq, L], as written by parallax_prefill for
- *               the same q, r, k, v, scales and dtype; o likewise.
+ *               the same q, r, k, v, window, scales and dtype; o likewise.
  *   workspace, workspace_bytes : DEVICE scratch of at least
  *               parallax_prefill_backward_workspace_bytes(B, Hq, L) bytes
  *               (16 bytes per query row).
@@ -192,8 +198,9 @@ size_t parallax_prefill_backward_workspace_bytes(int B, int Hq, int L);
 int parallax_prefill_backward(const void *q, const void *r, const void *k, const void *v,
                               const void *o, const void *d_o, const float *lse,
                               const float *sbar, void *dq, void *dr, void *dk, void *dv, int B,
-                              int Hq, int Hkv, int L, int D, float qk_scale, float rk_scale,
-                              int dtype, void *workspace, size_t workspace_bytes, void *stream);
+                              int Hq, int Hkv, int L, int D, int window, float qk_scale,
+                              float rk_scale, int dtype, void *workspace, size_t workspace_bytes,
+                              void *stream);
 
 #ifdef __cplusplus
 }

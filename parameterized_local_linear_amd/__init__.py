@@ -53,29 +53,29 @@ def lib() -> ctypes.CDLL:
         L.parallax_abi_version.restype = i32
         L.parallax_status_string.argtypes = [i32]
         L.parallax_status_string.restype = ctypes.c_char_p
-        L.parallax_decode_workspace_bytes.argtypes = [i32] * 7
+        L.parallax_decode_workspace_bytes.argtypes = [i32] * 8
         L.parallax_decode_workspace_bytes.restype = sz
-        L.parallax_decode_num_splits.argtypes = [i32] * 7
+        L.parallax_decode_num_splits.argtypes = [i32] * 8
         L.parallax_decode_num_splits.restype = i32
-        L.parallax_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, f32,
-                                      i32, i32, vp, sz, vp]
+        L.parallax_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
+                                      f32, i32, i32, vp, sz, vp]
         L.parallax_decode.restype = i32
-        L.softmax_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32,
-                                     vp, sz, vp]
+        L.softmax_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32,
+                                     i32, vp, sz, vp]
         L.softmax_decode.restype = i32
-        L.parallax_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
-                                       f32, i32, vp]
+        L.parallax_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                       f32, f32, i32, vp]
         L.parallax_prefill.restype = i32
         L.parallax_decode_record_bytes.argtypes = [i32, i32, i32, i32]
         L.parallax_decode_record_bytes.restype = sz
-        L.parallax_decode_partial.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, f32,
-                                              i32, i32, vp, sz, vp]
+        L.parallax_decode_partial.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
+                                              f32, i32, i32, vp, sz, vp]
         L.parallax_decode_partial.restype = i32
         L.parallax_decode_merge.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, vp]
         L.parallax_decode_merge.restype = i32
         L.parallax_prefill_backward_workspace_bytes.argtypes = [i32, i32, i32]
         L.parallax_prefill_backward_workspace_bytes.restype = sz
-        L.parallax_prefill_backward.argtypes = [vp] * 12 + [i32] * 5 + [f32, f32, i32, vp, sz, vp]
+        L.parallax_prefill_backward.argtypes = [vp] * 12 + [i32] * 6 + [f32, f32, i32, vp, sz, vp]
         L.parallax_prefill_backward.restype = i32
         _lib = L
     return _lib
@@ -106,17 +106,18 @@ def _check(t: torch.Tensor, name: str, dtype, device):
         raise ValueError(f"{name} must be contiguous")
 
 
-def decode_workspace_bytes(B, Hq, Hkv, D, kv_len, dtype_code, num_splits=0) -> int:
-    return int(lib().parallax_decode_workspace_bytes(B, Hq, Hkv, D, kv_len, dtype_code,
+def decode_workspace_bytes(B, Hq, Hkv, D, kv_len, dtype_code, num_splits=0, window=0) -> int:
+    return int(lib().parallax_decode_workspace_bytes(B, Hq, Hkv, D, kv_len, window, dtype_code,
                                                      num_splits))
 
 
-def decode_num_splits(B, Hq, Hkv, D, kv_len, dtype_code, num_splits=0) -> int:
-    return int(lib().parallax_decode_num_splits(B, Hq, Hkv, D, kv_len, dtype_code, num_splits))
+def decode_num_splits(B, Hq, Hkv, D, kv_len, dtype_code, num_splits=0, window=0) -> int:
+    return int(lib().parallax_decode_num_splits(B, Hq, Hkv, D, kv_len, window, dtype_code,
+                                                num_splits))
 
 
 def _decode_impl(q, r, k, v, qk_scale, rk_scale, cu_seqlens_k, kv_len, num_splits, out,
-                 workspace, parallax):
+                 workspace, parallax, window):
     L_ = lib()
     squeeze = q.dim() == 4
     if squeeze:                       # the pages' (B, 1, H, D)
@@ -159,19 +160,20 @@ def _decode_impl(q, r, k, v, qk_scale, rk_scale, cu_seqlens_k, kv_len, num_split
         _check(out, "out", dt, dev)
         if out.shape != (B, Hq, D):
             raise ValueError("out must be [B, Hq, D]")
-    need = decode_workspace_bytes(B, Hq, Hkv, D, int(kv_len), code, num_splits)
+    need = decode_workspace_bytes(B, Hq, Hkv, D, int(kv_len), code, num_splits, window)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     stream = _stream_handle(dev)
     if parallax:
         st = L_.parallax_decode(_ptr(q), _ptr(r), _ptr(k), _ptr(v), _ptr(out), _ptr(cu_seqlens_k),
-                                B, Hq, Hkv, D, int(kv_len), float(qk_scale), float(rk_scale), code,
-                                int(num_splits), _ptr(workspace), ws_bytes, stream)
+                                B, Hq, Hkv, D, int(kv_len), int(window), float(qk_scale),
+                                float(rk_scale), code, int(num_splits), _ptr(workspace), ws_bytes,
+                                stream)
         what = "parallax_decode"
     else:
         st = L_.softmax_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(cu_seqlens_k), B, Hq, Hkv,
-                               D, int(kv_len), float(qk_scale), code, int(num_splits),
+                               D, int(kv_len), int(window), float(qk_scale), code, int(num_splits),
                                _ptr(workspace), ws_bytes, stream)
         what = "softmax_decode"
     if st != 0:
@@ -180,22 +182,23 @@ def _decode_impl(q, r, k, v, qk_scale, rk_scale, cu_seqlens_k, kv_len, num_split
 
 
 def decode(q, r, k, v, qk_scale=None, rk_scale=1.0, *, cu_seqlens_k=None, kv_len=None,
-           num_splits=0, out=None, workspace=None):
+           num_splits=0, out=None, workspace=None, window=0):
     """Parallax decode. q, r: [B, Hq, D] (or [B, 1, Hq, D]); k, v: [B, kv_len, Hkv, D],
-    or packed [T, Hkv, D] with int32 ``cu_seqlens_k`` [B + 1] and ``kv_len`` = max length."""
+    or packed [T, Hkv, D] with int32 ``cu_seqlens_k`` [B + 1] and ``kv_len`` = max length.
+    ``window`` > 0: each sequence's last ``window`` keys only."""
     return _decode_impl(q, r, k, v, qk_scale, rk_scale, cu_seqlens_k, kv_len, num_splits, out,
-                        workspace, True)
+                        workspace, True, window)
 
 
 def softmax_decode(q, k, v, qk_scale=None, *, cu_seqlens_k=None, kv_len=None, num_splits=0,
-                   out=None, workspace=None):
+                   out=None, workspace=None, window=0):
     """Softmax-attention decode on the same kernels (the Parallax correction compiled out)."""
     return _decode_impl(q, None, k, v, qk_scale, 1.0, cu_seqlens_k, kv_len, num_splits, out,
-                        workspace, False)
+                        workspace, False, window)
 
 
 def decode_partial(q, r, k, v, qk_scale=None, rk_scale=1.0, *, cu_seqlens_k=None, kv_len=None,
-                   num_splits=0, records=None):
+                   num_splits=0, records=None, window=0):
     """Streaming half of decode: returns (records, n) with records a float32
     [B, Hq, n, 2D + 4] tensor (A, B, m, l, S, pi per split). r=None: softmax records."""
     L_ = lib()
@@ -214,13 +217,14 @@ def decode_partial(q, r, k, v, qk_scale=None, rk_scale=1.0, *, cu_seqlens_k=None
     code = _dtype_code(q)
     if qk_scale is None:
         qk_scale = 1.0 / math.sqrt(D)
-    n = decode_num_splits(B, Hq, Hkv, D, int(kv_len), code, num_splits)
+    n = decode_num_splits(B, Hq, Hkv, D, int(kv_len), code, num_splits, window)
     if n == 0:
         raise ParallaxError(1, "parallax_decode_partial")
     if records is None:
         records = torch.empty((B, Hq, n, 2 * D + 4), dtype=torch.float32, device=dev)
     st = L_.parallax_decode_partial(_ptr(q), _ptr(r), _ptr(k), _ptr(v), _ptr(cu_seqlens_k), B, Hq,
-                                    Hkv, D, int(kv_len), float(qk_scale), float(rk_scale), code,
+                                    Hkv, D, int(kv_len), int(window), float(qk_scale),
+                                    float(rk_scale), code,
                                     int(num_splits), _ptr(records),
                                     records.numel() * records.element_size(), _stream_handle(dev))
     if st != 0:
@@ -243,9 +247,10 @@ def decode_merge(records, dtype=torch.bfloat16, with_probe=True, out=None):
     return out
 
 
-def prefill(q, r, k, v, qk_scale=None, rk_scale=1.0, *, out=None, return_stats=False):
+def prefill(q, r, k, v, qk_scale=None, rk_scale=1.0, *, out=None, return_stats=False, window=0):
     """Causal Parallax prefill. q, r: [B, Hq, L, D]; k, v: [B, Hkv, L, D] -> o [B, Hq, L, D]
-    (plus fp32 lse and sbar [B, Hq, L] with return_stats=True)."""
+    (plus fp32 lse and sbar [B, Hq, L] with return_stats=True). ``window`` > 0: query i
+    sees keys i - window + 1 .. i."""
     L_ = lib()
     B, Hq, L, D = q.shape
     dev, dt = q.device, q.dtype
@@ -270,7 +275,7 @@ def prefill(q, r, k, v, qk_scale=None, rk_scale=1.0, *, out=None, return_stats=F
         lse = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
         sbar = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
     st = L_.parallax_prefill(_ptr(q), _ptr(r), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(sbar),
-                             B, Hq, Hkv, L, D, float(qk_scale), float(rk_scale), code,
+                             B, Hq, Hkv, L, D, int(window), float(qk_scale), float(rk_scale), code,
                              _stream_handle(dev))
     if st != 0:
         raise ParallaxError(st, "parallax_prefill")
@@ -278,7 +283,7 @@ def prefill(q, r, k, v, qk_scale=None, rk_scale=1.0, *, out=None, return_stats=F
 
 
 def prefill_backward(q, r, k, v, o, d_o, lse, sbar, qk_scale=None, rk_scale=1.0, *,
-                     workspace=None, out=None):
+                     workspace=None, out=None, window=0):
     """Gradients of the causal prefill: (dq, dr, dk, dv) for the upstream
     gradient ``d_o``, from the forward's o, lse and sbar (prefill with
     return_stats=True on the same inputs and scales). ``out``: optional
@@ -311,7 +316,8 @@ def prefill_backward(q, r, k, v, o, d_o, lse, sbar, qk_scale=None, rk_scale=1.0,
             raise ValueError(f"{name} must have shape {tuple(ref.shape)}")
     st = L_.parallax_prefill_backward(
         _ptr(q), _ptr(r), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse), _ptr(sbar), _ptr(dq),
-        _ptr(dr), _ptr(dk), _ptr(dv), B, Hq, Hkv, L, D, float(qk_scale), float(rk_scale),
+        _ptr(dr), _ptr(dk), _ptr(dv), B, Hq, Hkv, L, D, int(window), float(qk_scale),
+        float(rk_scale),
         _dtype_code(q), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream_handle(dev))
     if st != 0:
@@ -321,25 +327,27 @@ def prefill_backward(q, r, k, v, o, d_o, lse, sbar, qk_scale=None, rk_scale=1.0,
 
 class _ParallaxFunction(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, r, k, v, qk_scale, rk_scale):
-        o, lse, sbar = prefill(q, r, k, v, qk_scale, rk_scale, return_stats=True)
+    def forward(ctx, q, r, k, v, qk_scale, rk_scale, window):
+        o, lse, sbar = prefill(q, r, k, v, qk_scale, rk_scale, return_stats=True, window=window)
         ctx.save_for_backward(q, r, k, v, o, lse, sbar)
         ctx.scales = (qk_scale, rk_scale)
+        ctx.window = window
         return o
 
     @staticmethod
     def backward(ctx, d_o):
         q, r, k, v, o, lse, sbar = ctx.saved_tensors
-        grads = prefill_backward(q, r, k, v, o, d_o.contiguous(), lse, sbar, *ctx.scales)
-        return (*grads, None, None)
+        grads = prefill_backward(q, r, k, v, o, d_o.contiguous(), lse, sbar, *ctx.scales,
+                                 window=ctx.window)
+        return (*grads, None, None, None)
 
 
-def parallax_func(q, r, k, v, qk_scale=None, rk_scale=1.0):
+def parallax_func(q, r, k, v, qk_scale=None, rk_scale=1.0, *, window=0):
     """Causal Parallax attention on [B, H, L, D] tensors, differentiable in
-    q, r, k and v (the pages' training entry point)."""
+    q, r, k and v (the pages' training entry point); ``window`` as in prefill."""
     if torch.is_grad_enabled() and any(t.requires_grad for t in (q, r, k, v)):
-        return _ParallaxFunction.apply(q, r, k, v, qk_scale, rk_scale)
-    return prefill(q, r, k, v, qk_scale, rk_scale)
+        return _ParallaxFunction.apply(q, r, k, v, qk_scale, rk_scale, window)
+    return prefill(q, r, k, v, qk_scale, rk_scale, window=window)
 
 
 parallax_decode = decode

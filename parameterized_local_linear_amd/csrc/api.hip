@@ -35,8 +35,10 @@ int device_cu_count() {
 // normalisation into the streaming kernel and needs no workspace.
 constexpr int kTargetWavesPerCU = 4;
 constexpr int kMinKeysPerWave = 128;
-DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int kv_len, int dtype, int num_splits) {
+DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int kv_len, int window, int dtype,
+                       int num_splits) {
     DecodePlan p;
+    if (window > 0 && window < kv_len) kv_len = window;  // keys a query can see at most
     const int G = Hq / Hkv;
     const bool mfma = dtype == PLX_BF16 && D == 128 && (G == 1 || G == 2 || G == 4 || G == 8);
     p.path = mfma ? DecodePath::Mfma : DecodePath::Generic;
@@ -79,8 +81,8 @@ using plx::DecodePlan;
 // with 32-bit byte offsets.
 constexpr int kMaxPrefillLen = 1 << 22;
 
-static int check_decode_sizes(int B, int Hq, int Hkv, int D, int kv_len, int dtype) {
-    if (B < 1 || Hq < 1 || Hkv < 1 || kv_len < 1) return PLX_ERR_INVALID_ARG;
+static int check_decode_sizes(int B, int Hq, int Hkv, int D, int kv_len, int window, int dtype) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || kv_len < 1 || window < 0) return PLX_ERR_INVALID_ARG;
     if (Hq % Hkv != 0) return PLX_ERR_INVALID_ARG;
     if (B > 65535 || Hq > 65535) return PLX_ERR_UNSUPPORTED;
     if (dtype != PLX_F32 && dtype != PLX_BF16) return PLX_ERR_UNSUPPORTED;
@@ -103,27 +105,29 @@ const char *parallax_status_string(int status) {
     }
 }
 
-size_t parallax_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int kv_len, int dtype,
-                                       int num_splits) {
-    if (check_decode_sizes(B, Hq, Hkv, D, kv_len, dtype) != PLX_OK) return 0;
-    return plx::plan_decode(B, Hq, Hkv, D, kv_len, dtype, num_splits).ws_bytes;
+size_t parallax_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int kv_len, int window,
+                                       int dtype, int num_splits) {
+    if (check_decode_sizes(B, Hq, Hkv, D, kv_len, window, dtype) != PLX_OK) return 0;
+    return plx::plan_decode(B, Hq, Hkv, D, kv_len, window, dtype, num_splits).ws_bytes;
 }
 
-int parallax_decode_num_splits(int B, int Hq, int Hkv, int D, int kv_len, int dtype, int num_splits) {
-    if (check_decode_sizes(B, Hq, Hkv, D, kv_len, dtype) != PLX_OK) return 0;
-    return plx::plan_decode(B, Hq, Hkv, D, kv_len, dtype, num_splits).splits;
+int parallax_decode_num_splits(int B, int Hq, int Hkv, int D, int kv_len, int window, int dtype,
+                               int num_splits) {
+    if (check_decode_sizes(B, Hq, Hkv, D, kv_len, window, dtype) != PLX_OK) return 0;
+    return plx::plan_decode(B, Hq, Hkv, D, kv_len, window, dtype, num_splits).splits;
 }
 
 static int fill_decode_args(plx::DecodeArgs &a, const void *q, const void *r, const void *k,
                             const void *v, void *o, const int32_t *cu, int B, int Hq, int Hkv, int D,
-                            int kv_len, float qk_scale, float rk_scale, int dtype, int num_splits,
-                            bool parallax, DecodePlan &p) {
-    int st = check_decode_sizes(B, Hq, Hkv, D, kv_len, dtype);
+                            int kv_len, int window, float qk_scale, float rk_scale, int dtype,
+                            int num_splits, bool parallax, DecodePlan &p) {
+    int st = check_decode_sizes(B, Hq, Hkv, D, kv_len, window, dtype);
     if (st != PLX_OK) return st;
     if (!q || !k || !v || !o || (parallax && !r)) return PLX_ERR_INVALID_ARG;
     if (num_splits < 0) return PLX_ERR_INVALID_ARG;
-    if (!isfinite(qk_scale) || !isfinite(rk_scale)) return PLX_ERR_INVALID_ARG;
-    p = plx::plan_decode(B, Hq, Hkv, D, kv_len, dtype, num_splits);
+    // masked logits are -inf before scaling, so the scale must be positive
+    if (!isfinite(qk_scale) || !(qk_scale > 0.f) || !isfinite(rk_scale)) return PLX_ERR_INVALID_ARG;
+    p = plx::plan_decode(B, Hq, Hkv, D, kv_len, window, dtype, num_splits);
     a.q = q;
     a.r = r;
     a.k = k;
@@ -135,6 +139,7 @@ static int fill_decode_args(plx::DecodeArgs &a, const void *q, const void *r, co
     a.Hkv = Hkv;
     a.D = D;
     a.kv_len = kv_len;
+    a.window = window;
     a.zscale = qk_scale * plx::kLog2e;
     a.rk_scale = rk_scale;
     a.splits = p.splits;
@@ -145,13 +150,13 @@ static int fill_decode_args(plx::DecodeArgs &a, const void *q, const void *r, co
 }
 
 static int decode_common(const void *q, const void *r, const void *k, const void *v, void *o,
-                         const int32_t *cu, int B, int Hq, int Hkv, int D, int kv_len,
+                         const int32_t *cu, int B, int Hq, int Hkv, int D, int kv_len, int window,
                          float qk_scale, float rk_scale, int dtype, int num_splits, void *ws,
                          size_t ws_bytes, void *stream, bool parallax) {
     plx::DecodeArgs a;
     DecodePlan p;
-    int st = fill_decode_args(a, q, r, k, v, o, cu, B, Hq, Hkv, D, kv_len, qk_scale, rk_scale, dtype,
-                              num_splits, parallax, p);
+    int st = fill_decode_args(a, q, r, k, v, o, cu, B, Hq, Hkv, D, kv_len, window, qk_scale, rk_scale,
+                              dtype, num_splits, parallax, p);
     if (st != PLX_OK) return st;
     if (p.ws_bytes > 0 && (!ws || ws_bytes < p.ws_bytes)) return PLX_ERR_WORKSPACE;
     a.ws = reinterpret_cast<float *>(ws);
@@ -163,17 +168,17 @@ static int decode_common(const void *q, const void *r, const void *k, const void
 
 int parallax_decode(const void *q, const void *r, const void *k, const void *v, void *o,
                     const int32_t *cu_seqlens_k, int B, int Hq, int Hkv, int D, int kv_len,
-                    float qk_scale, float rk_scale, int dtype, int num_splits, void *workspace,
-                    size_t workspace_bytes, void *stream) {
-    return decode_common(q, r, k, v, o, cu_seqlens_k, B, Hq, Hkv, D, kv_len, qk_scale, rk_scale,
-                         dtype, num_splits, workspace, workspace_bytes, stream, true);
+                    int window, float qk_scale, float rk_scale, int dtype, int num_splits,
+                    void *workspace, size_t workspace_bytes, void *stream) {
+    return decode_common(q, r, k, v, o, cu_seqlens_k, B, Hq, Hkv, D, kv_len, window, qk_scale,
+                         rk_scale, dtype, num_splits, workspace, workspace_bytes, stream, true);
 }
 
 int softmax_decode(const void *q, const void *k, const void *v, void *o, const int32_t *cu_seqlens_k,
-                   int B, int Hq, int Hkv, int D, int kv_len, float qk_scale, int dtype, int num_splits,
-                   void *workspace, size_t workspace_bytes, void *stream) {
-    return decode_common(q, nullptr, k, v, o, cu_seqlens_k, B, Hq, Hkv, D, kv_len, qk_scale, 1.0f,
-                         dtype, num_splits, workspace, workspace_bytes, stream, false);
+                   int B, int Hq, int Hkv, int D, int kv_len, int window, float qk_scale, int dtype,
+                   int num_splits, void *workspace, size_t workspace_bytes, void *stream) {
+    return decode_common(q, nullptr, k, v, o, cu_seqlens_k, B, Hq, Hkv, D, kv_len, window, qk_scale,
+                         1.0f, dtype, num_splits, workspace, workspace_bytes, stream, false);
 }
 
 size_t parallax_decode_record_bytes(int B, int Hq, int D, int num_records) {
@@ -183,14 +188,14 @@ size_t parallax_decode_record_bytes(int B, int Hq, int D, int num_records) {
 
 int parallax_decode_partial(const void *q, const void *r, const void *k, const void *v,
                             const int32_t *cu_seqlens_k, int B, int Hq, int Hkv, int D, int kv_len,
-                            float qk_scale, float rk_scale, int dtype, int num_splits,
+                            int window, float qk_scale, float rk_scale, int dtype, int num_splits,
                             void *records, size_t records_bytes, void *stream) {
     plx::DecodeArgs a;
     DecodePlan p;
     const bool parallax = r != nullptr;
     // o is not written in this mode; any non-null value passes the checks
-    int st = fill_decode_args(a, q, r, k, v, records, cu_seqlens_k, B, Hq, Hkv, D, kv_len, qk_scale,
-                              rk_scale, dtype, num_splits, parallax, p);
+    int st = fill_decode_args(a, q, r, k, v, records, cu_seqlens_k, B, Hq, Hkv, D, kv_len, window,
+                              qk_scale, rk_scale, dtype, num_splits, parallax, p);
     if (st != PLX_OK) return st;
     if (!records || records_bytes < parallax_decode_record_bytes(B, Hq, D, p.splits))
         return PLX_ERR_WORKSPACE;
@@ -220,12 +225,13 @@ int parallax_decode_merge(const void *records, void *o, int B, int Hq, int D, in
 }
 
 int parallax_prefill(const void *q, const void *r, const void *k, const void *v, void *o, float *lse,
-                     float *sbar, int B, int Hq, int Hkv, int L, int D, float qk_scale, float rk_scale,
-                     int dtype, void *stream) {
-    if (B < 1 || Hq < 1 || Hkv < 1 || L < 1 || D < 1) return PLX_ERR_INVALID_ARG;
+                     float *sbar, int B, int Hq, int Hkv, int L, int D, int window, float qk_scale,
+                     float rk_scale, int dtype, void *stream) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || L < 1 || D < 1 || window < 0) return PLX_ERR_INVALID_ARG;
     if (Hq % Hkv != 0) return PLX_ERR_INVALID_ARG;
     if (!q || !r || !k || !v || !o) return PLX_ERR_INVALID_ARG;
-    if (!isfinite(qk_scale) || !isfinite(rk_scale)) return PLX_ERR_INVALID_ARG;
+    // masked logits are -inf before scaling, so the scale must be positive
+    if (!isfinite(qk_scale) || !(qk_scale > 0.f) || !isfinite(rk_scale)) return PLX_ERR_INVALID_ARG;
     if (dtype != PLX_F32 && dtype != PLX_BF16) return PLX_ERR_UNSUPPORTED;
     if (!plx::prefill_supported(D, dtype)) return PLX_ERR_UNSUPPORTED;
     if (B > 65535 || Hq > 65535 || L > kMaxPrefillLen) return PLX_ERR_UNSUPPORTED;
@@ -242,6 +248,7 @@ int parallax_prefill(const void *q, const void *r, const void *k, const void *v,
     a.Hkv = Hkv;
     a.L = L;
     a.D = D;
+    a.window = (window > 0 && window < L) ? window : L;
     a.zscale = qk_scale * plx::kLog2e;
     a.rk_scale = rk_scale;
     hipError_t err = plx::launch_prefill(a, dtype, reinterpret_cast<hipStream_t>(stream));
@@ -255,14 +262,15 @@ size_t parallax_prefill_backward_workspace_bytes(int B, int Hq, int L) {
 
 int parallax_prefill_backward(const void *q, const void *r, const void *k, const void *v, const void *o,
                               const void *d_o, const float *lse, const float *sbar, void *dq, void *dr,
-                              void *dk, void *dv, int B, int Hq, int Hkv, int L, int D, float qk_scale,
-                              float rk_scale, int dtype, void *workspace, size_t workspace_bytes,
-                              void *stream) {
-    if (B < 1 || Hq < 1 || Hkv < 1 || L < 1 || D < 1) return PLX_ERR_INVALID_ARG;
+                              void *dk, void *dv, int B, int Hq, int Hkv, int L, int D, int window,
+                              float qk_scale, float rk_scale, int dtype, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || L < 1 || D < 1 || window < 0) return PLX_ERR_INVALID_ARG;
     if (Hq % Hkv != 0) return PLX_ERR_INVALID_ARG;
     if (!q || !r || !k || !v || !o || !d_o || !lse || !sbar || !dq || !dr || !dk || !dv)
         return PLX_ERR_INVALID_ARG;
-    if (!isfinite(qk_scale) || !isfinite(rk_scale)) return PLX_ERR_INVALID_ARG;
+    // masked logits are -inf before scaling, so the scale must be positive
+    if (!isfinite(qk_scale) || !(qk_scale > 0.f) || !isfinite(rk_scale)) return PLX_ERR_INVALID_ARG;
     if (dtype != PLX_F32 && dtype != PLX_BF16) return PLX_ERR_UNSUPPORTED;
     if (!plx::prefill_supported(D, dtype)) return PLX_ERR_UNSUPPORTED;
     if (B > 65535 || Hq > 65535 || L > kMaxPrefillLen) return PLX_ERR_UNSUPPORTED;
@@ -287,6 +295,7 @@ int parallax_prefill_backward(const void *q, const void *r, const void *k, const
     a.Hkv = Hkv;
     a.L = L;
     a.D = D;
+    a.window = (window > 0 && window < L) ? window : L;
     a.zscale = qk_scale * plx::kLog2e;
     a.qk_scale = qk_scale;
     a.rk_scale = rk_scale;

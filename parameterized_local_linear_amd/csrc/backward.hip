@@ -104,10 +104,11 @@ __global__ __launch_bounds__(64) void bwd_rows_generic(BackwardArgs a) {
     const float lse2 = a.lse[row] * kLog2e;
     const float sb = a.sbar[row];
     const int end = i + 1;
+    const int first = max(0, i - a.window + 1);  // sliding window: keys first .. i
 
     // sweep 1: ubar = sum_j w_j g.v_j
     float ub = 0.f;
-    for (int j0 = 0; j0 < end; j0 += KPI) {
+    for (int j0 = first; j0 < end; j0 += KPI) {
         const int j = j0 + kgrp;
         const int jj = j < end ? j : end - 1;
         float kv[EPL], vv[EPL];
@@ -127,7 +128,7 @@ __global__ __launch_bounds__(64) void bwd_rows_generic(BackwardArgs a) {
     // sweep 2: dq, dr
     float dqa[EPL], dra[EPL];
     for (int e = 0; e < EPL; ++e) dqa[e] = dra[e] = 0.f;
-    for (int j0 = 0; j0 < end; j0 += KPI) {
+    for (int j0 = first; j0 < end; j0 += KPI) {
         const int j = j0 + kgrp;
         const int jj = j < end ? j : end - 1;
         float kv[EPL], vv[EPL];
@@ -181,9 +182,10 @@ __global__ __launch_bounds__(64) void bwd_keys_generic(BackwardArgs a) {
     for (int e = 0; e < EPL; ++e) dka[e] = dva[e] = 0.f;
     for (int hs = 0; hs < G; ++hs) {
         const int64_t rbase = ((int64_t)b * a.Hq + hkv * G + hs) * a.L;
-        for (int i0 = j; i0 < a.L; i0 += RPI) {
+        const int rend = min(a.L, j + a.window);  // rows that see key j
+        for (int i0 = j; i0 < rend; i0 += RPI) {
             const int i = i0 + rgrp;
-            const int ii = i < a.L ? i : a.L - 1;
+            const int ii = i < rend ? i : rend - 1;
             const int64_t row = rbase + ii;
             float qv[EPL], rv[EPL], gv[EPL];
             Frag<T>::load(reinterpret_cast<const T *>(a.q) + row * D + c * EPL, qv);
@@ -199,7 +201,7 @@ __global__ __launch_bounds__(64) void bwd_keys_generic(BackwardArgs a) {
             zp = row_sum<LPR>(zp);
             sp = row_sum<LPR>(sp);
             up = row_sum<LPR>(up);
-            const float w = i < a.L ? __builtin_amdgcn_exp2f(fmaf(zp, a.zscale, -st.lse2)) : 0.f;
+            const float w = i < rend ? __builtin_amdgcn_exp2f(fmaf(zp, a.zscale, -st.lse2)) : 0.f;
             const float sc = fmaf(sp, a.rk_scale, -st.sbar);
             const float pv = w * (1.0f + sc);
             const float ds = w * (up - st.ubar) * a.rk_scale;
@@ -322,6 +324,8 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_rows_mfma_bf16_d128(Backwa
     const int q0 = qt * RPH + (wave % WPH) * 16;
     const int kend = min(a.L, (qt + 1) * RPH);
     const int ntiles = (kend + TK - 1) / TK;
+    const int W = a.window;                          // query i sees keys i - W + 1 .. i
+    const int tile0 = max(0, qt * RPH - W + 1) / TK;  // first tile any row of the item sees
 
     const int64_t kvbase = ((int64_t)b * a.Hkv + hkv) * a.L * D;
     const uint32_t kvbytes = (uint32_t)((int64_t)a.L * D * 2);
@@ -336,7 +340,7 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_rows_mfma_bf16_d128(Backwa
         dma_rows<TK, NW>(krs, tile * TK, lk, wave, lane);
         dma_rows<TK, NW>(vrs, tile * TK, lv, wave, lane);
     };
-    dma_tile(0, lds_k0, lds_v0);
+    dma_tile(tile0, lds_k0, lds_v0);
 
     // per-wave B operands (query row n, k step u -> chunk g + 4u) and row scalars
     const int64_t rowbase = ((int64_t)b * a.Hq + hq) * a.L;
@@ -391,15 +395,17 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_rows_mfma_bf16_d128(Backwa
         auto step = [&](int tile, uint16_t *lk, uint16_t *lv, uint16_t *nk, uint16_t *nv) __attribute__((always_inline)) {
             if (tile + 1 < ntiles) dma_tile(tile + 1, nk, nv);
             const int t0 = tile * TK;
-            if (t0 <= q_last) {
-                const bool diag = t0 + TK - 1 > q0;
+            // tiles outside the wave's visible band are skipped; the mask is
+            // needed unless every key of the tile is visible to all 16 rows
+            if (t0 <= q_last && t0 + TK - 1 > q0 - W) {
+                const bool diag = !(t0 + TK - 1 <= q0 && t0 > q_last - W);
 #pragma unroll
                 for (int j = 0; j < NSUB; ++j) body(lk, lv, 32 * j, t0 + 32 * j, diag);
             }
             __syncthreads();
         };
         __syncthreads();
-        for (int tile = 0; tile < ntiles; tile += 2) {
+        for (int tile = tile0; tile < ntiles; tile += 2) {
             step(tile, lds_k0, lds_v0, lds_k1, lds_v1);
             if (tile + 1 < ntiles) step(tile + 1, lds_k1, lds_v1, lds_k0, lds_v0);
         }
@@ -416,7 +422,8 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_rows_mfma_bf16_d128(Backwa
             const float z = t < 4 ? z0[t] : z1[t - 4];
             const float u = t < 4 ? u0[t] : u1[t - 4];
             float w = __builtin_amdgcn_exp2f(fmaf(z, a.zscale, -lse2));
-            if (diag && key0 + g + 4 * t > row) w = 0.f;
+            const int key = key0 + g + 4 * t;
+            if (diag && (key > row || key <= row - W)) w = 0.f;
             ub_part = fmaf(w, u, ub_part);
         }
     });
@@ -426,7 +433,7 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_rows_mfma_bf16_d128(Backwa
     floatx4 accQ[8], accR[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) accQ[e] = accR[e] = floatx4{0.f, 0.f, 0.f, 0.f};
-    dma_tile(0, lds_k0, lds_v0);
+    dma_tile(tile0, lds_k0, lds_v0);
     sweep([&](const uint16_t *lk, const uint16_t *lv, int kl, int key0, bool diag) __attribute__((always_inline)) {
         floatx4 z0, z1, s0, s1, u0, u1;
         {
@@ -444,7 +451,8 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_rows_mfma_bf16_d128(Backwa
             const float s = t < 4 ? s0[t] : s1[t - 4];
             const float u = t < 4 ? u0[t] : u1[t - 4];
             float w = __builtin_amdgcn_exp2f(fmaf(z, a.zscale, -lse2));
-            if (diag && key0 + g + 4 * t > row) w = 0.f;
+            const int key = key0 + g + 4 * t;
+            if (diag && (key > row || key <= row - W)) w = 0.f;
             const float sc = fmaf(s, a.rk_scale, -sb);
             pz[t] = (__bf16)(w * (fmaf(sc, u, u) - fmaf(ubar, sc, delta)));
             ps[t] = (__bf16)(w * (u - ubar));
@@ -512,7 +520,9 @@ __global__ __launch_bounds__(64 * kKeyWaves) void bwd_keys_mfma_bf16_d128(Backwa
     const int hkv = grp % a.Hkv;
     const int k0 = kblk * KB;
     const int kw = k0 + 16 * KBW * wave;  // this wave's first key
-    const int nrt = (a.L - k0 + TR - 1) / TR;  // row tiles per query head
+    const int W = a.window;
+    const int rend = min(a.L, k0 + KB - 1 + W);  // rows k0 .. rend - 1 see some key of the block
+    const int nrt = (rend - k0 + TR - 1) / TR;   // row tiles per query head
     const int ntiles = G * nrt;
 
     const int64_t kvbase = ((int64_t)b * a.Hkv + hkv) * a.L * D;
@@ -594,7 +604,8 @@ __global__ __launch_bounds__(64 * kKeyWaves) void bwd_keys_mfma_bf16_d128(Backwa
             for (int c = 0; c < KBW; ++c) {
                 const float zz = z[c][t >> 2][t & 3], ss = s[c][t >> 2][t & 3], u = uu[c][t >> 2][t & 3];
                 float w = __builtin_amdgcn_exp2f(fmaf(zz, a.zscale, -st.lse2));
-                if (mask && (rw < kw + 16 * c + n || rw >= a.L)) w = 0.f;
+                const int key = kw + 16 * c + n;
+                if (mask && (rw < key || rw >= key + W || rw >= a.L)) w = 0.f;
                 const float sc = fmaf(ss, a.rk_scale, -st.sbar);
                 p1[c][t] = (__bf16)(w * (1.0f + sc));
                 pz[c][t] = (__bf16)(w * (fmaf(sc, u, u) - fmaf(st.ubar, sc, st.delta)) * a.qk_scale);
@@ -621,8 +632,9 @@ __global__ __launch_bounds__(64 * kKeyWaves) void bwd_keys_mfma_bf16_d128(Backwa
 #pragma unroll
         for (int j = 0; j < TR / 32; ++j) {
             const int rs = r0 + 32 * j;
-            if (rs + 31 >= kw) {  // wave-uniform: sub-tiles wholly above the wave's keys are skipped
-                const bool mask = rs < kw + 16 * KBW - 1 || rs + 31 >= a.L;
+            // wave-uniform: sub-tiles that see none of the wave's keys are skipped
+            if (rs + 31 >= kw && rs < kw + 16 * KBW - 1 + W) {
+                const bool mask = rs < kw + 16 * KBW - 1 || rs + 31 >= kw + W || rs + 31 >= a.L;
                 if (mask)
                     sub_tile(tq, tr, tg, ts, 32 * j, rs, true);
                 else

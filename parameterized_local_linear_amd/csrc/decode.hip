@@ -59,6 +59,10 @@ __device__ __forceinline__ SeqRange seq_range(const DecodeArgs &a, int b) {
         s.tok0 = (int64_t)b * a.kv_len;
         s.len = a.kv_len;
     }
+    if (a.window > 0 && s.len > a.window) {  // sliding window: the last `window` keys
+        s.tok0 += s.len - a.window;
+        s.len = a.window;
+    }
     return s;
 }
 

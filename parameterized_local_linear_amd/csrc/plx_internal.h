@@ -29,6 +29,7 @@ struct DecodeArgs {
     void *o;
     const int32_t *cu;  // device [B+1] or nullptr (dense cache)
     int B, Hq, Hkv, D, kv_len;
+    int window;         // > 0: a sequence's last `window` keys only; 0: all
     float zscale;       // qk_scale * log2(e)
     float rk_scale;
     int splits;         // >= 1
@@ -47,7 +48,8 @@ struct DecodePlan {
     size_t ws_bytes;
 };
 
-DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int kv_len, int dtype, int num_splits);
+DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int kv_len, int window, int dtype,
+                       int num_splits);
 
 // Streaming kernel (records, or o when a.fused).
 hipError_t launch_decode_split(const DecodeArgs &a, DecodePath path, int dtype, bool parallax,
@@ -60,6 +62,7 @@ struct PrefillArgs {
     void *o;
     float *lse, *sbar;
     int B, Hq, Hkv, L, D;
+    int window;         // query i sees keys i - window + 1 .. i (window = L: causal only)
     float zscale;       // qk_scale * log2(e)
     float rk_scale;
 };
@@ -79,6 +82,7 @@ struct BackwardArgs {
     void *dq, *dr, *dk, *dv;
     RowStat *rowstat;                    // workspace [B, Hq, L]
     int B, Hq, Hkv, L, D;
+    int window;                          // as in PrefillArgs, 1 .. L
     float zscale;                        // qk_scale * log2(e)
     float qk_scale, rk_scale;
 };

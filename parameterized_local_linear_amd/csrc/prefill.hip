@@ -75,10 +75,11 @@ __global__ __launch_bounds__(64) void prefill_generic(PrefillArgs a) {
         qv[e] *= a.zscale;
         rv[e] *= a.rk_scale;
     }
+    const int first = max(0, i - a.window + 1);  // sliding window: keys first .. i
     float piv;
     {
         float k0[EPL];
-        Vec16<T>::load(kb, k0);
+        Vec16<T>::load(kb + (int64_t)first * D, k0);
         float part = 0.f;
         for (int e = 0; e < EPL; ++e) part += rv[e] * k0[e];
         for (int off = 1; off < LPR; off <<= 1) part += __shfl_xor(part, off, LPR);
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(64) void prefill_generic(PrefillArgs a) {
         Bv[e] = 0.f;
     }
     const int end = i + 1;
-    for (int j0 = 0; j0 < end; j0 += KPI) {
+    for (int j0 = first; j0 < end; j0 += KPI) {
         const int j = j0 + kgrp;
         const bool valid = j < end;
         const int jj = valid ? j : end - 1;
@@ -174,8 +175,9 @@ __global__ __launch_bounds__(64) void prefill_generic(PrefillArgs a) {
 // (P never leaves registers), and the V^T operand read from the row-major
 // LDS tile with gfx950's transposing LDS read (ds_read_b64_tr_b16).
 //
-// Causality: keys j <= i. Tiles entirely above a wave's rows are skipped,
-// tiles crossing its diagonal are masked. Work items run heaviest-first
+// Causality: keys j <= i, and with a sliding window W also j > i - W. Tiles
+// entirely outside a wave's visible band are skipped, tiles crossing either
+// edge of the band are masked. Work items run heaviest-first
 // (last q-tile first), and the group index varies fastest so that all
 // q-tiles of one (sequence, KV head) land on one XCD when the number of
 // groups is a multiple of 8 (its L2 then holds that head's K/V).
@@ -216,6 +218,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_mfma_bf16_d128(Pre
     const int q0 = qt * RPH + (wave % WPH) * 16;    // this wave's first row
     const int kend = min(a.L, (qt + 1) * RPH);      // keys the workgroup needs
     const int ntiles = (kend + TK - 1) / TK;
+    const int W = a.window;                          // query i sees keys i - W + 1 .. i
+    const int tile0 = max(0, qt * RPH - W + 1) / TK;  // first tile any row of the item sees
 
     const uint16_t *qh = reinterpret_cast<const uint16_t *>(a.q);
     const uint16_t *rh = reinterpret_cast<const uint16_t *>(a.r);
@@ -244,7 +248,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_mfma_bf16_d128(Pre
             __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void *)(lv + kloc * D), 16, off, 0, 0, 0);
         }
     };
-    dma_tile(0, lds_k0, lds_v0);
+    dma_tile(tile0, lds_k0, lds_v0);
 
     // ---- per-wave query operands (k-step u) and the row's pivot
     bf16x8 qop[4], rop[4];
@@ -259,8 +263,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_mfma_bf16_d128(Pre
             qop[u] = load16(qp + 8 * (g + 4 * u));
             rop[u] = load16(rp + 8 * (g + 4 * u));
         }
-        // pivot: probe score of key 0 for each query row
-        const uint16_t *k0 = reinterpret_cast<const uint16_t *>(a.k) + kvbase;
+        // pivot: probe score of the row's first visible key
+        const uint16_t *k0 = reinterpret_cast<const uint16_t *>(a.k) + kvbase + (int64_t)max(0, row - W + 1) * D;
         float part = 0.f;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -271,7 +275,10 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_mfma_bf16_d128(Pre
         piv = xor_sum_rowgroups(part) * a.rk_scale;
     }
 
-    float m_run = -INFINITY, lsA = 0.f, lsS = 0.f;
+    // Reference max (log2 units). Finite from the start: with a sliding window
+    // a row can meet a sub-tile in which none of its keys is visible before
+    // it has seen any key, and exp2(-inf - m) must then be 0, not NaN.
+    float m_run = -1e30f, lsA = 0.f, lsS = 0.f;
     floatx4 accA[8], accB[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -367,7 +374,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_mfma_bf16_d128(Pre
         float rmax = -INFINITY;
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            if (diag && k0 + g + 4 * t > row) zr[t] = -INFINITY;
+            const int key = k0 + g + 4 * t;
+            if (diag && (key > row || key <= row - W)) zr[t] = -INFINITY;
             rmax = fmaxf(rmax, zr[t]);
         }
         // Lazy rescale: the lane-local max decides whether any logit of the
@@ -415,8 +423,10 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_mfma_bf16_d128(Pre
     auto tile_step = [&](int tile, uint16_t *lk, uint16_t *lv, uint16_t *nk, uint16_t *nv) __attribute__((always_inline)) {
         if (tile + 1 < ntiles) dma_tile(tile + 1, nk, nv);
         const int t0 = tile * TK;
-        if (t0 <= q_last) {  // wave-uniform: tiles above the wave's rows are skipped
-            if (t0 + TK - 1 <= q0)
+        // wave-uniform: tiles above the wave's rows or left of all their windows are skipped;
+        // a tile needs the mask unless every key is visible to all 16 rows
+        if (t0 <= q_last && t0 + TK - 1 > q0 - W) {
+            if (t0 + TK - 1 <= q0 && t0 > q_last - W)
                 tile_body(lk, lv, tile, false);
             else
                 tile_body(lk, lv, tile, true);
@@ -425,7 +435,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_mfma_bf16_d128(Pre
     };
 
     __syncthreads();
-    for (int tile = 0; tile < ntiles; tile += 2) {
+    for (int tile = tile0; tile < ntiles; tile += 2) {
         tile_step(tile, lds_k0, lds_v0, lds_k1, lds_v1);
         if (tile + 1 < ntiles) tile_step(tile + 1, lds_k1, lds_v1, lds_k0, lds_v0);
     }

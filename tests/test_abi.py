@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = plx.lib()
-    assert L.parallax_abi_version() == 1
+    assert L.parallax_abi_version() == 2
     for s in range(5):
         assert L.parallax_status_string(s).decode() == plx.STATUS[s]
     assert L.parallax_status_string(99) == b"unknown status"
@@ -42,18 +42,19 @@ def test_version_and_status_strings():
 
 def _decode(**kw):
     a = dict(q=FAKE, r=FAKE, k=FAKE, v=FAKE, o=FAKE, cu=None, B=1, Hq=4, Hkv=2, D=128, L=64,
-             qk=0.1, rk=1.0, dt=1, ns=0, ws=None, wsb=0, stream=None)
+             W=0, qk=0.1, rk=1.0, dt=1, ns=0, ws=None, wsb=0, stream=None)
     a.update(kw)
     return plx.lib().parallax_decode(a["q"], a["r"], a["k"], a["v"], a["o"], a["cu"], a["B"],
-                                     a["Hq"], a["Hkv"], a["D"], a["L"], a["qk"], a["rk"], a["dt"],
-                                     a["ns"], a["ws"], a["wsb"], a["stream"])
+                                     a["Hq"], a["Hkv"], a["D"], a["L"], a["W"], a["qk"], a["rk"],
+                                     a["dt"], a["ns"], a["ws"], a["wsb"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(B=0), 1), (dict(Hq=0), 1), (dict(L=0), 1), (dict(Hq=6, Hkv=4), 1),
     (dict(q=None), 1), (dict(r=None), 1), (dict(k=None), 1), (dict(o=None), 1),
     (dict(D=96), 2), (dict(D=256), 2), (dict(dt=2), 2), (dict(ns=-1), 1),
-    (dict(qk=float("nan")), 1), (dict(rk=float("inf")), 1),
+    (dict(qk=float("nan")), 1), (dict(rk=float("inf")), 1), (dict(qk=0.0), 1),
+    (dict(qk=-0.1), 1), (dict(W=-1), 1),
     (dict(ns=4, L=4096), 3), (dict(ns=4, L=4096, ws=FAKE, wsb=16), 3),
 ])
 def test_decode_rejects_on_host(kw, status):
@@ -64,16 +65,20 @@ def test_decode_rejects_on_host(kw, status):
 
 def test_softmax_decode_and_prefill_reject_on_host():
     L = plx.lib()
-    assert L.softmax_decode(FAKE, FAKE, FAKE, FAKE, None, 1, 4, 3, 128, 10, 0.1, 1, 0, None, 0,
+    assert L.softmax_decode(FAKE, FAKE, FAKE, FAKE, None, 1, 4, 3, 128, 10, 0, 0.1, 1, 0, None, 0,
                             None) == 1
-    assert L.softmax_decode(FAKE, FAKE, FAKE, FAKE, None, 1, 4, 2, 80, 10, 0.1, 1, 0, None, 0,
+    assert L.softmax_decode(FAKE, FAKE, FAKE, FAKE, None, 1, 4, 2, 80, 10, 0, 0.1, 1, 0, None, 0,
                             None) == 2
+    assert L.softmax_decode(FAKE, FAKE, FAKE, FAKE, None, 1, 4, 2, 128, 10, -3, 0.1, 1, 0, None, 0,
+                            None) == 1
     args = [FAKE] * 5 + [None, None]
-    assert L.parallax_prefill(*args, 1, 4, 2, 0, 128, 0.1, 1.0, 1, None) == 1
-    assert L.parallax_prefill(*args, 1, 4, 3, 16, 128, 0.1, 1.0, 1, None) == 1
-    assert L.parallax_prefill(*args, 1, 4, 2, 16, 72, 0.1, 1.0, 1, None) == 2
-    assert L.parallax_prefill(*args, 1, 4, 2, 16, 128, 0.1, 1.0, 5, None) == 2
-    assert L.parallax_prefill(None, *args[1:], 1, 4, 2, 16, 128, 0.1, 1.0, 1, None) == 1
+    assert L.parallax_prefill(*args, 1, 4, 2, 0, 128, 0, 0.1, 1.0, 1, None) == 1
+    assert L.parallax_prefill(*args, 1, 4, 3, 16, 128, 0, 0.1, 1.0, 1, None) == 1
+    assert L.parallax_prefill(*args, 1, 4, 2, 16, 72, 0, 0.1, 1.0, 1, None) == 2
+    assert L.parallax_prefill(*args, 1, 4, 2, 16, 128, 0, 0.1, 1.0, 5, None) == 2
+    assert L.parallax_prefill(*args, 1, 4, 2, 16, 128, -1, 0.1, 1.0, 1, None) == 1
+    assert L.parallax_prefill(*args, 1, 4, 2, 16, 128, 0, -0.1, 1.0, 1, None) == 1
+    assert L.parallax_prefill(None, *args[1:], 1, 4, 2, 16, 128, 0, 0.1, 1.0, 1, None) == 1
 
 
 def test_workspace_plan():
@@ -104,19 +109,20 @@ def test_workspace_plan():
 
 def _backward(**kw):
     a = dict(q=FAKE, r=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, sbar=FAKE, dq=FAKE,
-             dr=FAKE, dk=FAKE, dv=FAKE, B=1, Hq=4, Hkv=2, L=64, D=128, qk=0.1, rk=1.0, dt=1,
-             ws=None, wsb=0, stream=None)
+             dr=FAKE, dk=FAKE, dv=FAKE, B=1, Hq=4, Hkv=2, L=64, D=128, W=0, qk=0.1, rk=1.0,
+             dt=1, ws=None, wsb=0, stream=None)
     a.update(kw)
     return plx.lib().parallax_prefill_backward(
         a["q"], a["r"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["sbar"], a["dq"], a["dr"],
-        a["dk"], a["dv"], a["B"], a["Hq"], a["Hkv"], a["L"], a["D"], a["qk"], a["rk"], a["dt"],
-        a["ws"], a["wsb"], a["stream"])
+        a["dk"], a["dv"], a["B"], a["Hq"], a["Hkv"], a["L"], a["D"], a["W"], a["qk"], a["rk"],
+        a["dt"], a["ws"], a["wsb"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(B=0), 1), (dict(L=0), 1), (dict(Hq=6, Hkv=4), 1), (dict(q=None), 1),
     (dict(do=None), 1), (dict(lse=None), 1), (dict(sbar=None), 1), (dict(dk=None), 1),
     (dict(D=96), 2), (dict(dt=3), 2), (dict(L=(1 << 22) + 1), 2), (dict(rk=float("nan")), 1),
+    (dict(W=-2), 1), (dict(qk=0.0), 1),
     (dict(), 3), (dict(ws=FAKE, wsb=4 * 64 * 16 - 1), 3),
 ])
 def test_prefill_backward_rejects_on_host(kw, status):
