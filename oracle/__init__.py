@@ -219,3 +219,51 @@ def prefill_backward(q, r, k, v, do, *, qk_scale=None, rk_scale=1.0, units=None,
         return (dq.reshape(B, Hq, L, D), dr.reshape(B, Hq, L, D), dk.reshape(B, Hkv, L, D),
                 dv.reshape(B, Hkv, L, D))
     return dq, dr, dk, dv
+
+
+def _seq_dense(x, s0, s1):
+    """Packed [T, H, D] rows s0 .. s1 - 1 as a dense [1, H, n, D] array."""
+    return np.ascontiguousarray(x[s0:s1].transpose(1, 0, 2)[None])
+
+
+def prefill_varlen(q, r, k, v, cu_seqlens, *, qk_scale=None, rk_scale=1.0, window=0,
+                   stats=False):
+    """Causal prefill of packed sequences (the pages' parallax_varlen_func): q, r
+    [T, Hq, D], k, v [T, Hkv, D], sequence b = tokens cu[b] .. cu[b+1] - 1.
+    Each sequence is an independent causal prefill (the dense oracle on its
+    slice). Returns o [T, Hq, D] (and lse, sbar [T, Hq] with stats=True)."""
+    T, Hq, D = q.shape
+    o = np.zeros((T, Hq, D), dtype=np.float64)
+    lse = np.zeros((T, Hq), dtype=np.float64)
+    sbar = np.zeros((T, Hq), dtype=np.float64)
+    for s0, s1 in zip(cu_seqlens[:-1], cu_seqlens[1:]):
+        if s1 <= s0:
+            continue
+        res = prefill(_seq_dense(q, s0, s1), None if r is None else _seq_dense(r, s0, s1),
+                      _seq_dense(k, s0, s1), _seq_dense(v, s0, s1), qk_scale=qk_scale,
+                      rk_scale=rk_scale, window=window, stats=True)
+        o[s0:s1] = res[0][0].transpose(1, 0, 2)
+        lse[s0:s1] = res[1][0].T
+        sbar[s0:s1] = res[2][0].T
+    return (o, lse, sbar) if stats else o
+
+
+def prefill_varlen_backward(q, r, k, v, do, cu_seqlens, *, qk_scale=None, rk_scale=1.0,
+                            window=0):
+    """Gradients of prefill_varlen: (dq, dr [T, Hq, D], dk, dv [T, Hkv, D])."""
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    dq = np.zeros((T, Hq, D)); dr = np.zeros((T, Hq, D))
+    dk = np.zeros((T, Hkv, D)); dv = np.zeros((T, Hkv, D))
+    for s0, s1 in zip(cu_seqlens[:-1], cu_seqlens[1:]):
+        if s1 <= s0:
+            continue
+        g = prefill_backward(_seq_dense(q, s0, s1), None if r is None else _seq_dense(r, s0, s1),
+                             _seq_dense(k, s0, s1), _seq_dense(v, s0, s1),
+                             _seq_dense(do, s0, s1), qk_scale=qk_scale, rk_scale=rk_scale,
+                             window=window)
+        dq[s0:s1] = g[0][0].transpose(1, 0, 2)
+        dr[s0:s1] = g[1][0].transpose(1, 0, 2)
+        dk[s0:s1] = g[2][0].transpose(1, 0, 2)
+        dv[s0:s1] = g[3][0].transpose(1, 0, 2)
+    return dq, dr, dk, dv
