@@ -16,8 +16,9 @@ Also measured in the same run:
   * softmax_decode on the same inputs (the cost of the correction branch);
   * the CPU oracle on the same inputs (cpu_baseline), on the host's cores.
 
-Other workloads (--workload varlen | large | prefill | backward | grid) print
-their own line; backward times parallax_prefill_backward (row pass + key
+Other workloads (--workload varlen | large | prefill | backward | grid |
+prefill-varlen) print their own line; prefill-varlen times the packed
+forward and backward of 16 sequences of U{256..4096} tokens; backward times parallax_prefill_backward (row pass + key
 pass) on the causal-prefill shapes; grid runs the pages' own decode shapes
 (multi-head H = 8, B in {1, 32}, L in {512 .. 16384}) and reports a table.
 Prints one JSON line on stdout.
@@ -49,7 +50,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="long",
-                    choices=["long", "varlen", "large", "prefill", "backward", "grid"])
+                    choices=["long", "varlen", "large", "prefill", "backward", "grid",
+                             "prefill-varlen"])
     ap.add_argument("--num-splits", type=int, default=0, help="0: library plan")
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window (keys a query sees); 0: none")
@@ -443,6 +445,77 @@ def run_backward_workload(args, torch, plx, synth, oracle):
     return res
 
 
+def run_prefill_varlen_workload(args, torch, plx, synth, oracle):
+    spec = synth.prefill_varlen_spec()
+    lens = spec.lengths
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    T, Hq, Hkv, D, W = int(cu[-1]), spec.Hq, spec.Hkv, spec.D, args.window
+    arrs = {}
+    for name, tid, H, sc in (("q", synth.TID_Q, Hq, spec.scale), ("r", synth.TID_R, Hq, spec.scale),
+                             ("k", synth.TID_K, Hkv, spec.scale), ("v", synth.TID_V, Hkv, spec.scale),
+                             ("do", synth.TID_DO, Hq, 1.0)):
+        arrs[name] = synth.normal(spec.seed, tid, (T, H, D), sc, spec.dtype)
+    t = {n: torch.from_numpy(a).view(torch.bfloat16).cuda() for n, a in arrs.items()}
+    cu_t = torch.from_numpy(cu.astype(np.int32)).cuda()
+    max_len = int(lens.max())
+    out = torch.empty_like(t["q"])
+    lse = torch.empty((T, Hq), dtype=torch.float32, device="cuda")
+    sbar = torch.empty_like(lse)
+    grads = (torch.empty_like(t["q"]), torch.empty_like(t["r"]), torch.empty_like(t["k"]),
+             torch.empty_like(t["v"]))
+    ws = torch.empty(int(plx.lib().parallax_prefill_backward_workspace_bytes(1, Hq, T)),
+                     dtype=torch.uint8, device="cuda")
+    plx.prefill_varlen(t["q"], t["r"], t["k"], t["v"], cu_t, max_len, out=out, window=W)
+
+    def fwd(i):
+        plx.prefill_varlen(t["q"], t["r"], t["k"], t["v"], cu_t, max_len, out=out, window=W)
+
+    o, lse, sbar = plx.prefill_varlen(t["q"], t["r"], t["k"], t["v"], cu_t, max_len,
+                                      return_stats=True, window=W)
+
+    def bwd(i):
+        plx.prefill_varlen_backward(t["q"], t["r"], t["k"], t["v"], o, t["do"], lse, sbar, cu_t,
+                                    max_len, window=W, workspace=ws, out=grads)
+
+    steps = max(1, min(args.steps, 10))
+    warm = max(1, min(args.warmup, 2))
+    tf = graph_time(torch, fwd, steps, warm)
+    tb = graph_time(torch, bwd, steps, warm)
+    pairs = sum(visible_pairs(int(n), W) for n in lens)
+    flops = 8 * D * Hq * pairs
+    res = {
+        "metric": METRIC, "value": round(flops / tf / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": steps, "warmup": warm, "ms_per_step": round(tf * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": spec.name + (f" window{W}" if W > 0 else ""), "sequences": len(lens),
+                   "total_tokens": T, "max_len": max_len, "Hq": Hq, "Hkv": Hkv, "head_dim": D,
+                   "window": W},
+        "roofline": {"bound": "mfma", "kernel": "prefill (packed)",
+                     "achieved": round(flops / tf / 1e12, 2), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(flops / tf / 1e12 / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "avg_us": round(tf * 1e6, 1), "flops_per_launch": flops},
+        "backward_ms": round(tb * 1e3, 4),
+        "backward_tflops": round(2 * flops / tb / 1e12, 3),
+    }
+    # parity: the full output and gradients of three sequences
+    errs = []
+    for b in (0, len(lens) // 2, len(lens) - 1):
+        s0, s1 = int(cu[b]), int(cu[b + 1])
+        sub = {n: np.ascontiguousarray(a[s0:s1]) for n, a in arrs.items()}
+        scu = np.array([0, s1 - s0])
+        ref = oracle.prefill_varlen(sub["q"], sub["r"], sub["k"], sub["v"], scu, window=W)
+        got = out[s0:s1].float().cpu().numpy()
+        errs.append(float(np.abs(got - ref).max() / np.abs(ref).max()))
+        gref = oracle.prefill_varlen_backward(sub["q"], sub["r"], sub["k"], sub["v"], sub["do"],
+                                              scu, window=W)
+        for g, gr in zip(grads, gref):
+            a = g[s0:s1].float().cpu().numpy()
+            errs.append(float(np.abs(a - gr).max() / np.abs(gr).max()))
+    res["sampled_parity_max_norm_err"] = max(errs)
+    return res
+
+
 # The pages' H200 Parallax decode latencies for the same shapes (PyPI README of
 # parallax-kernel, small- and large-batch decode tables; q50, CUDA-graph replay).
 # Context only: another machine's numbers, not a target of this build.
@@ -557,6 +630,8 @@ def main():
         res = run_backward_workload(args, torch, plx, synth, oracle)
     elif args.workload == "grid":
         res = run_grid_workload(args, torch, plx, synth, oracle)
+    elif args.workload == "prefill-varlen":
+        res = run_prefill_varlen_workload(args, torch, plx, synth, oracle)
     else:
         res = run_decode_workload(args, torch, plx, synth, oracle)
     print(json.dumps(res), flush=True)

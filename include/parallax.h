@@ -202,6 +202,38 @@ int parallax_prefill_backward(const void *q, const void *r, const void *k, const
                               float rk_scale, int dtype, void *workspace, size_t workspace_bytes,
                               void *stream);
 
+/* ------------------------------------------------------------------------
+ * Packed-sequence (varlen) prefill and its backward (the pages name
+ * parallax_varlen_func next to parallax_func in the PyPI README's API
+ * listing): a batch of B sequences of different lengths stored back to back,
+ * each an independent causal prefill (with the optional window).
+ *
+ *   q, r, o, d_o, dq, dr : [total_tokens, Hq, D]
+ *   k, v, dk, dv         : [total_tokens, Hkv, D]
+ *   lse, sbar            : NULL (forward only) or DEVICE float [total_tokens, Hq]
+ *   cu_seqlens : DEVICE int32 [B + 1], non-decreasing from 0 to total_tokens;
+ *                sequence b owns tokens cu[b] .. cu[b+1] - 1. Read on the device
+ *                only, so not validated: lengths must not exceed max_len.
+ *   max_len    : the longest sequence (sizes the launch grid), >= 1.
+ *   workspace  : at least parallax_prefill_backward_workspace_bytes(1, Hq,
+ *                total_tokens) bytes.
+ * Other arguments, rules and errors as the dense calls; total_tokens == 0
+ * (every sequence empty) returns PLX_OK without a launch. max_len times
+ * max(Hq, Hkv) * D * element size must stay below 2^31 bytes.
+ * ---------------------------------------------------------------------- */
+int parallax_prefill_varlen(const void *q, const void *r, const void *k, const void *v, void *o,
+                            float *lse, float *sbar, const int32_t *cu_seqlens, int B, int Hq,
+                            int Hkv, int max_len, int total_tokens, int D, int window,
+                            float qk_scale, float rk_scale, int dtype, void *stream);
+
+int parallax_prefill_varlen_backward(const void *q, const void *r, const void *k, const void *v,
+                                     const void *o, const void *d_o, const float *lse,
+                                     const float *sbar, const int32_t *cu_seqlens, void *dq,
+                                     void *dr, void *dk, void *dv, int B, int Hq, int Hkv,
+                                     int max_len, int total_tokens, int D, int window,
+                                     float qk_scale, float rk_scale, int dtype, void *workspace,
+                                     size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

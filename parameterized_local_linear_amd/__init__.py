@@ -11,6 +11,8 @@ Entry points mirror the C ABI (include/parallax.h):
   softmax_decode(q, k, v, ...)     the same kernels with the probe path compiled out
   prefill(q, r, k, v, ...)         causal Parallax prefill on [B, H, L, D]
   prefill_backward(...)            its gradients dq, dr, dk, dv
+  prefill_varlen(...), prefill_varlen_backward(...)
+                                   the same on packed [T, H, D] sequences
 The pages' names: ``parallax_decode`` aliases decode, and ``parallax_func``
 is the prefill as a differentiable torch function (forward and backward on
 these kernels).
@@ -77,6 +79,11 @@ def lib() -> ctypes.CDLL:
         L.parallax_prefill_backward_workspace_bytes.restype = sz
         L.parallax_prefill_backward.argtypes = [vp] * 12 + [i32] * 6 + [f32, f32, i32, vp, sz, vp]
         L.parallax_prefill_backward.restype = i32
+        L.parallax_prefill_varlen.argtypes = [vp] * 8 + [i32] * 7 + [f32, f32, i32, vp]
+        L.parallax_prefill_varlen.restype = i32
+        L.parallax_prefill_varlen_backward.argtypes = [vp] * 13 + [i32] * 7 + [f32, f32, i32, vp,
+                                                                              sz, vp]
+        L.parallax_prefill_varlen_backward.restype = i32
         _lib = L
     return _lib
 
@@ -350,8 +357,110 @@ def parallax_func(q, r, k, v, qk_scale=None, rk_scale=1.0, *, window=0):
     return prefill(q, r, k, v, qk_scale, rk_scale, window=window)
 
 
+def _varlen_shapes(q, k, cu_seqlens, max_len):
+    if q.dim() != 3 or k.dim() != 3 or q.shape[0] != k.shape[0] or q.shape[2] != k.shape[2]:
+        raise ValueError("varlen q must be [T, Hq, D] and k [T, Hkv, D]")
+    _check(cu_seqlens, "cu_seqlens", torch.int32, q.device)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be int32 [B + 1]")
+    if max_len is None:  # one host read of the lengths when the caller does not know it
+        max_len = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item())
+    return cu_seqlens.numel() - 1, q.shape[1], k.shape[1], q.shape[2], max(int(max_len), 1)
+
+
+def prefill_varlen(q, r, k, v, cu_seqlens, max_len=None, qk_scale=None, rk_scale=1.0, *,
+                   out=None, return_stats=False, window=0):
+    """Causal prefill of packed sequences: q, r [T, Hq, D]; k, v [T, Hkv, D]; int32
+    ``cu_seqlens`` [B + 1]. Returns o [T, Hq, D] (plus fp32 lse, sbar [T, Hq])."""
+    L_ = lib()
+    dev, dt = q.device, q.dtype
+    for t, name in ((q, "q"), (r, "r"), (k, "k"), (v, "v")):
+        _check(t, name, dt, dev)
+    if r.shape != q.shape or v.shape != k.shape:
+        raise ValueError("r must have q's shape and v k's")
+    B, Hq, Hkv, D, max_len = _varlen_shapes(q, k, cu_seqlens, max_len)
+    T = q.shape[0]
+    if qk_scale is None:
+        qk_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    lse = sbar = None
+    if return_stats:
+        lse = torch.empty((T, Hq), dtype=torch.float32, device=dev)
+        sbar = torch.empty((T, Hq), dtype=torch.float32, device=dev)
+    st = L_.parallax_prefill_varlen(_ptr(q), _ptr(r), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                    _ptr(sbar), _ptr(cu_seqlens), B, Hq, Hkv, max_len, T, D,
+                                    int(window), float(qk_scale), float(rk_scale), _dtype_code(q),
+                                    _stream_handle(dev))
+    if st != 0:
+        raise ParallaxError(st, "parallax_prefill_varlen")
+    return (out, lse, sbar) if return_stats else out
+
+
+def prefill_varlen_backward(q, r, k, v, o, d_o, lse, sbar, cu_seqlens, max_len=None,
+                            qk_scale=None, rk_scale=1.0, *, window=0, workspace=None, out=None):
+    """Gradients (dq, dr, dk, dv) of prefill_varlen from its o, lse and sbar."""
+    L_ = lib()
+    dev, dt = q.device, q.dtype
+    for t, name in ((q, "q"), (r, "r"), (k, "k"), (v, "v"), (o, "o"), (d_o, "d_o")):
+        _check(t, name, dt, dev)
+    B, Hq, Hkv, D, max_len = _varlen_shapes(q, k, cu_seqlens, max_len)
+    T = q.shape[0]
+    for t, name in ((lse, "lse"), (sbar, "sbar")):
+        _check(t, name, torch.float32, dev)
+        if t.shape != (T, Hq):
+            raise ValueError(f"{name} must be float32 [T, Hq]")
+    if qk_scale is None:
+        qk_scale = 1.0 / math.sqrt(D)
+    need = int(L_.parallax_prefill_backward_workspace_bytes(1, Hq, max(T, 1)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = (torch.empty_like(q), torch.empty_like(r), torch.empty_like(k), torch.empty_like(v))
+    dq, dr, dk, dv = out
+    st = L_.parallax_prefill_varlen_backward(
+        _ptr(q), _ptr(r), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse), _ptr(sbar),
+        _ptr(cu_seqlens), _ptr(dq), _ptr(dr), _ptr(dk), _ptr(dv), B, Hq, Hkv, max_len, T, D,
+        int(window), float(qk_scale), float(rk_scale), _dtype_code(q), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream_handle(dev))
+    if st != 0:
+        raise ParallaxError(st, "parallax_prefill_varlen_backward")
+    return dq, dr, dk, dv
+
+
+class _ParallaxVarlenFunction(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, r, k, v, cu_seqlens, max_len, qk_scale, rk_scale, window):
+        o, lse, sbar = prefill_varlen(q, r, k, v, cu_seqlens, max_len, qk_scale, rk_scale,
+                                      return_stats=True, window=window)
+        ctx.save_for_backward(q, r, k, v, o, lse, sbar, cu_seqlens)
+        ctx.args = (max_len, qk_scale, rk_scale, window)
+        return o
+
+    @staticmethod
+    def backward(ctx, d_o):
+        q, r, k, v, o, lse, sbar, cu = ctx.saved_tensors
+        max_len, qk_scale, rk_scale, window = ctx.args
+        grads = prefill_varlen_backward(q, r, k, v, o, d_o.contiguous(), lse, sbar, cu, max_len,
+                                        qk_scale, rk_scale, window=window)
+        return (*grads, None, None, None, None, None)
+
+
+def parallax_varlen_func(q, r, k, v, cu_seqlens, max_len=None, qk_scale=None, rk_scale=1.0, *,
+                         window=0):
+    """Differentiable causal Parallax attention on packed sequences (the pages'
+    parallax_varlen_func): q, r [T, Hq, D]; k, v [T, Hkv, D]; int32 cu_seqlens [B + 1]."""
+    if max_len is None:
+        max_len = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item())
+    if torch.is_grad_enabled() and any(t.requires_grad for t in (q, r, k, v)):
+        return _ParallaxVarlenFunction.apply(q, r, k, v, cu_seqlens, max_len, qk_scale, rk_scale,
+                                             window)
+    return prefill_varlen(q, r, k, v, cu_seqlens, max_len, qk_scale, rk_scale, window=window)
+
+
 parallax_decode = decode
 
-__all__ = ["decode", "softmax_decode", "prefill", "prefill_backward", "decode_partial",
+__all__ = ["decode", "softmax_decode", "prefill", "prefill_backward", "prefill_varlen",
+           "prefill_varlen_backward", "parallax_varlen_func", "decode_partial",
            "decode_merge", "parallax_decode", "parallax_func", "decode_workspace_bytes",
            "decode_num_splits", "lib", "ParallaxError", "LIB_PATH"]

@@ -224,25 +224,25 @@ int parallax_decode_merge(const void *records, void *o, int B, int Hq, int D, in
     return err == hipSuccess ? PLX_OK : PLX_ERR_HIP;
 }
 
-int parallax_prefill(const void *q, const void *r, const void *k, const void *v, void *o, float *lse,
-                     float *sbar, int B, int Hq, int Hkv, int L, int D, int window, float qk_scale,
-                     float rk_scale, int dtype, void *stream) {
+}  // extern "C"
+
+// Checks shared by the prefill entry points (dense when cu == nullptr,
+// packed with `total` tokens otherwise); fills the sizes of `a`.
+template <typename Args>
+static int check_prefill(Args &a, const int32_t *cu, int B, int Hq, int Hkv, int L, int total, int D,
+                         int window, float qk_scale, float rk_scale, int dtype) {
     if (B < 1 || Hq < 1 || Hkv < 1 || L < 1 || D < 1 || window < 0) return PLX_ERR_INVALID_ARG;
     if (Hq % Hkv != 0) return PLX_ERR_INVALID_ARG;
-    if (!q || !r || !k || !v || !o) return PLX_ERR_INVALID_ARG;
+    if (cu && total < 0) return PLX_ERR_INVALID_ARG;
     // masked logits are -inf before scaling, so the scale must be positive
     if (!isfinite(qk_scale) || !(qk_scale > 0.f) || !isfinite(rk_scale)) return PLX_ERR_INVALID_ARG;
     if (dtype != PLX_F32 && dtype != PLX_BF16) return PLX_ERR_UNSUPPORTED;
     if (!plx::prefill_supported(D, dtype)) return PLX_ERR_UNSUPPORTED;
     if (B > 65535 || Hq > 65535 || L > kMaxPrefillLen) return PLX_ERR_UNSUPPORTED;
-    plx::PrefillArgs a;
-    a.q = q;
-    a.r = r;
-    a.k = k;
-    a.v = v;
-    a.o = o;
-    a.lse = lse;
-    a.sbar = sbar;
+    // one head of one sequence is addressed with 32-bit byte offsets
+    const long long row_bytes = (long long)(cu ? (Hq > Hkv ? Hq : Hkv) : 1) * D * (dtype == PLX_BF16 ? 2 : 4);
+    if ((long long)L * row_bytes >= 0x7fffffffLL) return PLX_ERR_UNSUPPORTED;
+    a.cu = cu;
     a.B = B;
     a.Hq = Hq;
     a.Hkv = Hkv;
@@ -251,32 +251,42 @@ int parallax_prefill(const void *q, const void *r, const void *k, const void *v,
     a.window = (window > 0 && window < L) ? window : L;
     a.zscale = qk_scale * plx::kLog2e;
     a.rk_scale = rk_scale;
+    return PLX_OK;
+}
+
+static int prefill_common(const void *q, const void *r, const void *k, const void *v, void *o, float *lse,
+                          float *sbar, const int32_t *cu, int B, int Hq, int Hkv, int L, int total, int D,
+                          int window, float qk_scale, float rk_scale, int dtype, void *stream) {
+    if (!q || !r || !k || !v || !o) return PLX_ERR_INVALID_ARG;
+    plx::PrefillArgs a;
+    int st = check_prefill(a, cu, B, Hq, Hkv, L, total, D, window, qk_scale, rk_scale, dtype);
+    if (st != PLX_OK) return st;
+    if (cu && total == 0) return PLX_OK;  // every sequence empty
+    a.q = q;
+    a.r = r;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.sbar = sbar;
     hipError_t err = plx::launch_prefill(a, dtype, reinterpret_cast<hipStream_t>(stream));
     return err == hipSuccess ? PLX_OK : PLX_ERR_HIP;
 }
 
-size_t parallax_prefill_backward_workspace_bytes(int B, int Hq, int L) {
-    if (B < 1 || Hq < 1 || L < 1) return 0;
-    return (size_t)B * Hq * L * sizeof(plx::RowStat);
-}
-
-int parallax_prefill_backward(const void *q, const void *r, const void *k, const void *v, const void *o,
-                              const void *d_o, const float *lse, const float *sbar, void *dq, void *dr,
-                              void *dk, void *dv, int B, int Hq, int Hkv, int L, int D, int window,
-                              float qk_scale, float rk_scale, int dtype, void *workspace,
-                              size_t workspace_bytes, void *stream) {
-    if (B < 1 || Hq < 1 || Hkv < 1 || L < 1 || D < 1 || window < 0) return PLX_ERR_INVALID_ARG;
-    if (Hq % Hkv != 0) return PLX_ERR_INVALID_ARG;
+static int backward_common(const void *q, const void *r, const void *k, const void *v, const void *o,
+                           const void *d_o, const float *lse, const float *sbar, const int32_t *cu,
+                           void *dq, void *dr, void *dk, void *dv, int B, int Hq, int Hkv, int L,
+                           int total, int D, int window, float qk_scale, float rk_scale, int dtype,
+                           void *workspace, size_t workspace_bytes, void *stream) {
     if (!q || !r || !k || !v || !o || !d_o || !lse || !sbar || !dq || !dr || !dk || !dv)
         return PLX_ERR_INVALID_ARG;
-    // masked logits are -inf before scaling, so the scale must be positive
-    if (!isfinite(qk_scale) || !(qk_scale > 0.f) || !isfinite(rk_scale)) return PLX_ERR_INVALID_ARG;
-    if (dtype != PLX_F32 && dtype != PLX_BF16) return PLX_ERR_UNSUPPORTED;
-    if (!plx::prefill_supported(D, dtype)) return PLX_ERR_UNSUPPORTED;
-    if (B > 65535 || Hq > 65535 || L > kMaxPrefillLen) return PLX_ERR_UNSUPPORTED;
-    if (!workspace || workspace_bytes < parallax_prefill_backward_workspace_bytes(B, Hq, L))
-        return PLX_ERR_WORKSPACE;
     plx::BackwardArgs a;
+    int st = check_prefill(a, cu, B, Hq, Hkv, L, total, D, window, qk_scale, rk_scale, dtype);
+    if (st != PLX_OK) return st;
+    if (cu && total == 0) return PLX_OK;  // every sequence empty
+    const size_t need = cu ? (size_t)Hq * total * sizeof(plx::RowStat)
+                           : (size_t)B * Hq * L * sizeof(plx::RowStat);
+    if (!workspace || workspace_bytes < need) return PLX_ERR_WORKSPACE;
     a.q = q;
     a.r = r;
     a.k = k;
@@ -290,17 +300,54 @@ int parallax_prefill_backward(const void *q, const void *r, const void *k, const
     a.dk = dk;
     a.dv = dv;
     a.rowstat = reinterpret_cast<plx::RowStat *>(workspace);
-    a.B = B;
-    a.Hq = Hq;
-    a.Hkv = Hkv;
-    a.L = L;
-    a.D = D;
-    a.window = (window > 0 && window < L) ? window : L;
-    a.zscale = qk_scale * plx::kLog2e;
+    a.total = cu ? total : 0;
     a.qk_scale = qk_scale;
-    a.rk_scale = rk_scale;
     hipError_t err = plx::launch_prefill_backward(a, dtype, reinterpret_cast<hipStream_t>(stream));
     return err == hipSuccess ? PLX_OK : PLX_ERR_HIP;
+}
+
+extern "C" {
+
+int parallax_prefill(const void *q, const void *r, const void *k, const void *v, void *o, float *lse,
+                     float *sbar, int B, int Hq, int Hkv, int L, int D, int window, float qk_scale,
+                     float rk_scale, int dtype, void *stream) {
+    return prefill_common(q, r, k, v, o, lse, sbar, nullptr, B, Hq, Hkv, L, 0, D, window, qk_scale,
+                          rk_scale, dtype, stream);
+}
+
+int parallax_prefill_varlen(const void *q, const void *r, const void *k, const void *v, void *o,
+                            float *lse, float *sbar, const int32_t *cu_seqlens, int B, int Hq, int Hkv,
+                            int max_len, int total_tokens, int D, int window, float qk_scale,
+                            float rk_scale, int dtype, void *stream) {
+    if (!cu_seqlens) return PLX_ERR_INVALID_ARG;
+    return prefill_common(q, r, k, v, o, lse, sbar, cu_seqlens, B, Hq, Hkv, max_len, total_tokens, D,
+                          window, qk_scale, rk_scale, dtype, stream);
+}
+
+size_t parallax_prefill_backward_workspace_bytes(int B, int Hq, int L) {
+    if (B < 1 || Hq < 1 || L < 1) return 0;
+    return (size_t)B * Hq * L * sizeof(plx::RowStat);
+}
+
+int parallax_prefill_backward(const void *q, const void *r, const void *k, const void *v, const void *o,
+                              const void *d_o, const float *lse, const float *sbar, void *dq, void *dr,
+                              void *dk, void *dv, int B, int Hq, int Hkv, int L, int D, int window,
+                              float qk_scale, float rk_scale, int dtype, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+    return backward_common(q, r, k, v, o, d_o, lse, sbar, nullptr, dq, dr, dk, dv, B, Hq, Hkv, L, 0, D,
+                           window, qk_scale, rk_scale, dtype, workspace, workspace_bytes, stream);
+}
+
+int parallax_prefill_varlen_backward(const void *q, const void *r, const void *k, const void *v,
+                                     const void *o, const void *d_o, const float *lse, const float *sbar,
+                                     const int32_t *cu_seqlens, void *dq, void *dr, void *dk, void *dv,
+                                     int B, int Hq, int Hkv, int max_len, int total_tokens, int D,
+                                     int window, float qk_scale, float rk_scale, int dtype,
+                                     void *workspace, size_t workspace_bytes, void *stream) {
+    if (!cu_seqlens) return PLX_ERR_INVALID_ARG;
+    return backward_common(q, r, k, v, o, d_o, lse, sbar, cu_seqlens, dq, dr, dk, dv, B, Hq, Hkv, max_len,
+                           total_tokens, D, window, qk_scale, rk_scale, dtype, workspace,
+                           workspace_bytes, stream);
 }
 
 }  // extern "C"

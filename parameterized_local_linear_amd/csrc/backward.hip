@@ -58,6 +58,13 @@ struct Frag<uint16_t> {
     }
 };
 
+// First row-statistics slot of (sequence, query head): the workspace holds
+// one RowStat per query row, [B, Hq, L] dense and [Hq, T] packed, so that
+// the rows of one head are contiguous in both layouts.
+__device__ __forceinline__ int64_t rowstat0(const PrefillSeq &s, int b, int h, int Hq, int L, int T) {
+    return s.packed ? (int64_t)h * T + s.tok0 : ((int64_t)b * Hq + h) * L;
+}
+
 // Sum over the LPR lanes that share one row of a wave.
 template <int LPR>
 __device__ __forceinline__ float row_sum(float x) {
@@ -88,21 +95,25 @@ __global__ __launch_bounds__(64) void bwd_rows_generic(BackwardArgs a) {
     const int hq = blockIdx.y;
     const int b = blockIdx.z;
     const int hkv = hq / (a.Hq / a.Hkv);
-    const int64_t row = ((int64_t)b * a.Hq + hq) * a.L + i;
-    const int64_t kvoff = ((int64_t)b * a.Hkv + hkv) * a.L * D + c * EPL;
+    const PrefillSeq sq = prefill_seq(a.cu, b, a.L);
+    if (i >= sq.len) return;  // past this sequence's end (packed batches)
+    const int ks = row_stride(sq, a.Hkv, D);
+    const int64_t row = row0_elem(sq, b, hq, a.Hq, a.L, D) + (int64_t)i * row_stride(sq, a.Hq, D);
+    const int64_t srow = stat0(sq, b, hq, a.Hq, a.L) + (int64_t)i * stat_stride(sq, a.Hq);
+    const int64_t kvoff = row0_elem(sq, b, hkv, a.Hkv, a.L, D) + c * EPL;
     const T *kb = reinterpret_cast<const T *>(a.k) + kvoff;
     const T *vb = reinterpret_cast<const T *>(a.v) + kvoff;
 
     float qv[EPL], rv[EPL], gv[EPL], ov[EPL];
-    Frag<T>::load(reinterpret_cast<const T *>(a.q) + row * D + c * EPL, qv);
-    Frag<T>::load(reinterpret_cast<const T *>(a.r) + row * D + c * EPL, rv);
-    Frag<T>::load(reinterpret_cast<const T *>(a.go) + row * D + c * EPL, gv);
-    Frag<T>::load(reinterpret_cast<const T *>(a.o) + row * D + c * EPL, ov);
+    Frag<T>::load(reinterpret_cast<const T *>(a.q) + row + c * EPL, qv);
+    Frag<T>::load(reinterpret_cast<const T *>(a.r) + row + c * EPL, rv);
+    Frag<T>::load(reinterpret_cast<const T *>(a.go) + row + c * EPL, gv);
+    Frag<T>::load(reinterpret_cast<const T *>(a.o) + row + c * EPL, ov);
     float part = 0.f;
     for (int e = 0; e < EPL; ++e) part += ov[e] * gv[e];
     const float delta = row_sum<LPR>(part);
-    const float lse2 = a.lse[row] * kLog2e;
-    const float sb = a.sbar[row];
+    const float lse2 = a.lse[srow] * kLog2e;
+    const float sb = a.sbar[srow];
     const int end = i + 1;
     const int first = max(0, i - a.window + 1);  // sliding window: keys first .. i
 
@@ -112,8 +123,8 @@ __global__ __launch_bounds__(64) void bwd_rows_generic(BackwardArgs a) {
         const int j = j0 + kgrp;
         const int jj = j < end ? j : end - 1;
         float kv[EPL], vv[EPL];
-        Frag<T>::load(kb + (int64_t)jj * D, kv);
-        Frag<T>::load(vb + (int64_t)jj * D, vv);
+        Frag<T>::load(kb + (int64_t)jj * ks, kv);
+        Frag<T>::load(vb + (int64_t)jj * ks, vv);
         float zp = 0.f, up = 0.f;
         for (int e = 0; e < EPL; ++e) {
             zp += qv[e] * kv[e];
@@ -132,8 +143,8 @@ __global__ __launch_bounds__(64) void bwd_rows_generic(BackwardArgs a) {
         const int j = j0 + kgrp;
         const int jj = j < end ? j : end - 1;
         float kv[EPL], vv[EPL];
-        Frag<T>::load(kb + (int64_t)jj * D, kv);
-        Frag<T>::load(vb + (int64_t)jj * D, vv);
+        Frag<T>::load(kb + (int64_t)jj * ks, kv);
+        Frag<T>::load(vb + (int64_t)jj * ks, vv);
         float zp = 0.f, sp = 0.f, up = 0.f;
         for (int e = 0; e < EPL; ++e) {
             zp += qv[e] * kv[e];
@@ -157,9 +168,9 @@ __global__ __launch_bounds__(64) void bwd_rows_generic(BackwardArgs a) {
         dra[e] = across_rows<LPR>(dra[e]) * a.rk_scale;
     }
     if (kgrp == 0) {
-        Frag<T>::store(reinterpret_cast<T *>(a.dq) + row * D + c * EPL, dqa);
-        Frag<T>::store(reinterpret_cast<T *>(a.dr) + row * D + c * EPL, dra);
-        if (c == 0) a.rowstat[row] = RowStat{lse2, sb, delta, ub};
+        Frag<T>::store(reinterpret_cast<T *>(a.dq) + row + c * EPL, dqa);
+        Frag<T>::store(reinterpret_cast<T *>(a.dr) + row + c * EPL, dra);
+        if (c == 0) a.rowstat[rowstat0(sq, b, hq, a.Hq, a.L, a.total) + i] = RowStat{lse2, sb, delta, ub};
     }
 }
 
@@ -175,23 +186,28 @@ __global__ __launch_bounds__(64) void bwd_keys_generic(BackwardArgs a) {
     const int hkv = blockIdx.y;
     const int b = blockIdx.z;
     const int G = a.Hq / a.Hkv;
-    const int64_t kvrow = ((int64_t)b * a.Hkv + hkv) * a.L + j;
+    const PrefillSeq sq = prefill_seq(a.cu, b, a.L);
+    if (j >= sq.len) return;  // past this sequence's end (packed batches)
+    const int qs = row_stride(sq, a.Hq, D);
+    const int64_t kvrow = row0_elem(sq, b, hkv, a.Hkv, a.L, D) + (int64_t)j * row_stride(sq, a.Hkv, D);
     float kv[EPL], vv[EPL], dka[EPL], dva[EPL];
-    Frag<T>::load(reinterpret_cast<const T *>(a.k) + kvrow * D + c * EPL, kv);
-    Frag<T>::load(reinterpret_cast<const T *>(a.v) + kvrow * D + c * EPL, vv);
+    Frag<T>::load(reinterpret_cast<const T *>(a.k) + kvrow + c * EPL, kv);
+    Frag<T>::load(reinterpret_cast<const T *>(a.v) + kvrow + c * EPL, vv);
     for (int e = 0; e < EPL; ++e) dka[e] = dva[e] = 0.f;
     for (int hs = 0; hs < G; ++hs) {
-        const int64_t rbase = ((int64_t)b * a.Hq + hkv * G + hs) * a.L;
-        const int rend = min(a.L, j + a.window);  // rows that see key j
+        const int hq = hkv * G + hs;
+        const int64_t rbase = row0_elem(sq, b, hq, a.Hq, a.L, D);
+        const int64_t sbase = rowstat0(sq, b, hq, a.Hq, a.L, a.total);
+        const int rend = min(sq.len, j + a.window);  // rows that see key j
         for (int i0 = j; i0 < rend; i0 += RPI) {
             const int i = i0 + rgrp;
             const int ii = i < rend ? i : rend - 1;
-            const int64_t row = rbase + ii;
+            const int64_t row = rbase + (int64_t)ii * qs;
             float qv[EPL], rv[EPL], gv[EPL];
-            Frag<T>::load(reinterpret_cast<const T *>(a.q) + row * D + c * EPL, qv);
-            Frag<T>::load(reinterpret_cast<const T *>(a.r) + row * D + c * EPL, rv);
-            Frag<T>::load(reinterpret_cast<const T *>(a.go) + row * D + c * EPL, gv);
-            const RowStat st = a.rowstat[row];
+            Frag<T>::load(reinterpret_cast<const T *>(a.q) + row + c * EPL, qv);
+            Frag<T>::load(reinterpret_cast<const T *>(a.r) + row + c * EPL, rv);
+            Frag<T>::load(reinterpret_cast<const T *>(a.go) + row + c * EPL, gv);
+            const RowStat st = a.rowstat[sbase + ii];
             float zp = 0.f, sp = 0.f, up = 0.f;
             for (int e = 0; e < EPL; ++e) {
                 zp += qv[e] * kv[e];
@@ -217,8 +233,8 @@ __global__ __launch_bounds__(64) void bwd_keys_generic(BackwardArgs a) {
         dva[e] = across_rows<LPR>(dva[e]);
     }
     if (rgrp == 0) {
-        Frag<T>::store(reinterpret_cast<T *>(a.dk) + kvrow * D + c * EPL, dka);
-        Frag<T>::store(reinterpret_cast<T *>(a.dv) + kvrow * D + c * EPL, dva);
+        Frag<T>::store(reinterpret_cast<T *>(a.dk) + kvrow + c * EPL, dka);
+        Frag<T>::store(reinterpret_cast<T *>(a.dv) + kvrow + c * EPL, dva);
     }
 }
 
@@ -271,11 +287,12 @@ __device__ __forceinline__ bf16x8 lds_transposed(const uint16_t *t, int x0, int 
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// Copy NROWS rows (a multiple of 4 * NW) starting at row `row0` of the
-// buffer behind `rs` into LDS tile `t`, shared by NW waves. Rows past the
-// buffer's range read as zeros.
+// Copy NROWS rows (a multiple of 4 * NW; `stride` elements apart in memory)
+// starting at row `row0` of the buffer behind `rs` into LDS tile `t`, shared
+// by NW waves. Rows past the buffer's range read as zeros.
 template <int NROWS, int NW>
-__device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t rs, int row0, uint16_t *t, int wave, int lane) {
+__device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t rs, int row0, int stride, uint16_t *t, int wave,
+                                         int lane) {
     constexpr int PER_WAVE = NROWS / (4 * NW);
     static_assert(PER_WAVE * 4 * NW == NROWS, "rows must split evenly over the waves");
 #pragma unroll
@@ -283,7 +300,7 @@ __device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t rs, int row0, ui
         const int xloc = 4 * (wave * PER_WAVE + j);
         const int x = xloc + (lane >> 4);
         const int chunk = (lane & 15) ^ tile_swz(x);
-        const int off = ((row0 + x) * 128 + chunk * 8) * 2;
+        const int off = ((row0 + x) * stride + chunk * 8) * 2;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(t + xloc * 128), 16, off, 0, 0, 0);
     }
 }
@@ -322,13 +339,17 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_rows_mfma_bf16_d128(Backwa
     const int hsub = grp % hgroups;
     const int hq = hkv * G + hsub * HPW + wave / WPH;
     const int q0 = qt * RPH + (wave % WPH) * 16;
-    const int kend = min(a.L, (qt + 1) * RPH);
+    const PrefillSeq sq = prefill_seq(a.cu, b, a.L);
+    const int L = sq.len;
+    if (qt * RPH >= L) return;  // work item past this sequence's end (packed batches)
+    const int kend = min(L, (qt + 1) * RPH);
     const int ntiles = (kend + TK - 1) / TK;
     const int W = a.window;                          // query i sees keys i - W + 1 .. i
     const int tile0 = max(0, qt * RPH - W + 1) / TK;  // first tile any row of the item sees
 
-    const int64_t kvbase = ((int64_t)b * a.Hkv + hkv) * a.L * D;
-    const uint32_t kvbytes = (uint32_t)((int64_t)a.L * D * 2);
+    const int64_t kvbase = row0_elem(sq, b, hkv, a.Hkv, a.L, D);
+    const int ks = row_stride(sq, a.Hkv, D);
+    const uint32_t kvbytes = (uint32_t)(((int64_t)(L - 1) * ks + D) * 2);  // this sequence only
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(reinterpret_cast<const uint16_t *>(a.k) + kvbase), 0, kvbytes, kBufferFlags);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
@@ -337,22 +358,26 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_rows_mfma_bf16_d128(Backwa
     __shared__ __attribute__((aligned(16))) uint16_t lds_k0[TK * D], lds_v0[TK * D];
     __shared__ __attribute__((aligned(16))) uint16_t lds_k1[TK * D], lds_v1[TK * D];
     auto dma_tile = [&](int tile, uint16_t *lk, uint16_t *lv) __attribute__((always_inline)) {
-        dma_rows<TK, NW>(krs, tile * TK, lk, wave, lane);
-        dma_rows<TK, NW>(vrs, tile * TK, lv, wave, lane);
+        dma_rows<TK, NW>(krs, tile * TK, ks, lk, wave, lane);
+        dma_rows<TK, NW>(vrs, tile * TK, ks, lv, wave, lane);
     };
     dma_tile(tile0, lds_k0, lds_v0);
 
     // per-wave B operands (query row n, k step u -> chunk g + 4u) and row scalars
-    const int64_t rowbase = ((int64_t)b * a.Hq + hq) * a.L;
+    const int64_t qbase = row0_elem(sq, b, hq, a.Hq, a.L, D);
+    const int qs = row_stride(sq, a.Hq, D);
+    const int64_t sbase = stat0(sq, b, hq, a.Hq, a.L);
+    const int ss = stat_stride(sq, a.Hq);
     const int row = q0 + n;
-    const int rowc = min(row, a.L - 1);
+    const int rowc = min(row, L - 1);
     bf16x8 qop[4], rop[4], gop[4];
     float delta;
     {
-        const uint16_t *qp = reinterpret_cast<const uint16_t *>(a.q) + (rowbase + rowc) * D;
-        const uint16_t *rp = reinterpret_cast<const uint16_t *>(a.r) + (rowbase + rowc) * D;
-        const uint16_t *gp = reinterpret_cast<const uint16_t *>(a.go) + (rowbase + rowc) * D;
-        const uint16_t *op = reinterpret_cast<const uint16_t *>(a.o) + (rowbase + rowc) * D;
+        const int64_t ro = qbase + (int64_t)rowc * qs;
+        const uint16_t *qp = reinterpret_cast<const uint16_t *>(a.q) + ro;
+        const uint16_t *rp = reinterpret_cast<const uint16_t *>(a.r) + ro;
+        const uint16_t *gp = reinterpret_cast<const uint16_t *>(a.go) + ro;
+        const uint16_t *op = reinterpret_cast<const uint16_t *>(a.o) + ro;
         float part = 0.f;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -365,8 +390,8 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_rows_mfma_bf16_d128(Backwa
         }
         delta = xor_sum_rowgroups(part);
     }
-    const float lse2 = a.lse[rowbase + rowc] * kLog2e;
-    const float sb = a.sbar[rowbase + rowc];
+    const float lse2 = a.lse[sbase + (int64_t)rowc * ss] * kLog2e;
+    const float sb = a.sbar[sbase + (int64_t)rowc * ss];
     const int kperm = (n >> 2) + 4 * (n & 3);
     const int q_last = q0 + 15;
 
@@ -467,10 +492,10 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_rows_mfma_bf16_d128(Backwa
         __builtin_amdgcn_s_setprio(0);
     });
 
-    if (row < a.L) {
+    if (row < L) {
         // block e, accumulator element i holds dim 16 e + 4 g + i
-        uint16_t *dq = reinterpret_cast<uint16_t *>(a.dq) + (rowbase + row) * D + 4 * g;
-        uint16_t *dr = reinterpret_cast<uint16_t *>(a.dr) + (rowbase + row) * D + 4 * g;
+        uint16_t *dq = reinterpret_cast<uint16_t *>(a.dq) + qbase + (int64_t)row * qs + 4 * g;
+        uint16_t *dr = reinterpret_cast<uint16_t *>(a.dr) + qbase + (int64_t)row * qs + 4 * g;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const floatx4 x = accQ[e] * a.qk_scale;
@@ -478,7 +503,7 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_rows_mfma_bf16_d128(Backwa
             *reinterpret_cast<uint2 *>(dq + 16 * e) = uint2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
             *reinterpret_cast<uint2 *>(dr + 16 * e) = uint2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
         }
-        if (g == 0) a.rowstat[rowbase + row] = RowStat{lse2, sb, delta, ubar};
+        if (g == 0) a.rowstat[rowstat0(sq, b, hq, a.Hq, a.L, a.total) + row] = RowStat{lse2, sb, delta, ubar};
     }
 }
 
@@ -519,19 +544,23 @@ __global__ __launch_bounds__(64 * kKeyWaves) void bwd_keys_mfma_bf16_d128(Backwa
     const int b = grp / a.Hkv;
     const int hkv = grp % a.Hkv;
     const int k0 = kblk * KB;
+    const PrefillSeq sq = prefill_seq(a.cu, b, a.L);
+    const int L = sq.len;
+    if (k0 >= L) return;  // key block past this sequence's end (packed batches)
     const int kw = k0 + 16 * KBW * wave;  // this wave's first key
     const int W = a.window;
-    const int rend = min(a.L, k0 + KB - 1 + W);  // rows k0 .. rend - 1 see some key of the block
+    const int rend = min(L, k0 + KB - 1 + W);  // rows k0 .. rend - 1 see some key of the block
     const int nrt = (rend - k0 + TR - 1) / TR;   // row tiles per query head
     const int ntiles = G * nrt;
 
-    const int64_t kvbase = ((int64_t)b * a.Hkv + hkv) * a.L * D;
+    const int64_t kvbase = row0_elem(sq, b, hkv, a.Hkv, a.L, D);
+    const int ks = row_stride(sq, a.Hkv, D);
     bf16x8 kop[KBW][4], vop[KBW][4];
 #pragma unroll
     for (int c = 0; c < KBW; ++c) {
-        const int kc = min(kw + 16 * c + n, a.L - 1);
-        const uint16_t *kp = reinterpret_cast<const uint16_t *>(a.k) + kvbase + (int64_t)kc * D;
-        const uint16_t *vp = reinterpret_cast<const uint16_t *>(a.v) + kvbase + (int64_t)kc * D;
+        const int kc = min(kw + 16 * c + n, L - 1);
+        const uint16_t *kp = reinterpret_cast<const uint16_t *>(a.k) + kvbase + (int64_t)kc * ks;
+        const uint16_t *vp = reinterpret_cast<const uint16_t *>(a.v) + kvbase + (int64_t)kc * ks;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             kop[c][u] = load16(kp + 8 * (g + 4 * u));
@@ -542,23 +571,25 @@ __global__ __launch_bounds__(64 * kKeyWaves) void bwd_keys_mfma_bf16_d128(Backwa
     __shared__ __attribute__((aligned(16))) uint16_t lq0[TR * D], lr0[TR * D], lg0[TR * D];
     __shared__ __attribute__((aligned(16))) uint16_t lq1[TR * D], lr1[TR * D], lg1[TR * D];
     __shared__ __attribute__((aligned(16))) RowStat ls0[TR], ls1[TR];
-    const uint32_t hbytes = (uint32_t)((int64_t)a.L * D * 2);
+    const int qs = row_stride(sq, a.Hq, D);
+    const uint32_t hbytes = (uint32_t)(((int64_t)(L - 1) * qs + D) * 2);  // one head of this sequence
     auto dma_tile = [&](int tile, uint16_t *tq, uint16_t *tr, uint16_t *tg, RowStat *ts) __attribute__((always_inline)) {
         const int hq = hkv * G + tile / nrt;
         const int r0 = k0 + (tile % nrt) * TR;
-        const int64_t rowbase = ((int64_t)b * a.Hq + hq) * a.L;
+        const int64_t qbase = row0_elem(sq, b, hq, a.Hq, a.L, D);
         const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(reinterpret_cast<const uint16_t *>(a.q) + rowbase * D), 0, hbytes, kBufferFlags);
+            (void *)(reinterpret_cast<const uint16_t *>(a.q) + qbase), 0, hbytes, kBufferFlags);
         const __amdgpu_buffer_rsrc_t rrs = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(reinterpret_cast<const uint16_t *>(a.r) + rowbase * D), 0, hbytes, kBufferFlags);
+            (void *)(reinterpret_cast<const uint16_t *>(a.r) + qbase), 0, hbytes, kBufferFlags);
         const __amdgpu_buffer_rsrc_t grs = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(reinterpret_cast<const uint16_t *>(a.go) + rowbase * D), 0, hbytes, kBufferFlags);
-        dma_rows<TR, NW>(qrs, r0, tq, wave, lane);
-        dma_rows<TR, NW>(rrs, r0, tr, wave, lane);
-        dma_rows<TR, NW>(grs, r0, tg, wave, lane);
+            (void *)(reinterpret_cast<const uint16_t *>(a.go) + qbase), 0, hbytes, kBufferFlags);
+        dma_rows<TR, NW>(qrs, r0, qs, tq, wave, lane);
+        dma_rows<TR, NW>(rrs, r0, qs, tr, wave, lane);
+        dma_rows<TR, NW>(grs, r0, qs, tg, wave, lane);
         if (wave == 0) {  // 64 rows x 16 bytes: one copy by one wave
             const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)(a.rowstat + rowbase), 0, (uint32_t)((int64_t)a.L * sizeof(RowStat)), kBufferFlags);
+                (void *)(a.rowstat + rowstat0(sq, b, hq, a.Hq, a.L, a.total)), 0,
+                (uint32_t)((int64_t)L * sizeof(RowStat)), kBufferFlags);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (lds_void *)ts, 16, (r0 + lane) * 16, 0, 0, 0);
         }
     };
@@ -605,7 +636,7 @@ __global__ __launch_bounds__(64 * kKeyWaves) void bwd_keys_mfma_bf16_d128(Backwa
                 const float zz = z[c][t >> 2][t & 3], ss = s[c][t >> 2][t & 3], u = uu[c][t >> 2][t & 3];
                 float w = __builtin_amdgcn_exp2f(fmaf(zz, a.zscale, -st.lse2));
                 const int key = kw + 16 * c + n;
-                if (mask && (rw < key || rw >= key + W || rw >= a.L)) w = 0.f;
+                if (mask && (rw < key || rw >= key + W || rw >= L)) w = 0.f;
                 const float sc = fmaf(ss, a.rk_scale, -st.sbar);
                 p1[c][t] = (__bf16)(w * (1.0f + sc));
                 pz[c][t] = (__bf16)(w * (fmaf(sc, u, u) - fmaf(st.ubar, sc, st.delta)) * a.qk_scale);
@@ -634,7 +665,7 @@ __global__ __launch_bounds__(64 * kKeyWaves) void bwd_keys_mfma_bf16_d128(Backwa
             const int rs = r0 + 32 * j;
             // wave-uniform: sub-tiles that see none of the wave's keys are skipped
             if (rs + 31 >= kw && rs < kw + 16 * KBW - 1 + W) {
-                const bool mask = rs < kw + 16 * KBW - 1 || rs + 31 >= kw + W || rs + 31 >= a.L;
+                const bool mask = rs < kw + 16 * KBW - 1 || rs + 31 >= kw + W || rs + 31 >= L;
                 if (mask)
                     sub_tile(tq, tr, tg, ts, 32 * j, rs, true);
                 else
@@ -652,10 +683,10 @@ __global__ __launch_bounds__(64 * kKeyWaves) void bwd_keys_mfma_bf16_d128(Backwa
 #pragma unroll
     for (int c = 0; c < KBW; ++c) {
         const int key = kw + 16 * c + n;
-        if (key < a.L) {
+        if (key < L) {
             // block e, accumulator element i holds dim 16 e + 4 g + i of the key
-            uint16_t *dk = reinterpret_cast<uint16_t *>(a.dk) + kvbase + (int64_t)key * D + 4 * g;
-            uint16_t *dv = reinterpret_cast<uint16_t *>(a.dv) + kvbase + (int64_t)key * D + 4 * g;
+            uint16_t *dk = reinterpret_cast<uint16_t *>(a.dk) + kvbase + (int64_t)key * ks + 4 * g;
+            uint16_t *dv = reinterpret_cast<uint16_t *>(a.dv) + kvbase + (int64_t)key * ks + 4 * g;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 *reinterpret_cast<uint2 *>(dk + 16 * e) =

@@ -72,4 +72,29 @@ __device__ __forceinline__ u32x4 buffer_load16_cached(__amdgpu_buffer_rsrc_t rs,
     return __builtin_amdgcn_raw_buffer_load_b128(rs, voffset, 0, kReusePolicy);
 }
 
+// Prefill tensors are dense [B, H, L, D] (cu == nullptr) or packed [T, H, D]
+// with sequence b at tokens cu[b] .. cu[b+1] - 1. Row i of head h of sequence
+// b starts at element row0_elem(...) + i * row_stride(...); the row
+// statistics (lse, sbar) are dense [B, H, L] or packed [T, H].
+struct PrefillSeq {
+    int tok0;  // first token of the sequence (packed), 0 (dense)
+    int len;
+    bool packed;
+};
+__device__ __forceinline__ PrefillSeq prefill_seq(const int32_t *cu, int b, int L) {
+    PrefillSeq s;
+    s.packed = cu != nullptr;
+    s.tok0 = s.packed ? cu[b] : 0;
+    s.len = s.packed ? cu[b + 1] - s.tok0 : L;
+    return s;
+}
+__device__ __forceinline__ int64_t row0_elem(const PrefillSeq &s, int b, int h, int H, int L, int D) {
+    return s.packed ? ((int64_t)s.tok0 * H + h) * D : ((int64_t)b * H + h) * L * D;
+}
+__device__ __forceinline__ int row_stride(const PrefillSeq &s, int H, int D) { return s.packed ? H * D : D; }
+__device__ __forceinline__ int64_t stat0(const PrefillSeq &s, int b, int h, int H, int L) {
+    return s.packed ? (int64_t)s.tok0 * H + h : ((int64_t)b * H + h) * L;
+}
+__device__ __forceinline__ int stat_stride(const PrefillSeq &s, int H) { return s.packed ? H : 1; }
+
 }  // namespace plx

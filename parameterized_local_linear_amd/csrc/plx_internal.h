@@ -61,7 +61,8 @@ struct PrefillArgs {
     const void *q, *r, *k, *v;
     void *o;
     float *lse, *sbar;
-    int B, Hq, Hkv, L, D;
+    const int32_t *cu;  // nullptr: dense [B, H, L, D]; else packed [T, H, D], cu [B + 1]
+    int B, Hq, Hkv, L, D;  // L: the (maximum) sequence length
     int window;         // query i sees keys i - window + 1 .. i (window = L: causal only)
     float zscale;       // qk_scale * log2(e)
     float rk_scale;
@@ -80,7 +81,9 @@ struct BackwardArgs {
     const void *q, *r, *k, *v, *o, *go;  // go: dLoss/do, layout of o
     const float *lse, *sbar;             // the forward's row statistics
     void *dq, *dr, *dk, *dv;
-    RowStat *rowstat;                    // workspace [B, Hq, L]
+    RowStat *rowstat;                    // workspace: [B, Hq, L] dense, [Hq, T] packed
+    const int32_t *cu;                   // as in PrefillArgs
+    int total;                           // T, the packed token count
     int B, Hq, Hkv, L, D;
     int window;                          // as in PrefillArgs, 1 .. L
     float zscale;                        // qk_scale * log2(e)

@@ -64,13 +64,17 @@ __global__ __launch_bounds__(64) void prefill_generic(PrefillArgs a) {
     const int hq = blockIdx.y;
     const int b = blockIdx.z;
     const int hkv = hq / (a.Hq / a.Hkv);
-    const int64_t row = ((int64_t)b * a.Hq + hq) * a.L + i;
-    const T *kb = reinterpret_cast<const T *>(a.k) + ((int64_t)b * a.Hkv + hkv) * a.L * D + c * EPL;
-    const T *vb = reinterpret_cast<const T *>(a.v) + ((int64_t)b * a.Hkv + hkv) * a.L * D + c * EPL;
+    const PrefillSeq sq = prefill_seq(a.cu, b, a.L);
+    if (i >= sq.len) return;  // past this sequence's end (packed batches)
+    const int ks = row_stride(sq, a.Hkv, D);
+    const int64_t row = row0_elem(sq, b, hq, a.Hq, a.L, D) + (int64_t)i * row_stride(sq, a.Hq, D);
+    const int64_t srow = stat0(sq, b, hq, a.Hq, a.L) + (int64_t)i * stat_stride(sq, a.Hq);
+    const T *kb = reinterpret_cast<const T *>(a.k) + row0_elem(sq, b, hkv, a.Hkv, a.L, D) + c * EPL;
+    const T *vb = reinterpret_cast<const T *>(a.v) + row0_elem(sq, b, hkv, a.Hkv, a.L, D) + c * EPL;
 
     float qv[EPL], rv[EPL];
-    Vec16<T>::load(reinterpret_cast<const T *>(a.q) + row * D + c * EPL, qv);
-    Vec16<T>::load(reinterpret_cast<const T *>(a.r) + row * D + c * EPL, rv);
+    Vec16<T>::load(reinterpret_cast<const T *>(a.q) + row + c * EPL, qv);
+    Vec16<T>::load(reinterpret_cast<const T *>(a.r) + row + c * EPL, rv);
     for (int e = 0; e < EPL; ++e) {
         qv[e] *= a.zscale;
         rv[e] *= a.rk_scale;
@@ -79,7 +83,7 @@ __global__ __launch_bounds__(64) void prefill_generic(PrefillArgs a) {
     float piv;
     {
         float k0[EPL];
-        Vec16<T>::load(kb + (int64_t)first * D, k0);
+        Vec16<T>::load(kb + (int64_t)first * ks, k0);
         float part = 0.f;
         for (int e = 0; e < EPL; ++e) part += rv[e] * k0[e];
         for (int off = 1; off < LPR; off <<= 1) part += __shfl_xor(part, off, LPR);
@@ -96,8 +100,8 @@ __global__ __launch_bounds__(64) void prefill_generic(PrefillArgs a) {
         const bool valid = j < end;
         const int jj = valid ? j : end - 1;
         float kv[EPL], vv[EPL];
-        Vec16<T>::load(kb + (int64_t)jj * D, kv);
-        Vec16<T>::load(vb + (int64_t)jj * D, vv);
+        Vec16<T>::load(kb + (int64_t)jj * ks, kv);
+        Vec16<T>::load(vb + (int64_t)jj * ks, vv);
         float zp = 0.f, sp = 0.f;
         for (int e = 0; e < EPL; ++e) {
             zp += qv[e] * kv[e];
@@ -143,10 +147,10 @@ __global__ __launch_bounds__(64) void prefill_generic(PrefillArgs a) {
     const float cA = 1.0f - S * inv_l;
     float ov[EPL];
     for (int e = 0; e < EPL; ++e) ov[e] = (A[e] * cA + Bv[e]) * inv_l;
-    Vec16<T>::store(reinterpret_cast<T *>(a.o) + row * D + c * EPL, ov);
+    Vec16<T>::store(reinterpret_cast<T *>(a.o) + row + c * EPL, ov);
     if (c == 0) {
-        if (a.lse) a.lse[row] = m * 0.6931471805599453f + logf(l);
-        if (a.sbar) a.sbar[row] = S * inv_l + piv;
+        if (a.lse) a.lse[srow] = m * 0.6931471805599453f + logf(l);
+        if (a.sbar) a.sbar[srow] = S * inv_l + piv;
     }
 }
 
@@ -216,15 +220,21 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_mfma_bf16_d128(Pre
     const int hsub = grp % hgroups;
     const int hq = hkv * G + hsub * HPW + wave / WPH;
     const int q0 = qt * RPH + (wave % WPH) * 16;    // this wave's first row
-    const int kend = min(a.L, (qt + 1) * RPH);      // keys the workgroup needs
+    const PrefillSeq sq = prefill_seq(a.cu, b, a.L);
+    const int L = sq.len;
+    if (qt * RPH >= L) return;  // work item past this sequence's end (packed batches)
+    const int kend = min(L, (qt + 1) * RPH);        // keys the workgroup needs
     const int ntiles = (kend + TK - 1) / TK;
     const int W = a.window;                          // query i sees keys i - W + 1 .. i
     const int tile0 = max(0, qt * RPH - W + 1) / TK;  // first tile any row of the item sees
 
     const uint16_t *qh = reinterpret_cast<const uint16_t *>(a.q);
     const uint16_t *rh = reinterpret_cast<const uint16_t *>(a.r);
-    const int64_t kvbase = ((int64_t)b * a.Hkv + hkv) * a.L * D;
-    const uint32_t kvbytes = (uint32_t)((int64_t)a.L * D * 2);
+    const int64_t kvbase = row0_elem(sq, b, hkv, a.Hkv, a.L, D);
+    const int ks = row_stride(sq, a.Hkv, D);                  // elements between keys
+    const uint32_t kvbytes = (uint32_t)(((int64_t)(L - 1) * ks + D) * 2);  // this sequence only
+    const int64_t qbase = row0_elem(sq, b, hq, a.Hq, a.L, D);
+    const int qs = row_stride(sq, a.Hq, D);
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(reinterpret_cast<const uint16_t *>(a.k) + kvbase), 0, kvbytes, kBufferFlags);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
@@ -243,7 +253,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_mfma_bf16_d128(Pre
             const int kloc = 4 * (wave * DMA + j);
             const int key = kloc + (lane >> 4);
             const int chunk = (lane & 15) ^ swz(key);
-            const int off = ((tile * TK + key) * D + chunk * 8) * 2;
+            const int off = ((tile * TK + key) * ks + chunk * 8) * 2;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void *)(lk + kloc * D), 16, off, 0, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void *)(lv + kloc * D), 16, off, 0, 0, 0);
         }
@@ -254,17 +264,16 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_mfma_bf16_d128(Pre
     bf16x8 qop[4], rop[4];
     float piv;
     {
-        const int64_t rowbase = ((int64_t)b * a.Hq + hq) * a.L;
-        const int row = min(q0 + n, a.L - 1);
-        const uint16_t *qp = qh + (rowbase + row) * D;
-        const uint16_t *rp = rh + (rowbase + row) * D;
+        const int row = min(q0 + n, L - 1);
+        const uint16_t *qp = qh + qbase + (int64_t)row * qs;
+        const uint16_t *rp = rh + qbase + (int64_t)row * qs;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             qop[u] = load16(qp + 8 * (g + 4 * u));
             rop[u] = load16(rp + 8 * (g + 4 * u));
         }
         // pivot: probe score of the row's first visible key
-        const uint16_t *k0 = reinterpret_cast<const uint16_t *>(a.k) + kvbase + (int64_t)max(0, row - W + 1) * D;
+        const uint16_t *k0 = reinterpret_cast<const uint16_t *>(a.k) + kvbase + (int64_t)max(0, row - W + 1) * ks;
         float part = 0.f;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -443,12 +452,12 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_mfma_bf16_d128(Pre
     // ---- epilogue: o = (A + B - (S / l) A) / l per row
     const float l = xor_sum_rowgroups(lsA);
     const float S = xor_sum_rowgroups(lsS);
-    if (row < a.L) {
+    if (row < L) {
         const float inv_l = 1.0f / l;
         const float cA = 1.0f - S * inv_l;
-        const int64_t ro = ((int64_t)b * a.Hq + hq) * a.L + row;
+        const int64_t ro = stat0(sq, b, hq, a.Hq, a.L) + (int64_t)row * stat_stride(sq, a.Hq);
         // readout block b, accumulator element i holds dim 16b + 4g + i
-        uint16_t *o = reinterpret_cast<uint16_t *>(a.o) + ro * D + 4 * g;
+        uint16_t *o = reinterpret_cast<uint16_t *>(a.o) + qbase + (int64_t)row * qs + 4 * g;
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
             float ov[4];

@@ -176,6 +176,27 @@ def prefill_spec(idx: int = 5) -> PrefillSpec:
                        1.0 / np.sqrt(128.0), BASE_SEED + 5)
 
 
+@dataclass
+class VarlenPrefillSpec:
+    name: str
+    lengths: np.ndarray
+    Hq: int
+    Hkv: int
+    D: int
+    dtype: int
+    scale: float
+    seed: int
+
+
+def prefill_varlen_spec() -> VarlenPrefillSpec:
+    """Packed training batch: 16 sequences of U{256 .. 4096} tokens, Hq16 Hkv8 D128 bf16
+    (the causal-prefill workload's heads with a length mix instead of one length)."""
+    seed = BASE_SEED + 40
+    lens = uniform_int(seed, TID_LENGTHS, 16, 256, 4096)
+    return VarlenPrefillSpec("varlen-prefill-bf16 16 seqs L~U[256,4096] Hq16 Hkv8 D128", lens, 16,
+                             8, 128, BF16, 1.0 / np.sqrt(128.0), seed)
+
+
 def decode_qr(spec: DecodeSpec, r_zero: bool = False):
     """q, r as [B, Hq, D] arrays of the spec's dtype."""
     shp = (spec.B, spec.Hq, spec.D)
