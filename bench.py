@@ -463,12 +463,14 @@ def run_prefill_varlen_workload(args, torch, plx, synth, oracle):
     sbar = torch.empty_like(lse)
     grads = (torch.empty_like(t["q"]), torch.empty_like(t["r"]), torch.empty_like(t["k"]),
              torch.empty_like(t["v"]))
-    ws = torch.empty(int(plx.lib().parallax_prefill_backward_workspace_bytes(1, Hq, T)),
+    ws = torch.empty(int(plx.lib().parallax_prefill_varlen_workspace_bytes(Hq, T, 1)),
                      dtype=torch.uint8, device="cuda")
-    plx.prefill_varlen(t["q"], t["r"], t["k"], t["v"], cu_t, max_len, out=out, window=W)
+    ws_f = torch.empty(int(plx.lib().parallax_prefill_varlen_workspace_bytes(Hq, T, 0)),
+                       dtype=torch.uint8, device="cuda")
 
     def fwd(i):
-        plx.prefill_varlen(t["q"], t["r"], t["k"], t["v"], cu_t, max_len, out=out, window=W)
+        plx.prefill_varlen(t["q"], t["r"], t["k"], t["v"], cu_t, max_len, out=out, window=W,
+                           workspace=ws_f)
 
     o, lse, sbar = plx.prefill_varlen(t["q"], t["r"], t["k"], t["v"], cu_t, max_len,
                                       return_stats=True, window=W)

@@ -215,16 +215,23 @@ int parallax_prefill_backward(const void *q, const void *r, const void *k, const
  *                sequence b owns tokens cu[b] .. cu[b+1] - 1. Read on the device
  *                only, so not validated: lengths must not exceed max_len.
  *   max_len    : the longest sequence (sizes the launch grid), >= 1.
- *   workspace  : at least parallax_prefill_backward_workspace_bytes(1, Hq,
- *                total_tokens) bytes.
+ *   workspace, workspace_bytes : DEVICE scratch of at least
+ *                parallax_prefill_varlen_workspace_bytes(Hq, total_tokens, 0)
+ *                bytes for the forward, (..., 1) for the backward: the work
+ *                queue counters of the persistent launch (cleared by the call
+ *                itself) and, for the backward, 16 bytes per query row.
+ *                Calls that share a workspace must not overlap in time.
  * Other arguments, rules and errors as the dense calls; total_tokens == 0
  * (every sequence empty) returns PLX_OK without a launch. max_len times
  * max(Hq, Hkv) * D * element size must stay below 2^31 bytes.
  * ---------------------------------------------------------------------- */
+size_t parallax_prefill_varlen_workspace_bytes(int Hq, int total_tokens, int backward);
+
 int parallax_prefill_varlen(const void *q, const void *r, const void *k, const void *v, void *o,
                             float *lse, float *sbar, const int32_t *cu_seqlens, int B, int Hq,
                             int Hkv, int max_len, int total_tokens, int D, int window,
-                            float qk_scale, float rk_scale, int dtype, void *stream);
+                            float qk_scale, float rk_scale, int dtype, void *workspace,
+                            size_t workspace_bytes, void *stream);
 
 int parallax_prefill_varlen_backward(const void *q, const void *r, const void *k, const void *v,
                                      const void *o, const void *d_o, const float *lse,

@@ -79,7 +79,9 @@ def lib() -> ctypes.CDLL:
         L.parallax_prefill_backward_workspace_bytes.restype = sz
         L.parallax_prefill_backward.argtypes = [vp] * 12 + [i32] * 6 + [f32, f32, i32, vp, sz, vp]
         L.parallax_prefill_backward.restype = i32
-        L.parallax_prefill_varlen.argtypes = [vp] * 8 + [i32] * 7 + [f32, f32, i32, vp]
+        L.parallax_prefill_varlen.argtypes = [vp] * 8 + [i32] * 7 + [f32, f32, i32, vp, sz, vp]
+        L.parallax_prefill_varlen_workspace_bytes.argtypes = [i32, i32, i32]
+        L.parallax_prefill_varlen_workspace_bytes.restype = sz
         L.parallax_prefill_varlen.restype = i32
         L.parallax_prefill_varlen_backward.argtypes = [vp] * 13 + [i32] * 7 + [f32, f32, i32, vp,
                                                                               sz, vp]
@@ -369,7 +371,7 @@ def _varlen_shapes(q, k, cu_seqlens, max_len):
 
 
 def prefill_varlen(q, r, k, v, cu_seqlens, max_len=None, qk_scale=None, rk_scale=1.0, *,
-                   out=None, return_stats=False, window=0):
+                   out=None, return_stats=False, window=0, workspace=None):
     """Causal prefill of packed sequences: q, r [T, Hq, D]; k, v [T, Hkv, D]; int32
     ``cu_seqlens`` [B + 1]. Returns o [T, Hq, D] (plus fp32 lse, sbar [T, Hq])."""
     L_ = lib()
@@ -388,9 +390,13 @@ def prefill_varlen(q, r, k, v, cu_seqlens, max_len=None, qk_scale=None, rk_scale
     if return_stats:
         lse = torch.empty((T, Hq), dtype=torch.float32, device=dev)
         sbar = torch.empty((T, Hq), dtype=torch.float32, device=dev)
+    if workspace is None:
+        need = int(L_.parallax_prefill_varlen_workspace_bytes(Hq, T, 0))
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     st = L_.parallax_prefill_varlen(_ptr(q), _ptr(r), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                                     _ptr(sbar), _ptr(cu_seqlens), B, Hq, Hkv, max_len, T, D,
                                     int(window), float(qk_scale), float(rk_scale), _dtype_code(q),
+                                    _ptr(workspace), workspace.numel() * workspace.element_size(),
                                     _stream_handle(dev))
     if st != 0:
         raise ParallaxError(st, "parallax_prefill_varlen")
@@ -412,7 +418,7 @@ def prefill_varlen_backward(q, r, k, v, o, d_o, lse, sbar, cu_seqlens, max_len=N
             raise ValueError(f"{name} must be float32 [T, Hq]")
     if qk_scale is None:
         qk_scale = 1.0 / math.sqrt(D)
-    need = int(L_.parallax_prefill_backward_workspace_bytes(1, Hq, max(T, 1)))
+    need = int(L_.parallax_prefill_varlen_workspace_bytes(Hq, T, 1))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     if out is None:

@@ -228,6 +228,10 @@ int parallax_decode_merge(const void *records, void *o, int B, int Hq, int D, in
 
 // Checks shared by the prefill entry points (dense when cu == nullptr,
 // packed with `total` tokens otherwise); fills the sizes of `a`.
+// Packed batches run persistent workgroups fed from per-XCD queues: the
+// workspace starts with their counters (16 ints used, 256 bytes reserved).
+constexpr size_t kQueueBytes = 256;
+
 template <typename Args>
 static int check_prefill(Args &a, const int32_t *cu, int B, int Hq, int Hkv, int L, int total, int D,
                          int window, float qk_scale, float rk_scale, int dtype) {
@@ -243,6 +247,8 @@ static int check_prefill(Args &a, const int32_t *cu, int B, int Hq, int Hkv, int
     const long long row_bytes = (long long)(cu ? (Hq > Hkv ? Hq : Hkv) : 1) * D * (dtype == PLX_BF16 ? 2 : 4);
     if ((long long)L * row_bytes >= 0x7fffffffLL) return PLX_ERR_UNSUPPORTED;
     a.cu = cu;
+    a.sched = nullptr;
+    a.workers = plx::device_cu_count();  // one workgroup per CU fits the LDS of each kernel
     a.B = B;
     a.Hq = Hq;
     a.Hkv = Hkv;
@@ -256,12 +262,15 @@ static int check_prefill(Args &a, const int32_t *cu, int B, int Hq, int Hkv, int
 
 static int prefill_common(const void *q, const void *r, const void *k, const void *v, void *o, float *lse,
                           float *sbar, const int32_t *cu, int B, int Hq, int Hkv, int L, int total, int D,
-                          int window, float qk_scale, float rk_scale, int dtype, void *stream) {
+                          int window, float qk_scale, float rk_scale, int dtype, void *ws, size_t ws_bytes,
+                          void *stream) {
     if (!q || !r || !k || !v || !o) return PLX_ERR_INVALID_ARG;
     plx::PrefillArgs a;
     int st = check_prefill(a, cu, B, Hq, Hkv, L, total, D, window, qk_scale, rk_scale, dtype);
     if (st != PLX_OK) return st;
+    if (cu && (!ws || ws_bytes < kQueueBytes)) return PLX_ERR_WORKSPACE;
     if (cu && total == 0) return PLX_OK;  // every sequence empty
+    if (cu) a.sched = reinterpret_cast<int *>(ws);
     a.q = q;
     a.r = r;
     a.k = k;
@@ -284,9 +293,13 @@ static int backward_common(const void *q, const void *r, const void *k, const vo
     int st = check_prefill(a, cu, B, Hq, Hkv, L, total, D, window, qk_scale, rk_scale, dtype);
     if (st != PLX_OK) return st;
     if (cu && total == 0) return PLX_OK;  // every sequence empty
-    const size_t need = cu ? (size_t)Hq * total * sizeof(plx::RowStat)
+    const size_t need = cu ? kQueueBytes + (size_t)Hq * total * sizeof(plx::RowStat)
                            : (size_t)B * Hq * L * sizeof(plx::RowStat);
     if (!workspace || workspace_bytes < need) return PLX_ERR_WORKSPACE;
+    if (cu) {
+        a.sched = reinterpret_cast<int *>(workspace);
+        workspace = reinterpret_cast<char *>(workspace) + kQueueBytes;
+    }
     a.q = q;
     a.r = r;
     a.k = k;
@@ -312,16 +325,22 @@ int parallax_prefill(const void *q, const void *r, const void *k, const void *v,
                      float *sbar, int B, int Hq, int Hkv, int L, int D, int window, float qk_scale,
                      float rk_scale, int dtype, void *stream) {
     return prefill_common(q, r, k, v, o, lse, sbar, nullptr, B, Hq, Hkv, L, 0, D, window, qk_scale,
-                          rk_scale, dtype, stream);
+                          rk_scale, dtype, nullptr, 0, stream);
+}
+
+size_t parallax_prefill_varlen_workspace_bytes(int Hq, int total_tokens, int backward) {
+    if (Hq < 1 || total_tokens < 0) return 0;
+    return kQueueBytes + (backward ? (size_t)Hq * total_tokens * sizeof(plx::RowStat) : 0);
 }
 
 int parallax_prefill_varlen(const void *q, const void *r, const void *k, const void *v, void *o,
                             float *lse, float *sbar, const int32_t *cu_seqlens, int B, int Hq, int Hkv,
                             int max_len, int total_tokens, int D, int window, float qk_scale,
-                            float rk_scale, int dtype, void *stream) {
+                            float rk_scale, int dtype, void *workspace, size_t workspace_bytes,
+                            void *stream) {
     if (!cu_seqlens) return PLX_ERR_INVALID_ARG;
     return prefill_common(q, r, k, v, o, lse, sbar, cu_seqlens, B, Hq, Hkv, max_len, total_tokens, D,
-                          window, qk_scale, rk_scale, dtype, stream);
+                          window, qk_scale, rk_scale, dtype, workspace, workspace_bytes, stream);
 }
 
 size_t parallax_prefill_backward_workspace_bytes(int B, int Hq, int L) {

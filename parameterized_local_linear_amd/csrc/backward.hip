@@ -315,7 +315,7 @@ __device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t rs, int row0, in
 //   sweep 2: Z^T, S^T = K R^T, U^T, then dQ^T += K^T dZ^T,
 //            dR^T += K^T dS^T with K^T read transposed       (40 MFMAs)
 template <int HPW>
-__global__ __launch_bounds__(64 * kBwdWaves) void bwd_rows_mfma_bf16_d128(BackwardArgs a) {
+__device__ __forceinline__ void bwd_rows_item(const BackwardArgs &a, const int item) {
     constexpr int D = 128;
     constexpr int NW = kBwdWaves;
     constexpr int WPH = NW / HPW;
@@ -331,7 +331,6 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_rows_mfma_bf16_d128(Backwa
     const int hgroups = G / HPW;
     const int NG = a.B * a.Hkv * hgroups;
     const int QT = (a.L + RPH - 1) / RPH;
-    const int item = blockIdx.x;
     const int grp = item % NG;
     const int qt = QT - 1 - item / NG;
     const int b = grp / (a.Hkv * hgroups);
@@ -526,7 +525,7 @@ __global__ __launch_bounds__(64 * kBwdWaves) void bwd_rows_mfma_bf16_d128(Backwa
 constexpr int kKeyWaves = 4;
 constexpr int kKeyBlocksPerWave = 2;  // 16-key column blocks per wave
 
-__global__ __launch_bounds__(64 * kKeyWaves) void bwd_keys_mfma_bf16_d128(BackwardArgs a) {
+__device__ __forceinline__ void bwd_keys_item(const BackwardArgs &a, const int item) {
     constexpr int D = 128;
     constexpr int NW = kKeyWaves;
     constexpr int KBW = kKeyBlocksPerWave;
@@ -539,8 +538,8 @@ __global__ __launch_bounds__(64 * kKeyWaves) void bwd_keys_mfma_bf16_d128(Backwa
 
     const int G = a.Hq / a.Hkv;
     const int NG = a.B * a.Hkv;
-    const int grp = blockIdx.x % NG;
-    const int kblk = blockIdx.x / NG;
+    const int grp = item % NG;
+    const int kblk = item / NG;
     const int b = grp / a.Hkv;
     const int hkv = grp % a.Hkv;
     const int k0 = kblk * KB;
@@ -698,6 +697,33 @@ __global__ __launch_bounds__(64 * kKeyWaves) void bwd_keys_mfma_bf16_d128(Backwa
     }
 }
 
+// PERSIST = false: one work item per workgroup (dense batches); true: a
+// persistent grid drawing items from per-XCD queues (packed batches; the
+// row pass uses counters 0..7, the key pass 8..15).
+template <int HPW, bool PERSIST>
+__global__ __launch_bounds__(64 * kBwdWaves) void bwd_rows_mfma_bf16_d128(BackwardArgs a) {
+    if (!PERSIST) {
+        bwd_rows_item<HPW>(a, blockIdx.x);
+        return;
+    }
+    constexpr int RPH = 16 * kBwdWaves / HPW;
+    const int n_items = a.B * a.Hkv * (a.Hq / a.Hkv / HPW) * ((a.L + RPH - 1) / RPH);
+    for (int item = next_item(a.sched, n_items); item >= 0; item = next_item(a.sched, n_items))
+        bwd_rows_item<HPW>(a, item);
+}
+
+template <bool PERSIST>
+__global__ __launch_bounds__(64 * kKeyWaves) void bwd_keys_mfma_bf16_d128(BackwardArgs a) {
+    if (!PERSIST) {
+        bwd_keys_item(a, blockIdx.x);
+        return;
+    }
+    constexpr int KB = 16 * kKeyBlocksPerWave * kKeyWaves;
+    const int n_items = a.B * a.Hkv * ((a.L + KB - 1) / KB);
+    for (int item = next_item(a.sched + 8, n_items); item >= 0; item = next_item(a.sched + 8, n_items))
+        bwd_keys_item(a, item);
+}
+
 template <typename T, int D>
 hipError_t launch_generic(const BackwardArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL((bwd_rows_generic<T, D>), dim3(a.L, a.Hq, a.B), dim3(64), 0, stream, a);
@@ -718,16 +744,33 @@ hipError_t launch_prefill_backward(const BackwardArgs &a, int dtype, hipStream_t
         constexpr int kb = 16 * kKeyBlocksPerWave * kKeyWaves;
         const long key_items = (long)a.B * a.Hkv * ((a.L + kb - 1) / kb);
         if (row_items <= 0x7fffffffL && key_items <= 0x7fffffffL) {
-            if (hpw == 2)
-                hipLaunchKernelGGL((bwd_rows_mfma_bf16_d128<2>), dim3((unsigned)row_items),
+            // persistent workers, a multiple of 8 so that every XCD share is drained
+            auto workers = [&](long items) { return (unsigned)(((items < a.workers ? items : a.workers) + 7) / 8 * 8); };
+            hipError_t err;
+            if (a.sched) {
+                err = launch_zero_counters(a.sched, 16, stream);
+                if (err != hipSuccess) return err;
+                if (hpw == 2)
+                    hipLaunchKernelGGL((bwd_rows_mfma_bf16_d128<2, true>), dim3(workers(row_items)),
+                                       dim3(64 * kBwdWaves), 0, stream, a);
+                else
+                    hipLaunchKernelGGL((bwd_rows_mfma_bf16_d128<1, true>), dim3(workers(row_items)),
+                                       dim3(64 * kBwdWaves), 0, stream, a);
+            } else if (hpw == 2) {
+                hipLaunchKernelGGL((bwd_rows_mfma_bf16_d128<2, false>), dim3((unsigned)row_items),
                                    dim3(64 * kBwdWaves), 0, stream, a);
-            else
-                hipLaunchKernelGGL((bwd_rows_mfma_bf16_d128<1>), dim3((unsigned)row_items),
+            } else {
+                hipLaunchKernelGGL((bwd_rows_mfma_bf16_d128<1, false>), dim3((unsigned)row_items),
                                    dim3(64 * kBwdWaves), 0, stream, a);
-            hipError_t err = hipGetLastError();
+            }
+            err = hipGetLastError();
             if (err != hipSuccess) return err;
-            hipLaunchKernelGGL(bwd_keys_mfma_bf16_d128, dim3((unsigned)key_items), dim3(64 * kKeyWaves), 0,
-                               stream, a);
+            if (a.sched)
+                hipLaunchKernelGGL((bwd_keys_mfma_bf16_d128<true>), dim3(workers(key_items)),
+                                   dim3(64 * kKeyWaves), 0, stream, a);
+            else
+                hipLaunchKernelGGL((bwd_keys_mfma_bf16_d128<false>), dim3((unsigned)key_items),
+                                   dim3(64 * kKeyWaves), 0, stream, a);
             return hipGetLastError();
         }
     }

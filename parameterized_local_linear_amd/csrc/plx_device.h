@@ -97,4 +97,21 @@ __device__ __forceinline__ int64_t stat0(const PrefillSeq &s, int b, int h, int 
 }
 __device__ __forceinline__ int stat_stride(const PrefillSeq &s, int H) { return s.packed ? H : 1; }
 
+// Dynamic work queue of a persistent launch (packed batches, whose grid would
+// otherwise hold a workgroup for every (sequence, tile) slot up to the longest
+// sequence). Workgroup w draws from the share of XCD x = w % 8 (consecutive
+// workgroup ids are dispatched to consecutive XCDs): items x, x + 8, x + 16,
+// ... in order, through counter x, so that the items of one (sequence, KV
+// head) group stay on one XCD and its L2. Returns -1 when the share is
+// exhausted. Two workgroup barriers; called by every thread.
+__device__ __forceinline__ int next_item(int *counters, int n_items) {
+    __shared__ int slot;
+    const int x = blockIdx.x & 7;
+    if (threadIdx.x == 0) slot = atomicAdd(&counters[x], 1);
+    __syncthreads();
+    const long item = (long)slot * 8 + x;
+    __syncthreads();
+    return item < n_items ? (int)item : -1;
+}
+
 }  // namespace plx

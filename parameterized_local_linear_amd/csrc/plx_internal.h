@@ -62,6 +62,8 @@ struct PrefillArgs {
     void *o;
     float *lse, *sbar;
     const int32_t *cu;  // nullptr: dense [B, H, L, D]; else packed [T, H, D], cu [B + 1]
+    int *sched;         // nullptr: one work item per workgroup; else 8 zeroed queue counters
+    int workers;        // workgroups of a persistent launch (when sched != nullptr)
     int B, Hq, Hkv, L, D;  // L: the (maximum) sequence length
     int window;         // query i sees keys i - window + 1 .. i (window = L: causal only)
     float zscale;       // qk_scale * log2(e)
@@ -84,6 +86,8 @@ struct BackwardArgs {
     RowStat *rowstat;                    // workspace: [B, Hq, L] dense, [Hq, T] packed
     const int32_t *cu;                   // as in PrefillArgs
     int total;                           // T, the packed token count
+    int *sched;                          // nullptr, or 16 zeroed queue counters (rows 0..7, keys 8..15)
+    int workers;                         // workgroups of a persistent launch
     int B, Hq, Hkv, L, D;
     int window;                          // as in PrefillArgs, 1 .. L
     float zscale;                        // qk_scale * log2(e)
@@ -91,5 +95,9 @@ struct BackwardArgs {
 };
 
 hipError_t launch_prefill_backward(const BackwardArgs &a, int dtype, hipStream_t stream);
+
+// Zero n (<= 64) int counters on the stream (a kernel, so that it can be
+// captured in a graph).
+hipError_t launch_zero_counters(int *c, int n, hipStream_t stream);
 
 }  // namespace plx

@@ -192,8 +192,10 @@ constexpr int kPrefillWaves = 8;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
+// One work item; returns before any barrier when the item lies past its
+// sequence's end.
 template <int HPW>
-__global__ __launch_bounds__(64 * kPrefillWaves) void prefill_mfma_bf16_d128(PrefillArgs a) {
+__device__ __forceinline__ void prefill_item(const PrefillArgs &a, const int item) {
     constexpr int D = 128;
     constexpr int NW = kPrefillWaves;
     constexpr int WPH = NW / HPW;       // waves per head
@@ -212,7 +214,6 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_mfma_bf16_d128(Pre
     const int hgroups = G / HPW;                    // head groups per KV head
     const int NG = a.B * a.Hkv * hgroups;           // groups
     const int QT = (a.L + RPH - 1) / RPH;           // q-tiles per group
-    const int item = blockIdx.x;
     const int grp = item % NG;
     const int qt = QT - 1 - item / NG;
     const int b = grp / (a.Hkv * hgroups);
@@ -472,7 +473,30 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_mfma_bf16_d128(Pre
     }
 }
 
+// PERSIST = false: one work item per workgroup (dense batches); true: a
+// persistent grid drawing items from the per-XCD queues (packed batches).
+template <int HPW, bool PERSIST>
+__global__ __launch_bounds__(64 * kPrefillWaves) void prefill_mfma_bf16_d128(PrefillArgs a) {
+    if (!PERSIST) {
+        prefill_item<HPW>(a, blockIdx.x);
+        return;
+    }
+    const int n_items = a.B * a.Hkv * (a.Hq / a.Hkv / HPW) * ((a.L + 16 * kPrefillWaves / HPW - 1) /
+                                                            (16 * kPrefillWaves / HPW));
+    for (int item = next_item(a.sched, n_items); item >= 0; item = next_item(a.sched, n_items))
+        prefill_item<HPW>(a, item);
+}
+
+__global__ void zero_counters(int *c, int n) {
+    if ((int)threadIdx.x < n) c[threadIdx.x] = 0;
+}
+
 }  // namespace
+
+hipError_t launch_zero_counters(int *c, int n, hipStream_t stream) {
+    hipLaunchKernelGGL(zero_counters, dim3(1), dim3(64), 0, stream, c, n);
+    return hipGetLastError();
+}
 
 bool prefill_supported(int D, int dtype) { return (D == 64 || D == 128) && (dtype == 0 || dtype == 1); }
 
@@ -483,11 +507,22 @@ hipError_t launch_prefill(const PrefillArgs &a, int dtype, hipStream_t stream) {
         const int rph = 16 * kPrefillWaves / hpw;
         const long items = (long)a.B * a.Hkv * (G / hpw) * ((a.L + rph - 1) / rph);
         if (items <= 0x7fffffffL) {
-            dim3 grid((unsigned)items), block(64 * kPrefillWaves);
-            if (hpw == 2)
-                hipLaunchKernelGGL((prefill_mfma_bf16_d128<2>), grid, block, 0, stream, a);
+            long wgs = items;
+            if (a.sched) {
+                // persistent workers, a multiple of 8 so that every XCD share is drained
+                wgs = ((items < a.workers ? items : a.workers) + 7) / 8 * 8;
+                hipError_t err = launch_zero_counters(a.sched, 8, stream);
+                if (err != hipSuccess) return err;
+            }
+            dim3 grid((unsigned)wgs), block(64 * kPrefillWaves);
+            if (hpw == 2 && a.sched)
+                hipLaunchKernelGGL((prefill_mfma_bf16_d128<2, true>), grid, block, 0, stream, a);
+            else if (hpw == 2)
+                hipLaunchKernelGGL((prefill_mfma_bf16_d128<2, false>), grid, block, 0, stream, a);
+            else if (a.sched)
+                hipLaunchKernelGGL((prefill_mfma_bf16_d128<1, true>), grid, block, 0, stream, a);
             else
-                hipLaunchKernelGGL((prefill_mfma_bf16_d128<1>), grid, block, 0, stream, a);
+                hipLaunchKernelGGL((prefill_mfma_bf16_d128<1, false>), grid, block, 0, stream, a);
             return hipGetLastError();
         }
     }

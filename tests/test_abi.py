@@ -141,13 +141,21 @@ def test_varlen_prefill_rejects_on_host():
     L = plx.lib()
     p8 = [FAKE] * 5 + [None, None]
     # cu_seqlens missing, negative total, too long a packed head, empty batch is a no-op
-    assert L.parallax_prefill_varlen(*p8, None, 2, 4, 2, 64, 100, 128, 0, 0.1, 1.0, 1, None) == 1
-    assert L.parallax_prefill_varlen(*p8, FAKE, 2, 4, 2, 64, -1, 128, 0, 0.1, 1.0, 1, None) == 1
-    assert L.parallax_prefill_varlen(*p8, FAKE, 2, 64, 8, 1 << 21, 100, 128, 0, 0.1, 1.0, 1,
+    ws = (FAKE, 256)
+    assert L.parallax_prefill_varlen(*p8, None, 2, 4, 2, 64, 100, 128, 0, 0.1, 1.0, 1, *ws,
+                                     None) == 1
+    assert L.parallax_prefill_varlen(*p8, FAKE, 2, 4, 2, 64, -1, 128, 0, 0.1, 1.0, 1, *ws,
+                                     None) == 1
+    assert L.parallax_prefill_varlen(*p8, FAKE, 2, 64, 8, 1 << 21, 100, 128, 0, 0.1, 1.0, 1, *ws,
                                      None) == 2
-    assert L.parallax_prefill_varlen(*p8, FAKE, 2, 4, 2, 64, 0, 128, 0, 0.1, 1.0, 1, None) == 0
+    assert L.parallax_prefill_varlen(*p8, FAKE, 2, 4, 2, 64, 100, 128, 0, 0.1, 1.0, 1, FAKE, 255,
+                                     None) == 3
+    assert L.parallax_prefill_varlen(*p8, FAKE, 2, 4, 2, 64, 0, 128, 0, 0.1, 1.0, 1, *ws,
+                                     None) == 0
+    assert L.parallax_prefill_varlen_workspace_bytes(4, 100, 0) == 256
+    assert L.parallax_prefill_varlen_workspace_bytes(4, 100, 1) == 256 + 4 * 100 * 16
     b13 = [FAKE] * 8 + [FAKE] + [FAKE] * 4
     assert L.parallax_prefill_varlen_backward(*b13, 2, 4, 2, 64, 100, 128, 0, 0.1, 1.0, 1, None,
                                               0, None) == 3
     assert L.parallax_prefill_varlen_backward(*b13, 2, 4, 2, 64, 100, 128, 0, 0.1, 1.0, 1, FAKE,
-                                              4 * 100 * 16 - 1, None) == 3
+                                              256 + 4 * 100 * 16 - 1, None) == 3
