@@ -34,7 +34,7 @@ int device_cu_count() {
 // with at least kMinKeysPerWave keys per wave; one split fuses the final
 // normalisation into the streaming kernel and needs no workspace.
 constexpr int kTargetWavesPerCU = 4;
-constexpr int kMinKeysPerWave = 128;
+constexpr int kMinKeysPerWave = 32;  // one tile: short sequences split for latency
 DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int kv_len, int window, int dtype,
                        int num_splits) {
     DecodePlan p;

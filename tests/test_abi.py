@@ -100,11 +100,14 @@ def test_workspace_plan():
         assert cur >= prev
         prev = cur
     assert ws(0, 16, 8, 128, 64, 1, 0) == 0 and ns(1, 16, 5, 128, 64, 1, 0) == 0
-    # the automatic plan keeps at least 128 keys per wave (4 waves per split on the MFMA path)
+    # the automatic plan keeps at least one 32-key tile per wave (4 waves per split on the
+    # MFMA path, 1 on the generic one) and targets one workgroup per CU
     s = ns(1, 16, 8, 128, 32768, 1, 0)
-    assert 1 < s <= 32768 // 512
-    s = ns(1, 16, 8, 64, 32768, 1, 0)
     assert 1 < s <= 32768 // 128
+    s = ns(1, 16, 8, 64, 32768, 1, 0)
+    assert 1 < s <= 32768 // 32
+    assert ns(1, 8, 8, 128, 1024, 1, 0) == 8       # short sequence: split down to 128 keys
+    assert ns(2048, 16, 8, 128, 2048, 1, 0) == 1   # large batch: one split
 
 
 def _backward(**kw):
