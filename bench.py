@@ -387,7 +387,10 @@ def run_backward_workload(args, torch, plx, synth, oracle):
         arrs[name] = synth.normal(spec.seed, tid, (B, H, L, D), sc, spec.dtype)
     t = {n: torch.from_numpy(a).view(torch.bfloat16).cuda() for n, a in arrs.items()}
     W = args.window
-    o, lse, sbar = plx.prefill(t["q"], t["r"], t["k"], t["v"], return_stats=True, window=W)
+    # the forward stores the softmax readout, as the autograd entry point does
+    vbar = torch.empty_like(t["q"])
+    o, lse, sbar = plx.prefill(t["q"], t["r"], t["k"], t["v"], return_stats=True, window=W,
+                               vbar_out=vbar)
     grads = (torch.empty_like(t["q"]), torch.empty_like(t["r"]), torch.empty_like(t["k"]),
              torch.empty_like(t["v"]))
     ws = torch.empty(int(plx.lib().parallax_prefill_backward_workspace_bytes(B, Hq, L)),
@@ -395,7 +398,7 @@ def run_backward_workload(args, torch, plx, synth, oracle):
 
     def step(i):
         plx.prefill_backward(t["q"], t["r"], t["k"], t["v"], o, t["do"], lse, sbar,
-                             workspace=ws, out=grads, window=W)
+                             workspace=ws, out=grads, window=W, vbar=vbar)
 
     steps = max(1, min(args.steps, 10))
     warm = max(1, min(args.warmup, 2))
@@ -415,7 +418,7 @@ def run_backward_workload(args, torch, plx, synth, oracle):
                      "achieved": round(flops / ts / 1e12, 2), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(flops / ts / 1e12 / BF16_PEAK_TFLOPS, 4),
                      "traffic": None, "avg_us": round(ts * 1e6, 1), "flops_per_launch": flops,
-                     "executed_flops_per_launch": flops * 13 // 8},
+                     "executed_flops_per_launch": flops * 11 // 8},
     }
     # parity and CPU baseline: the oracle's complete gradients of one (sequence, KV head) unit
     units = np.array([[0, 0]])
@@ -472,12 +475,13 @@ def run_prefill_varlen_workload(args, torch, plx, synth, oracle):
         plx.prefill_varlen(t["q"], t["r"], t["k"], t["v"], cu_t, max_len, out=out, window=W,
                            workspace=ws_f)
 
+    vbar = torch.empty_like(t["q"])
     o, lse, sbar = plx.prefill_varlen(t["q"], t["r"], t["k"], t["v"], cu_t, max_len,
-                                      return_stats=True, window=W)
+                                      return_stats=True, window=W, vbar_out=vbar)
 
     def bwd(i):
         plx.prefill_varlen_backward(t["q"], t["r"], t["k"], t["v"], o, t["do"], lse, sbar, cu_t,
-                                    max_len, window=W, workspace=ws, out=grads)
+                                    max_len, window=W, workspace=ws, out=grads, vbar=vbar)
 
     steps = max(1, min(args.steps, 10))
     warm = max(1, min(args.warmup, 2))

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define PARALLAX_ABI_VERSION 2
+#define PARALLAX_ABI_VERSION 3
 
 typedef enum {
     PLX_OK = 0,
@@ -164,13 +164,17 @@ int parallax_decode_merge(const void *records, void *o, int B, int Hq, int D, in
  *   k, v    : [B, Hkv, L, D]
  *   lse     : NULL or DEVICE float [B, Hq, L]: m + ln(sum_j exp(z_j - m))
  *   sbar    : NULL or DEVICE float [B, Hq, L]: sum_j w_j s_j
- *             (the row statistics a backward pass needs; not on the pages)
+ *   vbar    : NULL or DEVICE [B, Hq, L, D] in dtype: the softmax readout
+ *             sum_j w_j v_j (o without the correction)
+ *             (statistics for a backward pass; not on the pages. With vbar
+ *             the backward skips one of its two sweeps over the keys, at the
+ *             cost of one more o-sized activation)
  *   D == 128 and dtype == PLX_BF16 run on bf16 MFMA with fp32 accumulation;
  *   other D in {64, 128} and PLX_F32 run on a plain fp32 kernel. L <= 2^22.
  * ---------------------------------------------------------------------- */
 int parallax_prefill(const void *q, const void *r, const void *k, const void *v, void *o,
-                     float *lse, float *sbar, int B, int Hq, int Hkv, int L, int D, int window,
-                     float qk_scale, float rk_scale, int dtype, void *stream);
+                     float *lse, float *sbar, void *vbar, int B, int Hq, int Hkv, int L, int D,
+                     int window, float qk_scale, float rk_scale, int dtype, void *stream);
 
 /* ------------------------------------------------------------------------
  * Backward of the causal prefill (PyPI README, "Training (Triton)": the
@@ -187,6 +191,7 @@ int parallax_prefill(const void *q, const void *r, const void *k, const void *v,
  *                                              query heads of each KV head)
  *   lse, sbar : DEVICE float [B, Hq, L], as written by parallax_prefill for
  *               the same q, r, k, v, window, scales and dtype; o likewise.
+ *   vbar      : NULL, or the vbar that forward call wrote.
  *   workspace, workspace_bytes : DEVICE scratch of at least
  *               parallax_prefill_backward_workspace_bytes(B, Hq, L) bytes
  *               (16 bytes per query row).
@@ -197,10 +202,10 @@ size_t parallax_prefill_backward_workspace_bytes(int B, int Hq, int L);
 
 int parallax_prefill_backward(const void *q, const void *r, const void *k, const void *v,
                               const void *o, const void *d_o, const float *lse,
-                              const float *sbar, void *dq, void *dr, void *dk, void *dv, int B,
-                              int Hq, int Hkv, int L, int D, int window, float qk_scale,
-                              float rk_scale, int dtype, void *workspace, size_t workspace_bytes,
-                              void *stream);
+                              const float *sbar, const void *vbar, void *dq, void *dr, void *dk,
+                              void *dv, int B, int Hq, int Hkv, int L, int D, int window,
+                              float qk_scale, float rk_scale, int dtype, void *workspace,
+                              size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * Packed-sequence (varlen) prefill and its backward (the pages name
@@ -211,6 +216,7 @@ int parallax_prefill_backward(const void *q, const void *r, const void *k, const
  *   q, r, o, d_o, dq, dr : [total_tokens, Hq, D]
  *   k, v, dk, dv         : [total_tokens, Hkv, D]
  *   lse, sbar            : NULL (forward only) or DEVICE float [total_tokens, Hq]
+ *   vbar                 : NULL or DEVICE [total_tokens, Hq, D], as in the dense calls
  *   cu_seqlens : DEVICE int32 [B + 1], non-decreasing from 0 to total_tokens;
  *                sequence b owns tokens cu[b] .. cu[b+1] - 1. Read on the device
  *                only, so not validated: lengths must not exceed max_len.
@@ -228,15 +234,16 @@ int parallax_prefill_backward(const void *q, const void *r, const void *k, const
 size_t parallax_prefill_varlen_workspace_bytes(int Hq, int total_tokens, int backward);
 
 int parallax_prefill_varlen(const void *q, const void *r, const void *k, const void *v, void *o,
-                            float *lse, float *sbar, const int32_t *cu_seqlens, int B, int Hq,
-                            int Hkv, int max_len, int total_tokens, int D, int window,
+                            float *lse, float *sbar, void *vbar, const int32_t *cu_seqlens, int B,
+                            int Hq, int Hkv, int max_len, int total_tokens, int D, int window,
                             float qk_scale, float rk_scale, int dtype, void *workspace,
                             size_t workspace_bytes, void *stream);
 
 int parallax_prefill_varlen_backward(const void *q, const void *r, const void *k, const void *v,
                                      const void *o, const void *d_o, const float *lse,
-                                     const float *sbar, const int32_t *cu_seqlens, void *dq,
-                                     void *dr, void *dk, void *dv, int B, int Hq, int Hkv,
+                                     const float *sbar, const void *vbar,
+                                     const int32_t *cu_seqlens, void *dq, void *dr, void *dk,
+                                     void *dv, int B, int Hq, int Hkv,
                                      int max_len, int total_tokens, int D, int window,
                                      float qk_scale, float rk_scale, int dtype, void *workspace,
                                      size_t workspace_bytes, void *stream);

@@ -65,8 +65,7 @@ def lib() -> ctypes.CDLL:
         L.softmax_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32,
                                      i32, vp, sz, vp]
         L.softmax_decode.restype = i32
-        L.parallax_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
-                                       f32, f32, i32, vp]
+        L.parallax_prefill.argtypes = [vp] * 8 + [i32] * 6 + [f32, f32, i32, vp]
         L.parallax_prefill.restype = i32
         L.parallax_decode_record_bytes.argtypes = [i32, i32, i32, i32]
         L.parallax_decode_record_bytes.restype = sz
@@ -77,13 +76,13 @@ def lib() -> ctypes.CDLL:
         L.parallax_decode_merge.restype = i32
         L.parallax_prefill_backward_workspace_bytes.argtypes = [i32, i32, i32]
         L.parallax_prefill_backward_workspace_bytes.restype = sz
-        L.parallax_prefill_backward.argtypes = [vp] * 12 + [i32] * 6 + [f32, f32, i32, vp, sz, vp]
+        L.parallax_prefill_backward.argtypes = [vp] * 13 + [i32] * 6 + [f32, f32, i32, vp, sz, vp]
         L.parallax_prefill_backward.restype = i32
-        L.parallax_prefill_varlen.argtypes = [vp] * 8 + [i32] * 7 + [f32, f32, i32, vp, sz, vp]
+        L.parallax_prefill_varlen.argtypes = [vp] * 9 + [i32] * 7 + [f32, f32, i32, vp, sz, vp]
         L.parallax_prefill_varlen_workspace_bytes.argtypes = [i32, i32, i32]
         L.parallax_prefill_varlen_workspace_bytes.restype = sz
         L.parallax_prefill_varlen.restype = i32
-        L.parallax_prefill_varlen_backward.argtypes = [vp] * 13 + [i32] * 7 + [f32, f32, i32, vp,
+        L.parallax_prefill_varlen_backward.argtypes = [vp] * 14 + [i32] * 7 + [f32, f32, i32, vp,
                                                                               sz, vp]
         L.parallax_prefill_varlen_backward.restype = i32
         _lib = L
@@ -256,10 +255,12 @@ def decode_merge(records, dtype=torch.bfloat16, with_probe=True, out=None):
     return out
 
 
-def prefill(q, r, k, v, qk_scale=None, rk_scale=1.0, *, out=None, return_stats=False, window=0):
+def prefill(q, r, k, v, qk_scale=None, rk_scale=1.0, *, out=None, return_stats=False, window=0,
+            vbar_out=None):
     """Causal Parallax prefill. q, r: [B, Hq, L, D]; k, v: [B, Hkv, L, D] -> o [B, Hq, L, D]
     (plus fp32 lse and sbar [B, Hq, L] with return_stats=True). ``window`` > 0: query i
-    sees keys i - window + 1 .. i."""
+    sees keys i - window + 1 .. i. ``vbar_out``: optional tensor shaped like o that
+    receives the softmax readout (a backward statistic)."""
     L_ = lib()
     B, Hq, L, D = q.shape
     dev, dt = q.device, q.dtype
@@ -283,8 +284,12 @@ def prefill(q, r, k, v, qk_scale=None, rk_scale=1.0, *, out=None, return_stats=F
     if return_stats:
         lse = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
         sbar = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
+    if vbar_out is not None:
+        _check(vbar_out, "vbar_out", dt, dev)
+        if vbar_out.shape != q.shape:
+            raise ValueError("vbar_out must have q's shape")
     st = L_.parallax_prefill(_ptr(q), _ptr(r), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(sbar),
-                             B, Hq, Hkv, L, D, int(window), float(qk_scale), float(rk_scale), code,
+                             _ptr(vbar_out), B, Hq, Hkv, L, D, int(window), float(qk_scale), float(rk_scale), code,
                              _stream_handle(dev))
     if st != 0:
         raise ParallaxError(st, "parallax_prefill")
@@ -292,7 +297,7 @@ def prefill(q, r, k, v, qk_scale=None, rk_scale=1.0, *, out=None, return_stats=F
 
 
 def prefill_backward(q, r, k, v, o, d_o, lse, sbar, qk_scale=None, rk_scale=1.0, *,
-                     workspace=None, out=None, window=0):
+                     workspace=None, out=None, window=0, vbar=None):
     """Gradients of the causal prefill: (dq, dr, dk, dv) for the upstream
     gradient ``d_o``, from the forward's o, lse and sbar (prefill with
     return_stats=True on the same inputs and scales). ``out``: optional
@@ -323,8 +328,13 @@ def prefill_backward(q, r, k, v, o, d_o, lse, sbar, qk_scale=None, rk_scale=1.0,
         _check(t, name, dt, dev)
         if t.shape != ref.shape:
             raise ValueError(f"{name} must have shape {tuple(ref.shape)}")
+    if vbar is not None:
+        _check(vbar, "vbar", dt, dev)
+        if vbar.shape != q.shape:
+            raise ValueError("vbar must have q's shape")
     st = L_.parallax_prefill_backward(
-        _ptr(q), _ptr(r), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse), _ptr(sbar), _ptr(dq),
+        _ptr(q), _ptr(r), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse), _ptr(sbar), _ptr(vbar),
+        _ptr(dq),
         _ptr(dr), _ptr(dk), _ptr(dv), B, Hq, Hkv, L, D, int(window), float(qk_scale),
         float(rk_scale),
         _dtype_code(q), _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -336,26 +346,30 @@ def prefill_backward(q, r, k, v, o, d_o, lse, sbar, qk_scale=None, rk_scale=1.0,
 
 class _ParallaxFunction(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, r, k, v, qk_scale, rk_scale, window):
-        o, lse, sbar = prefill(q, r, k, v, qk_scale, rk_scale, return_stats=True, window=window)
-        ctx.save_for_backward(q, r, k, v, o, lse, sbar)
+    def forward(ctx, q, r, k, v, qk_scale, rk_scale, window, save_vbar):
+        vbar = torch.empty_like(q) if save_vbar else None
+        o, lse, sbar = prefill(q, r, k, v, qk_scale, rk_scale, return_stats=True, window=window,
+                               vbar_out=vbar)
+        ctx.save_for_backward(q, r, k, v, o, lse, sbar, vbar)
         ctx.scales = (qk_scale, rk_scale)
         ctx.window = window
         return o
 
     @staticmethod
     def backward(ctx, d_o):
-        q, r, k, v, o, lse, sbar = ctx.saved_tensors
+        q, r, k, v, o, lse, sbar, vbar = ctx.saved_tensors
         grads = prefill_backward(q, r, k, v, o, d_o.contiguous(), lse, sbar, *ctx.scales,
-                                 window=ctx.window)
-        return (*grads, None, None, None)
+                                 window=ctx.window, vbar=vbar)
+        return (*grads, None, None, None, None)
 
 
-def parallax_func(q, r, k, v, qk_scale=None, rk_scale=1.0, *, window=0):
+def parallax_func(q, r, k, v, qk_scale=None, rk_scale=1.0, *, window=0, save_vbar=True):
     """Causal Parallax attention on [B, H, L, D] tensors, differentiable in
-    q, r, k and v (the pages' training entry point); ``window`` as in prefill."""
+    q, r, k and v (the pages' training entry point); ``window`` as in prefill.
+    ``save_vbar`` keeps the softmax readout for the backward (one more o-sized
+    activation, one sweep over the keys fewer in the backward)."""
     if torch.is_grad_enabled() and any(t.requires_grad for t in (q, r, k, v)):
-        return _ParallaxFunction.apply(q, r, k, v, qk_scale, rk_scale, window)
+        return _ParallaxFunction.apply(q, r, k, v, qk_scale, rk_scale, window, save_vbar)
     return prefill(q, r, k, v, qk_scale, rk_scale, window=window)
 
 
@@ -371,7 +385,7 @@ def _varlen_shapes(q, k, cu_seqlens, max_len):
 
 
 def prefill_varlen(q, r, k, v, cu_seqlens, max_len=None, qk_scale=None, rk_scale=1.0, *,
-                   out=None, return_stats=False, window=0, workspace=None):
+                   out=None, return_stats=False, window=0, workspace=None, vbar_out=None):
     """Causal prefill of packed sequences: q, r [T, Hq, D]; k, v [T, Hkv, D]; int32
     ``cu_seqlens`` [B + 1]. Returns o [T, Hq, D] (plus fp32 lse, sbar [T, Hq])."""
     L_ = lib()
@@ -393,8 +407,12 @@ def prefill_varlen(q, r, k, v, cu_seqlens, max_len=None, qk_scale=None, rk_scale
     if workspace is None:
         need = int(L_.parallax_prefill_varlen_workspace_bytes(Hq, T, 0))
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if vbar_out is not None:
+        _check(vbar_out, "vbar_out", dt, dev)
+        if vbar_out.shape != q.shape:
+            raise ValueError("vbar_out must have q's shape")
     st = L_.parallax_prefill_varlen(_ptr(q), _ptr(r), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
-                                    _ptr(sbar), _ptr(cu_seqlens), B, Hq, Hkv, max_len, T, D,
+                                    _ptr(sbar), _ptr(vbar_out), _ptr(cu_seqlens), B, Hq, Hkv, max_len, T, D,
                                     int(window), float(qk_scale), float(rk_scale), _dtype_code(q),
                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
                                     _stream_handle(dev))
@@ -404,7 +422,8 @@ def prefill_varlen(q, r, k, v, cu_seqlens, max_len=None, qk_scale=None, rk_scale
 
 
 def prefill_varlen_backward(q, r, k, v, o, d_o, lse, sbar, cu_seqlens, max_len=None,
-                            qk_scale=None, rk_scale=1.0, *, window=0, workspace=None, out=None):
+                            qk_scale=None, rk_scale=1.0, *, window=0, workspace=None, out=None,
+                            vbar=None):
     """Gradients (dq, dr, dk, dv) of prefill_varlen from its o, lse and sbar."""
     L_ = lib()
     dev, dt = q.device, q.dtype
@@ -424,8 +443,12 @@ def prefill_varlen_backward(q, r, k, v, o, d_o, lse, sbar, cu_seqlens, max_len=N
     if out is None:
         out = (torch.empty_like(q), torch.empty_like(r), torch.empty_like(k), torch.empty_like(v))
     dq, dr, dk, dv = out
+    if vbar is not None:
+        _check(vbar, "vbar", dt, dev)
+        if vbar.shape != q.shape:
+            raise ValueError("vbar must have q's shape")
     st = L_.parallax_prefill_varlen_backward(
-        _ptr(q), _ptr(r), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse), _ptr(sbar),
+        _ptr(q), _ptr(r), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse), _ptr(sbar), _ptr(vbar),
         _ptr(cu_seqlens), _ptr(dq), _ptr(dr), _ptr(dk), _ptr(dv), B, Hq, Hkv, max_len, T, D,
         int(window), float(qk_scale), float(rk_scale), _dtype_code(q), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream_handle(dev))
@@ -436,31 +459,32 @@ def prefill_varlen_backward(q, r, k, v, o, d_o, lse, sbar, cu_seqlens, max_len=N
 
 class _ParallaxVarlenFunction(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, r, k, v, cu_seqlens, max_len, qk_scale, rk_scale, window):
+    def forward(ctx, q, r, k, v, cu_seqlens, max_len, qk_scale, rk_scale, window, save_vbar):
+        vbar = torch.empty_like(q) if save_vbar else None
         o, lse, sbar = prefill_varlen(q, r, k, v, cu_seqlens, max_len, qk_scale, rk_scale,
-                                      return_stats=True, window=window)
-        ctx.save_for_backward(q, r, k, v, o, lse, sbar, cu_seqlens)
+                                      return_stats=True, window=window, vbar_out=vbar)
+        ctx.save_for_backward(q, r, k, v, o, lse, sbar, cu_seqlens, vbar)
         ctx.args = (max_len, qk_scale, rk_scale, window)
         return o
 
     @staticmethod
     def backward(ctx, d_o):
-        q, r, k, v, o, lse, sbar, cu = ctx.saved_tensors
+        q, r, k, v, o, lse, sbar, cu, vbar = ctx.saved_tensors
         max_len, qk_scale, rk_scale, window = ctx.args
         grads = prefill_varlen_backward(q, r, k, v, o, d_o.contiguous(), lse, sbar, cu, max_len,
-                                        qk_scale, rk_scale, window=window)
-        return (*grads, None, None, None, None, None)
+                                        qk_scale, rk_scale, window=window, vbar=vbar)
+        return (*grads, None, None, None, None, None, None)
 
 
 def parallax_varlen_func(q, r, k, v, cu_seqlens, max_len=None, qk_scale=None, rk_scale=1.0, *,
-                         window=0):
+                         window=0, save_vbar=True):
     """Differentiable causal Parallax attention on packed sequences (the pages'
     parallax_varlen_func): q, r [T, Hq, D]; k, v [T, Hkv, D]; int32 cu_seqlens [B + 1]."""
     if max_len is None:
         max_len = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item())
     if torch.is_grad_enabled() and any(t.requires_grad for t in (q, r, k, v)):
         return _ParallaxVarlenFunction.apply(q, r, k, v, cu_seqlens, max_len, qk_scale, rk_scale,
-                                             window)
+                                             window, save_vbar)
     return prefill_varlen(q, r, k, v, cu_seqlens, max_len, qk_scale, rk_scale, window=window)
 
 

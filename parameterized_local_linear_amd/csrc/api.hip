@@ -261,7 +261,7 @@ static int check_prefill(Args &a, const int32_t *cu, int B, int Hq, int Hkv, int
 }
 
 static int prefill_common(const void *q, const void *r, const void *k, const void *v, void *o, float *lse,
-                          float *sbar, const int32_t *cu, int B, int Hq, int Hkv, int L, int total, int D,
+                          float *sbar, void *vbar, const int32_t *cu, int B, int Hq, int Hkv, int L, int total, int D,
                           int window, float qk_scale, float rk_scale, int dtype, void *ws, size_t ws_bytes,
                           void *stream) {
     if (!q || !r || !k || !v || !o) return PLX_ERR_INVALID_ARG;
@@ -278,12 +278,14 @@ static int prefill_common(const void *q, const void *r, const void *k, const voi
     a.o = o;
     a.lse = lse;
     a.sbar = sbar;
+    a.vbar = vbar;
     hipError_t err = plx::launch_prefill(a, dtype, reinterpret_cast<hipStream_t>(stream));
     return err == hipSuccess ? PLX_OK : PLX_ERR_HIP;
 }
 
 static int backward_common(const void *q, const void *r, const void *k, const void *v, const void *o,
-                           const void *d_o, const float *lse, const float *sbar, const int32_t *cu,
+                           const void *d_o, const float *lse, const float *sbar, const void *vbar,
+                           const int32_t *cu,
                            void *dq, void *dr, void *dk, void *dv, int B, int Hq, int Hkv, int L,
                            int total, int D, int window, float qk_scale, float rk_scale, int dtype,
                            void *workspace, size_t workspace_bytes, void *stream) {
@@ -308,6 +310,7 @@ static int backward_common(const void *q, const void *r, const void *k, const vo
     a.go = d_o;
     a.lse = lse;
     a.sbar = sbar;
+    a.vbar = vbar;
     a.dq = dq;
     a.dr = dr;
     a.dk = dk;
@@ -322,9 +325,9 @@ static int backward_common(const void *q, const void *r, const void *k, const vo
 extern "C" {
 
 int parallax_prefill(const void *q, const void *r, const void *k, const void *v, void *o, float *lse,
-                     float *sbar, int B, int Hq, int Hkv, int L, int D, int window, float qk_scale,
-                     float rk_scale, int dtype, void *stream) {
-    return prefill_common(q, r, k, v, o, lse, sbar, nullptr, B, Hq, Hkv, L, 0, D, window, qk_scale,
+                     float *sbar, void *vbar, int B, int Hq, int Hkv, int L, int D, int window,
+                     float qk_scale, float rk_scale, int dtype, void *stream) {
+    return prefill_common(q, r, k, v, o, lse, sbar, vbar, nullptr, B, Hq, Hkv, L, 0, D, window, qk_scale,
                           rk_scale, dtype, nullptr, 0, stream);
 }
 
@@ -334,12 +337,12 @@ size_t parallax_prefill_varlen_workspace_bytes(int Hq, int total_tokens, int bac
 }
 
 int parallax_prefill_varlen(const void *q, const void *r, const void *k, const void *v, void *o,
-                            float *lse, float *sbar, const int32_t *cu_seqlens, int B, int Hq, int Hkv,
+                            float *lse, float *sbar, void *vbar, const int32_t *cu_seqlens, int B, int Hq, int Hkv,
                             int max_len, int total_tokens, int D, int window, float qk_scale,
                             float rk_scale, int dtype, void *workspace, size_t workspace_bytes,
                             void *stream) {
     if (!cu_seqlens) return PLX_ERR_INVALID_ARG;
-    return prefill_common(q, r, k, v, o, lse, sbar, cu_seqlens, B, Hq, Hkv, max_len, total_tokens, D,
+    return prefill_common(q, r, k, v, o, lse, sbar, vbar, cu_seqlens, B, Hq, Hkv, max_len, total_tokens, D,
                           window, qk_scale, rk_scale, dtype, workspace, workspace_bytes, stream);
 }
 
@@ -349,22 +352,23 @@ size_t parallax_prefill_backward_workspace_bytes(int B, int Hq, int L) {
 }
 
 int parallax_prefill_backward(const void *q, const void *r, const void *k, const void *v, const void *o,
-                              const void *d_o, const float *lse, const float *sbar, void *dq, void *dr,
+                              const void *d_o, const float *lse, const float *sbar, const void *vbar,
+                              void *dq, void *dr,
                               void *dk, void *dv, int B, int Hq, int Hkv, int L, int D, int window,
                               float qk_scale, float rk_scale, int dtype, void *workspace,
                               size_t workspace_bytes, void *stream) {
-    return backward_common(q, r, k, v, o, d_o, lse, sbar, nullptr, dq, dr, dk, dv, B, Hq, Hkv, L, 0, D,
+    return backward_common(q, r, k, v, o, d_o, lse, sbar, vbar, nullptr, dq, dr, dk, dv, B, Hq, Hkv, L, 0, D,
                            window, qk_scale, rk_scale, dtype, workspace, workspace_bytes, stream);
 }
 
 int parallax_prefill_varlen_backward(const void *q, const void *r, const void *k, const void *v,
                                      const void *o, const void *d_o, const float *lse, const float *sbar,
-                                     const int32_t *cu_seqlens, void *dq, void *dr, void *dk, void *dv,
+                                     const void *vbar, const int32_t *cu_seqlens, void *dq, void *dr, void *dk, void *dv,
                                      int B, int Hq, int Hkv, int max_len, int total_tokens, int D,
                                      int window, float qk_scale, float rk_scale, int dtype,
                                      void *workspace, size_t workspace_bytes, void *stream) {
     if (!cu_seqlens) return PLX_ERR_INVALID_ARG;
-    return backward_common(q, r, k, v, o, d_o, lse, sbar, cu_seqlens, dq, dr, dk, dv, B, Hq, Hkv, max_len,
+    return backward_common(q, r, k, v, o, d_o, lse, sbar, vbar, cu_seqlens, dq, dr, dk, dv, B, Hq, Hkv, max_len,
                            total_tokens, D, window, qk_scale, rk_scale, dtype, workspace,
                            workspace_bytes, stream);
 }

@@ -117,9 +117,16 @@ __global__ __launch_bounds__(64) void bwd_rows_generic(BackwardArgs a) {
     const int end = i + 1;
     const int first = max(0, i - a.window + 1);  // sliding window: keys first .. i
 
-    // sweep 1: ubar = sum_j w_j g.v_j
+    // sweep 1: ubar = sum_j w_j g.v_j, or g . vbar from the forward's softmax readout
     float ub = 0.f;
-    for (int j0 = first; j0 < end; j0 += KPI) {
+    if (a.vbar) {
+        float vv[EPL];
+        Frag<T>::load(reinterpret_cast<const T *>(a.vbar) + row + c * EPL, vv);
+        float vp = 0.f;
+        for (int e = 0; e < EPL; ++e) vp += vv[e] * gv[e];
+        ub = row_sum<LPR>(vp);
+    }
+    for (int j0 = first; j0 < end && !a.vbar; j0 += KPI) {
         const int j = j0 + kgrp;
         const int jj = j < end ? j : end - 1;
         float kv[EPL], vv[EPL];
@@ -134,7 +141,7 @@ __global__ __launch_bounds__(64) void bwd_rows_generic(BackwardArgs a) {
         up = row_sum<LPR>(up);
         if (j < end) ub += __builtin_amdgcn_exp2f(fmaf(zp, a.zscale, -lse2)) * up;
     }
-    ub = across_rows<LPR>(ub);
+    if (!a.vbar) ub = across_rows<LPR>(ub);
 
     // sweep 2: dq, dr
     float dqa[EPL], dra[EPL];
@@ -360,7 +367,7 @@ __device__ __forceinline__ void bwd_rows_item(const BackwardArgs &a, const int i
         dma_rows<TK, NW>(krs, tile * TK, ks, lk, wave, lane);
         dma_rows<TK, NW>(vrs, tile * TK, ks, lv, wave, lane);
     };
-    dma_tile(tile0, lds_k0, lds_v0);
+    dma_tile(tile0, lds_k0, lds_v0);  // the first sweep's first tile
 
     // per-wave B operands (query row n, k step u -> chunk g + 4u) and row scalars
     const int64_t qbase = row0_elem(sq, b, hq, a.Hq, a.L, D);
@@ -370,24 +377,30 @@ __device__ __forceinline__ void bwd_rows_item(const BackwardArgs &a, const int i
     const int row = q0 + n;
     const int rowc = min(row, L - 1);
     bf16x8 qop[4], rop[4], gop[4];
-    float delta;
+    float delta, ubar_fwd;
     {
         const int64_t ro = qbase + (int64_t)rowc * qs;
         const uint16_t *qp = reinterpret_cast<const uint16_t *>(a.q) + ro;
         const uint16_t *rp = reinterpret_cast<const uint16_t *>(a.r) + ro;
         const uint16_t *gp = reinterpret_cast<const uint16_t *>(a.go) + ro;
         const uint16_t *op = reinterpret_cast<const uint16_t *>(a.o) + ro;
-        float part = 0.f;
+        const uint16_t *vp = reinterpret_cast<const uint16_t *>(a.vbar ? a.vbar : a.o) + ro;
+        float part = 0.f, vpart = 0.f;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             qop[u] = load16(qp + 8 * (g + 4 * u));
             rop[u] = load16(rp + 8 * (g + 4 * u));
             gop[u] = load16(gp + 8 * (g + 4 * u));
             const bf16x8 ov = load16(op + 8 * (g + 4 * u));
+            const bf16x8 vv = load16(vp + 8 * (g + 4 * u));
 #pragma unroll
-            for (int e = 0; e < 8; ++e) part += (float)ov[e] * (float)gop[u][e];
+            for (int e = 0; e < 8; ++e) {
+                part += (float)ov[e] * (float)gop[u][e];
+                vpart += (float)vv[e] * (float)gop[u][e];
+            }
         }
         delta = xor_sum_rowgroups(part);
+        ubar_fwd = xor_sum_rowgroups(vpart);  // g . vbar, used when the forward stored vbar
     }
     const float lse2 = a.lse[sbase + (int64_t)rowc * ss] * kLog2e;
     const float sb = a.sbar[sbase + (int64_t)rowc * ss];
@@ -435,8 +448,9 @@ __device__ __forceinline__ void bwd_rows_item(const BackwardArgs &a, const int i
         }
     };
 
-    // ---- sweep 1: ubar
+    // ---- sweep 1: ubar = sum_j w_j g.v_j (skipped when the forward stored vbar)
     float ub_part = 0.f;
+    if (!a.vbar)
     sweep([&](const uint16_t *lk, const uint16_t *lv, int kl, int key0, bool diag) __attribute__((always_inline)) {
         floatx4 z0, z1, u0, u1;
         contract(load_rows(lk, kl), qop, z0, z1);
@@ -451,13 +465,13 @@ __device__ __forceinline__ void bwd_rows_item(const BackwardArgs &a, const int i
             ub_part = fmaf(w, u, ub_part);
         }
     });
-    const float ubar = xor_sum_rowgroups(ub_part);
+    const float ubar = a.vbar ? ubar_fwd : xor_sum_rowgroups(ub_part);
 
     // ---- sweep 2: dq, dr
     floatx4 accQ[8], accR[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) accQ[e] = accR[e] = floatx4{0.f, 0.f, 0.f, 0.f};
-    dma_tile(tile0, lds_k0, lds_v0);
+    if (!a.vbar) dma_tile(tile0, lds_k0, lds_v0);  // sweep 1 consumed the first copy
     sweep([&](const uint16_t *lk, const uint16_t *lv, int kl, int key0, bool diag) __attribute__((always_inline)) {
         floatx4 z0, z1, s0, s1, u0, u1;
         {

@@ -61,6 +61,7 @@ struct PrefillArgs {
     const void *q, *r, *k, *v;
     void *o;
     float *lse, *sbar;
+    void *vbar;         // nullptr, or the softmax readout sum_j w_j v_j (layout and dtype of o)
     const int32_t *cu;  // nullptr: dense [B, H, L, D]; else packed [T, H, D], cu [B + 1]
     int *sched;         // nullptr: one work item per workgroup; else 8 zeroed queue counters
     int workers;        // workgroups of a persistent launch (when sched != nullptr)
@@ -82,6 +83,8 @@ struct RowStat {
 struct BackwardArgs {
     const void *q, *r, *k, *v, *o, *go;  // go: dLoss/do, layout of o
     const float *lse, *sbar;             // the forward's row statistics
+    const void *vbar;                    // nullptr, or the forward's softmax readout (then
+                                         // ubar = dLoss/do . vbar needs no sweep of the keys)
     void *dq, *dr, *dk, *dv;
     RowStat *rowstat;                    // workspace: [B, Hq, L] dense, [Hq, T] packed
     const int32_t *cu;                   // as in PrefillArgs

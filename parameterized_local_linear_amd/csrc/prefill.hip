@@ -148,6 +148,10 @@ __global__ __launch_bounds__(64) void prefill_generic(PrefillArgs a) {
     float ov[EPL];
     for (int e = 0; e < EPL; ++e) ov[e] = (A[e] * cA + Bv[e]) * inv_l;
     Vec16<T>::store(reinterpret_cast<T *>(a.o) + row + c * EPL, ov);
+    if (a.vbar) {
+        for (int e = 0; e < EPL; ++e) ov[e] = A[e] * inv_l;
+        Vec16<T>::store(reinterpret_cast<T *>(a.vbar) + row + c * EPL, ov);
+    }
     if (c == 0) {
         if (a.lse) a.lse[srow] = m * 0.6931471805599453f + logf(l);
         if (a.sbar) a.sbar[srow] = S * inv_l + piv;
@@ -465,6 +469,13 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs &a, const int ite
 #pragma unroll
             for (int i = 0; i < 4; ++i) ov[i] = (accA[b][i] * cA + accB[b][i]) * inv_l;
             *reinterpret_cast<uint2 *>(o + 16 * b) = uint2{pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3])};
+        }
+        if (a.vbar) {  // the softmax readout A / l, for a backward pass
+            uint16_t *vb = reinterpret_cast<uint16_t *>(a.vbar) + qbase + (int64_t)row * qs + 4 * g;
+#pragma unroll
+            for (int b = 0; b < 8; ++b)
+                *reinterpret_cast<uint2 *>(vb + 16 * b) = uint2{pack_bf16x2(accA[b][0] * inv_l, accA[b][1] * inv_l),
+                                                                pack_bf16x2(accA[b][2] * inv_l, accA[b][3] * inv_l)};
         }
         if (g == 0) {
             if (a.lse) a.lse[ro] = m_run * 0.6931471805599453f + logf(l);

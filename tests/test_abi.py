@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = plx.lib()
-    assert L.parallax_abi_version() == 2
+    assert L.parallax_abi_version() == 3
     for s in range(5):
         assert L.parallax_status_string(s).decode() == plx.STATUS[s]
     assert L.parallax_status_string(99) == b"unknown status"
@@ -71,7 +71,7 @@ def test_softmax_decode_and_prefill_reject_on_host():
                             None) == 2
     assert L.softmax_decode(FAKE, FAKE, FAKE, FAKE, None, 1, 4, 2, 128, 10, -3, 0.1, 1, 0, None, 0,
                             None) == 1
-    args = [FAKE] * 5 + [None, None]
+    args = [FAKE] * 5 + [None, None, None]
     assert L.parallax_prefill(*args, 1, 4, 2, 0, 128, 0, 0.1, 1.0, 1, None) == 1
     assert L.parallax_prefill(*args, 1, 4, 3, 16, 128, 0, 0.1, 1.0, 1, None) == 1
     assert L.parallax_prefill(*args, 1, 4, 2, 16, 72, 0, 0.1, 1.0, 1, None) == 2
@@ -111,12 +111,13 @@ def test_workspace_plan():
 
 
 def _backward(**kw):
-    a = dict(q=FAKE, r=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, sbar=FAKE, dq=FAKE,
+    a = dict(q=FAKE, r=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, sbar=FAKE, vbar=None, dq=FAKE,
              dr=FAKE, dk=FAKE, dv=FAKE, B=1, Hq=4, Hkv=2, L=64, D=128, W=0, qk=0.1, rk=1.0,
              dt=1, ws=None, wsb=0, stream=None)
     a.update(kw)
     return plx.lib().parallax_prefill_backward(
-        a["q"], a["r"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["sbar"], a["dq"], a["dr"],
+        a["q"], a["r"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["sbar"], a["vbar"], a["dq"],
+        a["dr"],
         a["dk"], a["dv"], a["B"], a["Hq"], a["Hkv"], a["L"], a["D"], a["W"], a["qk"], a["rk"],
         a["dt"], a["ws"], a["wsb"], a["stream"])
 
@@ -142,7 +143,7 @@ def test_prefill_backward_workspace_size():
 
 def test_varlen_prefill_rejects_on_host():
     L = plx.lib()
-    p8 = [FAKE] * 5 + [None, None]
+    p8 = [FAKE] * 5 + [None, None, None]
     # cu_seqlens missing, negative total, too long a packed head, empty batch is a no-op
     ws = (FAKE, 256)
     assert L.parallax_prefill_varlen(*p8, None, 2, 4, 2, 64, 100, 128, 0, 0.1, 1.0, 1, *ws,
@@ -157,7 +158,7 @@ def test_varlen_prefill_rejects_on_host():
                                      None) == 0
     assert L.parallax_prefill_varlen_workspace_bytes(4, 100, 0) == 256
     assert L.parallax_prefill_varlen_workspace_bytes(4, 100, 1) == 256 + 4 * 100 * 16
-    b13 = [FAKE] * 8 + [FAKE] + [FAKE] * 4
+    b13 = [FAKE] * 8 + [None] + [FAKE] + [FAKE] * 4
     assert L.parallax_prefill_varlen_backward(*b13, 2, 4, 2, 64, 100, 128, 0, 0.1, 1.0, 1, None,
                                               0, None) == 3
     assert L.parallax_prefill_varlen_backward(*b13, 2, 4, 2, 64, 100, 128, 0, 0.1, 1.0, 1, FAKE,

@@ -35,10 +35,11 @@ def inputs(B, Hq, Hkv, L, D, dtype, scale, seed):
     return q, r, k, v, do
 
 
-def gpu_backward(host, dtype, qk_scale=None, rk_scale=1.0, keep_on_gpu=False):
+def gpu_backward(host, dtype, qk_scale=None, rk_scale=1.0, keep_on_gpu=False, use_vbar=False):
     q, r, k, v, do = (to_gpu(x, dtype) for x in host)
-    o, lse, sbar = plx.prefill(q, r, k, v, qk_scale, rk_scale, return_stats=True)
-    grads = plx.prefill_backward(q, r, k, v, o, do, lse, sbar, qk_scale, rk_scale)
+    vbar = torch.empty_like(q) if use_vbar else None
+    o, lse, sbar = plx.prefill(q, r, k, v, qk_scale, rk_scale, return_stats=True, vbar_out=vbar)
+    grads = plx.prefill_backward(q, r, k, v, o, do, lse, sbar, qk_scale, rk_scale, vbar=vbar)
     return grads if keep_on_gpu else [from_gpu(g) for g in grads]
 
 
@@ -64,6 +65,22 @@ def test_backward_small(dtype, D, L):
     got = gpu_backward(host, dtype)
     ref = oracle.prefill_backward(*host)
     check(got, ref, dtype, f"L={L} D={D}")
+
+
+@pytest.mark.parametrize("dtype,D", [(synth.BF16, 128), (synth.F32, 64), (synth.BF16, 64)])
+@pytest.mark.parametrize("L", [1, 130, 257])
+def test_backward_with_stored_vbar(dtype, D, L):
+    # the forward's softmax readout replaces the backward's first sweep over the keys
+    host = inputs(2, 4, 2, L, D, dtype, S128 if D == 128 else 1.0, 240 + L)
+    q, r, k, v, do = (to_gpu(x, dtype) for x in host)
+    vbar = torch.empty_like(q)
+    plx.prefill(q, r, k, v, vbar_out=vbar)
+    # vbar is the softmax readout: the oracle at r = 0
+    tol = 1e-5 if dtype == synth.F32 else 1e-2
+    ref_vbar = oracle.prefill(*host[:1], None, *host[2:4])
+    assert np.abs(from_gpu(vbar) - ref_vbar).max() <= tol * np.abs(ref_vbar).max()
+    check(gpu_backward(host, dtype, use_vbar=True), oracle.prefill_backward(*host), dtype,
+          f"vbar L={L} D={D}")
 
 
 @pytest.mark.parametrize("Hq,Hkv", [(2, 2), (3, 1), (8, 2), (4, 1)])
@@ -103,9 +120,10 @@ def test_backward_r_zero_is_softmax_attention_gradient():
 def test_backward_deterministic_and_autograd_entry_point():
     host = inputs(2, 4, 2, 150, 128, synth.BF16, S128, 180)
     q, r, k, v, do = (to_gpu(x, synth.BF16) for x in host)
-    o, lse, sbar = plx.prefill(q, r, k, v, return_stats=True)
-    g1 = plx.prefill_backward(q, r, k, v, o, do, lse, sbar)
-    g2 = plx.prefill_backward(q, r, k, v, o, do, lse, sbar)
+    vbar = torch.empty_like(q)
+    o, lse, sbar = plx.prefill(q, r, k, v, return_stats=True, vbar_out=vbar)
+    g1 = plx.prefill_backward(q, r, k, v, o, do, lse, sbar, vbar=vbar)
+    g2 = plx.prefill_backward(q, r, k, v, o, do, lse, sbar, vbar=vbar)
     for a, b in zip(g1, g2):
         assert torch.equal(a, b)
     leaves = [t.clone().requires_grad_(True) for t in (q, r, k, v)]
@@ -134,7 +152,7 @@ def test_backward_full_size_units():
     spec = synth.prefill_spec(5)
     B, Hq, Hkv, L, D = spec.B, spec.Hq, spec.Hkv, spec.L, spec.D
     host = inputs(B, Hq, Hkv, L, D, synth.BF16, spec.scale, spec.seed)
-    got = gpu_backward(host, synth.BF16, keep_on_gpu=True)
+    got = gpu_backward(host, synth.BF16, keep_on_gpu=True, use_vbar=True)
     G = Hq // Hkv
     units = np.array([[0, 0], [B - 1, Hkv - 1]])
     ref = oracle.prefill_backward(*host, units=units)

@@ -52,6 +52,11 @@ def test_varlen_forward_and_backward(dtype, D, W):
     got = plx.prefill_varlen_backward(*t[:4], o, t[4], lse, sbar, cu_t, window=W)
     ref_g = oracle.prefill_varlen_backward(*host, cu, window=W)
     check_grads([from_gpu(g) for g in got], ref_g, dtype, f"varlen W={W}")
+    # and with the forward's softmax readout in place of the first sweep
+    vbar = torch.empty_like(t[0])
+    plx.prefill_varlen(*t[:4], cu_t, window=W, vbar_out=vbar)
+    got = plx.prefill_varlen_backward(*t[:4], o, t[4], lse, sbar, cu_t, window=W, vbar=vbar)
+    check_grads([from_gpu(g) for g in got], ref_g, dtype, f"varlen vbar W={W}")
 
 
 @pytest.mark.parametrize("Hq,Hkv", [(2, 2), (8, 2), (3, 1)])
@@ -80,8 +85,9 @@ def test_varlen_matches_dense_batch_and_autograd_entry_point():
     leaves = [x.clone().requires_grad_(True) for x in t[:4]]
     out = plx.parallax_varlen_func(*leaves, cu_t)
     out.backward(t[4])
-    o, lse, sbar = plx.prefill_varlen(*t[:4], cu_t, return_stats=True)
-    ref = plx.prefill_varlen_backward(*t[:4], o, t[4], lse, sbar, cu_t)
+    vbar = torch.empty_like(t[0])
+    o, lse, sbar = plx.prefill_varlen(*t[:4], cu_t, return_stats=True, vbar_out=vbar)
+    ref = plx.prefill_varlen_backward(*t[:4], o, t[4], lse, sbar, cu_t, vbar=vbar)
     for leaf, g in zip(leaves, ref):
         assert torch.equal(leaf.grad, g)
 

@@ -89,8 +89,10 @@ def test_decode_window_packed_varlen(splits):
 def test_backward_window(dtype, D, L, W):
     host = prefill_inputs(2, 4, 2, L, D, dtype, S128 if D == 128 else 1.0, 350 + L + W, True)
     t = [to_gpu(x, dtype) for x in host]
-    o, lse, sbar = plx.prefill(*t[:4], return_stats=True, window=W)
-    got = [from_gpu(g) for g in plx.prefill_backward(*t[:4], o, t[4], lse, sbar, window=W)]
+    vbar = torch.empty_like(t[0]) if L != 257 else None  # both backward variants
+    o, lse, sbar = plx.prefill(*t[:4], return_stats=True, window=W, vbar_out=vbar)
+    got = [from_gpu(g) for g in plx.prefill_backward(*t[:4], o, t[4], lse, sbar, window=W,
+                                                      vbar=vbar)]
     ref = oracle.prefill_backward(*host, window=W)
     largest = max(np.abs(b).max() for b in ref)
     for name, a, b in zip(("dq", "dr", "dk", "dv"), got, ref):
