@@ -88,10 +88,16 @@ const char *parallax_status_string(int status);
  *   num_splits : 0 lets the library choose how many key ranges (splits)
  *             each sequence is cut into; >= 1 forces that many. With more
  *             than one split the per-split streaming states are written
- *             to the workspace and merged by a second kernel.
+ *             to the workspace and merged by a second kernel. A packed
+ *             cache (cu_seqlens_k != NULL) with num_splits == 0, no window
+ *             and the matrix-core path (bf16, D == 128, Hq / Hkv in
+ *             {1, 2, 4, 8}) is instead cut into equal token ranges per KV
+ *             head across all sequences (one range per workgroup), which
+ *             balances a mix of lengths.
  *   workspace, workspace_bytes : device scratch of at least
  *             parallax_decode_workspace_bytes(...) bytes for the same
- *             arguments (may be NULL when that size is 0).
+ *             arguments (may be NULL when that size is 0). The size covers
+ *             either plan, dense or packed.
  * Returns PLX_OK or an error status.
  * ---------------------------------------------------------------------- */
 size_t parallax_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int kv_len, int window,
@@ -118,9 +124,10 @@ int parallax_decode_num_splits(int B, int Hq, int Hkv, int D, int kv_len, int wi
 
 /* ------------------------------------------------------------------------
  * Decode in two halves: the streaming kernel that writes one record per
- * (sequence, query head, split), and the merge of records into o.
- * parallax_decode is exactly partial + merge (or one fused kernel when the
- * plan has a single split). Exposed so that records can be produced where
+ * (sequence, query head, split), and the merge of records into o. For the
+ * per-sequence split plan parallax_decode is exactly partial + merge (or one
+ * fused kernel when the plan has a single split); these two calls always use
+ * that plan, also for packed caches. Exposed so that records can be produced where
  * the keys live and merged elsewhere -- e.g. a long sequence whose key
  * range is cut across devices: each device streams its range, the records
  * are gathered, one merge produces o -- and so that each half can be timed.

@@ -105,10 +105,27 @@ const char *parallax_status_string(int status) {
     }
 }
 
+// Packed caches with an automatic plan and no window run the stream-K kernel:
+// each KV head's tokens in equal ranges, one workgroup per range and about
+// one workgroup per CU. Returns its range count, or 0 where it does not apply
+// (the per-sequence split plan then runs).
+static int streamk_parts(const DecodePlan &p, int Hkv, int window, int num_splits) {
+    if (p.path != plx::DecodePath::Mfma || window != 0 || num_splits != 0) return 0;
+    const int parts = plx::device_cu_count() / Hkv;
+    return parts < 1 ? 1 : (parts > 65535 ? 65535 : parts);
+}
+static size_t streamk_bytes(int B, int Hq, int D, int parts) {
+    return (size_t)Hq * ((size_t)parts + B - 1) * plx::partial_floats(D) * sizeof(float);
+}
+
 size_t parallax_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int kv_len, int window,
                                        int dtype, int num_splits) {
     if (check_decode_sizes(B, Hq, Hkv, D, kv_len, window, dtype) != PLX_OK) return 0;
-    return plx::plan_decode(B, Hq, Hkv, D, kv_len, window, dtype, num_splits).ws_bytes;
+    const DecodePlan p = plx::plan_decode(B, Hq, Hkv, D, kv_len, window, dtype, num_splits);
+    // the same size must also cover a packed cache's stream-K plan
+    const int parts = streamk_parts(p, Hkv, window, num_splits);
+    const size_t sk = parts ? streamk_bytes(B, Hq, D, parts) : 0;
+    return p.ws_bytes > sk ? p.ws_bytes : sk;
 }
 
 int parallax_decode_num_splits(int B, int Hq, int Hkv, int D, int kv_len, int window, int dtype,
@@ -144,6 +161,7 @@ static int fill_decode_args(plx::DecodeArgs &a, const void *q, const void *r, co
     a.rk_scale = rk_scale;
     a.splits = p.splits;
     a.chunk = p.chunk;
+    a.sk_parts = 0;
     a.ws = nullptr;
     a.fused = p.splits == 1;
     return PLX_OK;
@@ -158,6 +176,13 @@ static int decode_common(const void *q, const void *r, const void *k, const void
     int st = fill_decode_args(a, q, r, k, v, o, cu, B, Hq, Hkv, D, kv_len, window, qk_scale, rk_scale,
                               dtype, num_splits, parallax, p);
     if (st != PLX_OK) return st;
+    if (cu) {
+        a.sk_parts = streamk_parts(p, Hkv, window, num_splits);
+        if (a.sk_parts) {
+            a.fused = false;
+            p.ws_bytes = streamk_bytes(B, Hq, D, a.sk_parts);
+        }
+    }
     if (p.ws_bytes > 0 && (!ws || ws_bytes < p.ws_bytes)) return PLX_ERR_WORKSPACE;
     a.ws = reinterpret_cast<float *>(ws);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);

@@ -89,9 +89,15 @@ __device__ __forceinline__ SeqRange seq_range(const DecodeArgs &a, int b) {
 // Readout MFMA e (e = 0..7): A row m <- dim 8m + e, so output row 4g + i is
 // dim 32g + 8i + e: lane (g, n) accumulates P-row n over dims 32g .. 32g+31.
 // -------------------------------------------------------------------------
+// Keys start .. end - 1 (sequence-relative, non-empty) of sequence b, whose
+// first token is seq_tok0, for KV head hkv: writes the G heads' records at
+// record index rbase + h * rstride, or o when `fused`. Ends with a workgroup
+// barrier, so a workgroup may stream several ranges in a row.
 template <int G, bool PLX>
-__global__ __launch_bounds__(64 * kDecodeWaves)
-void decode_mfma_bf16_d128(DecodeArgs a) {
+__device__ __forceinline__ void decode_range(const DecodeArgs &a, const int hkv, const int b,
+                                             const int64_t seq_tok0, const int start, const int end,
+                                             const int64_t rbase, const int64_t rstride,
+                                             const bool fused) {
     constexpr int D = 128;
     constexpr int NR = PLX ? 2 : 1;
     constexpr int NV = NR * G;
@@ -101,12 +107,6 @@ void decode_mfma_bf16_d128(DecodeArgs a) {
     const int wave = threadIdx.x >> 6;
     const int n = lane & 15;
     const int g = lane >> 4;
-    const int hkv = blockIdx.x;
-    const int split = blockIdx.y;
-    const int b = blockIdx.z;
-
-    const SeqRange sr = seq_range(a, b);
-    const int start = split * a.chunk;
     const bool live = n < NV;
     const int h = live ? n / NR : 0;  // head within the group
     const int kind = live ? n % NR : 0;
@@ -118,26 +118,12 @@ void decode_mfma_bf16_d128(DecodeArgs a) {
     const uint16_t *kh = reinterpret_cast<const uint16_t *>(a.k);
     const uint16_t *vh = reinterpret_cast<const uint16_t *>(a.v);
 
-    if (sr.len <= 0 || start >= sr.len) {
-        // Nothing to stream: a fused call writes the zero output of an empty
-        // sequence, otherwise the records are marked empty for the merge.
-        if (a.fused) {
-            uint16_t *o = reinterpret_cast<uint16_t *>(a.o) + row0 * D;
-            for (int i = threadIdx.x; i < G * D; i += 64 * W) o[i] = 0;
-        } else if (threadIdx.x < G) {
-            float *rec = a.ws + ((row0 + threadIdx.x) * a.splits + split) * partial_floats(D);
-            reinterpret_cast<float4 *>(rec + 2 * D)[0] = float4{-INFINITY, 0.f, 0.f, 0.f};
-        }
-        return;
-    }
-    const int end = min(start + a.chunk, sr.len);
-
     // K/V of this split through buffer resources whose range ends at the
     // split's last key: tail lanes past `end` read zeros (their logits are
     // masked below), all addressing is 32-bit offsets from a scalar base.
     const int64_t tok_stride = (int64_t)a.Hkv * D;  // elements between consecutive tokens
     const int ts_bytes = (int)(tok_stride * 2);
-    const int64_t split0 = (sr.tok0 + start) * tok_stride + (int64_t)hkv * D;
+    const int64_t split0 = (seq_tok0 + start) * tok_stride + (int64_t)hkv * D;
     const uint32_t span = (uint32_t)(((int64_t)(end - start - 1) * tok_stride + D) * 2);
     const __amdgpu_buffer_rsrc_t krs =
         __builtin_amdgcn_make_buffer_rsrc((void *)(kh + split0), 0, span, kBufferFlags);
@@ -189,7 +175,7 @@ void decode_mfma_bf16_d128(DecodeArgs a) {
     // Pivot pi = rk_scale * r_h . k_0 on the probe lanes (same for every split).
     float piv = 0.0f;
     if (PLX) {
-        const uint16_t *kfirst = kh + sr.tok0 * tok_stride + (int64_t)hkv * D;
+        const uint16_t *kfirst = kh + seq_tok0 * tok_stride + (int64_t)hkv * D;
         float part = 0.0f;
         for (int u = 0; u < 4; ++u) {
             bf16x8 k0 = load16(kfirst + 8 * (g + 4 * u));
@@ -310,7 +296,7 @@ void decode_mfma_bf16_d128(DecodeArgs a) {
     }
     __syncthreads();
 
-    if (!a.fused) {
+    if (!fused) {
         // record element (column n, dim d) for every live column
         for (int idx = threadIdx.x; idx < NV * D; idx += 64 * W) {
             const int cn = idx / D, d = idx % D;
@@ -323,7 +309,7 @@ void decode_mfma_bf16_d128(DecodeArgs a) {
                 const float mw = sm_m[w][cn];
                 if (mw != -INFINITY) val += __builtin_amdgcn_exp2f(mw - M) * sm_acc[w][cn][d];
             }
-            float *rec = a.ws + ((row0 + cn / NR) * a.splits + split) * partial_floats(D);
+            float *rec = a.ws + (rbase + (cn / NR) * rstride) * partial_floats(D);
             rec[(cn % NR) * D + d] = val;
         }
         if (threadIdx.x < NV) {
@@ -335,7 +321,7 @@ void decode_mfma_bf16_d128(DecodeArgs a) {
                 const float mw = sm_m[w][cn];
                 if (mw != -INFINITY) sum += __builtin_amdgcn_exp2f(mw - M) * sm_l[w][cn];
             }
-            float *rec = a.ws + ((row0 + cn / NR) * a.splits + split) * partial_floats(D);
+            float *rec = a.ws + (rbase + (cn / NR) * rstride) * partial_floats(D);
             if (cn % NR == 0) {
                 rec[2 * D + 0] = M;
                 rec[2 * D + 1] = sum;
@@ -348,6 +334,7 @@ void decode_mfma_bf16_d128(DecodeArgs a) {
                 rec[2 * D + 3] = sm_piv[cn];
             }
         }
+        __syncthreads();  // the LDS may be reused by the workgroup's next range
         return;
     }
 
@@ -374,6 +361,68 @@ void decode_mfma_bf16_d128(DecodeArgs a) {
         const float inv_l = 1.0f / l;
         const float val = PLX ? (A * (1.0f - S * inv_l) + Bv) * inv_l : A * inv_l;
         reinterpret_cast<uint16_t *>(a.o)[(row0 + hh) * D + d] = f32_to_bf16(val);
+    }
+}
+
+// One workgroup per (KV head, split, sequence): the split's keys of its
+// sequence. An empty split writes an empty record (or, fused, o = 0).
+template <int G, bool PLX>
+__global__ __launch_bounds__(64 * kDecodeWaves)
+void decode_mfma_bf16_d128(DecodeArgs a) {
+    constexpr int D = 128;
+    const int hkv = blockIdx.x;
+    const int split = blockIdx.y;
+    const int b = blockIdx.z;
+    const SeqRange sr = seq_range(a, b);
+    const int start = split * a.chunk;
+    const int64_t row0 = (int64_t)b * a.Hq + (int64_t)hkv * G;  // first query row of the group
+    if (sr.len <= 0 || start >= sr.len) {
+        // Nothing to stream: a fused call writes the zero output of an empty
+        // sequence, otherwise the records are marked empty for the merge.
+        if (a.fused) {
+            uint16_t *o = reinterpret_cast<uint16_t *>(a.o) + row0 * D;
+            for (int i = threadIdx.x; i < G * D; i += 64 * kDecodeWaves) o[i] = 0;
+        } else if (threadIdx.x < G) {
+            float *rec = a.ws + ((row0 + threadIdx.x) * a.splits + split) * partial_floats(D);
+            reinterpret_cast<float4 *>(rec + 2 * D)[0] = float4{-INFINITY, 0.f, 0.f, 0.f};
+        }
+        return;
+    }
+    decode_range<G, PLX>(a, hkv, b, sr.tok0, start, min(start + a.chunk, sr.len),
+                         row0 * a.splits + split, a.splits, a.fused);
+}
+
+// Packed batches (stream-K): the tokens of one KV head, all sequences back to
+// back, are cut into a.sk_parts equal ranges, one workgroup each, so every
+// workgroup streams the same number of keys whatever the length mix. A range
+// that crosses sequence boundaries yields one record per sequence piece;
+// piece (range w, sequence b) goes to record slot w + b of its query head
+// (unique: when range w + k overlaps sequence b - k, sequence b starts after
+// range w ends), [Hq][sk_parts + B - 1] records in all.
+template <int G, bool PLX>
+__global__ __launch_bounds__(64 * kDecodeWaves)
+void decode_mfma_streamk(DecodeArgs a) {
+    const int part = blockIdx.x;
+    const int hkv = blockIdx.y;
+    const int T = a.cu[a.B];
+    const int R = (T + a.sk_parts - 1) / a.sk_parts;
+    const int t_lo = part * R;
+    const int t_hi = min(T, t_lo + R);
+    if (t_lo >= t_hi) return;
+    // first sequence holding token t_lo: the last b with cu[b] <= t_lo
+    int lo = 0, hi = a.B - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (a.cu[mid] <= t_lo) lo = mid; else hi = mid - 1;
+    }
+    const int64_t ns = a.sk_parts + a.B - 1;
+    for (int b = lo; b < a.B; ++b) {
+        const int s0 = a.cu[b], s1 = a.cu[b + 1];
+        if (s0 >= t_hi) break;
+        const int p0 = max(t_lo, s0), p1 = min(t_hi, s1);
+        if (p0 >= p1) continue;  // empty sequence, or one that ends before the range
+        decode_range<G, PLX>(a, hkv, b, s0, p0 - s0, p1 - s0, (int64_t)hkv * G * ns + part + b, ns,
+                             false);
     }
 }
 
@@ -581,9 +630,20 @@ __global__ __launch_bounds__(256) void decode_reduce(DecodeArgs a) {
     const int hq = blockIdx.x;
     const int b = blockIdx.y;
     const int d = blockIdx.z * DS + (lane < DS ? lane : 0);
-    const int ns = a.splits;
-    const float *base = a.ws + ((int64_t)b * a.Hq + hq) * ns * partial_floats(D);
-    const float piv0 = PLX ? base[2 * D + 3] : 0.f;
+    // this (sequence, head)'s records: a.splits of them, or, for a stream-K
+    // plan, the slots b + w of the ranges w that overlap the sequence
+    int ns = a.splits;
+    int64_t first = ((int64_t)b * a.Hq + hq) * ns;
+    if (a.sk_parts) {
+        const int T = a.cu[a.B];
+        const int R = (T + a.sk_parts - 1) / a.sk_parts;
+        const int s0 = a.cu[b], s1 = a.cu[b + 1];
+        const int w_lo = s1 > s0 ? s0 / R : 0;
+        ns = s1 > s0 ? (s1 - 1) / R - w_lo + 1 : 0;
+        first = (int64_t)hq * (a.sk_parts + a.B - 1) + b + w_lo;
+    }
+    const float *base = a.ws + first * partial_floats(D);
+    const float piv0 = PLX && ns > 0 ? base[2 * D + 3] : 0.f;
 
     float m = -INFINITY, l = 0.f, S = 0.f, A = 0.f, Bv = 0.f;
     for (int i0 = w; i0 < ns; i0 += 4 * kBatch) {
@@ -648,9 +708,20 @@ __global__ __launch_bounds__(256) void decode_reduce(DecodeArgs a) {
 
 template <bool PLX>
 hipError_t launch_mfma(const DecodeArgs &a, hipStream_t stream) {
-    dim3 grid(a.Hkv, a.splits, a.B);
     dim3 block(64 * kDecodeWaves);
     const int G = a.Hq / a.Hkv;
+    if (a.sk_parts) {
+        dim3 grid(a.sk_parts, a.Hkv);
+        switch (G) {
+            case 1: hipLaunchKernelGGL((decode_mfma_streamk<1, PLX>), grid, block, 0, stream, a); break;
+            case 2: hipLaunchKernelGGL((decode_mfma_streamk<2, PLX>), grid, block, 0, stream, a); break;
+            case 4: hipLaunchKernelGGL((decode_mfma_streamk<4, PLX>), grid, block, 0, stream, a); break;
+            case 8: hipLaunchKernelGGL((decode_mfma_streamk<8, PLX>), grid, block, 0, stream, a); break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
+    dim3 grid(a.Hkv, a.splits, a.B);
     switch (G) {
         case 1: hipLaunchKernelGGL((decode_mfma_bf16_d128<1, PLX>), grid, block, 0, stream, a); break;
         case 2: hipLaunchKernelGGL((decode_mfma_bf16_d128<2, PLX>), grid, block, 0, stream, a); break;

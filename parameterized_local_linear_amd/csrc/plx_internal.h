@@ -34,7 +34,8 @@ struct DecodeArgs {
     float rk_scale;
     int splits;         // >= 1
     int chunk;          // keys per split, multiple of 32
-    float *ws;          // records [B][Hq][splits], written unless fused
+    int sk_parts;       // 0, or the stream-K plan's ranges per KV head (packed batches)
+    float *ws;          // records [B][Hq][splits] ([Hq][sk_parts + B - 1] stream-K), unless fused
     bool fused;         // one split and no records: write o directly
 };
 

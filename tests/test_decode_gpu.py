@@ -265,3 +265,35 @@ def test_pages_decode_grid_full_output(spec):
     assert_parity(from_gpu(plx.decode(*t)), oracle.decode(q, r, k, v), spec.dtype, spec.name)
     assert_parity(from_gpu(plx.softmax_decode(t[0], t[2], t[3])), oracle.decode(q, None, k, v),
                   spec.dtype, spec.name + " softmax")
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("lens", [
+    [0, 0, 1, 0],                                  # almost nothing to stream
+    [5000],                                        # one sequence cut into many ranges
+    [3, 0, 700, 1, 1, 0, 2500, 31, 32, 33, 0],     # ranges crossing many boundaries
+    [129] * 40,                                    # more sequences than ranges per head
+], ids=["tiny", "one-long", "mixed", "many-short"])
+def test_packed_stream_k_plan(G, lens):
+    """Packed caches with the automatic plan stream each KV head's tokens in equal ranges
+    (records per sequence piece, merged per sequence): every length pattern and group size
+    against the oracle, softmax baseline included."""
+    lens = np.array(lens, dtype=np.int64)
+    Hkv = 2
+    q, r, k, v = decode_inputs(len(lens), G * Hkv, Hkv, 128, lens, synth.BF16, 1.0, 500 + G,
+                               packed=True)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    t = [to_gpu(x, synth.BF16) for x in (q, r, k, v)]
+    cu_t = torch.from_numpy(cu).cuda()
+    kw = dict(cu_seqlens_k=cu_t, kv_len=max(int(lens.max()), 1))
+    o = from_gpu(plx.decode(*t, **kw))
+    o0 = from_gpu(plx.softmax_decode(t[0], t[2], t[3], **kw))
+    assert np.all(o[lens == 0] == 0.0) and np.all(o0[lens == 0] == 0.0)
+    live = lens > 0
+    if live.any():
+        ref = oracle.decode(q, r, k, v, seq_start=cu[:-1].astype(np.int64), seq_len=lens)
+        ref0 = oracle.decode(q, None, k, v, seq_start=cu[:-1].astype(np.int64), seq_len=lens)
+        assert_parity(o[live], ref[live], synth.BF16, "stream-K")
+        assert_parity(o0[live], ref0[live], synth.BF16, "stream-K softmax")
+    # repeated calls are bit-identical
+    assert np.array_equal(from_gpu(plx.decode(*t, **kw)), o)
