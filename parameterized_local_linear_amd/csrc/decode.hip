@@ -137,50 +137,63 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, const int hkv,
 
     // The whole offset goes in the VGPR operand: the range check of a raw
     // buffer access covers the VGPR and immediate offsets, not soffset.
-    auto load_tile = [&](int t0, bf16x8 *kt, bf16x8 *vt) {
+    auto load_k = [&](int t0, bf16x8 *kt) {
         const int tb = (t0 - start) * ts_bytes;  // wave-uniform
-        const int k0o = tb + koff0, k1o = tb + koff1, vo = tb + voff;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            kt[u] = buffer_load16(krs, k0o + 64 * u);
-            kt[4 + u] = buffer_load16(krs, k1o + 64 * u);
+            kt[u] = buffer_load16(krs, tb + koff0 + 64 * u);
+            kt[4 + u] = buffer_load16(krs, tb + koff1 + 64 * u);
         }
+    };
+    auto load_v = [&](int t0, bf16x8 *vt) {
+        const int vo = (t0 - start) * ts_bytes + voff;
 #pragma unroll
         for (int t = 0; t < 8; ++t) vt[t] = buffer_load16(vrs, vo + 4 * t * ts_bytes);
     };
 
+    // B operand of the score MFMA (vector n, dims 8(g + 4u) .. +8) and, for
+    // the pivot, the sequence's first key: loaded before the K/V tiles, so
+    // that waiting for them (loads complete in order) leaves the tiles in
+    // flight. Dead columns load head 0's row and are zeroed afterwards.
+    bf16x8 qr[4], kf[4];
+    {
+        const uint16_t *src = (kind == 0 ? qh : rh) + ((int64_t)b * a.Hq + hq) * D;
+        const uint16_t *kfirst = kh + seq_tok0 * tok_stride + (int64_t)hkv * D;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) qr[u] = load16(src + 8 * (g + 4 * u));
+        if (PLX) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) kf[u] = load16(kfirst + 8 * (g + 4 * u));
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
     // Two tile buffers per wave: while one tile is consumed the next is in
     // flight. Loads are never predicated: a tile past `end` lies outside the
     // buffer range and reads zeros without touching memory, so every step
-    // issues the same loads and waits for exactly the tile it consumes.
+    // issues the same loads and waits for exactly the tile it consumes. A
+    // tile's K registers take the next loads as soon as its scores are
+    // issued, its V registers after its readout.
     constexpr int kStride = 32 * W;  // keys between a wave's consecutive tiles
     bf16x8 kA[8], vA[8], kB[8], vB[8];
     int t0 = start + 32 * wave;
-    load_tile(t0, kA, vA);  // first tiles in flight before anything else is read
-    load_tile(t0 + kStride, kB, vB);
+    load_k(t0, kA);
+    load_v(t0, vA);
+    load_k(t0 + kStride, kB);
+    load_v(t0 + kStride, vB);
 
-    // B operand of the score MFMA: vector n, dims 8(g + 4u) .. +8.
-    bf16x8 qr[4];
-    {
-        const uint16_t *src = (kind == 0 ? qh : rh) + ((int64_t)b * a.Hq + hq) * D;
-        for (int u = 0; u < 4; ++u) {
-            if (live) {
-                qr[u] = load16(src + 8 * (g + 4 * u));
-            } else {
-                for (int e = 0; e < 8; ++e) qr[u][e] = (__bf16)0.0f;
-            }
-        }
+    if (!live) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            for (int e = 0; e < 8; ++e) qr[u][e] = (__bf16)0.0f;
     }
-
     // Pivot pi = rk_scale * r_h . k_0 on the probe lanes (same for every split).
     float piv = 0.0f;
     if (PLX) {
-        const uint16_t *kfirst = kh + seq_tok0 * tok_stride + (int64_t)hkv * D;
         float part = 0.0f;
-        for (int u = 0; u < 4; ++u) {
-            bf16x8 k0 = load16(kfirst + 8 * (g + 4 * u));
-            for (int e = 0; e < 8; ++e) part += (float)qr[u][e] * (float)k0[e];
-        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            for (int e = 0; e < 8; ++e) part += (float)qr[u][e] * (float)kf[u][e];
         part = xor_sum_rowgroups(part);
         piv = part * a.rk_scale;
     }
@@ -206,6 +219,7 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, const int hkv,
             sc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt[u], qr[u], sc0, 0, 0, 0);
             sc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt[4 + u], qr[u], sc1, 0, 0, 0);
         }
+        load_k(t0 + 2 * kStride, kt);  // this buffer's next K tile
         float raw[8], zr[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -266,8 +280,7 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, const int hkv,
 #pragma unroll
         for (int e = 0; e < 8; ++e)
             acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vT[e], pf, acc[e], 0, 0, 0);
-        // this buffer takes the tile two steps ahead
-        load_tile(t0 + 2 * kStride, kt, vt);
+        load_v(t0 + 2 * kStride, vt);  // and its next V tile
         t0 += kStride;
     };
 

@@ -297,3 +297,34 @@ def test_packed_stream_k_plan(G, lens):
         assert_parity(o0[live], ref0[live], synth.BF16, "stream-K softmax")
     # repeated calls are bit-identical
     assert np.array_equal(from_gpu(plx.decode(*t, **kw)), o)
+
+
+def test_split_decode_dirty_workspace_and_graph_replays():
+    """Split plans need no clearing of the workspace: one full of garbage, repeated calls
+    and replays of a captured graph (with eager calls between them) all give the eager
+    result."""
+    B, Hq, Hkv, D, L = 2, 16, 8, 128, 3000
+    q, r, k, v = decode_inputs(B, Hq, Hkv, D, [L] * B, synth.BF16, S128, 520)
+    t = [to_gpu(x, synth.BF16) for x in (q, r, k, v)]
+    ref = oracle.decode(q, r, k, v)
+    for splits in (0, 3, 7, 24):
+        need = plx.decode_workspace_bytes(B, Hq, Hkv, D, L, plx.PLX_BF16, splits)
+        ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")  # garbage words
+        eager = plx.decode(*t, num_splits=splits, workspace=ws)
+        assert_parity(from_gpu(eager), ref, synth.BF16, f"splits={splits}")
+        assert torch.equal(plx.decode(*t, num_splits=splits, workspace=ws), eager)
+        out = torch.empty_like(eager)
+        stream = torch.cuda.Stream()
+        with torch.cuda.stream(stream):
+            plx.decode(*t, num_splits=splits, workspace=ws, out=out)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            plx.decode(*t, num_splits=splits, workspace=ws, out=out)
+        for _ in range(4):
+            out.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, eager), f"graph replay, splits={splits}"
+            # eager work on the same workspace between replays
+            assert torch.equal(plx.decode(*t, num_splits=splits, workspace=ws), eager)
