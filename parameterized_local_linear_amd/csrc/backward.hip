@@ -253,9 +253,13 @@ __global__ __launch_bounds__(64) void bwd_keys_generic(BackwardArgs a) {
 //
 // Tiles in LDS are row-major 256-byte rows (one key or one query row of 128
 // bf16) with 16-byte chunk c of row x stored at slot c ^ swz(x & 15),
-// swz(x) = 4 (x & 3) + (x >> 2), filled by the buffer unit directly
-// (buffer_load ... lds). Plain 16-byte reads of a row chunk and the
-// transposing 64-bit reads (ds_read_b64_tr_b16) both hit distinct banks.
+// swz(x) = 2 ((x >> 2) & 3) + 9 (x & 1), filled by the buffer unit directly
+// (buffer_load ... lds). For the row orders used below (permuted rows for
+// the plain reads, rows g + 4 t for the transposed ones), the plain 16-byte
+// reads of a row chunk (served eight lanes at a time: eight distinct
+// slot & 7) and the transposing 64-bit reads (ds_read_b64_tr_b16, served 32
+// lanes at a time over all 64 banks: 16 distinct slots) are both free of
+// bank conflicts.
 //
 // Permuted score rows: the score MFMA's A row m is loaded from tile row
 // (m >> 2) + 4 (m & 3) (+16 for the second 16-row block), so the result lane
@@ -270,7 +274,7 @@ constexpr int kBwdRowsPerTile = 64;   // key pass: query rows per LDS tile
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ int tile_swz(int x) { return ((x & 3) << 2) | ((x >> 2) & 3); }
+__device__ __forceinline__ int tile_swz(int x) { return 2 * ((x >> 2) & 3) + 9 * (x & 1); }
 
 // 16-byte chunk `chunk` of tile row x.
 __device__ __forceinline__ bf16x8 lds_chunk(const uint16_t *t, int x, int chunk) {

@@ -171,8 +171,11 @@ __global__ __launch_bounds__(64) void prefill_generic(PrefillArgs a) {
 // next tile's copy is issued before the current tile is consumed and only
 // waited for at the end of the tile. LDS rows are 256 bytes, with 16-byte
 // chunk c of key k stored at chunk slot c ^ swz(k & 15),
-// swz(x) = 4 (x & 3) + (x >> 2): every group of eight lanes of an operand
-// read touches eight distinct 16-byte bank groups.
+// swz(x) = 2 ((x >> 2) & 3) + 9 (x & 1). Both operand reads are then free of
+// LDS bank conflicts (checked with the bank-conflict counter): the 128-bit K
+// reads, served eight lanes at a time, see eight distinct values of
+// slot & 7, and the transposing 64-bit V reads, served 32 lanes at a time
+// over all 64 banks, see 16 distinct slots, each with both 8-byte halves.
 //
 // Per 32-key sub-tile the wave computes, as in the decode kernel but with
 // query columns instead of head/probe columns:
@@ -249,7 +252,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs &a, const int ite
     // for a tile's copy only where that tile is read)
     __shared__ __attribute__((aligned(16))) uint16_t lds_k0[TK * D], lds_v0[TK * D];
     __shared__ __attribute__((aligned(16))) uint16_t lds_k1[TK * D], lds_v1[TK * D];
-    auto swz = [](int key) { return ((key & 3) << 2) | ((key >> 2) & 3); };
+    auto swz = [](int key) { return 2 * ((key >> 2) & 3) + 9 * (key & 1); };
     // copy j of this wave: keys 4 (wave * DMA + j) + lane / 16; lane writes LDS
     // slot lane % 16 of its key, i.e. fetches chunk (lane % 16) ^ swz(key)
     auto dma_tile = [&](int tile, uint16_t *lk, uint16_t *lv) __attribute__((always_inline)) {
@@ -354,7 +357,6 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs &a, const int ite
     auto scores = [&](const KOp &op) __attribute__((always_inline)) {
         Scores sc;
         sc.z0 = sc.z1 = sc.s0 = sc.s1 = floatx4{0.f, 0.f, 0.f, 0.f};
-        __builtin_amdgcn_s_setprio(1);  // matrix-core bursts go first; the other wave's VALU fills in
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             sc.z0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.k[0][u], qop[u], sc.z0, 0, 0, 0);
@@ -362,17 +364,14 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs &a, const int ite
             sc.s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.k[0][u], rop[u], sc.s0, 0, 0, 0);
             sc.s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.k[1][u], rop[u], sc.s1, 0, 0, 0);
         }
-        __builtin_amdgcn_s_setprio(0);
         return sc;
     };
     auto pv = [&](const Probs &p, const VOp &vo) __attribute__((always_inline)) {
-        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             accA[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vo.v[e], p.pa, accA[e], 0, 0, 0);
             accB[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vo.v[e], p.ps, accB[e], 0, 0, 0);
         }
-        __builtin_amdgcn_s_setprio(0);
     };
     // softmax update of the sub-tile at key k0: rescales the accumulators when
     // the reference max is raised, returns the bf16 P and P o S' operands
