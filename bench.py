@@ -531,7 +531,7 @@ def run_prefill_varlen_workload(args, torch, plx, synth, oracle):
 
 # The pages' H200 Parallax decode latencies for the same shapes (PyPI README of
 # parallax-kernel, small- and large-batch decode tables; q50, CUDA-graph replay).
-# Context only: another machine's numbers, not a target of this build.
+# Context only: another machine's numbers, not a target.
 PAGES_H200_PARALLAX_US = {(1, 512): 5.79, (1, 1024): 6.48, (1, 4096): 8.61, (1, 16384): 21.53,
                           (32, 512): 24.02, (32, 1024): 39.55, (32, 4096): 279.96,
                           (32, 16384): 1094.37}
@@ -624,7 +624,7 @@ def main():
     global EAGER
     EAGER = args.eager
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported by this build "
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported "
               "(the decode and prefill paths are single-GPU kernels).", file=sys.stderr)
         sys.exit(2)
     import torch
