@@ -195,6 +195,7 @@ __global__ __launch_bounds__(64) void prefill_generic(PrefillArgs a) {
 // -------------------------------------------------------------------------
 constexpr int kPrefillKeys = 128;  // keys per LDS tile
 constexpr int kPrefillWaves = 8;
+constexpr int kDenseWorkersPerCU = 4;  // persistent workgroups per CU for dense batches
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -483,16 +484,22 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs &a, const int ite
     }
 }
 
-// PERSIST = false: one work item per workgroup (dense batches); true: a
-// persistent grid drawing items from the per-XCD queues (packed batches).
-template <int HPW, bool PERSIST>
+// Persistent grid. A packed batch (a.sched != nullptr) draws items from the
+// per-XCD queues; a dense batch takes items w, w + grid, w + 2 grid, ... in
+// order: heaviest first, and with a grid that is a multiple of 8, every item
+// of a (sequence, KV head) group on the group's XCD. Either way each item is
+// computed whole by one workgroup.
+template <int HPW>
 __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_mfma_bf16_d128(PrefillArgs a) {
-    if (!PERSIST) {
-        prefill_item<HPW>(a, blockIdx.x);
-        return;
-    }
     const int n_items = a.B * a.Hkv * (a.Hq / a.Hkv / HPW) * ((a.L + 16 * kPrefillWaves / HPW - 1) /
                                                             (16 * kPrefillWaves / HPW));
+    if (!a.sched) {
+        for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+            prefill_item<HPW>(a, item);
+            __syncthreads();  // the next item's first copy overwrites this one's LDS
+        }
+        return;
+    }
     for (int item = next_item(a.sched, n_items); item >= 0; item = next_item(a.sched, n_items))
         prefill_item<HPW>(a, item);
 }
@@ -517,22 +524,21 @@ hipError_t launch_prefill(const PrefillArgs &a, int dtype, hipStream_t stream) {
         const int rph = 16 * kPrefillWaves / hpw;
         const long items = (long)a.B * a.Hkv * (G / hpw) * ((a.L + rph - 1) / rph);
         if (items <= 0x7fffffffL) {
-            long wgs = items;
+            // persistent workers, a multiple of 8 so that every XCD share is drained:
+            // one per CU draining the queues of a packed batch, kDenseWorkersPerCU per
+            // CU striding over a dense batch's items (fewer launches of a workgroup
+            // than items, and a shorter tail; measured 2% faster than one per item)
+            const long cap = (long)a.workers * (a.sched ? 1 : kDenseWorkersPerCU);
+            const long wgs = ((items < cap ? items : cap) + 7) / 8 * 8;
             if (a.sched) {
-                // persistent workers, a multiple of 8 so that every XCD share is drained
-                wgs = ((items < a.workers ? items : a.workers) + 7) / 8 * 8;
                 hipError_t err = launch_zero_counters(a.sched, 8, stream);
                 if (err != hipSuccess) return err;
             }
             dim3 grid((unsigned)wgs), block(64 * kPrefillWaves);
-            if (hpw == 2 && a.sched)
-                hipLaunchKernelGGL((prefill_mfma_bf16_d128<2, true>), grid, block, 0, stream, a);
-            else if (hpw == 2)
-                hipLaunchKernelGGL((prefill_mfma_bf16_d128<2, false>), grid, block, 0, stream, a);
-            else if (a.sched)
-                hipLaunchKernelGGL((prefill_mfma_bf16_d128<1, true>), grid, block, 0, stream, a);
+            if (hpw == 2)
+                hipLaunchKernelGGL((prefill_mfma_bf16_d128<2>), grid, block, 0, stream, a);
             else
-                hipLaunchKernelGGL((prefill_mfma_bf16_d128<1, false>), grid, block, 0, stream, a);
+                hipLaunchKernelGGL((prefill_mfma_bf16_d128<1>), grid, block, 0, stream, a);
             return hipGetLastError();
         }
     }
