@@ -31,8 +31,10 @@
  *    launch: a failing check returns a status and touches no memory.
  *    Launch failures return PLX_ERR_HIP. Work is enqueued on `stream`
  *    (a hipStream_t; NULL is the default stream); nothing synchronises.
- *  - Results do not depend on timing: no atomics, a fixed split plan, so
- *    repeated calls return bit-identical outputs.
+ *  - Results do not depend on timing: a fixed split plan and no atomic
+ *    accumulation (the only atomics, the work-queue counters of packed
+ *    prefill and backward batches, decide which workgroup computes an item,
+ *    never how), so repeated calls return bit-identical outputs.
  *  - Non-finite inputs propagate; they are not checked.
  *  - qk_scale must be finite and > 0, rk_scale finite (else INVALID_ARG).
  *  - window (sliding-window attention; the PyPI README's overview calls it

@@ -64,8 +64,9 @@ struct PrefillArgs {
     float *lse, *sbar;
     void *vbar;         // nullptr, or the softmax readout sum_j w_j v_j (layout and dtype of o)
     const int32_t *cu;  // nullptr: dense [B, H, L, D]; else packed [T, H, D], cu [B + 1]
-    int *sched;         // nullptr: one work item per workgroup; else 8 zeroed queue counters
-    int workers;        // workgroups of a persistent launch (when sched != nullptr)
+    int *sched;         // nullptr: persistent workgroups stride over the work items (dense
+                        // batches); else 8 zeroed queue counters they draw items from
+    int workers;        // compute units of the device (sizes the persistent grid)
     int B, Hq, Hkv, L, D;  // L: the (maximum) sequence length
     int window;         // query i sees keys i - window + 1 .. i (window = L: causal only)
     float zscale;       // qk_scale * log2(e)
