@@ -1,0 +1,146 @@
+"""Seeded random-shape sweep against the oracle.
+
+Each case draws its shape, dtype, head group, layout (dense or packed, with empty
+sequences), window, split count and scales from a fixed numpy generator, so the
+cases are the same on every run. Decode cases run both entry points (Parallax and
+the softmax baseline); prefill cases check o, lse, sbar and the four gradients.
+Group sizes 3 take the generic kernels, the others the matrix-core ones. Bars as
+in the other parity tests: max-norm 1e-2 (bf16) / 1e-5 (fp32) for outputs, 1e-2 /
+1e-4 for gradients, except bf16 gradients of unscaled inputs: 3e-2.
+
+Why unscaled bf16 gradients get a wider bar: the backward takes delta = g.o from
+the forward's stored bf16 output (as FlashAttention's backward does), and o
+carries the forward's rounding of its bf16 matrix operands. In
+dz_j = w_j (c_j u_j - ubar (s_j - sbar) - delta), dz_j is the small difference
+of terms about |c_j| = |1 + s_j - sbar| times larger, so delta's error, small
+against those terms, is about |c_j| times larger against dz_j. With unscaled
+N(0,1) inputs at D = 128 the probe scores are sqrt(D) ~ 11 times those of the
+pages' scaled inputs, and c reaches about 30 on rows with few keys. One such row (two keys with s = 8.1 and -26.6) measured dq at
+1.7e-2 of max |dq|; recomputing that row in double with delta taken from the
+GPU's o left a 0.35% difference. Scaled inputs stay far below 1e-2.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parameterized_local_linear_amd as plx
+import synth
+from gpu_util import assert_parity, from_gpu, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+GTOL = {synth.F32: 1e-4, synth.BF16: 1e-2}
+GTOL_BF16_UNSCALED = 3e-2
+
+
+def _draw_common(g):
+    dtype = synth.BF16 if g.random() < 0.7 else synth.F32
+    D = 128 if (dtype == synth.BF16 and g.random() < 0.75) else int(g.choice([64, 128]))
+    G = int(g.choice([1, 2, 3, 4, 8]))
+    Hkv = int(g.choice([1, 2, 3, 4]))
+    scale = float(g.choice([1.0, 1.0 / math.sqrt(D)]))
+    qk = float(g.choice([1.0 / math.sqrt(D), 0.3]))
+    rk = float(g.choice([1.0, 0.5]))
+    return dtype, D, G, Hkv, scale, qk, rk
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_random_decode(case):
+    g = np.random.default_rng(7100 + case)
+    dtype, D, G, Hkv, scale, qk, rk = _draw_common(g)
+    Hq = G * Hkv
+    B = int(g.integers(1, 6))
+    packed = bool(g.random() < 0.5)
+    if packed:
+        lens = g.integers(0, 2500, size=B)
+        lens[int(g.integers(0, B))] = int(g.integers(1, 2500))  # at least one non-empty
+    else:
+        lens = np.full(B, int(g.integers(1, 2500)))
+    W = int(g.choice([0, 0, 1, 17, 300, 5000]))
+    splits = int(g.choice([0, 0, 1, 2, 7]))
+    seed = 7200 + case
+    q, r, k, v = (synth.normal(seed, tid, shp, scale, dtype) for tid, shp in (
+        (synth.TID_Q, (B, Hq, D)), (synth.TID_R, (B, Hq, D)),
+        (synth.TID_K, (int(lens.sum()), Hkv, D) if packed else (B, int(lens[0]), Hkv, D)),
+        (synth.TID_V, (int(lens.sum()), Hkv, D) if packed else (B, int(lens[0]), Hkv, D))))
+    t = [to_gpu(x, dtype) for x in (q, r, k, v)]
+    what = f"case {case}: B={B} Hq={Hq} Hkv={Hkv} D={D} lens={lens.tolist()} W={W} splits={splits}"
+    if packed:
+        cu = np.concatenate([[0], np.cumsum(lens)])
+        cu_t = torch.from_numpy(cu.astype(np.int32)).cuda()
+        kw = dict(cu_seqlens_k=cu_t, kv_len=int(lens.max()), num_splits=splits, window=W)
+        okw = dict(seq_start=cu[:-1], seq_len=lens, window=W)
+    else:
+        kw = dict(num_splits=splits, window=W)
+        okw = dict(window=W)
+    live = lens > 0
+    o = from_gpu(plx.decode(*t, qk, rk, **kw))
+    ref = oracle.decode(q, r, k, v, qk_scale=qk, rk_scale=rk, **okw)
+    assert np.all(o[~live] == 0), what
+    assert_parity(o[live], ref[live], dtype, what)
+    o0 = from_gpu(plx.softmax_decode(t[0], t[2], t[3], qk, **kw))
+    ref0 = oracle.decode(q, None, k, v, qk_scale=qk, **okw)
+    assert np.all(o0[~live] == 0), what
+    assert_parity(o0[live], ref0[live], dtype, "softmax " + what)
+
+
+def _check_grads(got, ref, dtype, what, unscaled):
+    tol = GTOL_BF16_UNSCALED if (dtype == synth.BF16 and unscaled) else GTOL[dtype]
+    largest = max(np.abs(b).max() for b in ref)
+    for name, a, b in zip(("dq", "dr", "dk", "dv"), got, ref):
+        bmax = np.abs(b).max()
+        err = np.abs(a - b).max() / (bmax if bmax > 0 else largest)
+        assert err <= tol, f"{what} {name}: {err:.3e}"
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_random_prefill_and_backward(case):
+    g = np.random.default_rng(7300 + case)
+    dtype, D, G, Hkv, scale, qk, rk = _draw_common(g)
+    G = min(G, 4)
+    Hq = G * Hkv
+    packed = bool(g.random() < 0.4)
+    W = int(g.choice([0, 0, 1, 33, 200]))
+    seed = 7400 + case
+    what = f"case {case}: Hq={Hq} Hkv={Hkv} D={D} W={W}"
+    if packed:
+        lens = g.integers(0, 400, size=int(g.integers(1, 5)))
+        lens[0] = max(int(lens[0]), 1)
+        T = int(lens.sum())
+        cu = np.concatenate([[0], np.cumsum(lens)])
+        q, r, k, v = (synth.normal(seed, tid, (T, H, D), scale, dtype) for tid, H in (
+            (synth.TID_Q, Hq), (synth.TID_R, Hq), (synth.TID_K, Hkv), (synth.TID_V, Hkv)))
+        do = synth.normal(seed, synth.TID_DO, (T, Hq, D), 1.0, dtype)
+        t = [to_gpu(x, dtype) for x in (q, r, k, v, do)]
+        cu_t = torch.from_numpy(cu.astype(np.int32)).cuda()
+        what += f" lens={lens.tolist()}"
+        o, lse, sbar = plx.prefill_varlen(*t[:4], cu_t, None, qk, rk, return_stats=True, window=W)
+        ref, ref_lse, ref_sbar = oracle.prefill_varlen(q, r, k, v, cu, qk_scale=qk, rk_scale=rk,
+                                                       window=W, stats=True)
+        grads = plx.prefill_varlen_backward(*t[:4], o, t[4], lse, sbar, cu_t, None, qk, rk,
+                                            window=W)
+        ref_g = oracle.prefill_varlen_backward(q, r, k, v, do, cu, qk_scale=qk, rk_scale=rk,
+                                               window=W)
+    else:
+        B = int(g.integers(1, 4))
+        L = int(g.integers(1, 400))
+        q, r, k, v = (synth.normal(seed, tid, (B, H, L, D), scale, dtype) for tid, H in (
+            (synth.TID_Q, Hq), (synth.TID_R, Hq), (synth.TID_K, Hkv), (synth.TID_V, Hkv)))
+        do = synth.normal(seed, synth.TID_DO, (B, Hq, L, D), 1.0, dtype)
+        t = [to_gpu(x, dtype) for x in (q, r, k, v, do)]
+        what += f" B={B} L={L}"
+        o, lse, sbar = plx.prefill(*t[:4], qk, rk, return_stats=True, window=W)
+        ref, ref_lse, ref_sbar = oracle.prefill(q, r, k, v, qk_scale=qk, rk_scale=rk, window=W,
+                                                stats=True)
+        grads = plx.prefill_backward(*t[:4], o, t[4], lse, sbar, qk, rk, window=W)
+        ref_g = oracle.prefill_backward(q, r, k, v, do, qk_scale=qk, rk_scale=rk, window=W)
+    assert_parity(from_gpu(o), ref, dtype, what)
+    lse = lse.cpu().numpy().astype(np.float64)
+    assert np.abs(lse - ref_lse).max() <= 1e-4 * max(1.0, np.abs(ref_lse).max()), what
+    stol = 1e-4 if dtype == synth.F32 else 1e-2
+    sbar = sbar.cpu().numpy().astype(np.float64)
+    assert np.abs(sbar - ref_sbar).max() <= stol * max(1.0, np.abs(ref_sbar).max()), what
+    _check_grads([from_gpu(x) for x in grads], ref_g, dtype, what, unscaled=scale == 1.0)
