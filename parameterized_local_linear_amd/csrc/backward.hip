@@ -618,6 +618,7 @@ __device__ __forceinline__ void bwd_keys_item(const BackwardArgs &a, const int i
 #pragma unroll
         for (int e = 0; e < 8; ++e) accK[c][e] = accV[c][e] = floatx4{0.f, 0.f, 0.f, 0.f};
     const int rperm = (n >> 2) + 4 * (n & 3);
+    const float rk_over_qk = a.rk_scale / a.qk_scale;  // qk_scale > 0 (checked by the API)
 
     // one 32-row sub-tile at tile row xl (global row rs)
     auto sub_tile = [&](const uint16_t *tq, const uint16_t *tr, const uint16_t *tg, const RowStat *ts,
@@ -655,9 +656,11 @@ __device__ __forceinline__ void bwd_keys_item(const BackwardArgs &a, const int i
                 const int key = kw + 16 * c + n;
                 if (mask && (rw < key || rw >= key + W || rw >= L)) w = 0.f;
                 const float sc = fmaf(ss, a.rk_scale, -st.sbar);
-                p1[c][t] = (__bf16)(w * (1.0f + sc));
-                pz[c][t] = (__bf16)(w * (fmaf(sc, u, u) - fmaf(st.ubar, sc, st.delta)) * a.qk_scale);
-                ps[c][t] = (__bf16)(w * (u - st.ubar) * a.rk_scale);
+                p1[c][t] = (__bf16)fmaf(w, sc, w);  // w (1 + sc)
+                // dk = qk_scale (sum dz q + (rk_scale / qk_scale) sum ds r): qk_scale is
+                // applied once to the accumulator, not to every element
+                pz[c][t] = (__bf16)(w * (fmaf(sc, u, u) - fmaf(st.ubar, sc, st.delta)));
+                ps[c][t] = (__bf16)(w * (u - st.ubar) * rk_over_qk);
             }
         }
 #pragma unroll
@@ -707,7 +710,8 @@ __device__ __forceinline__ void bwd_keys_item(const BackwardArgs &a, const int i
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 *reinterpret_cast<uint2 *>(dk + 16 * e) =
-                    uint2{pack_bf16x2(accK[c][e][0], accK[c][e][1]), pack_bf16x2(accK[c][e][2], accK[c][e][3])};
+                    uint2{pack_bf16x2(accK[c][e][0] * a.qk_scale, accK[c][e][1] * a.qk_scale),
+                          pack_bf16x2(accK[c][e][2] * a.qk_scale, accK[c][e][3] * a.qk_scale)};
                 *reinterpret_cast<uint2 *>(dv + 16 * e) =
                     uint2{pack_bf16x2(accV[c][e][0], accV[c][e][1]), pack_bf16x2(accV[c][e][2], accV[c][e][3])};
             }
