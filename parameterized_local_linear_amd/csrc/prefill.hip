@@ -426,11 +426,14 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs &a, const int ite
         return pr;
     };
     // one tile: its sub-tiles in order
+    // (on a masked tile, sub-tiles that hold none of the wave's keys are skipped)
     auto tile_body = [&](const uint16_t *lk, const uint16_t *lv, int tile, bool diag) __attribute__((always_inline)) {
         const int t0 = tile * TK;
 #pragma unroll
         for (int j = 0; j < NSUB; ++j) {
-            const Probs p = softmax(scores(load_k(lk, 32 * j)), t0 + 32 * j, diag);
+            const int k0 = t0 + 32 * j;
+            if (diag && (k0 > q_last || k0 + 31 <= q0 - W)) continue;  // wave-uniform
+            const Probs p = softmax(scores(load_k(lk, 32 * j)), k0, diag);
             pv(p, load_vT(lv, 32 * j));
         }
     };
