@@ -441,7 +441,12 @@ __device__ __forceinline__ void bwd_rows_item(const BackwardArgs &a, const int i
             if (t0 <= q_last && t0 + TK - 1 > q0 - W) {
                 const bool diag = !(t0 + TK - 1 <= q0 && t0 > q_last - W);
 #pragma unroll
-                for (int j = 0; j < NSUB; ++j) body(lk, lv, 32 * j, t0 + 32 * j, diag);
+                for (int j = 0; j < NSUB; ++j) {
+                    const int k0 = t0 + 32 * j;
+                    // on a masked tile, sub-tiles with none of the wave's keys are skipped
+                    if (diag && (k0 > q_last || k0 + 31 <= q0 - W)) continue;
+                    body(lk, lv, 32 * j, k0, diag);
+                }
             }
             __syncthreads();
         };
