@@ -56,10 +56,11 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int kv_len, int window, in
         splits = (int)s;
     }
     if (splits > max_splits) splits = max_splits;
-    // A split's keys (plus the 64 keys its streaming loop reads ahead) must
-    // span less than 2^31 bytes: the kernels address them with 32-bit offsets.
+    // A split's keys, plus the keys its streaming loop reads ahead (up to two
+    // 128-key strides and one 32-key tile past the split's end), must span less
+    // than 2^31 bytes: the kernels address them with 32-bit offsets.
     const long long tok_bytes = (long long)Hkv * D * (dtype == PLX_BF16 ? 2 : 4);
-    const long long max_keys = (0x7fffffffLL - 1024) / tok_bytes - 96;
+    const long long max_keys = (0x7fffffffLL - 1024) / tok_bytes - 320;
     const long long min_splits = (kv_len + max_keys - 1) / max_keys;
     if (splits < min_splits) splits = (int)min_splits;
     if (splits > 65535) splits = 65535;  // grid.y limit

@@ -163,3 +163,18 @@ def test_varlen_prefill_rejects_on_host():
                                               0, None) == 3
     assert L.parallax_prefill_varlen_backward(*b13, 2, 4, 2, 64, 100, 128, 0, 0.1, 1.0, 1, FAKE,
                                               256 + 4 * 100 * 16 - 1, None) == 3
+
+
+@pytest.mark.parametrize("Hkv,D,code", [(64, 128, plx.PLX_BF16), (8, 128, plx.PLX_F32),
+                                        (128, 64, plx.PLX_F32), (1, 64, plx.PLX_BF16)])
+def test_split_plan_keeps_read_ahead_inside_32bit_offsets(Hkv, D, code):
+    """Kernels address a split's keys with 32-bit byte offsets, and the streaming loop
+    reads up to two 128-key strides and a 32-key tile past the split's end: every plan,
+    even a forced single split over a huge cache, must keep that inside 2^31 bytes."""
+    tok = Hkv * D * (2 if code == plx.PLX_BF16 else 4)
+    for kv_len in (1 << 20, (1 << 21) + 77, 1 << 24):
+        for forced in (0, 1, 3):
+            s = plx.decode_num_splits(1, Hkv, Hkv, D, kv_len, code, forced)
+            per = -(-kv_len // s)
+            chunk = -(-per // 128) * 128
+            assert (chunk + 2 * 128 + 32) * tok + 1024 < 2 ** 31, (kv_len, forced, s)
