@@ -35,6 +35,15 @@ int device_cu_count() {
 // normalisation into the streaming kernel and needs no workspace.
 constexpr int kTargetWavesPerCU = 4;
 constexpr int kMinKeysPerWave = 32;  // one tile: short sequences split for latency
+// Most keys one split (or stream-K range) may hold: its keys, plus the keys
+// its streaming loop reads ahead (up to two 128-key strides and one 32-key
+// tile past its end), must span less than 2^31 bytes, since the kernels
+// address them with 32-bit offsets.
+static long long max_split_keys(int Hkv, int D, int dtype) {
+    const long long tok_bytes = (long long)Hkv * D * (dtype == PLX_BF16 ? 2 : 4);
+    return (0x7fffffffLL - 1024) / tok_bytes - 320;
+}
+
 DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int kv_len, int window, int dtype,
                        int num_splits) {
     DecodePlan p;
@@ -56,11 +65,7 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int kv_len, int window, in
         splits = (int)s;
     }
     if (splits > max_splits) splits = max_splits;
-    // A split's keys, plus the keys its streaming loop reads ahead (up to two
-    // 128-key strides and one 32-key tile past the split's end), must span less
-    // than 2^31 bytes: the kernels address them with 32-bit offsets.
-    const long long tok_bytes = (long long)Hkv * D * (dtype == PLX_BF16 ? 2 : 4);
-    const long long max_keys = (0x7fffffffLL - 1024) / tok_bytes - 320;
+    const long long max_keys = max_split_keys(Hkv, D, dtype);
     const long long min_splits = (kv_len + max_keys - 1) / max_keys;
     if (splits < min_splits) splits = (int)min_splits;
     if (splits > 65535) splits = 65535;  // grid.y limit
@@ -112,10 +117,14 @@ const char *parallax_status_string(int status) {
 // 1 per CU 238 us, 2 per CU 229 us, 3 per CU 239 us). Returns the range
 // count per KV head, or 0 where it does not apply (the per-sequence split
 // plan then runs).
-static int streamk_parts(const DecodePlan &p, int Hkv, int window, int num_splits) {
+static int streamk_parts(const DecodePlan &p, int B, int Hkv, int D, int kv_len, int dtype,
+                         int window, int num_splits) {
     if (p.path != plx::DecodePath::Mfma || window != 0 || num_splits != 0) return 0;
-    const int parts = 2 * plx::device_cu_count() / Hkv;
-    return parts < 1 ? 1 : (parts > 65535 ? 65535 : parts);
+    int parts = 2 * plx::device_cu_count() / Hkv;
+    parts = parts < 1 ? 1 : (parts > 65535 ? 65535 : parts);
+    // the cache holds at most B * kv_len tokens; a range must fit 32-bit offsets
+    const long long range = ((long long)B * kv_len + parts - 1) / parts;
+    return range <= plx::max_split_keys(Hkv, D, dtype) ? parts : 0;
 }
 static size_t streamk_bytes(int B, int Hq, int D, int parts) {
     return (size_t)Hq * ((size_t)parts + B - 1) * plx::partial_floats(D) * sizeof(float);
@@ -126,7 +135,7 @@ size_t parallax_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int kv_len
     if (check_decode_sizes(B, Hq, Hkv, D, kv_len, window, dtype) != PLX_OK) return 0;
     const DecodePlan p = plx::plan_decode(B, Hq, Hkv, D, kv_len, window, dtype, num_splits);
     // the same size must also cover a packed cache's stream-K plan
-    const int parts = streamk_parts(p, Hkv, window, num_splits);
+    const int parts = streamk_parts(p, B, Hkv, D, kv_len, dtype, window, num_splits);
     const size_t sk = parts ? streamk_bytes(B, Hq, D, parts) : 0;
     return p.ws_bytes > sk ? p.ws_bytes : sk;
 }
@@ -180,7 +189,7 @@ static int decode_common(const void *q, const void *r, const void *k, const void
                               dtype, num_splits, parallax, p);
     if (st != PLX_OK) return st;
     if (cu) {
-        a.sk_parts = streamk_parts(p, Hkv, window, num_splits);
+        a.sk_parts = streamk_parts(p, B, Hkv, D, kv_len, dtype, window, num_splits);
         if (a.sk_parts) {
             a.fused = false;
             p.ws_bytes = streamk_bytes(B, Hq, D, a.sk_parts);
