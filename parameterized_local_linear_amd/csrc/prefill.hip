@@ -188,7 +188,8 @@ __global__ __launch_bounds__(64) void prefill_generic(PrefillArgs a) {
 //
 // Causality: keys j <= i, and with a sliding window W also j > i - W. Tiles
 // entirely outside a wave's visible band are skipped, tiles crossing either
-// edge of the band are masked. Work items run heaviest-first
+// edge of the band are masked (and their 32-key sub-tiles holding none of the
+// wave's keys skipped). Work items run heaviest-first
 // (last q-tile first), and the group index varies fastest so that all
 // q-tiles of one (sequence, KV head) land on one XCD when the number of
 // groups is a multiple of 8 (its L2 then holds that head's K/V).
