@@ -47,13 +47,13 @@ def _bind(path: str):
     lib = ctypes.CDLL(path)
     vp, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
     lib.oracle_decode.argtypes = [vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, dbl, dbl,
-                                  i64, i64, vp, vp]
+                                  i64, vp, i64, i64, i64, vp, vp]
     lib.oracle_decode.restype = i32
     lib.oracle_prefill.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, dbl, dbl,
-                                   i64, i64, vp, vp, vp, vp]
+                                   i64, vp, i64, i64, vp, vp, vp, vp]
     lib.oracle_prefill.restype = i32
     lib.oracle_prefill_backward.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
-                                            dbl, dbl, i64, i64, vp, vp, vp, vp, vp]
+                                            dbl, dbl, i64, vp, i64, i64, vp, vp, vp, vp, vp]
     lib.oracle_prefill_backward.restype = i32
     return lib
 
@@ -104,8 +104,20 @@ def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
+BLOCK = 128  # block-sparse mask granularity of the GPU library (the oracle takes any)
+
+
+def _mask(block_mask, shape):
+    """A block mask as contiguous uint8 of the given shape (None stays None)."""
+    if block_mask is None:
+        return None
+    m = np.ascontiguousarray(np.asarray(block_mask) != 0, dtype=np.uint8)
+    assert m.shape == tuple(shape), f"block mask shape {m.shape}, expected {tuple(shape)}"
+    return m
+
+
 def decode(q, r, k, v, *, seq_start=None, seq_len=None, Hkv=None, qk_scale=None, rk_scale=1.0,
-           rows=None, window=0):
+           rows=None, window=0, block_mask=None, block=BLOCK):
     """Parallax decode rows.
 
     q, r: [B, Hq, D] (r may be None: r = 0, plain softmax attention).
@@ -113,6 +125,9 @@ def decode(q, r, k, v, *, seq_start=None, seq_len=None, Hkv=None, qk_scale=None,
     ``seq_len`` giving each sequence's token range.
     rows: optional int array [n, 2] of (b, h); default all rows.
     window: W > 0 keeps each sequence's last W keys (0: all).
+    block_mask: optional [B, Hkv, nkb] (nonzero: visible) over key blocks of
+    ``block`` positions, nkb >= ceil(longest sequence / block); the block
+    holding a sequence's last key is always visible.
     Returns float64 [B, Hq, D] (or [n, D] when rows is given).
     """
     dt = _dtype_of(q)
@@ -135,6 +150,11 @@ def decode(q, r, k, v, *, seq_start=None, seq_len=None, Hkv=None, qk_scale=None,
     seq_start = np.ascontiguousarray(seq_start, dtype=np.int64)
     seq_len = np.ascontiguousarray(seq_len, dtype=np.int64)
     tau = 1.0 / math.sqrt(D) if qk_scale is None else float(qk_scale)
+    mcols = 0
+    if block_mask is not None:
+        mcols = np.asarray(block_mask).shape[-1]
+        assert mcols * block >= int(seq_len.max(initial=0))
+        block_mask = _mask(block_mask, (B, Hkv, mcols))
     if rows is not None:
         rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 2)
         out = np.empty((rows.shape[0], D), dtype=np.float64)
@@ -143,19 +163,24 @@ def decode(q, r, k, v, *, seq_start=None, seq_len=None, Hkv=None, qk_scale=None,
         out = np.empty((B, Hq, D), dtype=np.float64)
         n = B * Hq
     rc = _load().oracle_decode(_ptr(q), _ptr(r), _ptr(k), _ptr(v), dt, _ptr(seq_start),
-                               _ptr(seq_len), B, Hq, Hkv, D, tau, float(rk_scale), int(window), n,
-                               _ptr(rows), _ptr(out))
+                               _ptr(seq_len), B, Hq, Hkv, D, tau, float(rk_scale), int(window),
+                               _ptr(block_mask), int(block), int(mcols), n, _ptr(rows),
+                               _ptr(out))
     if rc != 0:
         raise RuntimeError(f"oracle_decode failed ({rc})")
     return out
 
 
-def prefill(q, r, k, v, *, qk_scale=None, rk_scale=1.0, rows=None, stats=False, window=0):
+def prefill(q, r, k, v, *, qk_scale=None, rk_scale=1.0, rows=None, stats=False, window=0,
+            block_mask=None, block=BLOCK):
     """Causal Parallax prefill rows.
 
     q, r: [B, Hq, L, D] (r may be None); k, v: [B, Hkv, L, D].
     rows: optional int array [n, 3] of (b, h, i).
     window: W > 0 limits query i to keys i - W + 1 .. i (0: causal only).
+    block_mask: optional [B, Hkv, nb, nb], nb = ceil(L / block): entry
+    [qb, kb] (nonzero: visible) lets query block qb see key block kb; the
+    diagonal block is always visible.
     Returns o float64 [B, Hq, L, D] (or [n, D]); with stats=True also lse and sbar.
     """
     dt = _dtype_of(q)
@@ -165,6 +190,8 @@ def prefill(q, r, k, v, *, qk_scale=None, rk_scale=1.0, rows=None, stats=False, 
     B, Hq, L, D = q.shape
     Hkv = k.shape[1]
     tau = 1.0 / math.sqrt(D) if qk_scale is None else float(qk_scale)
+    nb = -(-L // block)
+    block_mask = _mask(block_mask, (B, Hkv, nb, nb))
     if rows is not None:
         rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 3)
         n = rows.shape[0]
@@ -177,19 +204,21 @@ def prefill(q, r, k, v, *, qk_scale=None, rk_scale=1.0, rows=None, stats=False, 
         lse = np.empty((B, Hq, L), dtype=np.float64)
         sbar = np.empty((B, Hq, L), dtype=np.float64)
     rc = _load().oracle_prefill(_ptr(q), _ptr(r), _ptr(k), _ptr(v), dt, B, Hq, Hkv, L, D, tau,
-                                float(rk_scale), int(window), n, _ptr(rows), _ptr(out), _ptr(lse),
-                                _ptr(sbar))
+                                float(rk_scale), int(window), _ptr(block_mask), int(block), n,
+                                _ptr(rows), _ptr(out), _ptr(lse), _ptr(sbar))
     if rc != 0:
         raise RuntimeError(f"oracle_prefill failed ({rc})")
     return (out, lse, sbar) if stats else out
 
 
-def prefill_backward(q, r, k, v, do, *, qk_scale=None, rk_scale=1.0, units=None, window=0):
+def prefill_backward(q, r, k, v, do, *, qk_scale=None, rk_scale=1.0, units=None, window=0,
+                     block_mask=None, block=BLOCK):
     """Gradients of the causal Parallax prefill for the upstream gradient ``do``.
 
     q, r, do: [B, Hq, L, D] (r may be None: r = 0); k, v: [B, Hkv, L, D].
     units: optional int array [n, 2] of (b, hkv): only the query heads reading
     those KV heads (and those KV heads' keys) are differentiated.
+    window, block_mask, block: as in prefill.
     Returns float64 (dq, dr, dk, dv): [B, Hq, L, D] and [B, Hkv, L, D], or with
     ``units`` [n, g, L, D] and [n, L, D].
     """
@@ -201,6 +230,8 @@ def prefill_backward(q, r, k, v, do, *, qk_scale=None, rk_scale=1.0, units=None,
     Hkv = k.shape[1]
     g = Hq // Hkv
     tau = 1.0 / math.sqrt(D) if qk_scale is None else float(qk_scale)
+    nb = -(-L // block)
+    block_mask = _mask(block_mask, (B, Hkv, nb, nb))
     if units is not None:
         units = np.ascontiguousarray(units, dtype=np.int64).reshape(-1, 2)
         n = units.shape[0]
@@ -211,8 +242,9 @@ def prefill_backward(q, r, k, v, do, *, qk_scale=None, rk_scale=1.0, units=None,
     dk = np.empty((n, L, D), dtype=np.float64)
     dv = np.empty((n, L, D), dtype=np.float64)
     rc = _load().oracle_prefill_backward(_ptr(q), _ptr(r), _ptr(k), _ptr(v), _ptr(do), dt, B, Hq,
-                                         Hkv, L, D, tau, float(rk_scale), int(window), n,
-                                         _ptr(units), _ptr(dq), _ptr(dr), _ptr(dk), _ptr(dv))
+                                         Hkv, L, D, tau, float(rk_scale), int(window),
+                                         _ptr(block_mask), int(block), n, _ptr(units), _ptr(dq),
+                                         _ptr(dr), _ptr(dk), _ptr(dv))
     if rc != 0:
         raise RuntimeError(f"oracle_prefill_backward failed ({rc})")
     if units is None:
@@ -226,22 +258,34 @@ def _seq_dense(x, s0, s1):
     return np.ascontiguousarray(x[s0:s1].transpose(1, 0, 2)[None])
 
 
+def _seq_mask(block_mask, b, n, block):
+    """Sequence b's block mask for length n, from a [B, Hkv, nb, nb] mask over
+    the longest sequence (None stays None)."""
+    if block_mask is None:
+        return None
+    nb = -(-n // block)
+    return np.ascontiguousarray(np.asarray(block_mask)[b:b + 1, :, :nb, :nb])
+
+
 def prefill_varlen(q, r, k, v, cu_seqlens, *, qk_scale=None, rk_scale=1.0, window=0,
-                   stats=False):
+                   stats=False, block_mask=None, block=BLOCK):
     """Causal prefill of packed sequences (the pages' parallax_varlen_func): q, r
     [T, Hq, D], k, v [T, Hkv, D], sequence b = tokens cu[b] .. cu[b+1] - 1.
     Each sequence is an independent causal prefill (the dense oracle on its
-    slice). Returns o [T, Hq, D] (and lse, sbar [T, Hq] with stats=True)."""
+    slice). block_mask: optional [B, Hkv, nb, nb] over sequence-local blocks,
+    nb = ceil(longest length / block). Returns o [T, Hq, D] (and lse, sbar
+    [T, Hq] with stats=True)."""
     T, Hq, D = q.shape
     o = np.zeros((T, Hq, D), dtype=np.float64)
     lse = np.zeros((T, Hq), dtype=np.float64)
     sbar = np.zeros((T, Hq), dtype=np.float64)
-    for s0, s1 in zip(cu_seqlens[:-1], cu_seqlens[1:]):
+    for b, (s0, s1) in enumerate(zip(cu_seqlens[:-1], cu_seqlens[1:])):
         if s1 <= s0:
             continue
         res = prefill(_seq_dense(q, s0, s1), None if r is None else _seq_dense(r, s0, s1),
                       _seq_dense(k, s0, s1), _seq_dense(v, s0, s1), qk_scale=qk_scale,
-                      rk_scale=rk_scale, window=window, stats=True)
+                      rk_scale=rk_scale, window=window, stats=True,
+                      block_mask=_seq_mask(block_mask, b, s1 - s0, block), block=block)
         o[s0:s1] = res[0][0].transpose(1, 0, 2)
         lse[s0:s1] = res[1][0].T
         sbar[s0:s1] = res[2][0].T
@@ -249,19 +293,20 @@ def prefill_varlen(q, r, k, v, cu_seqlens, *, qk_scale=None, rk_scale=1.0, windo
 
 
 def prefill_varlen_backward(q, r, k, v, do, cu_seqlens, *, qk_scale=None, rk_scale=1.0,
-                            window=0):
+                            window=0, block_mask=None, block=BLOCK):
     """Gradients of prefill_varlen: (dq, dr [T, Hq, D], dk, dv [T, Hkv, D])."""
     T, Hq, D = q.shape
     Hkv = k.shape[1]
     dq = np.zeros((T, Hq, D)); dr = np.zeros((T, Hq, D))
     dk = np.zeros((T, Hkv, D)); dv = np.zeros((T, Hkv, D))
-    for s0, s1 in zip(cu_seqlens[:-1], cu_seqlens[1:]):
+    for b, (s0, s1) in enumerate(zip(cu_seqlens[:-1], cu_seqlens[1:])):
         if s1 <= s0:
             continue
         g = prefill_backward(_seq_dense(q, s0, s1), None if r is None else _seq_dense(r, s0, s1),
                              _seq_dense(k, s0, s1), _seq_dense(v, s0, s1),
                              _seq_dense(do, s0, s1), qk_scale=qk_scale, rk_scale=rk_scale,
-                             window=window)
+                             window=window, block_mask=_seq_mask(block_mask, b, s1 - s0, block),
+                             block=block)
         dq[s0:s1] = g[0][0].transpose(1, 0, 2)
         dr[s0:s1] = g[1][0].transpose(1, 0, 2)
         dk[s0:s1] = g[2][0].transpose(1, 0, 2)

@@ -36,6 +36,14 @@
  * a prefill query i sees keys max(0, i - W + 1) .. i (itself and the W - 1
  * before it), and a decode query of a sequence of n cached keys sees its last
  * min(n, W) keys. W = 0 means no window.
+ *
+ * Block-sparse masks (the same overview calls block sparsity structurally
+ * compatible and defines none): keys and prefill queries are cut into blocks
+ * of `block` positions from the start of their sequence; a byte mask per
+ * (sequence, KV head) marks which key blocks a query block sees, on top of
+ * causality and the window. A query always sees its own block (prefill: the
+ * diagonal block; decode: the block holding the sequence's last key), so no
+ * row is left without keys.
  */
 #include <math.h>
 #include <omp.h>
@@ -61,13 +69,14 @@ static double elem(const void *p, int dtype, size_t i)
 
 /*
  * One output row. q/r at element offsets q_off/r_off (r may be NULL: r = 0).
- * Key/value j (0 <= j < n) starts at element kv_off + j * kv_stride.
+ * The n visible keys are positions keys[0 .. n-1] (keys == NULL: 0 .. n-1);
+ * key/value at position p starts at element kv_off + p * kv_stride.
  * z and s are caller scratch of n doubles each.
  */
 static void one_row(const void *q, size_t q_off, const void *r, size_t r_off,
-                    const void *k, const void *v, size_t kv_off, size_t kv_stride, int64_t n,
-                    int D, int dtype, double tau, double rho, double *o, double *lse,
-                    double *sbar, double *z, double *s)
+                    const void *k, const void *v, size_t kv_off, size_t kv_stride,
+                    const int64_t *keys, int64_t n, int D, int dtype, double tau, double rho,
+                    double *o, double *lse, double *sbar, double *z, double *s)
 {
     if (n <= 0) {
         for (int d = 0; d < D; ++d)
@@ -80,7 +89,7 @@ static void one_row(const void *q, size_t q_off, const void *r, size_t r_off,
     }
     /* logits and probe scores */
     for (int64_t j = 0; j < n; ++j) {
-        size_t kb = kv_off + (size_t)j * kv_stride;
+        size_t kb = kv_off + (size_t)(keys ? keys[j] : j) * kv_stride;
         double zq = 0.0, sr = 0.0;
         for (int d = 0; d < D; ++d) {
             double kd = elem(k, dtype, kb + d);
@@ -111,7 +120,7 @@ static void one_row(const void *q, size_t q_off, const void *r, size_t r_off,
     for (int d = 0; d < D; ++d)
         o[d] = 0.0;
     for (int64_t j = 0; j < n; ++j) {
-        size_t vb = kv_off + (size_t)j * kv_stride;
+        size_t vb = kv_off + (size_t)(keys ? keys[j] : j) * kv_stride;
         double wj = z[j];
         double cj = z[j] * (s[j] - sb);
         for (int d = 0; d < D; ++d) {
@@ -131,11 +140,18 @@ static void one_row(const void *q, size_t q_off, const void *r, size_t r_off,
  * has seq_start[b] = b * L). rows: n_rows (b, h) pairs, or NULL for all
  * B * Hq rows in order. o: [n_rows, D].
  */
+/*
+ * block_mask: NULL, or bytes [B, Hkv, mask_cols]; byte kb (nonzero: visible)
+ * covers key positions kb * block .. kb * block + block - 1 of the sequence.
+ */
 int oracle_decode(const void *q, const void *r, const void *k, const void *v, int dtype,
                   const int64_t *seq_start, const int64_t *seq_len, int B, int Hq, int Hkv, int D,
-                  double tau, double rho, int64_t window, int64_t n_rows, const int64_t *rows,
+                  double tau, double rho, int64_t window, const uint8_t *block_mask,
+                  int64_t block, int64_t mask_cols, int64_t n_rows, const int64_t *rows,
                   double *o)
 {
+    if (block_mask && block <= 0)
+        return 1;
     if (Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || B <= 0)
         return 1;
     int g = Hq / Hkv;
@@ -149,7 +165,8 @@ int oracle_decode(const void *q, const void *r, const void *k, const void *v, in
     {
         double *z = (double *)malloc(sizeof(double) * (size_t)(nmax > 0 ? nmax : 1));
         double *s = (double *)malloc(sizeof(double) * (size_t)(nmax > 0 ? nmax : 1));
-        if (!z || !s) {
+        int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)(nmax > 0 ? nmax : 1));
+        if (!z || !s || !keys) {
 #pragma omp atomic write
             bad = 1;
         } else {
@@ -159,18 +176,28 @@ int oracle_decode(const void *q, const void *r, const void *k, const void *v, in
                 int64_t h = rows ? rows[2 * t + 1] : t % Hq;
                 int64_t hk = h / g;
                 size_t qo = ((size_t)b * Hq + (size_t)h) * (size_t)D;
-                int64_t n = seq_len[b], first = 0; /* visible keys: the last min(n, W) */
-                if (window > 0 && n > window) {
-                    first = n - window;
-                    n = window;
+                int64_t len = seq_len[b], first = 0; /* window: the last min(len, W) */
+                if (window > 0 && len > window)
+                    first = len - window;
+                size_t kvo = ((size_t)seq_start[b] * Hkv + (size_t)hk) * (size_t)D;
+                /* visible positions: first .. len - 1, minus masked blocks
+                   other than the one holding the last key */
+                int64_t n = 0;
+                for (int64_t p = first; p < len; ++p) {
+                    int vis = 1;
+                    if (block_mask && p / block != (len - 1) / block)
+                        vis = block_mask[((size_t)b * Hkv + (size_t)hk) * (size_t)mask_cols +
+                                         (size_t)(p / block)] != 0;
+                    if (vis)
+                        keys[n++] = p;
                 }
-                size_t kvo = ((size_t)(seq_start[b] + first) * Hkv + (size_t)hk) * (size_t)D;
-                one_row(q, qo, r, qo, k, v, kvo, (size_t)Hkv * D, n, D, dtype, tau, rho,
+                one_row(q, qo, r, qo, k, v, kvo, (size_t)Hkv * D, keys, n, D, dtype, tau, rho,
                         o + (size_t)t * D, NULL, NULL, z, s);
             }
         }
         free(z);
         free(s);
+        free(keys);
     }
     return bad ? 2 : 0;
 }
@@ -179,13 +206,30 @@ int oracle_decode(const void *q, const void *r, const void *k, const void *v, in
  * Causal prefill: q, r [B, Hq, L, D]; K, V [B, Hkv, L, D]. rows: n_rows
  * (b, h, i) triples, or NULL for all B * Hq * L rows in order.
  * o: [n_rows, D]; lse, sbar: [n_rows] or NULL.
+ * block_mask: NULL, or bytes [B, Hkv, nb, nb], nb = ceil(L / block); byte
+ * [qb][kb] (nonzero: visible) lets query block qb see key block kb.
  */
+
+/* Visible key positions of prefill row i (of KV head unit mask row `mrow`,
+   nb blocks per side, or mrow == NULL for no mask) into keys; returns the count. */
+static int64_t prefill_keys(int64_t i, int64_t window, const uint8_t *mrow, int64_t block,
+                            int64_t nb, int64_t *keys)
+{
+    int64_t first = (window > 0 && i + 1 > window) ? i + 1 - window : 0, n = 0;
+    for (int64_t p = first; p <= i; ++p)
+        if (!mrow || p / block == i / block || mrow[(size_t)(i / block) * nb + p / block])
+            keys[n++] = p;
+    return n;
+}
+
 int oracle_prefill(const void *q, const void *r, const void *k, const void *v, int dtype, int B,
                    int Hq, int Hkv, int L, int D, double tau, double rho, int64_t window,
-                   int64_t n_rows, const int64_t *rows, double *o, double *lse, double *sbar)
+                   const uint8_t *block_mask, int64_t block, int64_t n_rows, const int64_t *rows,
+                   double *o, double *lse, double *sbar)
 {
-    if (Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || B <= 0 || L <= 0)
+    if (Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || B <= 0 || L <= 0 || (block_mask && block <= 0))
         return 1;
+    int64_t nb = block_mask ? (L + block - 1) / block : 0;
     int g = Hq / Hkv;
     int64_t total = rows ? n_rows : (int64_t)B * Hq * L;
     int bad = 0;
@@ -193,7 +237,8 @@ int oracle_prefill(const void *q, const void *r, const void *k, const void *v, i
     {
         double *z = (double *)malloc(sizeof(double) * (size_t)L);
         double *s = (double *)malloc(sizeof(double) * (size_t)L);
-        if (!z || !s) {
+        int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)L);
+        if (!z || !s || !keys) {
 #pragma omp atomic write
             bad = 1;
         } else {
@@ -211,15 +256,18 @@ int oracle_prefill(const void *q, const void *r, const void *k, const void *v, i
                 }
                 int64_t hk = h / g;
                 size_t qo = (((size_t)b * Hq + (size_t)h) * (size_t)L + (size_t)i) * (size_t)D;
-                int64_t first = (window > 0 && i + 1 > window) ? i + 1 - window : 0;
-                size_t kvo = (((size_t)b * Hkv + (size_t)hk) * (size_t)L + (size_t)first) *
-                             (size_t)D;
-                one_row(q, qo, r, qo, k, v, kvo, (size_t)D, i + 1 - first, D, dtype, tau, rho,
+                size_t kvo = ((size_t)b * Hkv + (size_t)hk) * (size_t)L * (size_t)D;
+                const uint8_t *mrow =
+                    block_mask ? block_mask + ((size_t)b * Hkv + (size_t)hk) * (size_t)(nb * nb)
+                               : NULL;
+                int64_t n = prefill_keys(i, window, mrow, block, nb, keys);
+                one_row(q, qo, r, qo, k, v, kvo, (size_t)D, keys, n, D, dtype, tau, rho,
                         o + (size_t)t * D, lse ? lse + t : NULL, sbar ? sbar + t : NULL, z, s);
             }
         }
         free(z);
         free(s);
+        free(keys);
     }
     return bad ? 2 : 0;
 }
@@ -243,13 +291,14 @@ int oracle_prefill(const void *q, const void *r, const void *k, const void *v, i
  * (r = 0); dr is still the gradient at r = 0.
  */
 static void row_backward(const void *q, const void *r, const void *k, const void *v,
-                         const void *go, size_t q_off, size_t kv_off, int64_t n, int D, int dtype,
-                         double tau, double rho, double *dq, double *dr, double *dk, double *dv,
-                         double *w, double *s, double *aw, double *as)
+                         const void *go, size_t q_off, size_t kv_off, const int64_t *keys,
+                         int64_t n, int D, int dtype, double tau, double rho, double *dq,
+                         double *dr, double *dk, double *dv, double *w, double *s, double *aw,
+                         double *as)
 {
     /* forward steps: logits, probe scores, softmax, probe mean */
     for (int64_t j = 0; j < n; ++j) {
-        size_t kb = kv_off + (size_t)j * D;
+        size_t kb = kv_off + (size_t)keys[j] * D;
         double zq = 0.0, sr = 0.0;
         for (int d = 0; d < D; ++d) {
             double kd = elem(k, dtype, kb + d);
@@ -278,7 +327,7 @@ static void row_backward(const void *q, const void *r, const void *k, const void
     /* reverse of o = sum_j w_j v_j + sum_j w_j (s_j - sbar) v_j */
     double a_sb = 0.0;
     for (int64_t j = 0; j < n; ++j) {
-        size_t vb = kv_off + (size_t)j * D;
+        size_t vb = kv_off + (size_t)keys[j] * D;
         double t = 0.0;
         for (int d = 0; d < D; ++d)
             t += elem(go, dtype, q_off + d) * elem(v, dtype, vb + d);
@@ -287,7 +336,7 @@ static void row_backward(const void *q, const void *r, const void *k, const void
         a_sb -= w[j] * t;
         double cv = w[j] * (1.0 + s[j] - sb);
         for (int d = 0; d < D; ++d)
-            dv[(size_t)j * D + d] += cv * elem(go, dtype, q_off + d);
+            dv[(size_t)keys[j] * D + d] += cv * elem(go, dtype, q_off + d);
     }
     /* reverse of sbar = sum_j w_j s_j */
     for (int64_t j = 0; j < n; ++j) {
@@ -302,13 +351,13 @@ static void row_backward(const void *q, const void *r, const void *k, const void
         aw[j] = w[j] * (aw[j] - waw);
     /* reverse of s_j = rho r.k_j and z_j = tau q.k_j */
     for (int64_t j = 0; j < n; ++j) {
-        size_t kb = kv_off + (size_t)j * D;
+        size_t kb = kv_off + (size_t)keys[j] * D;
         double cz = tau * aw[j], cs = rho * as[j];
         for (int d = 0; d < D; ++d) {
             double kd = elem(k, dtype, kb + d);
             dq[d] += cz * kd;
             dr[d] += cs * kd;
-            dk[(size_t)j * D + d] += cz * elem(q, dtype, q_off + d) +
+            dk[(size_t)keys[j] * D + d] += cz * elem(q, dtype, q_off + d) +
                                      (r ? cs * elem(r, dtype, q_off + d) : 0.0);
         }
     }
@@ -316,11 +365,13 @@ static void row_backward(const void *q, const void *r, const void *k, const void
 
 int oracle_prefill_backward(const void *q, const void *r, const void *k, const void *v,
                             const void *go, int dtype, int B, int Hq, int Hkv, int L, int D,
-                            double tau, double rho, int64_t window, int64_t n_units,
-                            const int64_t *units, double *dq, double *dr, double *dk, double *dv)
+                            double tau, double rho, int64_t window, const uint8_t *block_mask,
+                            int64_t block, int64_t n_units, const int64_t *units, double *dq,
+                            double *dr, double *dk, double *dv)
 {
-    if (Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || B <= 0 || L <= 0)
+    if (Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || B <= 0 || L <= 0 || (block_mask && block <= 0))
         return 1;
+    int64_t nb = block_mask ? (L + block - 1) / block : 0;
     int g = Hq / Hkv;
     int64_t total = units ? n_units : (int64_t)B * Hkv;
     size_t LD = (size_t)L * D;
@@ -333,13 +384,16 @@ int oracle_prefill_backward(const void *q, const void *r, const void *k, const v
         memset(dk_u, 0, sizeof(double) * LD);
         memset(dv_u, 0, sizeof(double) * LD);
         int64_t nrows = (int64_t)g * L;
+        const uint8_t *mrow =
+            block_mask ? block_mask + ((size_t)b * Hkv + (size_t)hk) * (size_t)(nb * nb) : NULL;
 #pragma omp parallel
         {
             /* per-thread key-gradient sums, added into the unit in thread order */
             double *dk_t = (double *)calloc(LD, sizeof(double));
             double *dv_t = (double *)calloc(LD, sizeof(double));
             double *scr = (double *)malloc(sizeof(double) * 4 * (size_t)L);
-            if (!dk_t || !dv_t || !scr) {
+            int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)L);
+            if (!dk_t || !dv_t || !scr || !keys) {
 #pragma omp atomic write
                 bad = 1;
             } else {
@@ -353,11 +407,10 @@ int oracle_prefill_backward(const void *q, const void *r, const void *k, const v
                         dq[ro + d] = 0.0;
                         dr[ro + d] = 0.0;
                     }
-                    int64_t first = (window > 0 && i + 1 > window) ? i + 1 - window : 0;
-                    size_t fo = (size_t)first * D;
-                    row_backward(q, r, k, v, go, qo, kvo + fo, i + 1 - first, D, dtype, tau, rho,
-                                 dq + ro, dr + ro, dk_t + fo, dv_t + fo, scr, scr + L,
-                                 scr + 2 * (size_t)L, scr + 3 * (size_t)L);
+                    int64_t n = prefill_keys(i, window, mrow, block, nb, keys);
+                    row_backward(q, r, k, v, go, qo, kvo, keys, n, D, dtype, tau, rho, dq + ro,
+                                 dr + ro, dk_t, dv_t, scr, scr + L, scr + 2 * (size_t)L,
+                                 scr + 3 * (size_t)L);
                 }
 #pragma omp for ordered schedule(static, 1)
                 for (int th = 0; th < omp_get_num_threads(); ++th) {
@@ -371,6 +424,7 @@ int oracle_prefill_backward(const void *q, const void *r, const void *k, const v
             free(dk_t);
             free(dv_t);
             free(scr);
+            free(keys);
         }
     }
     return bad ? 2 : 0;

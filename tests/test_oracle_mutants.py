@@ -29,7 +29,7 @@ MUTANTS = {
                   "int64_t hk = h % Hkv;\n                size_t qo = ((size_t)b"),
     "prefill gqa index": ("int64_t hk = h / g;\n                size_t qo = (((size_t)b",
                           "int64_t hk = h % Hkv;\n                size_t qo = (((size_t)b"),
-    "causal off by one": ("(size_t)D, i + 1 - first, D, dtype", "(size_t)D, i - first, D, dtype"),
+    "causal off by one": ("for (int64_t p = first; p <= i; ++p)", "for (int64_t p = first; p < i; ++p)"),
     "logit scale dropped": ("z[j] = tau * zq;", "z[j] = zq;"),
     "keys and values swapped": (
         "double kd = elem(k, dtype, kb + d);\n            zq += elem(q, dtype, q_off + d) * kd;"
@@ -38,16 +38,23 @@ MUTANTS = {
         "\n            if (r)\n                sr += elem(r, dtype, r_off"),
     "sample covariance": ("z[j] /= l;", "z[j] /= (l - z[j] / l * 0.5);"),
     "prefill window off by one": (
-        "int64_t first = (window > 0 && i + 1 > window) ? i + 1 - window : 0;\n                size_t kvo",
-        "int64_t first = (window > 0 && i + 1 > window) ? i - window : 0;\n                size_t kvo"),
-    "decode window keeps the first keys": ("first = n - window;", "first = 0;"),
+        "int64_t first = (window > 0 && i + 1 > window) ? i + 1 - window : 0, n = 0;",
+        "int64_t first = (window > 0 && i + 1 > window) ? i - window : 0, n = 0;"),
+    "decode window keeps the first keys": ("first = len - window;", "first = 0;"),
+    "block mask diagonal not forced": ("if (!mrow || p / block == i / block || mrow[",
+                                       "if (!mrow || mrow["),
+    "block mask transposed": ("mrow[(size_t)(i / block) * nb + p / block]",
+                              "mrow[(size_t)(p / block) * nb + i / block]"),
+    "decode mask drops the last-block rule": ("if (block_mask && p / block != (len - 1) / block)",
+                                              "if (block_mask)"),
+    "decode mask ignored": ("(size_t)(p / block)] != 0;", "(size_t)(p / block)] != 2;"),
 }
 
 # mistakes in the reverse pass (the forward code is untouched)
 BACKWARD_MUTANTS = {
     "bwd sbar adjoint dropped": ("a_sb -= w[j] * t;", "a_sb -= 0.0 * t;"),
     "bwd softmax jacobian sign": ("aw[j] = w[j] * (aw[j] - waw);", "aw[j] = w[j] * (aw[j] + waw);"),
-    "bwd causal off by one": ("kvo + fo, i + 1 - first, D", "kvo + fo, i - first, D"),
+    "bwd causal off by one": ("qo, kvo, keys, n, D, dtype", "qo, kvo, keys, n - 1, D, dtype"),
     "bwd probe adjoint uses q": ("cs * elem(r, dtype, q_off + d)", "cs * elem(q, dtype, q_off + d)"),
     "bwd dv without correction": ("double cv = w[j] * (1.0 + s[j] - sb);", "double cv = w[j];"),
     "bwd dq misses tau": ("double cz = tau * aw[j], cs", "double cz = aw[j], cs"),
@@ -99,6 +106,28 @@ def independent_checks_pass():
     vd = np.ascontiguousarray(V.transpose(0, 2, 1, 3))
     ok &= np.abs(oracle.decode(np.ascontiguousarray(Q[:, :, 18]), None, kd, vd, window=4)
                  - refw[:, :, 18]).max() < 1e-12
+    # block-sparse masks (blocks of 4 positions) against SDPA with the element mask
+    bm = g.random((1, 2, 5, 5)) < 0.5
+    bm[0, 0, 2, 2] = bm[0, 1, 4, 4] = False  # diagonal entries must not matter
+    qb, kb = i // 4, j // 4
+    em = np.stack([(j <= i) & ((qb == kb) | bm[0, h // 2][qb, kb]) for h in range(4)])[None]
+    refb = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(Q), torch.from_numpy(K), torch.from_numpy(V),
+        attn_mask=torch.from_numpy(em), enable_gqa=True).numpy()
+    ok &= np.abs(oracle.prefill(Q, None, K, V, block_mask=bm, block=4) - refb).max() < 1e-12
+    dm = g.random((2, 2, 6)) < 0.5
+    dm[0, 0, 5] = dm[1, 1, 5] = False  # the block holding the last key is always visible
+    dm[1, 0, :5] = False
+    jj = np.arange(23)
+    em_d = np.stack([np.stack([(jj // 4 == 5) | dm[b, h // 2][jj // 4] for h in range(4)])
+                     for b in range(2)])[:, :, None]
+    refd = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[:, :, None], torch.from_numpy(np.ascontiguousarray(
+            k.transpose(0, 2, 1, 3))), torch.from_numpy(np.ascontiguousarray(
+                v.transpose(0, 2, 1, 3))), attn_mask=torch.from_numpy(em_d), scale=tau,
+        enable_gqa=True)[:, :, 0].numpy()
+    ok &= np.abs(oracle.decode(q, None, k, v, qk_scale=tau, block_mask=dm, block=4) - refd).max() \
+        < 1e-12
     # correction = weighted covariance
     L, D = 30, 5
     q1, r1 = g.standard_normal((1, 1, D)), g.standard_normal((1, 1, D))
