@@ -55,6 +55,10 @@ def parse():
     ap.add_argument("--num-splits", type=int, default=0, help="0: library plan")
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window (keys a query sees); 0: none")
+    ap.add_argument("--block-density", type=float, default=0.0,
+                    help="> 0: a seeded block-sparse mask (128-position blocks, one per "
+                         "sequence and KV head) with this fraction of blocks visible (decode, "
+                         "prefill and backward workloads; no window)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the CPU oracle sample")
@@ -89,6 +93,32 @@ def visible_pairs(L, W):
     if W <= 0 or W >= L:
         return L * (L + 1) // 2
     return W * (W + 1) // 2 + (L - W) * W
+
+
+MASK_SEED = 4242
+MASK_BLOCK = 128
+
+
+def prefill_mask(synth, B, Hkv, L, density):
+    """The seeded prefill block mask [B, Hkv, nb, nb], or None."""
+    if density <= 0:
+        return None
+    nb = -(-L // MASK_BLOCK)
+    return synth.block_mask(MASK_SEED, (B, Hkv, nb, nb), density)
+
+
+def masked_pairs(m, L):
+    """Visible (query, key) pairs of one query head per (sequence, KV head), summed:
+    causal pairs inside each diagonal block, whole 128 x 128 blocks below it where
+    the mask shows them."""
+    nb = m.shape[-1]
+    total = 0
+    for qb in range(nb):
+        rows = min(L, (qb + 1) * MASK_BLOCK) - qb * MASK_BLOCK
+        diag = rows * (rows + 1) // 2
+        below = int(m[:, :, qb, :qb].sum()) * rows * MASK_BLOCK
+        total += diag * m.shape[0] * m.shape[1] + below
+    return total
 
 
 def graph_time(torch, fn, steps, warmup):
@@ -211,7 +241,13 @@ def run_decode_workload(args, torch, plx, synth, oracle):
     out_s = torch.empty_like(out)
     recs = torch.empty((spec.B, spec.Hq, splits, 2 * spec.D + 4), dtype=torch.float32,
                        device="cuda")
-    kw = dict(cu_seqlens_k=cu_t, kv_len=spec.L, num_splits=ns, window=W)
+    mask = None
+    if args.block_density > 0:
+        assert W == 0, "block masks are benchmarked without a window"
+        mask = synth.block_mask(MASK_SEED, (spec.B, spec.Hkv, -(-spec.L // MASK_BLOCK)),
+                                args.block_density)
+    kw = dict(cu_seqlens_k=cu_t, kv_len=spec.L, num_splits=ns, window=W,
+              block_mask=None if mask is None else torch.from_numpy(mask).cuda())
 
     def step(i):
         c = i % copies
@@ -237,6 +273,18 @@ def run_decode_workload(args, torch, plx, synth, oracle):
     # algorithmic bytes: K + V over the visible keys, plus q, r and o
     T_vis = int(np.minimum(lens, W).sum()) if W > 0 else T
     kv_vis = kv_bytes * T_vis // T
+    if mask is not None:
+        # per (sequence, KV head): the visible blocks' keys (the last key's block always)
+        head_keys = 0
+        for b in range(spec.B):
+            n = int(lens[b])
+            if n == 0:
+                continue
+            nb_b = -(-n // MASK_BLOCK)
+            last = n - (nb_b - 1) * MASK_BLOCK
+            head_keys += spec.Hkv * last + int(mask[b, :, :nb_b - 1].sum()) * MASK_BLOCK
+        T_vis = head_keys / spec.Hkv  # key rows of all heads, in units of tokens
+        kv_vis = int(head_keys * 2 * spec.D * 2)
     qr_bytes = 2 * q.numel() * 2
     o_bytes = out.numel() * 2
     step_bytes = kv_vis + qr_bytes + o_bytes
@@ -255,9 +303,11 @@ def run_decode_workload(args, torch, plx, synth, oracle):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": spec.name + (f" window{W}" if W > 0 else ""), "B": spec.B,
-                   "Hq": spec.Hq, "Hkv": spec.Hkv, "head_dim": spec.D, "kv_len": spec.L,
-                   "total_kv_tokens": T, "visible_kv_tokens": T_vis, "window": W,
+        "config": {"workload": spec.name + (f" window{W}" if W > 0 else "")
+                   + (f" block-density{args.block_density}" if mask is not None else ""),
+                   "B": spec.B, "Hq": spec.Hq, "Hkv": spec.Hkv, "head_dim": spec.D,
+                   "kv_len": spec.L, "total_kv_tokens": T, "visible_kv_tokens": T_vis,
+                   "window": W, "block_density": args.block_density,
                    "kv_cache_copies": copies, "splits": splits},
         "hbm_tb_s": round(step_bytes / t_step / 1e12, 4),
         "hbm_frac_of_8tbs": round(step_bytes / t_step / 1e9 / HBM_PEAK_GBS, 4),
@@ -269,11 +319,12 @@ def run_decode_workload(args, torch, plx, synth, oracle):
                      "decode_mfma_bf16_d128 (streaming, split records)",
                      "achieved": round(kern_bytes / t_kern / 1e9, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(kern_bytes / t_kern / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(spec.name, splits) if W == 0 else None,
+                     "traffic": measured_traffic(spec.name, splits)
+                     if W == 0 and mask is None else None,
                      "avg_us": round(t_kern * 1e6, 3),
                      "bytes_per_launch": kern_bytes},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and mask is None:
         if varlen or spec.B > 64:
             # bounded sample: the first sequences, regenerated from the same streams
             nb = 4 if spec.B > 64 else 8
@@ -315,7 +366,9 @@ def run_decode_workload(args, torch, plx, synth, oracle):
         k_h = synth.decode_kv_rows(spec, synth.TID_K, int(cu[b]), toks)[None]
         v_h = synth.decode_kv_rows(spec, synth.TID_V, int(cu[b]), toks)[None]
         ref = oracle.decode(np.ascontiguousarray(q_np[b:b + 1]), np.ascontiguousarray(r_np[b:b + 1]),
-                            k_h, v_h, window=W)[0, h]
+                            k_h, v_h, window=W,
+                            block_mask=None if mask is None else mask[b:b + 1, :,
+                                                                      :-(-toks // MASK_BLOCK)])[0, h]
         errs.append(float(np.abs(o_full[b, h] - ref).max() / np.abs(ref).max()))
     res["sampled_parity_max_norm_err"] = max(errs)
     return res
@@ -333,21 +386,27 @@ def run_prefill_workload(args, torch, plx, synth, oracle):
     out = torch.empty_like(t["q"])
 
     W = args.window
+    mask = prefill_mask(synth, B, Hkv, L, args.block_density)
+    assert mask is None or W == 0, "block masks are benchmarked without a window"
+    mask_t = None if mask is None else torch.from_numpy(mask).cuda()
 
     def step(i):
-        plx.prefill(t["q"], t["r"], t["k"], t["v"], out=out, window=W)
+        plx.prefill(t["q"], t["r"], t["k"], t["v"], out=out, window=W, block_mask=mask_t)
 
     steps = max(1, min(args.steps, 20))
     warm = max(1, min(args.warmup, 3))
     ts = graph_time(torch, step, steps, warm)
-    flops = 8 * D * Hq * B * visible_pairs(L, W)
+    pairs = B * visible_pairs(L, W) if mask is None else masked_pairs(mask, L)
+    flops = 8 * D * Hq * pairs if mask is None else 8 * D * (Hq // Hkv) * pairs
     res = {
         "metric": METRIC, "value": round(flops / ts / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": steps, "warmup": warm, "ms_per_step": round(ts * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": spec.name + (f" window{W}" if W > 0 else ""), "B": B, "Hq": Hq,
-                   "Hkv": Hkv, "L": L, "head_dim": D, "window": W},
+        "config": {"workload": spec.name + (f" window{W}" if W > 0 else "")
+                   + (f" block-density{args.block_density}" if mask is not None else ""),
+                   "B": B, "Hq": Hq, "Hkv": Hkv, "L": L, "head_dim": D, "window": W,
+                   "block_density": args.block_density},
         "roofline": {"bound": "mfma", "kernel": "prefill", "achieved": round(flops / ts / 1e12, 2),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(flops / ts / 1e12 / BF16_PEAK_TFLOPS, 4), "traffic": None,
@@ -355,11 +414,12 @@ def run_prefill_workload(args, torch, plx, synth, oracle):
     }
     rows = np.array([[0, 0, 0], [B - 1, Hq - 1, L - 1], [3, 5, 1000], [7, 8, 2047]])
     o = out.float().cpu().numpy()
-    ref = oracle.prefill(arrs["q"], arrs["r"], arrs["k"], arrs["v"], rows=rows, window=W)
+    ref = oracle.prefill(arrs["q"], arrs["r"], arrs["k"], arrs["v"], rows=rows, window=W,
+                         block_mask=mask)
     got = o[rows[:, 0], rows[:, 1], rows[:, 2]]
     res["sampled_parity_max_norm_err"] = float(
         (np.abs(got - ref).max(axis=1) / np.abs(ref).max(axis=1)).max())  # worst row
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and mask is None:
         # bounded sample: rows spread over the causal range, scaled by visible keys
         g = np.random.default_rng(0)
         n = 512
@@ -394,10 +454,13 @@ def run_backward_workload(args, torch, plx, synth, oracle):
         arrs[name] = synth.normal(spec.seed, tid, (B, H, L, D), sc, spec.dtype)
     t = {n: torch.from_numpy(a).view(torch.bfloat16).cuda() for n, a in arrs.items()}
     W = args.window
+    mask = prefill_mask(synth, B, Hkv, L, args.block_density)
+    assert mask is None or W == 0, "block masks are benchmarked without a window"
+    mask_t = None if mask is None else torch.from_numpy(mask).cuda()
     # the forward stores the softmax readout, as the autograd entry point does
     vbar = torch.empty_like(t["q"])
     o, lse, sbar = plx.prefill(t["q"], t["r"], t["k"], t["v"], return_stats=True, window=W,
-                               vbar_out=vbar)
+                               vbar_out=vbar, block_mask=mask_t)
     grads = (torch.empty_like(t["q"]), torch.empty_like(t["r"]), torch.empty_like(t["k"]),
              torch.empty_like(t["v"]))
     ws = torch.empty(int(plx.lib().parallax_prefill_backward_workspace_bytes(B, Hq, L)),
@@ -405,22 +468,25 @@ def run_backward_workload(args, torch, plx, synth, oracle):
 
     def step(i):
         plx.prefill_backward(t["q"], t["r"], t["k"], t["v"], o, t["do"], lse, sbar,
-                             workspace=ws, out=grads, window=W, vbar=vbar)
+                             workspace=ws, out=grads, window=W, vbar=vbar, block_mask=mask_t)
 
     steps = max(1, min(args.steps, 10))
     warm = max(1, min(args.warmup, 2))
     ts = graph_time(torch, step, steps, warm)
     # algorithmic: 8 contractions of 2D flops per visible (query, key) pair and query head --
     # recompute Z, S, U; dV; dQ, dR; dK from dZ and dS
-    flops = 16 * D * Hq * B * visible_pairs(L, W)
+    pairs = B * visible_pairs(L, W) if mask is None else masked_pairs(mask, L)
+    flops = 16 * D * Hq * pairs if mask is None else 16 * D * (Hq // Hkv) * pairs
     res = {
         "metric": METRIC, "value": round(flops / ts / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": steps, "warmup": warm, "ms_per_step": round(ts * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "causal-prefill-backward-bf16 B8 L4096 Hq16 Hkv8 D128"
-                               + (f" window{W}" if W > 0 else ""), "B": B, "Hq": Hq, "Hkv": Hkv,
-                   "L": L, "head_dim": D, "window": W},
+                               + (f" window{W}" if W > 0 else "")
+                               + (f" block-density{args.block_density}" if mask is not None
+                                  else ""), "B": B, "Hq": Hq, "Hkv": Hkv,
+                   "L": L, "head_dim": D, "window": W, "block_density": args.block_density},
         "roofline": {"bound": "mfma", "kernel": "prefill_backward (row pass + key pass)",
                      "achieved": round(flops / ts / 1e12, 2), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(flops / ts / 1e12 / BF16_PEAK_TFLOPS, 4),
@@ -434,7 +500,7 @@ def run_backward_workload(args, torch, plx, synth, oracle):
     reps = 0
     while True:
         ref = oracle.prefill_backward(arrs["q"], arrs["r"], arrs["k"], arrs["v"], arrs["do"],
-                                      units=units, window=W)
+                                      units=units, window=W, block_mask=mask)
         reps += 1
         if args.no_cpu_baseline or time.perf_counter() - tt > args.cpu_seconds:
             break
@@ -445,7 +511,7 @@ def run_backward_workload(args, torch, plx, synth, oracle):
         a = a.float().cpu().numpy()
         errs[name] = float(np.abs(a - b[0]).max() / np.abs(b[0]).max())
     res["sampled_parity_max_norm_err"] = errs
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and mask is None:
         sec_full = per * B * Hkv
         res["cpu_baseline"] = {"value": round(flops / sec_full / 1e12, 6), "unit": "TFLOP/s",
                                "cores": omp_threads(), "kind": "oracle",

@@ -42,6 +42,22 @@
  *    lets a prefill query i see keys max(0, i - W + 1) .. i, and a decode
  *    query see the last min(n, W) of its sequence's n cached keys. < 0 is
  *    INVALID_ARG.
+ *  - block_mask (block-sparse attention; the same overview calls block
+ *    sparsity structurally compatible and defines none): NULL = none, else
+ *    a DEVICE array of bytes (nonzero = visible) over blocks of
+ *    PLX_MASK_BLOCK positions counted from the start of each sequence, one
+ *    mask per (sequence, KV head), shared by that KV head's query heads:
+ *      decode  [B, Hkv, ceil(kv_len / PLX_MASK_BLOCK)]: byte kb shows key
+ *              positions kb*128 .. kb*128 + 127 to the sequence's query;
+ *      prefill [B, Hkv, nb, nb], nb = ceil(L / PLX_MASK_BLOCK) (L = max_len
+ *              for packed calls): byte [qb][kb] shows key block kb to query
+ *              block qb; only kb < qb is read.
+ *    It applies on top of causality and the window. A query always sees its
+ *    own block (prefill: the diagonal block; decode: the block holding the
+ *    sequence's last key), so every row keeps at least one key. Hidden
+ *    blocks are neither read nor computed on the matrix-core paths. The
+ *    mask is read on the device only and not validated; a backward call must
+ *    get the mask its forward call got.
  */
 #ifndef PARALLAX_H
 #define PARALLAX_H
@@ -53,7 +69,10 @@
 extern "C" {
 #endif
 
-#define PARALLAX_ABI_VERSION 3
+#define PARALLAX_ABI_VERSION 4
+
+/* Block size of block_mask, in positions (keys and prefill queries). */
+#define PLX_MASK_BLOCK 128
 
 typedef enum {
     PLX_OK = 0,
@@ -107,8 +126,9 @@ size_t parallax_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int kv_len
 
 int parallax_decode(const void *q, const void *r, const void *k, const void *v, void *o,
                     const int32_t *cu_seqlens_k, int B, int Hq, int Hkv, int D, int kv_len,
-                    int window, float qk_scale, float rk_scale, int dtype, int num_splits,
-                    void *workspace, size_t workspace_bytes, void *stream);
+                    int window, const uint8_t *block_mask, float qk_scale, float rk_scale,
+                    int dtype, int num_splits, void *workspace, size_t workspace_bytes,
+                    void *stream);
 
 /* Plain softmax-attention decode on the same kernels and loader with the
  * probe path compiled out: o = sum_j w_j v_j. The baseline against which the
@@ -116,8 +136,8 @@ int parallax_decode(const void *q, const void *r, const void *k, const void *v, 
  * parallax_decode without r and rk_scale. Uses the same workspace size. */
 int softmax_decode(const void *q, const void *k, const void *v, void *o,
                    const int32_t *cu_seqlens_k, int B, int Hq, int Hkv, int D, int kv_len,
-                   int window, float qk_scale, int dtype, int num_splits, void *workspace,
-                   size_t workspace_bytes, void *stream);
+                   int window, const uint8_t *block_mask, float qk_scale, int dtype,
+                   int num_splits, void *workspace, size_t workspace_bytes, void *stream);
 
 /* The split count parallax_decode / softmax_decode use for these
  * arguments (num_splits resolved when it is 0), or 0 when they are invalid. */
@@ -154,8 +174,9 @@ size_t parallax_decode_record_bytes(int B, int Hq, int D, int num_records);
  * `records` is NULL or too small. */
 int parallax_decode_partial(const void *q, const void *r, const void *k, const void *v,
                             const int32_t *cu_seqlens_k, int B, int Hq, int Hkv, int D, int kv_len,
-                            int window, float qk_scale, float rk_scale, int dtype, int num_splits,
-                            void *records, size_t records_bytes, void *stream);
+                            int window, const uint8_t *block_mask, float qk_scale,
+                            float rk_scale, int dtype, int num_splits, void *records,
+                            size_t records_bytes, void *stream);
 
 /* Merge records[B][Hq][num_records] (DEVICE) into o [B, Hq, D] (DEVICE,
  * dtype): o = (A + B - (S / l) A) / l over the combined state, or A / l
@@ -183,7 +204,8 @@ int parallax_decode_merge(const void *records, void *o, int B, int Hq, int D, in
  * ---------------------------------------------------------------------- */
 int parallax_prefill(const void *q, const void *r, const void *k, const void *v, void *o,
                      float *lse, float *sbar, void *vbar, int B, int Hq, int Hkv, int L, int D,
-                     int window, float qk_scale, float rk_scale, int dtype, void *stream);
+                     int window, const uint8_t *block_mask, float qk_scale, float rk_scale,
+                     int dtype, void *stream);
 
 /* ------------------------------------------------------------------------
  * Backward of the causal prefill (PyPI README, "Training (Triton)": the
@@ -213,8 +235,8 @@ int parallax_prefill_backward(const void *q, const void *r, const void *k, const
                               const void *o, const void *d_o, const float *lse,
                               const float *sbar, const void *vbar, void *dq, void *dr, void *dk,
                               void *dv, int B, int Hq, int Hkv, int L, int D, int window,
-                              float qk_scale, float rk_scale, int dtype, void *workspace,
-                              size_t workspace_bytes, void *stream);
+                              const uint8_t *block_mask, float qk_scale, float rk_scale,
+                              int dtype, void *workspace, size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * Packed-sequence (varlen) prefill and its backward (the pages name
@@ -245,8 +267,8 @@ size_t parallax_prefill_varlen_workspace_bytes(int Hq, int total_tokens, int bac
 int parallax_prefill_varlen(const void *q, const void *r, const void *k, const void *v, void *o,
                             float *lse, float *sbar, void *vbar, const int32_t *cu_seqlens, int B,
                             int Hq, int Hkv, int max_len, int total_tokens, int D, int window,
-                            float qk_scale, float rk_scale, int dtype, void *workspace,
-                            size_t workspace_bytes, void *stream);
+                            const uint8_t *block_mask, float qk_scale, float rk_scale, int dtype,
+                            void *workspace, size_t workspace_bytes, void *stream);
 
 int parallax_prefill_varlen_backward(const void *q, const void *r, const void *k, const void *v,
                                      const void *o, const void *d_o, const float *lse,
@@ -254,8 +276,9 @@ int parallax_prefill_varlen_backward(const void *q, const void *r, const void *k
                                      const int32_t *cu_seqlens, void *dq, void *dr, void *dk,
                                      void *dv, int B, int Hq, int Hkv,
                                      int max_len, int total_tokens, int D, int window,
-                                     float qk_scale, float rk_scale, int dtype, void *workspace,
-                                     size_t workspace_bytes, void *stream);
+                                     const uint8_t *block_mask, float qk_scale, float rk_scale,
+                                     int dtype, void *workspace, size_t workspace_bytes,
+                                     void *stream);
 
 #ifdef __cplusplus
 }

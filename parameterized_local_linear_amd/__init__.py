@@ -59,31 +59,32 @@ def lib() -> ctypes.CDLL:
         L.parallax_decode_workspace_bytes.restype = sz
         L.parallax_decode_num_splits.argtypes = [i32] * 8
         L.parallax_decode_num_splits.restype = i32
-        L.parallax_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
-                                      f32, i32, i32, vp, sz, vp]
+        L.parallax_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp,
+                                      f32, f32, i32, i32, vp, sz, vp]
         L.parallax_decode.restype = i32
-        L.softmax_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32,
-                                     i32, vp, sz, vp]
+        L.softmax_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, f32,
+                                     i32, i32, vp, sz, vp]
         L.softmax_decode.restype = i32
-        L.parallax_prefill.argtypes = [vp] * 8 + [i32] * 6 + [f32, f32, i32, vp]
+        L.parallax_prefill.argtypes = [vp] * 8 + [i32] * 6 + [vp, f32, f32, i32, vp]
         L.parallax_prefill.restype = i32
         L.parallax_decode_record_bytes.argtypes = [i32, i32, i32, i32]
         L.parallax_decode_record_bytes.restype = sz
-        L.parallax_decode_partial.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
-                                              f32, i32, i32, vp, sz, vp]
+        L.parallax_decode_partial.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp,
+                                              f32, f32, i32, i32, vp, sz, vp]
         L.parallax_decode_partial.restype = i32
         L.parallax_decode_merge.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, vp]
         L.parallax_decode_merge.restype = i32
         L.parallax_prefill_backward_workspace_bytes.argtypes = [i32, i32, i32]
         L.parallax_prefill_backward_workspace_bytes.restype = sz
-        L.parallax_prefill_backward.argtypes = [vp] * 13 + [i32] * 6 + [f32, f32, i32, vp, sz, vp]
+        L.parallax_prefill_backward.argtypes = [vp] * 13 + [i32] * 6 + [vp, f32, f32, i32, vp, sz,
+                                                                         vp]
         L.parallax_prefill_backward.restype = i32
-        L.parallax_prefill_varlen.argtypes = [vp] * 9 + [i32] * 7 + [f32, f32, i32, vp, sz, vp]
+        L.parallax_prefill_varlen.argtypes = [vp] * 9 + [i32] * 7 + [vp, f32, f32, i32, vp, sz, vp]
         L.parallax_prefill_varlen_workspace_bytes.argtypes = [i32, i32, i32]
         L.parallax_prefill_varlen_workspace_bytes.restype = sz
         L.parallax_prefill_varlen.restype = i32
-        L.parallax_prefill_varlen_backward.argtypes = [vp] * 14 + [i32] * 7 + [f32, f32, i32, vp,
-                                                                              sz, vp]
+        L.parallax_prefill_varlen_backward.argtypes = [vp] * 14 + [i32] * 7 + [vp, f32, f32, i32,
+                                                                              vp, sz, vp]
         L.parallax_prefill_varlen_backward.restype = i32
         _lib = L
     return _lib
@@ -114,6 +115,20 @@ def _check(t: torch.Tensor, name: str, dtype, device):
         raise ValueError(f"{name} must be contiguous")
 
 
+MASK_BLOCK = 128  # positions per block of a block-sparse mask
+
+
+def _check_mask(m, shape, device):
+    """A block mask: None, or a contiguous bool / uint8 GPU tensor of `shape`."""
+    if m is None:
+        return None
+    if not m.is_cuda or m.device != device or m.dtype not in (torch.bool, torch.uint8):
+        raise ValueError(f"block_mask must be a bool or uint8 tensor on {device}")
+    if not m.is_contiguous() or tuple(m.shape) != tuple(shape):
+        raise ValueError(f"block_mask must be contiguous {tuple(shape)}")
+    return m
+
+
 def decode_workspace_bytes(B, Hq, Hkv, D, kv_len, dtype_code, num_splits=0, window=0) -> int:
     return int(lib().parallax_decode_workspace_bytes(B, Hq, Hkv, D, kv_len, window, dtype_code,
                                                      num_splits))
@@ -125,7 +140,7 @@ def decode_num_splits(B, Hq, Hkv, D, kv_len, dtype_code, num_splits=0, window=0)
 
 
 def _decode_impl(q, r, k, v, qk_scale, rk_scale, cu_seqlens_k, kv_len, num_splits, out,
-                 workspace, parallax, window):
+                 workspace, parallax, window, block_mask=None):
     L_ = lib()
     squeeze = q.dim() == 4
     if squeeze:                       # the pages' (B, 1, H, D)
@@ -160,6 +175,7 @@ def _decode_impl(q, r, k, v, qk_scale, rk_scale, cu_seqlens_k, kv_len, num_split
             raise ValueError("packed decode needs kv_len (the maximum sequence length)")
         Hkv = k.shape[1]
     code = _dtype_code(q)
+    _check_mask(block_mask, (B, Hkv, -(-int(kv_len) // MASK_BLOCK)), dev)
     if qk_scale is None:
         qk_scale = 1.0 / math.sqrt(D)
     if out is None:
@@ -175,14 +191,14 @@ def _decode_impl(q, r, k, v, qk_scale, rk_scale, cu_seqlens_k, kv_len, num_split
     stream = _stream_handle(dev)
     if parallax:
         st = L_.parallax_decode(_ptr(q), _ptr(r), _ptr(k), _ptr(v), _ptr(out), _ptr(cu_seqlens_k),
-                                B, Hq, Hkv, D, int(kv_len), int(window), float(qk_scale),
-                                float(rk_scale), code, int(num_splits), _ptr(workspace), ws_bytes,
-                                stream)
+                                B, Hq, Hkv, D, int(kv_len), int(window), _ptr(block_mask),
+                                float(qk_scale), float(rk_scale), code, int(num_splits),
+                                _ptr(workspace), ws_bytes, stream)
         what = "parallax_decode"
     else:
         st = L_.softmax_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(cu_seqlens_k), B, Hq, Hkv,
-                               D, int(kv_len), int(window), float(qk_scale), code, int(num_splits),
-                               _ptr(workspace), ws_bytes, stream)
+                               D, int(kv_len), int(window), _ptr(block_mask), float(qk_scale),
+                               code, int(num_splits), _ptr(workspace), ws_bytes, stream)
         what = "softmax_decode"
     if st != 0:
         raise ParallaxError(st, what)
@@ -190,23 +206,25 @@ def _decode_impl(q, r, k, v, qk_scale, rk_scale, cu_seqlens_k, kv_len, num_split
 
 
 def decode(q, r, k, v, qk_scale=None, rk_scale=1.0, *, cu_seqlens_k=None, kv_len=None,
-           num_splits=0, out=None, workspace=None, window=0):
+           num_splits=0, out=None, workspace=None, window=0, block_mask=None):
     """Parallax decode. q, r: [B, Hq, D] (or [B, 1, Hq, D]); k, v: [B, kv_len, Hkv, D],
     or packed [T, Hkv, D] with int32 ``cu_seqlens_k`` [B + 1] and ``kv_len`` = max length.
-    ``window`` > 0: each sequence's last ``window`` keys only."""
+    ``window`` > 0: each sequence's last ``window`` keys only. ``block_mask``: optional
+    bool/uint8 [B, Hkv, ceil(kv_len / 128)] over 128-key blocks (the block holding a
+    sequence's last key is always visible)."""
     return _decode_impl(q, r, k, v, qk_scale, rk_scale, cu_seqlens_k, kv_len, num_splits, out,
-                        workspace, True, window)
+                        workspace, True, window, block_mask)
 
 
 def softmax_decode(q, k, v, qk_scale=None, *, cu_seqlens_k=None, kv_len=None, num_splits=0,
-                   out=None, workspace=None, window=0):
+                   out=None, workspace=None, window=0, block_mask=None):
     """Softmax-attention decode on the same kernels (the Parallax correction compiled out)."""
     return _decode_impl(q, None, k, v, qk_scale, 1.0, cu_seqlens_k, kv_len, num_splits, out,
-                        workspace, False, window)
+                        workspace, False, window, block_mask)
 
 
 def decode_partial(q, r, k, v, qk_scale=None, rk_scale=1.0, *, cu_seqlens_k=None, kv_len=None,
-                   num_splits=0, records=None, window=0):
+                   num_splits=0, records=None, window=0, block_mask=None):
     """Streaming half of decode: returns (records, n) with records a float32
     [B, Hq, n, 2D + 4] tensor (A, B, m, l, S, pi per split). r=None: softmax records."""
     L_ = lib()
@@ -223,6 +241,7 @@ def decode_partial(q, r, k, v, qk_scale=None, rk_scale=1.0, *, cu_seqlens_k=None
         _check(cu_seqlens_k, "cu_seqlens_k", torch.int32, dev)
         Hkv = k.shape[1]
     code = _dtype_code(q)
+    _check_mask(block_mask, (B, Hkv, -(-int(kv_len) // MASK_BLOCK)), dev)
     if qk_scale is None:
         qk_scale = 1.0 / math.sqrt(D)
     n = decode_num_splits(B, Hq, Hkv, D, int(kv_len), code, num_splits, window)
@@ -231,8 +250,8 @@ def decode_partial(q, r, k, v, qk_scale=None, rk_scale=1.0, *, cu_seqlens_k=None
     if records is None:
         records = torch.empty((B, Hq, n, 2 * D + 4), dtype=torch.float32, device=dev)
     st = L_.parallax_decode_partial(_ptr(q), _ptr(r), _ptr(k), _ptr(v), _ptr(cu_seqlens_k), B, Hq,
-                                    Hkv, D, int(kv_len), int(window), float(qk_scale),
-                                    float(rk_scale), code,
+                                    Hkv, D, int(kv_len), int(window), _ptr(block_mask),
+                                    float(qk_scale), float(rk_scale), code,
                                     int(num_splits), _ptr(records),
                                     records.numel() * records.element_size(), _stream_handle(dev))
     if st != 0:
@@ -256,11 +275,13 @@ def decode_merge(records, dtype=torch.bfloat16, with_probe=True, out=None):
 
 
 def prefill(q, r, k, v, qk_scale=None, rk_scale=1.0, *, out=None, return_stats=False, window=0,
-            vbar_out=None):
+            vbar_out=None, block_mask=None):
     """Causal Parallax prefill. q, r: [B, Hq, L, D]; k, v: [B, Hkv, L, D] -> o [B, Hq, L, D]
     (plus fp32 lse and sbar [B, Hq, L] with return_stats=True). ``window`` > 0: query i
     sees keys i - window + 1 .. i. ``vbar_out``: optional tensor shaped like o that
-    receives the softmax readout (a backward statistic)."""
+    receives the softmax readout (a backward statistic). ``block_mask``: optional
+    bool/uint8 [B, Hkv, nb, nb], nb = ceil(L / 128): [qb, kb] lets query block qb see
+    key block kb (the diagonal block is always visible)."""
     L_ = lib()
     B, Hq, L, D = q.shape
     dev, dt = q.device, q.dtype
@@ -272,6 +293,8 @@ def prefill(q, r, k, v, qk_scale=None, rk_scale=1.0, *, out=None, return_stats=F
         raise ValueError("k, v must be [B, Hkv, L, D]")
     Hkv = k.shape[1]
     code = _dtype_code(q)
+    nb = -(-L // MASK_BLOCK)
+    _check_mask(block_mask, (B, Hkv, nb, nb), dev)
     if qk_scale is None:
         qk_scale = 1.0 / math.sqrt(D)
     if out is None:
@@ -289,15 +312,15 @@ def prefill(q, r, k, v, qk_scale=None, rk_scale=1.0, *, out=None, return_stats=F
         if vbar_out.shape != q.shape:
             raise ValueError("vbar_out must have q's shape")
     st = L_.parallax_prefill(_ptr(q), _ptr(r), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(sbar),
-                             _ptr(vbar_out), B, Hq, Hkv, L, D, int(window), float(qk_scale), float(rk_scale), code,
-                             _stream_handle(dev))
+                             _ptr(vbar_out), B, Hq, Hkv, L, D, int(window), _ptr(block_mask),
+                             float(qk_scale), float(rk_scale), code, _stream_handle(dev))
     if st != 0:
         raise ParallaxError(st, "parallax_prefill")
     return (out, lse, sbar) if return_stats else out
 
 
 def prefill_backward(q, r, k, v, o, d_o, lse, sbar, qk_scale=None, rk_scale=1.0, *,
-                     workspace=None, out=None, window=0, vbar=None):
+                     workspace=None, out=None, window=0, vbar=None, block_mask=None):
     """Gradients of the causal prefill: (dq, dr, dk, dv) for the upstream
     gradient ``d_o``, from the forward's o, lse and sbar (prefill with
     return_stats=True on the same inputs and scales). ``out``: optional
@@ -316,6 +339,8 @@ def prefill_backward(q, r, k, v, o, d_o, lse, sbar, qk_scale=None, rk_scale=1.0,
     if k.shape != v.shape or k.dim() != 4 or k.shape[0] != B or k.shape[2] != L or k.shape[3] != D:
         raise ValueError("k, v must be [B, Hkv, L, D]")
     Hkv = k.shape[1]
+    nb = -(-L // MASK_BLOCK)
+    _check_mask(block_mask, (B, Hkv, nb, nb), dev)
     if qk_scale is None:
         qk_scale = 1.0 / math.sqrt(D)
     need = int(L_.parallax_prefill_backward_workspace_bytes(B, Hq, L))
@@ -335,8 +360,8 @@ def prefill_backward(q, r, k, v, o, d_o, lse, sbar, qk_scale=None, rk_scale=1.0,
     st = L_.parallax_prefill_backward(
         _ptr(q), _ptr(r), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse), _ptr(sbar), _ptr(vbar),
         _ptr(dq),
-        _ptr(dr), _ptr(dk), _ptr(dv), B, Hq, Hkv, L, D, int(window), float(qk_scale),
-        float(rk_scale),
+        _ptr(dr), _ptr(dk), _ptr(dv), B, Hq, Hkv, L, D, int(window), _ptr(block_mask),
+        float(qk_scale), float(rk_scale),
         _dtype_code(q), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream_handle(dev))
     if st != 0:
@@ -346,31 +371,33 @@ def prefill_backward(q, r, k, v, o, d_o, lse, sbar, qk_scale=None, rk_scale=1.0,
 
 class _ParallaxFunction(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, r, k, v, qk_scale, rk_scale, window, save_vbar):
+    def forward(ctx, q, r, k, v, qk_scale, rk_scale, window, save_vbar, block_mask):
         vbar = torch.empty_like(q) if save_vbar else None
         o, lse, sbar = prefill(q, r, k, v, qk_scale, rk_scale, return_stats=True, window=window,
-                               vbar_out=vbar)
-        ctx.save_for_backward(q, r, k, v, o, lse, sbar, vbar)
+                               vbar_out=vbar, block_mask=block_mask)
+        ctx.save_for_backward(q, r, k, v, o, lse, sbar, vbar, block_mask)
         ctx.scales = (qk_scale, rk_scale)
         ctx.window = window
         return o
 
     @staticmethod
     def backward(ctx, d_o):
-        q, r, k, v, o, lse, sbar, vbar = ctx.saved_tensors
+        q, r, k, v, o, lse, sbar, vbar, block_mask = ctx.saved_tensors
         grads = prefill_backward(q, r, k, v, o, d_o.contiguous(), lse, sbar, *ctx.scales,
-                                 window=ctx.window, vbar=vbar)
-        return (*grads, None, None, None, None)
+                                 window=ctx.window, vbar=vbar, block_mask=block_mask)
+        return (*grads, None, None, None, None, None)
 
 
-def parallax_func(q, r, k, v, qk_scale=None, rk_scale=1.0, *, window=0, save_vbar=True):
+def parallax_func(q, r, k, v, qk_scale=None, rk_scale=1.0, *, window=0, save_vbar=True,
+                  block_mask=None):
     """Causal Parallax attention on [B, H, L, D] tensors, differentiable in
-    q, r, k and v (the pages' training entry point); ``window`` as in prefill.
-    ``save_vbar`` keeps the softmax readout for the backward (one more o-sized
-    activation, one sweep over the keys fewer in the backward)."""
+    q, r, k and v (the pages' training entry point); ``window`` and ``block_mask``
+    as in prefill. ``save_vbar`` keeps the softmax readout for the backward (one
+    more o-sized activation, one sweep over the keys fewer in the backward)."""
     if torch.is_grad_enabled() and any(t.requires_grad for t in (q, r, k, v)):
-        return _ParallaxFunction.apply(q, r, k, v, qk_scale, rk_scale, window, save_vbar)
-    return prefill(q, r, k, v, qk_scale, rk_scale, window=window)
+        return _ParallaxFunction.apply(q, r, k, v, qk_scale, rk_scale, window, save_vbar,
+                                       block_mask)
+    return prefill(q, r, k, v, qk_scale, rk_scale, window=window, block_mask=block_mask)
 
 
 def _varlen_shapes(q, k, cu_seqlens, max_len):
@@ -385,9 +412,12 @@ def _varlen_shapes(q, k, cu_seqlens, max_len):
 
 
 def prefill_varlen(q, r, k, v, cu_seqlens, max_len=None, qk_scale=None, rk_scale=1.0, *,
-                   out=None, return_stats=False, window=0, workspace=None, vbar_out=None):
+                   out=None, return_stats=False, window=0, workspace=None, vbar_out=None,
+                   block_mask=None):
     """Causal prefill of packed sequences: q, r [T, Hq, D]; k, v [T, Hkv, D]; int32
-    ``cu_seqlens`` [B + 1]. Returns o [T, Hq, D] (plus fp32 lse, sbar [T, Hq])."""
+    ``cu_seqlens`` [B + 1]. Returns o [T, Hq, D] (plus fp32 lse, sbar [T, Hq]).
+    ``block_mask``: optional [B, Hkv, nb, nb], nb = ceil(max_len / 128), over
+    sequence-local blocks."""
     L_ = lib()
     dev, dt = q.device, q.dtype
     for t, name in ((q, "q"), (r, "r"), (k, "k"), (v, "v")):
@@ -396,6 +426,8 @@ def prefill_varlen(q, r, k, v, cu_seqlens, max_len=None, qk_scale=None, rk_scale
         raise ValueError("r must have q's shape and v k's")
     B, Hq, Hkv, D, max_len = _varlen_shapes(q, k, cu_seqlens, max_len)
     T = q.shape[0]
+    nb = -(-max_len // MASK_BLOCK)
+    _check_mask(block_mask, (B, Hkv, nb, nb), dev)
     if qk_scale is None:
         qk_scale = 1.0 / math.sqrt(D)
     if out is None:
@@ -413,7 +445,8 @@ def prefill_varlen(q, r, k, v, cu_seqlens, max_len=None, qk_scale=None, rk_scale
             raise ValueError("vbar_out must have q's shape")
     st = L_.parallax_prefill_varlen(_ptr(q), _ptr(r), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                                     _ptr(sbar), _ptr(vbar_out), _ptr(cu_seqlens), B, Hq, Hkv, max_len, T, D,
-                                    int(window), float(qk_scale), float(rk_scale), _dtype_code(q),
+                                    int(window), _ptr(block_mask), float(qk_scale),
+                                    float(rk_scale), _dtype_code(q),
                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
                                     _stream_handle(dev))
     if st != 0:
@@ -423,7 +456,7 @@ def prefill_varlen(q, r, k, v, cu_seqlens, max_len=None, qk_scale=None, rk_scale
 
 def prefill_varlen_backward(q, r, k, v, o, d_o, lse, sbar, cu_seqlens, max_len=None,
                             qk_scale=None, rk_scale=1.0, *, window=0, workspace=None, out=None,
-                            vbar=None):
+                            vbar=None, block_mask=None):
     """Gradients (dq, dr, dk, dv) of prefill_varlen from its o, lse and sbar."""
     L_ = lib()
     dev, dt = q.device, q.dtype
@@ -435,6 +468,8 @@ def prefill_varlen_backward(q, r, k, v, o, d_o, lse, sbar, cu_seqlens, max_len=N
         _check(t, name, torch.float32, dev)
         if t.shape != (T, Hq):
             raise ValueError(f"{name} must be float32 [T, Hq]")
+    nb = -(-max_len // MASK_BLOCK)
+    _check_mask(block_mask, (B, Hkv, nb, nb), dev)
     if qk_scale is None:
         qk_scale = 1.0 / math.sqrt(D)
     need = int(L_.parallax_prefill_varlen_workspace_bytes(Hq, T, 1))
@@ -450,7 +485,8 @@ def prefill_varlen_backward(q, r, k, v, o, d_o, lse, sbar, cu_seqlens, max_len=N
     st = L_.parallax_prefill_varlen_backward(
         _ptr(q), _ptr(r), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse), _ptr(sbar), _ptr(vbar),
         _ptr(cu_seqlens), _ptr(dq), _ptr(dr), _ptr(dk), _ptr(dv), B, Hq, Hkv, max_len, T, D,
-        int(window), float(qk_scale), float(rk_scale), _dtype_code(q), _ptr(workspace),
+        int(window), _ptr(block_mask), float(qk_scale), float(rk_scale), _dtype_code(q),
+        _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream_handle(dev))
     if st != 0:
         raise ParallaxError(st, "parallax_prefill_varlen_backward")
@@ -459,33 +495,37 @@ def prefill_varlen_backward(q, r, k, v, o, d_o, lse, sbar, cu_seqlens, max_len=N
 
 class _ParallaxVarlenFunction(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, r, k, v, cu_seqlens, max_len, qk_scale, rk_scale, window, save_vbar):
+    def forward(ctx, q, r, k, v, cu_seqlens, max_len, qk_scale, rk_scale, window, save_vbar,
+                block_mask):
         vbar = torch.empty_like(q) if save_vbar else None
         o, lse, sbar = prefill_varlen(q, r, k, v, cu_seqlens, max_len, qk_scale, rk_scale,
-                                      return_stats=True, window=window, vbar_out=vbar)
-        ctx.save_for_backward(q, r, k, v, o, lse, sbar, cu_seqlens, vbar)
+                                      return_stats=True, window=window, vbar_out=vbar,
+                                      block_mask=block_mask)
+        ctx.save_for_backward(q, r, k, v, o, lse, sbar, cu_seqlens, vbar, block_mask)
         ctx.args = (max_len, qk_scale, rk_scale, window)
         return o
 
     @staticmethod
     def backward(ctx, d_o):
-        q, r, k, v, o, lse, sbar, cu, vbar = ctx.saved_tensors
+        q, r, k, v, o, lse, sbar, cu, vbar, block_mask = ctx.saved_tensors
         max_len, qk_scale, rk_scale, window = ctx.args
         grads = prefill_varlen_backward(q, r, k, v, o, d_o.contiguous(), lse, sbar, cu, max_len,
-                                        qk_scale, rk_scale, window=window, vbar=vbar)
-        return (*grads, None, None, None, None, None, None)
+                                        qk_scale, rk_scale, window=window, vbar=vbar,
+                                        block_mask=block_mask)
+        return (*grads, None, None, None, None, None, None, None)
 
 
 def parallax_varlen_func(q, r, k, v, cu_seqlens, max_len=None, qk_scale=None, rk_scale=1.0, *,
-                         window=0, save_vbar=True):
+                         window=0, save_vbar=True, block_mask=None):
     """Differentiable causal Parallax attention on packed sequences (the pages'
     parallax_varlen_func): q, r [T, Hq, D]; k, v [T, Hkv, D]; int32 cu_seqlens [B + 1]."""
     if max_len is None:
         max_len = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item())
     if torch.is_grad_enabled() and any(t.requires_grad for t in (q, r, k, v)):
         return _ParallaxVarlenFunction.apply(q, r, k, v, cu_seqlens, max_len, qk_scale, rk_scale,
-                                             window, save_vbar)
-    return prefill_varlen(q, r, k, v, cu_seqlens, max_len, qk_scale, rk_scale, window=window)
+                                             window, save_vbar, block_mask)
+    return prefill_varlen(q, r, k, v, cu_seqlens, max_len, qk_scale, rk_scale, window=window,
+                          block_mask=block_mask)
 
 
 parallax_decode = decode

@@ -39,9 +39,12 @@ constexpr int kMinKeysPerWave = 32;  // one tile: short sequences split for late
 // its streaming loop reads ahead (up to two 128-key strides and one 32-key
 // tile past its end), must span less than 2^31 bytes, since the kernels
 // address them with 32-bit offsets.
+// A range is also at most kMaxRangeKeys keys, whose block-sparse visibility a
+// workgroup stages in LDS.
 static long long max_split_keys(int Hkv, int D, int dtype) {
     const long long tok_bytes = (long long)Hkv * D * (dtype == PLX_BF16 ? 2 : 4);
-    return (0x7fffffffLL - 1024) / tok_bytes - 320;
+    const long long by_offsets = (0x7fffffffLL - 1024) / tok_bytes - 320;
+    return by_offsets < kMaxRangeKeys ? by_offsets : kMaxRangeKeys;
 }
 
 DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int kv_len, int window, int dtype,
@@ -148,8 +151,9 @@ int parallax_decode_num_splits(int B, int Hq, int Hkv, int D, int kv_len, int wi
 
 static int fill_decode_args(plx::DecodeArgs &a, const void *q, const void *r, const void *k,
                             const void *v, void *o, const int32_t *cu, int B, int Hq, int Hkv, int D,
-                            int kv_len, int window, float qk_scale, float rk_scale, int dtype,
-                            int num_splits, bool parallax, DecodePlan &p) {
+                            int kv_len, int window, const uint8_t *block_mask, float qk_scale,
+                            float rk_scale, int dtype, int num_splits, bool parallax,
+                            DecodePlan &p) {
     int st = check_decode_sizes(B, Hq, Hkv, D, kv_len, window, dtype);
     if (st != PLX_OK) return st;
     if (!q || !k || !v || !o || (parallax && !r)) return PLX_ERR_INVALID_ARG;
@@ -169,6 +173,8 @@ static int fill_decode_args(plx::DecodeArgs &a, const void *q, const void *r, co
     a.D = D;
     a.kv_len = kv_len;
     a.window = window;
+    a.block_mask = block_mask;
+    a.mask_cols = (kv_len + plx::kMaskBlock - 1) / plx::kMaskBlock;
     a.zscale = qk_scale * plx::kLog2e;
     a.rk_scale = rk_scale;
     a.splits = p.splits;
@@ -181,12 +187,12 @@ static int fill_decode_args(plx::DecodeArgs &a, const void *q, const void *r, co
 
 static int decode_common(const void *q, const void *r, const void *k, const void *v, void *o,
                          const int32_t *cu, int B, int Hq, int Hkv, int D, int kv_len, int window,
-                         float qk_scale, float rk_scale, int dtype, int num_splits, void *ws,
-                         size_t ws_bytes, void *stream, bool parallax) {
+                         const uint8_t *block_mask, float qk_scale, float rk_scale, int dtype,
+                         int num_splits, void *ws, size_t ws_bytes, void *stream, bool parallax) {
     plx::DecodeArgs a;
     DecodePlan p;
-    int st = fill_decode_args(a, q, r, k, v, o, cu, B, Hq, Hkv, D, kv_len, window, qk_scale, rk_scale,
-                              dtype, num_splits, parallax, p);
+    int st = fill_decode_args(a, q, r, k, v, o, cu, B, Hq, Hkv, D, kv_len, window, block_mask,
+                              qk_scale, rk_scale, dtype, num_splits, parallax, p);
     if (st != PLX_OK) return st;
     if (cu) {
         a.sk_parts = streamk_parts(p, B, Hkv, D, kv_len, dtype, window, num_splits);
@@ -205,17 +211,21 @@ static int decode_common(const void *q, const void *r, const void *k, const void
 
 int parallax_decode(const void *q, const void *r, const void *k, const void *v, void *o,
                     const int32_t *cu_seqlens_k, int B, int Hq, int Hkv, int D, int kv_len,
-                    int window, float qk_scale, float rk_scale, int dtype, int num_splits,
-                    void *workspace, size_t workspace_bytes, void *stream) {
-    return decode_common(q, r, k, v, o, cu_seqlens_k, B, Hq, Hkv, D, kv_len, window, qk_scale,
-                         rk_scale, dtype, num_splits, workspace, workspace_bytes, stream, true);
+                    int window, const uint8_t *block_mask, float qk_scale, float rk_scale,
+                    int dtype, int num_splits, void *workspace, size_t workspace_bytes,
+                    void *stream) {
+    return decode_common(q, r, k, v, o, cu_seqlens_k, B, Hq, Hkv, D, kv_len, window, block_mask,
+                         qk_scale, rk_scale, dtype, num_splits, workspace, workspace_bytes, stream,
+                         true);
 }
 
 int softmax_decode(const void *q, const void *k, const void *v, void *o, const int32_t *cu_seqlens_k,
-                   int B, int Hq, int Hkv, int D, int kv_len, int window, float qk_scale, int dtype,
-                   int num_splits, void *workspace, size_t workspace_bytes, void *stream) {
-    return decode_common(q, nullptr, k, v, o, cu_seqlens_k, B, Hq, Hkv, D, kv_len, window, qk_scale,
-                         1.0f, dtype, num_splits, workspace, workspace_bytes, stream, false);
+                   int B, int Hq, int Hkv, int D, int kv_len, int window,
+                   const uint8_t *block_mask, float qk_scale, int dtype, int num_splits,
+                   void *workspace, size_t workspace_bytes, void *stream) {
+    return decode_common(q, nullptr, k, v, o, cu_seqlens_k, B, Hq, Hkv, D, kv_len, window,
+                         block_mask, qk_scale, 1.0f, dtype, num_splits, workspace, workspace_bytes,
+                         stream, false);
 }
 
 size_t parallax_decode_record_bytes(int B, int Hq, int D, int num_records) {
@@ -225,14 +235,15 @@ size_t parallax_decode_record_bytes(int B, int Hq, int D, int num_records) {
 
 int parallax_decode_partial(const void *q, const void *r, const void *k, const void *v,
                             const int32_t *cu_seqlens_k, int B, int Hq, int Hkv, int D, int kv_len,
-                            int window, float qk_scale, float rk_scale, int dtype, int num_splits,
-                            void *records, size_t records_bytes, void *stream) {
+                            int window, const uint8_t *block_mask, float qk_scale, float rk_scale,
+                            int dtype, int num_splits, void *records, size_t records_bytes,
+                            void *stream) {
     plx::DecodeArgs a;
     DecodePlan p;
     const bool parallax = r != nullptr;
     // o is not written in this mode; any non-null value passes the checks
     int st = fill_decode_args(a, q, r, k, v, records, cu_seqlens_k, B, Hq, Hkv, D, kv_len, window,
-                              qk_scale, rk_scale, dtype, num_splits, parallax, p);
+                              block_mask, qk_scale, rk_scale, dtype, num_splits, parallax, p);
     if (st != PLX_OK) return st;
     if (!records || records_bytes < parallax_decode_record_bytes(B, Hq, D, p.splits))
         return PLX_ERR_WORKSPACE;
@@ -271,7 +282,8 @@ constexpr size_t kQueueBytes = 256;
 
 template <typename Args>
 static int check_prefill(Args &a, const int32_t *cu, int B, int Hq, int Hkv, int L, int total, int D,
-                         int window, float qk_scale, float rk_scale, int dtype) {
+                         int window, const uint8_t *block_mask, float qk_scale, float rk_scale,
+                         int dtype) {
     if (B < 1 || Hq < 1 || Hkv < 1 || L < 1 || D < 1 || window < 0) return PLX_ERR_INVALID_ARG;
     if (Hq % Hkv != 0) return PLX_ERR_INVALID_ARG;
     if (cu && total < 0) return PLX_ERR_INVALID_ARG;
@@ -292,6 +304,7 @@ static int check_prefill(Args &a, const int32_t *cu, int B, int Hq, int Hkv, int
     a.L = L;
     a.D = D;
     a.window = (window > 0 && window < L) ? window : L;
+    a.block_mask = block_mask;
     a.zscale = qk_scale * plx::kLog2e;
     a.rk_scale = rk_scale;
     return PLX_OK;
@@ -299,11 +312,12 @@ static int check_prefill(Args &a, const int32_t *cu, int B, int Hq, int Hkv, int
 
 static int prefill_common(const void *q, const void *r, const void *k, const void *v, void *o, float *lse,
                           float *sbar, void *vbar, const int32_t *cu, int B, int Hq, int Hkv, int L, int total, int D,
-                          int window, float qk_scale, float rk_scale, int dtype, void *ws, size_t ws_bytes,
-                          void *stream) {
+                          int window, const uint8_t *block_mask, float qk_scale, float rk_scale,
+                          int dtype, void *ws, size_t ws_bytes, void *stream) {
     if (!q || !r || !k || !v || !o) return PLX_ERR_INVALID_ARG;
     plx::PrefillArgs a;
-    int st = check_prefill(a, cu, B, Hq, Hkv, L, total, D, window, qk_scale, rk_scale, dtype);
+    int st = check_prefill(a, cu, B, Hq, Hkv, L, total, D, window, block_mask, qk_scale, rk_scale,
+                           dtype);
     if (st != PLX_OK) return st;
     if (cu && (!ws || ws_bytes < kQueueBytes)) return PLX_ERR_WORKSPACE;
     if (cu && total == 0) return PLX_OK;  // every sequence empty
@@ -324,12 +338,14 @@ static int backward_common(const void *q, const void *r, const void *k, const vo
                            const void *d_o, const float *lse, const float *sbar, const void *vbar,
                            const int32_t *cu,
                            void *dq, void *dr, void *dk, void *dv, int B, int Hq, int Hkv, int L,
-                           int total, int D, int window, float qk_scale, float rk_scale, int dtype,
-                           void *workspace, size_t workspace_bytes, void *stream) {
+                           int total, int D, int window, const uint8_t *block_mask, float qk_scale,
+                           float rk_scale, int dtype, void *workspace, size_t workspace_bytes,
+                           void *stream) {
     if (!q || !r || !k || !v || !o || !d_o || !lse || !sbar || !dq || !dr || !dk || !dv)
         return PLX_ERR_INVALID_ARG;
     plx::BackwardArgs a;
-    int st = check_prefill(a, cu, B, Hq, Hkv, L, total, D, window, qk_scale, rk_scale, dtype);
+    int st = check_prefill(a, cu, B, Hq, Hkv, L, total, D, window, block_mask, qk_scale, rk_scale,
+                           dtype);
     if (st != PLX_OK) return st;
     if (cu && total == 0) return PLX_OK;  // every sequence empty
     const size_t need = cu ? kQueueBytes + (size_t)Hq * total * sizeof(plx::RowStat)
@@ -363,9 +379,10 @@ extern "C" {
 
 int parallax_prefill(const void *q, const void *r, const void *k, const void *v, void *o, float *lse,
                      float *sbar, void *vbar, int B, int Hq, int Hkv, int L, int D, int window,
-                     float qk_scale, float rk_scale, int dtype, void *stream) {
-    return prefill_common(q, r, k, v, o, lse, sbar, vbar, nullptr, B, Hq, Hkv, L, 0, D, window, qk_scale,
-                          rk_scale, dtype, nullptr, 0, stream);
+                     const uint8_t *block_mask, float qk_scale, float rk_scale, int dtype,
+                     void *stream) {
+    return prefill_common(q, r, k, v, o, lse, sbar, vbar, nullptr, B, Hq, Hkv, L, 0, D, window,
+                          block_mask, qk_scale, rk_scale, dtype, nullptr, 0, stream);
 }
 
 size_t parallax_prefill_varlen_workspace_bytes(int Hq, int total_tokens, int backward) {
@@ -375,12 +392,13 @@ size_t parallax_prefill_varlen_workspace_bytes(int Hq, int total_tokens, int bac
 
 int parallax_prefill_varlen(const void *q, const void *r, const void *k, const void *v, void *o,
                             float *lse, float *sbar, void *vbar, const int32_t *cu_seqlens, int B, int Hq, int Hkv,
-                            int max_len, int total_tokens, int D, int window, float qk_scale,
-                            float rk_scale, int dtype, void *workspace, size_t workspace_bytes,
-                            void *stream) {
+                            int max_len, int total_tokens, int D, int window,
+                            const uint8_t *block_mask, float qk_scale, float rk_scale, int dtype,
+                            void *workspace, size_t workspace_bytes, void *stream) {
     if (!cu_seqlens) return PLX_ERR_INVALID_ARG;
     return prefill_common(q, r, k, v, o, lse, sbar, vbar, cu_seqlens, B, Hq, Hkv, max_len, total_tokens, D,
-                          window, qk_scale, rk_scale, dtype, workspace, workspace_bytes, stream);
+                          window, block_mask, qk_scale, rk_scale, dtype, workspace, workspace_bytes,
+                          stream);
 }
 
 size_t parallax_prefill_backward_workspace_bytes(int B, int Hq, int L) {
@@ -392,22 +410,24 @@ int parallax_prefill_backward(const void *q, const void *r, const void *k, const
                               const void *d_o, const float *lse, const float *sbar, const void *vbar,
                               void *dq, void *dr,
                               void *dk, void *dv, int B, int Hq, int Hkv, int L, int D, int window,
-                              float qk_scale, float rk_scale, int dtype, void *workspace,
-                              size_t workspace_bytes, void *stream) {
+                              const uint8_t *block_mask, float qk_scale, float rk_scale, int dtype,
+                              void *workspace, size_t workspace_bytes, void *stream) {
     return backward_common(q, r, k, v, o, d_o, lse, sbar, vbar, nullptr, dq, dr, dk, dv, B, Hq, Hkv, L, 0, D,
-                           window, qk_scale, rk_scale, dtype, workspace, workspace_bytes, stream);
+                           window, block_mask, qk_scale, rk_scale, dtype, workspace,
+                           workspace_bytes, stream);
 }
 
 int parallax_prefill_varlen_backward(const void *q, const void *r, const void *k, const void *v,
                                      const void *o, const void *d_o, const float *lse, const float *sbar,
                                      const void *vbar, const int32_t *cu_seqlens, void *dq, void *dr, void *dk, void *dv,
                                      int B, int Hq, int Hkv, int max_len, int total_tokens, int D,
-                                     int window, float qk_scale, float rk_scale, int dtype,
-                                     void *workspace, size_t workspace_bytes, void *stream) {
+                                     int window, const uint8_t *block_mask, float qk_scale,
+                                     float rk_scale, int dtype, void *workspace,
+                                     size_t workspace_bytes, void *stream) {
     if (!cu_seqlens) return PLX_ERR_INVALID_ARG;
     return backward_common(q, r, k, v, o, d_o, lse, sbar, vbar, cu_seqlens, dq, dr, dk, dv, B, Hq, Hkv, max_len,
-                           total_tokens, D, window, qk_scale, rk_scale, dtype, workspace,
-                           workspace_bytes, stream);
+                           total_tokens, D, window, block_mask, qk_scale, rk_scale, dtype,
+                           workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -116,6 +116,14 @@ __global__ __launch_bounds__(64) void bwd_rows_generic(BackwardArgs a) {
     const float sb = a.sbar[srow];
     const int end = i + 1;
     const int first = max(0, i - a.window + 1);  // sliding window: keys first .. i
+    // block-sparse: key j is visible iff its block is the row's own or the mask shows it
+    const int nb = (a.L + kMaskBlock - 1) >> kMaskShift;
+    const int qb = i >> kMaskShift;
+    const uint8_t *mrow =
+        a.block_mask ? a.block_mask + (((int64_t)b * a.Hkv + hkv) * nb + qb) * nb : nullptr;
+    auto visible = [&](int j) {
+        return j < end && (!mrow || (j >> kMaskShift) == qb || mrow[j >> kMaskShift] != 0);
+    };
 
     // sweep 1: ubar = sum_j w_j g.v_j, or g . vbar from the forward's softmax readout
     float ub = 0.f;
@@ -139,7 +147,7 @@ __global__ __launch_bounds__(64) void bwd_rows_generic(BackwardArgs a) {
         }
         zp = row_sum<LPR>(zp);
         up = row_sum<LPR>(up);
-        if (j < end) ub += __builtin_amdgcn_exp2f(fmaf(zp, a.zscale, -lse2)) * up;
+        if (visible(j)) ub += __builtin_amdgcn_exp2f(fmaf(zp, a.zscale, -lse2)) * up;
     }
     if (!a.vbar) ub = across_rows<LPR>(ub);
 
@@ -161,7 +169,7 @@ __global__ __launch_bounds__(64) void bwd_rows_generic(BackwardArgs a) {
         zp = row_sum<LPR>(zp);
         sp = row_sum<LPR>(sp);
         up = row_sum<LPR>(up);
-        const float w = j < end ? __builtin_amdgcn_exp2f(fmaf(zp, a.zscale, -lse2)) : 0.f;
+        const float w = visible(j) ? __builtin_amdgcn_exp2f(fmaf(zp, a.zscale, -lse2)) : 0.f;
         const float sc = fmaf(sp, a.rk_scale, -sb);  // s_j - sbar
         const float ds = w * (up - ub);
         const float dz = w * (fmaf(sc, up, up) - fmaf(ub, sc, delta));
@@ -201,6 +209,11 @@ __global__ __launch_bounds__(64) void bwd_keys_generic(BackwardArgs a) {
     Frag<T>::load(reinterpret_cast<const T *>(a.k) + kvrow + c * EPL, kv);
     Frag<T>::load(reinterpret_cast<const T *>(a.v) + kvrow + c * EPL, vv);
     for (int e = 0; e < EPL; ++e) dka[e] = dva[e] = 0.f;
+    // block-sparse: row i sees key j iff j's block is i's own or the mask shows it
+    const int nb = (a.L + kMaskBlock - 1) >> kMaskShift;
+    const int kb = j >> kMaskShift;
+    const uint8_t *mcol =
+        a.block_mask ? a.block_mask + ((int64_t)b * a.Hkv + hkv) * nb * nb + kb : nullptr;
     for (int hs = 0; hs < G; ++hs) {
         const int hq = hkv * G + hs;
         const int64_t rbase = row0_elem(sq, b, hq, a.Hq, a.L, D);
@@ -224,7 +237,9 @@ __global__ __launch_bounds__(64) void bwd_keys_generic(BackwardArgs a) {
             zp = row_sum<LPR>(zp);
             sp = row_sum<LPR>(sp);
             up = row_sum<LPR>(up);
-            const float w = i < rend ? __builtin_amdgcn_exp2f(fmaf(zp, a.zscale, -st.lse2)) : 0.f;
+            const bool vis = i < rend && (!mcol || (i >> kMaskShift) == kb ||
+                                          mcol[(int64_t)(i >> kMaskShift) * nb] != 0);
+            const float w = vis ? __builtin_amdgcn_exp2f(fmaf(zp, a.zscale, -st.lse2)) : 0.f;
             const float sc = fmaf(sp, a.rk_scale, -st.sbar);
             const float pv = w * (1.0f + sc);
             const float ds = w * (up - st.ubar) * a.rk_scale;
@@ -325,7 +340,7 @@ __device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t rs, int row0, in
 //   sweep 1: Z^T = K Q^T, U^T = V G^T                        (16 MFMAs)
 //   sweep 2: Z^T, S^T = K R^T, U^T, then dQ^T += K^T dZ^T,
 //            dR^T += K^T dS^T with K^T read transposed       (40 MFMAs)
-template <int HPW>
+template <int HPW, bool MASK>
 __device__ __forceinline__ void bwd_rows_item(const BackwardArgs &a, const int item) {
     constexpr int D = 128;
     constexpr int NW = kBwdWaves;
@@ -371,7 +386,19 @@ __device__ __forceinline__ void bwd_rows_item(const BackwardArgs &a, const int i
         dma_rows<TK, NW>(krs, tile * TK, ks, lk, wave, lane);
         dma_rows<TK, NW>(vrs, tile * TK, ks, lv, wave, lane);
     };
-    dma_tile(tile0, lds_k0, lds_v0);  // the first sweep's first tile
+    // block-sparse: the key tiles (= key blocks) this item's query block sees
+    static_assert(TK == kMaskBlock && kMaskBlock % RPH == 0, "a tile is one mask block");
+    const int qb = (qt * RPH) >> kMaskShift;
+    const int nb = (a.L + kMaskBlock - 1) >> kMaskShift;
+    const uint8_t *mrow = MASK ? a.block_mask + (((int64_t)b * a.Hkv + hkv) * nb + qb) * nb : nullptr;
+    uint64_t vbits = 0;
+    int vbase = -64;
+    auto next_tile = [&](int t) {
+        if constexpr (!MASK) return t;
+        return next_visible(t, ntiles, vbits, vbase, [&](int u) { return u == qb || mrow[u] != 0; });
+    };
+    const int first_tile = next_tile(tile0);  // the diagonal tile is always visible
+    dma_tile(first_tile, lds_k0, lds_v0);     // the first sweep's first tile
 
     // per-wave B operands (query row n, k step u -> chunk g + 4u) and row scalars
     const int64_t qbase = row0_elem(sq, b, hq, a.Hq, a.L, D);
@@ -433,8 +460,8 @@ __device__ __forceinline__ void bwd_rows_item(const BackwardArgs &a, const int i
     };
     // the sweep over this wave's key tiles; body(lk, lv, kl, key0, diag)
     auto sweep = [&](auto &&body) __attribute__((always_inline)) {
-        auto step = [&](int tile, uint16_t *lk, uint16_t *lv, uint16_t *nk, uint16_t *nv) __attribute__((always_inline)) {
-            if (tile + 1 < ntiles) dma_tile(tile + 1, nk, nv);
+        auto step = [&](int tile, int nxt, uint16_t *lk, uint16_t *lv, uint16_t *nk, uint16_t *nv) __attribute__((always_inline)) {
+            if (nxt < ntiles) dma_tile(nxt, nk, nv);
             const int t0 = tile * TK;
             // tiles outside the wave's visible band are skipped; the mask is
             // needed unless every key of the tile is visible to all 16 rows
@@ -451,9 +478,23 @@ __device__ __forceinline__ void bwd_rows_item(const BackwardArgs &a, const int i
             __syncthreads();
         };
         __syncthreads();
-        for (int tile = tile0; tile < ntiles; tile += 2) {
-            step(tile, lds_k0, lds_v0, lds_k1, lds_v1);
-            if (tile + 1 < ntiles) step(tile + 1, lds_k1, lds_v1, lds_k0, lds_v0);
+        if constexpr (!MASK) {
+            for (int tile = tile0; tile < ntiles; tile += 2) {
+                step(tile, tile + 1, lds_k0, lds_v0, lds_k1, lds_v1);
+                if (tile + 1 < ntiles) step(tile + 1, tile + 2, lds_k1, lds_v1, lds_k0, lds_v0);
+            }
+        } else {
+            int tile = first_tile;
+            while (true) {
+                int nxt = next_tile(tile + 1);
+                step(tile, nxt, lds_k0, lds_v0, lds_k1, lds_v1);
+                if (nxt >= ntiles) break;
+                tile = nxt;
+                nxt = next_tile(tile + 1);
+                step(tile, nxt, lds_k1, lds_v1, lds_k0, lds_v0);
+                if (nxt >= ntiles) break;
+                tile = nxt;
+            }
         }
     };
 
@@ -480,7 +521,7 @@ __device__ __forceinline__ void bwd_rows_item(const BackwardArgs &a, const int i
     floatx4 accQ[8], accR[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) accQ[e] = accR[e] = floatx4{0.f, 0.f, 0.f, 0.f};
-    if (!a.vbar) dma_tile(tile0, lds_k0, lds_v0);  // sweep 1 consumed the first copy
+    if (!a.vbar) dma_tile(first_tile, lds_k0, lds_v0);  // sweep 1 consumed the first copy
     sweep([&](const uint16_t *lk, const uint16_t *lv, int kl, int key0, bool diag) __attribute__((always_inline)) {
         floatx4 z0, z1, s0, s1, u0, u1;
         {
@@ -548,6 +589,7 @@ __device__ __forceinline__ void bwd_rows_item(const BackwardArgs &a, const int i
 constexpr int kKeyWaves = 4;
 constexpr int kKeyBlocksPerWave = 2;  // 16-key column blocks per wave
 
+template <bool MASK>
 __device__ __forceinline__ void bwd_keys_item(const BackwardArgs &a, const int item) {
     constexpr int D = 128;
     constexpr int NW = kKeyWaves;
@@ -574,6 +616,22 @@ __device__ __forceinline__ void bwd_keys_item(const BackwardArgs &a, const int i
     const int rend = min(L, k0 + KB - 1 + W);  // rows k0 .. rend - 1 see some key of the block
     const int nrt = (rend - k0 + TR - 1) / TR;   // row tiles per query head
     const int ntiles = G * nrt;
+    // block-sparse: row tile t (of head t / nrt) lies in query block
+    // (k0 + (t % nrt) TR) / 128, which sees this key block if it is the
+    // block itself or the mask shows it
+    static_assert(KB == kMaskBlock && kMaskBlock % TR == 0, "a key block is one mask block");
+    const int kblock = k0 >> kMaskShift;
+    const int nb = (a.L + kMaskBlock - 1) >> kMaskShift;
+    const uint8_t *mcol = MASK ? a.block_mask + ((int64_t)b * a.Hkv + hkv) * nb * nb + kblock : nullptr;
+    uint64_t vbits = 0;
+    int vbase = -64;
+    auto next_tile = [&](int t) {
+        if constexpr (!MASK) return t;
+        return next_visible(t, ntiles, vbits, vbase, [&](int u) {
+            const int qbk = (k0 + (u % nrt) * TR) >> kMaskShift;
+            return qbk == kblock || mcol[(int64_t)qbk * nb] != 0;
+        });
+    };
 
     const int64_t kvbase = row0_elem(sq, b, hkv, a.Hkv, a.L, D);
     const int ks = row_stride(sq, a.Hkv, D);
@@ -615,7 +673,8 @@ __device__ __forceinline__ void bwd_keys_item(const BackwardArgs &a, const int i
             __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (lds_void *)ts, 16, (r0 + lane) * 16, 0, 0, 0);
         }
     };
-    dma_tile(0, lq0, lr0, lg0, ls0);
+    int tile = next_tile(0);  // the diagonal block's rows always see the block
+    dma_tile(tile, lq0, lr0, lg0, ls0);
 
     floatx4 accK[KBW][8], accV[KBW][8];
 #pragma unroll
@@ -681,9 +740,9 @@ __device__ __forceinline__ void bwd_keys_item(const BackwardArgs &a, const int i
             }
         }
     };
-    auto step = [&](int tile, uint16_t *tq, uint16_t *tr, uint16_t *tg, RowStat *ts, uint16_t *nq,
-                    uint16_t *nr, uint16_t *ng, RowStat *ns) __attribute__((always_inline)) {
-        if (tile + 1 < ntiles) dma_tile(tile + 1, nq, nr, ng, ns);
+    auto step = [&](int tile, int nxt, uint16_t *tq, uint16_t *tr, uint16_t *tg, RowStat *ts,
+                    uint16_t *nq, uint16_t *nr, uint16_t *ng, RowStat *ns) __attribute__((always_inline)) {
+        if (nxt < ntiles) dma_tile(nxt, nq, nr, ng, ns);
         const int r0 = k0 + (tile % nrt) * TR;
 #pragma unroll
         for (int j = 0; j < TR / 32; ++j) {
@@ -700,9 +759,22 @@ __device__ __forceinline__ void bwd_keys_item(const BackwardArgs &a, const int i
         __syncthreads();
     };
     __syncthreads();
-    for (int tile = 0; tile < ntiles; tile += 2) {
-        step(tile, lq0, lr0, lg0, ls0, lq1, lr1, lg1, ls1);
-        if (tile + 1 < ntiles) step(tile + 1, lq1, lr1, lg1, ls1, lq0, lr0, lg0, ls0);
+    if constexpr (!MASK) {
+        for (; tile < ntiles; tile += 2) {
+            step(tile, tile + 1, lq0, lr0, lg0, ls0, lq1, lr1, lg1, ls1);
+            if (tile + 1 < ntiles) step(tile + 1, tile + 2, lq1, lr1, lg1, ls1, lq0, lr0, lg0, ls0);
+        }
+    } else {
+        while (true) {
+            int nxt = next_tile(tile + 1);
+            step(tile, nxt, lq0, lr0, lg0, ls0, lq1, lr1, lg1, ls1);
+            if (nxt >= ntiles) break;
+            tile = nxt;
+            nxt = next_tile(tile + 1);
+            step(tile, nxt, lq1, lr1, lg1, ls1, lq0, lr0, lg0, ls0);
+            if (nxt >= ntiles) break;
+            tile = nxt;
+        }
     }
 
 #pragma unroll
@@ -727,28 +799,28 @@ __device__ __forceinline__ void bwd_keys_item(const BackwardArgs &a, const int i
 // PERSIST = false: one work item per workgroup (dense batches); true: a
 // persistent grid drawing items from per-XCD queues (packed batches; the
 // row pass uses counters 0..7, the key pass 8..15).
-template <int HPW, bool PERSIST>
+template <int HPW, bool PERSIST, bool MASK>
 __global__ __launch_bounds__(64 * kBwdWaves) void bwd_rows_mfma_bf16_d128(BackwardArgs a) {
     if (!PERSIST) {
-        bwd_rows_item<HPW>(a, blockIdx.x);
+        bwd_rows_item<HPW, MASK>(a, blockIdx.x);
         return;
     }
     constexpr int RPH = 16 * kBwdWaves / HPW;
     const int n_items = a.B * a.Hkv * (a.Hq / a.Hkv / HPW) * ((a.L + RPH - 1) / RPH);
     for (int item = next_item(a.sched, n_items); item >= 0; item = next_item(a.sched, n_items))
-        bwd_rows_item<HPW>(a, item);
+        bwd_rows_item<HPW, MASK>(a, item);
 }
 
-template <bool PERSIST>
+template <bool PERSIST, bool MASK>
 __global__ __launch_bounds__(64 * kKeyWaves) void bwd_keys_mfma_bf16_d128(BackwardArgs a) {
     if (!PERSIST) {
-        bwd_keys_item(a, blockIdx.x);
+        bwd_keys_item<MASK>(a, blockIdx.x);
         return;
     }
     constexpr int KB = 16 * kKeyBlocksPerWave * kKeyWaves;
     const int n_items = a.B * a.Hkv * ((a.L + KB - 1) / KB);
     for (int item = next_item(a.sched + 8, n_items); item >= 0; item = next_item(a.sched + 8, n_items))
-        bwd_keys_item(a, item);
+        bwd_keys_item<MASK>(a, item);
 }
 
 template <typename T, int D>
@@ -757,6 +829,42 @@ hipError_t launch_generic(const BackwardArgs &a, hipStream_t stream) {
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL((bwd_keys_generic<T, D>), dim3(a.L, a.Hkv, a.B), dim3(64), 0, stream, a);
+    return hipGetLastError();
+}
+
+
+
+// The row pass, then the key pass, on matrix cores (MASK: a block mask is given).
+template <bool MASK>
+hipError_t launch_mfma_passes(const BackwardArgs &a, int hpw, long row_items, long key_items,
+                              hipStream_t stream) {
+    // persistent workers, a multiple of 8 so that every XCD share is drained
+    auto workers = [&](long items) { return (unsigned)(((items < a.workers ? items : a.workers) + 7) / 8 * 8); };
+    hipError_t err;
+    if (a.sched) {
+        err = launch_zero_counters(a.sched, 16, stream);
+        if (err != hipSuccess) return err;
+        if (hpw == 2)
+            hipLaunchKernelGGL((bwd_rows_mfma_bf16_d128<2, true, MASK>), dim3(workers(row_items)),
+                               dim3(64 * kBwdWaves), 0, stream, a);
+        else
+            hipLaunchKernelGGL((bwd_rows_mfma_bf16_d128<1, true, MASK>), dim3(workers(row_items)),
+                               dim3(64 * kBwdWaves), 0, stream, a);
+    } else if (hpw == 2) {
+        hipLaunchKernelGGL((bwd_rows_mfma_bf16_d128<2, false, MASK>), dim3((unsigned)row_items),
+                           dim3(64 * kBwdWaves), 0, stream, a);
+    } else {
+        hipLaunchKernelGGL((bwd_rows_mfma_bf16_d128<1, false, MASK>), dim3((unsigned)row_items),
+                           dim3(64 * kBwdWaves), 0, stream, a);
+    }
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    if (a.sched)
+        hipLaunchKernelGGL((bwd_keys_mfma_bf16_d128<true, MASK>), dim3(workers(key_items)),
+                           dim3(64 * kKeyWaves), 0, stream, a);
+    else
+        hipLaunchKernelGGL((bwd_keys_mfma_bf16_d128<false, MASK>), dim3((unsigned)key_items),
+                           dim3(64 * kKeyWaves), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -770,36 +878,9 @@ hipError_t launch_prefill_backward(const BackwardArgs &a, int dtype, hipStream_t
         const long row_items = (long)a.B * a.Hkv * (G / hpw) * ((a.L + rph - 1) / rph);
         constexpr int kb = 16 * kKeyBlocksPerWave * kKeyWaves;
         const long key_items = (long)a.B * a.Hkv * ((a.L + kb - 1) / kb);
-        if (row_items <= 0x7fffffffL && key_items <= 0x7fffffffL) {
-            // persistent workers, a multiple of 8 so that every XCD share is drained
-            auto workers = [&](long items) { return (unsigned)(((items < a.workers ? items : a.workers) + 7) / 8 * 8); };
-            hipError_t err;
-            if (a.sched) {
-                err = launch_zero_counters(a.sched, 16, stream);
-                if (err != hipSuccess) return err;
-                if (hpw == 2)
-                    hipLaunchKernelGGL((bwd_rows_mfma_bf16_d128<2, true>), dim3(workers(row_items)),
-                                       dim3(64 * kBwdWaves), 0, stream, a);
-                else
-                    hipLaunchKernelGGL((bwd_rows_mfma_bf16_d128<1, true>), dim3(workers(row_items)),
-                                       dim3(64 * kBwdWaves), 0, stream, a);
-            } else if (hpw == 2) {
-                hipLaunchKernelGGL((bwd_rows_mfma_bf16_d128<2, false>), dim3((unsigned)row_items),
-                                   dim3(64 * kBwdWaves), 0, stream, a);
-            } else {
-                hipLaunchKernelGGL((bwd_rows_mfma_bf16_d128<1, false>), dim3((unsigned)row_items),
-                                   dim3(64 * kBwdWaves), 0, stream, a);
-            }
-            err = hipGetLastError();
-            if (err != hipSuccess) return err;
-            if (a.sched)
-                hipLaunchKernelGGL((bwd_keys_mfma_bf16_d128<true>), dim3(workers(key_items)),
-                                   dim3(64 * kKeyWaves), 0, stream, a);
-            else
-                hipLaunchKernelGGL((bwd_keys_mfma_bf16_d128<false>), dim3((unsigned)key_items),
-                                   dim3(64 * kKeyWaves), 0, stream, a);
-            return hipGetLastError();
-        }
+        if (row_items <= 0x7fffffffL && key_items <= 0x7fffffffL)
+            return a.block_mask ? launch_mfma_passes<true>(a, hpw, row_items, key_items, stream)
+                                : launch_mfma_passes<false>(a, hpw, row_items, key_items, stream);
     }
     if (dtype == 1)
         return a.D == 64 ? launch_generic<uint16_t, 64>(a, stream) : launch_generic<uint16_t, 128>(a, stream);

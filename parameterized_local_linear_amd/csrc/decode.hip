@@ -58,8 +58,10 @@ typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ int kswz(int key) { return 2 * ((key >> 2) & 3) + 9 * (key & 1); }
 
 struct SeqRange {
-    int64_t tok0;  // first token of the sequence in the K/V arrays
-    int len;
+    int64_t tok0;  // first token of the visible range in the K/V arrays
+    int len;       // keys in the visible range
+    int pos0;      // sequence position of the range's first key (window start)
+    int last_blk;  // block-sparse: block of the sequence's last key (always visible)
 };
 
 __device__ __forceinline__ SeqRange seq_range(const DecodeArgs &a, int b) {
@@ -72,11 +74,19 @@ __device__ __forceinline__ SeqRange seq_range(const DecodeArgs &a, int b) {
         s.tok0 = (int64_t)b * a.kv_len;
         s.len = a.kv_len;
     }
+    s.pos0 = 0;
+    s.last_blk = (s.len - 1) >> kMaskShift;
     if (a.window > 0 && s.len > a.window) {  // sliding window: the last `window` keys
-        s.tok0 += s.len - a.window;
+        s.pos0 = s.len - a.window;
+        s.tok0 += s.pos0;
         s.len = a.window;
     }
     return s;
+}
+
+// Block-sparse visibility of a sequence's key block (uniform), nullptr: all.
+__device__ __forceinline__ const uint8_t *mask_row(const DecodeArgs &a, int b, int hkv) {
+    return a.block_mask ? a.block_mask + ((int64_t)b * a.Hkv + hkv) * a.mask_cols : nullptr;
 }
 
 // -------------------------------------------------------------------------
@@ -102,13 +112,24 @@ __device__ __forceinline__ SeqRange seq_range(const DecodeArgs &a, int b) {
 // Readout MFMA e (e = 0..7): A row m <- dim 8m + e, so output row 4g + i is
 // dim 32g + 8i + e: lane (g, n) accumulates P-row n over dims 32g .. 32g+31.
 // -------------------------------------------------------------------------
-// Keys start .. end - 1 (sequence-relative, non-empty) of sequence b, whose
-// first token is seq_tok0, for KV head hkv: writes the G heads' records at
-// record index rbase + h * rstride, or o when `fused`. Ends with a workgroup
-// barrier, so a workgroup may stream several ranges in a row.
-template <int G, bool PLX>
+// Keys start .. end - 1 (range-relative, non-empty) of sequence b, whose
+// range starts at token seq_tok0 and sequence position pos0, for KV head
+// hkv: writes the G heads' records at record index rbase + h * rstride, or o
+// when `fused`. Ends with a workgroup barrier, so a workgroup may stream
+// several ranges in a row.
+//
+// MASK (a block mask is given): the waves walk the visible 128-key blocks of
+// the range only -- wave w takes keys 32w .. 32w + 31 of each -- so every
+// load in flight is a visible tile. With nvsplit > 0 the range is the whole
+// window (start = 0) and this workgroup takes the vsplit-th of nvsplit equal
+// shares of its visible blocks, which balances the splits whatever the mask.
+// Keys outside start .. end - 1 of a block that straddles the range's edge
+// are masked per key.
+template <int G, bool PLX, bool MASK>
 __device__ __forceinline__ void decode_range(const DecodeArgs &a, const int hkv, const int b,
                                              const int64_t seq_tok0, const int start, const int end,
+                                             const int pos0, const int last_blk,
+                                             const int vsplit, const int nvsplit,
                                              const int64_t rbase, const int64_t rstride,
                                              const bool fused) {
     constexpr int D = 128;
@@ -148,10 +169,51 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, const int hkv,
     const int koff1 = (16 + kperm) * ts_bytes + 16 * g;  // block 1
     const int voff = g * ts_bytes + 16 * n;              // key g + 4t at + 4t keys
 
+    // Block-sparse: the visibility of the blocks this range touches, staged in
+    // LDS by all threads at once (the block holding the sequence's last key is
+    // always visible); each wave then walks the visible ones with a 64-block
+    // ballot window. A tile past the walk's end reads past the buffer range.
+    __shared__ uint8_t svis[MASK ? kMaxRangeBlocks : 1];
+    __shared__ int svis_total;
+    const int blk0 = (pos0 + start) >> kMaskShift;
+    const int nblk = MASK ? ((pos0 + end - 1) >> kMaskShift) - blk0 + 1 : 0;
+    int walk_first = 0, walk_count = 0;  // ordinal share of the visible blocks (MASK)
+    uint64_t wbits = 0;
+    int wbase = -64;
+    if constexpr (MASK) {
+        const uint8_t *mrow = mask_row(a, b, hkv);
+        if (threadIdx.x == 0) svis_total = 0;
+        __syncthreads();
+        int mine = 0;
+        for (int i = threadIdx.x; i < nblk; i += 64 * W) {
+            const bool v = blk0 + i == last_blk || mrow[blk0 + i] != 0;
+            svis[i] = v ? 1 : 0;
+            mine += v ? 1 : 0;
+        }
+        if (nvsplit > 0 && mine > 0) atomicAdd(&svis_total, mine);
+        __syncthreads();
+        if (nvsplit > 0) {
+            const int per = (svis_total + nvsplit - 1) / nvsplit;
+            walk_first = vsplit * per;
+            walk_count = max(0, min(svis_total - walk_first, per));
+        } else {
+            walk_count = nblk;  // every visible block of the range
+        }
+    }
+    // next visible block index (relative to blk0) at or after i, or nblk
+    auto next_block = [&](int i) {
+        return next_visible(i, nblk, wbits, wbase, [&](int u) { return svis[u] != 0; });
+    };
+    const int oob = (end - start + kMaskBlock) * ts_bytes;  // a tile offset past the buffer range
+    auto tile_offset = [&](int t) {
+        if constexpr (!MASK) return (t - start) * ts_bytes;  // past `end`: outside the range too
+        return t < end ? (t - start) * ts_bytes : oob;
+    };
+
     // The whole offset goes in the VGPR operand: the range check of a raw
     // buffer access covers the VGPR and immediate offsets, not soffset.
     auto load_k = [&](int t0, bf16x8 *kt) {
-        const int tb = (t0 - start) * ts_bytes;  // wave-uniform
+        const int tb = tile_offset(t0);  // wave-uniform
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             kt[u] = buffer_load16(krs, tb + koff0 + 64 * u);
@@ -159,7 +221,7 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, const int hkv,
         }
     };
     auto load_v = [&](int t0, bf16x8 *vt) {
-        const int vo = (t0 - start) * ts_bytes + voff;
+        const int vo = tile_offset(t0) + voff;
 #pragma unroll
         for (int t = 0; t < 8; ++t) vt[t] = buffer_load16(vrs, vo + 4 * t * ts_bytes);
     };
@@ -171,7 +233,7 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, const int hkv,
     __shared__ __attribute__((aligned(16))) uint16_t sk1[kDecodeKInLds ? W * 32 * D : 8];
     auto dma_k = [&](int t0, uint16_t *slot) __attribute__((always_inline)) {
         uint16_t *base = slot + wave * 32 * D;
-        const int tb = (t0 - start) * ts_bytes;
+        const int tb = tile_offset(t0);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int key = 4 * j + (lane >> 4);
@@ -219,10 +281,42 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, const int hkv,
     constexpr int kStride = 32 * W;  // keys between a wave's consecutive tiles
     bf16x8 kA[8], vA[8], kB[8], vB[8];
     int t0 = start + 32 * wave;
-    if constexpr (kDecodeKInLds) dma_k(t0, sk0); else load_k(t0, kA);
-    load_v(t0, vA);
-    if constexpr (kDecodeKInLds) dma_k(t0 + kStride, sk1); else load_k(t0 + kStride, kB);
-    load_v(t0 + kStride, vB);
+    // MASK: the walk's first two tiles (end: none). The walk starts at the
+    // walk_first-th visible block.
+    int tw[2] = {end, end};
+    int wblk = -1;
+    if constexpr (MASK) {
+        // the walk_first-th visible block: skip whole 64-block windows by their
+        // popcount, then clear the remaining lower set bits of the window
+        int i = 0, skip_n = walk_first;
+        while (skip_n > 0 && i < nblk) {
+            const int u = i + lane;
+            uint64_t m = __builtin_amdgcn_ballot_w64(u < nblk && svis[u] != 0);
+            const int c = __builtin_popcountll(m);
+            if (c <= skip_n) {
+                skip_n -= c;
+                i += 64;
+            } else {
+                for (; skip_n > 0; --skip_n) m &= m - 1;
+                i += __builtin_ctzll(m);
+            }
+        }
+        for (int k = 0; k < 2 && k < walk_count; ++k) {
+            wblk = next_block(k == 0 ? i : wblk + 1);
+            tw[k] = ((blk0 + wblk) << kMaskShift) + 32 * wave - pos0;
+        }
+    }
+    if constexpr (MASK) {
+        if constexpr (kDecodeKInLds) dma_k(tw[0], sk0); else load_k(tw[0], kA);
+        load_v(tw[0], vA);
+        if constexpr (kDecodeKInLds) dma_k(tw[1], sk1); else load_k(tw[1], kB);
+        load_v(tw[1], vB);
+    } else {
+        if constexpr (kDecodeKInLds) dma_k(t0, sk0); else load_k(t0, kA);
+        load_v(t0, vA);
+        if constexpr (kDecodeKInLds) dma_k(t0 + kStride, sk1); else load_k(t0 + kStride, kB);
+        load_v(t0 + kStride, vB);
+    }
 
     if (!live) {
 #pragma unroll
@@ -244,7 +338,10 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, const int hkv,
     // raised when a tile's max exceeds it by more than kRescaleSlack (or on
     // the first tile), so the accumulators are rarely rescaled; terms are
     // then at most 2^kRescaleSlack, far from fp32 or bf16 overflow.
-    float m_run = -INFINITY;
+    // (MASK: finite, because a wave's quarter of a block that straddles the
+    // range's edge can lie wholly outside the range, and exp2(-inf - m_run)
+    // must then be 0; a wave that saw no key is marked -inf again below.)
+    float m_run = MASK ? -1e30f : -INFINITY;
     float lsum = 0.0f;  // per-lane partial: sum p (n even) or sum p s' (n odd)
     floatx4 acc[8];
     for (int e = 0; e < 8; ++e) acc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -253,7 +350,10 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, const int hkv,
     const float fa = (PLX && kind) ? a.rk_scale : 0.f;
     const float fc = (PLX && kind) ? -piv : 1.f;
 
-    auto step = [&](bool tail, bf16x8 *kt, bf16x8 *vt, uint16_t *slot) {
+    // Consume the tile at t0 (range-relative), then issue this buffer's loads
+    // for the tile at tn. masked: some keys of the tile lie outside start ..
+    // end - 1 (the range's tail, or the edge of a straddling block).
+    auto step = [&](bool masked, bf16x8 *kt, bf16x8 *vt, uint16_t *slot, int t0, int tn) {
         // ---- both score sets from one K tile
         bf16x8 kl[8];
         if constexpr (kDecodeKInLds) {
@@ -267,7 +367,7 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, const int hkv,
             sc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt[4 + u], qr[u], sc1, 0, 0, 0);
         }
         // this buffer's next K tile, as soon as the scores hold its operands
-        if constexpr (kDecodeKInLds) dma_k(t0 + 2 * kStride, slot); else load_k(t0 + 2 * kStride, kt);
+        if constexpr (kDecodeKInLds) dma_k(tn, slot); else load_k(tn, kt);
         float raw[8], zr[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -281,7 +381,8 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, const int hkv,
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             zr[t] = PLX ? dpp_pair_even(raw[t]) : raw[t];
-            if (tail && g + 4 * t >= nvalid) zr[t] = -INFINITY;
+            if (masked && (g + 4 * t >= nvalid || (MASK && t0 + g + 4 * t < start)))
+                zr[t] = -INFINITY;
             rmax = fmaxf(rmax, zr[t]);
         }
         // lazy rescale, decided for the whole wave from the lane-local max;
@@ -328,19 +429,51 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, const int hkv,
 #pragma unroll
         for (int e = 0; e < 8; ++e)
             acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vT[e], pf, acc[e], 0, 0, 0);
-        load_v(t0 + 2 * kStride, vt);  // and its next V tile
-        t0 += kStride;
+        load_v(tn, vt);  // and its next V tile
     };
 
-    while (true) {
-        if (t0 >= end) break;
-        if (t0 + 32 <= end) step(false, kA, vA, sk0); else step(true, kA, vA, sk0);
-        if (t0 >= end) break;
-        if (t0 + 32 <= end) step(false, kB, vB, sk1); else step(true, kB, vB, sk1);
+    if constexpr (!MASK) {
+        while (true) {
+            if (t0 >= end) break;
+            if (t0 + 32 <= end) step(false, kA, vA, sk0, t0, t0 + 2 * kStride);
+            else step(true, kA, vA, sk0, t0, t0 + 2 * kStride);
+            t0 += kStride;
+            if (t0 >= end) break;
+            if (t0 + 32 <= end) step(false, kB, vB, sk1, t0, t0 + 2 * kStride);
+            else step(true, kB, vB, sk1, t0, t0 + 2 * kStride);
+            t0 += kStride;
+        }
+    } else {
+        // tiles cur (buffer A), nx1 (buffer B), nx2 as range-relative t0;
+        // `end` marks a finished walk
+        int cur = tw[0], nx1 = tw[1], done = 2;
+        while (true) {
+            if (cur >= end) break;
+            int nx2 = end;
+            if (done < walk_count) {
+                wblk = next_block(wblk + 1);
+                nx2 = ((blk0 + wblk) << kMaskShift) + 32 * wave - pos0;
+                ++done;
+            }
+            step(cur < start || cur + 32 > end, kA, vA, sk0, cur, nx2);
+            cur = nx1;
+            nx1 = nx2;
+            if (cur >= end) break;
+            nx2 = end;
+            if (done < walk_count) {
+                wblk = next_block(wblk + 1);
+                nx2 = ((blk0 + wblk) << kMaskShift) + 32 * wave - pos0;
+                ++done;
+            }
+            step(cur < start || cur + 32 > end, kB, vB, sk1, cur, nx2);
+            cur = nx1;
+            nx1 = nx2;
+        }
     }
     // the read-ahead copies land in LDS before the workgroup moves on (or ends)
     if constexpr (kDecodeKInLds) __syncthreads();
 
+    if (MASK && m_run < -1e29f) m_run = -INFINITY;  // no visible key in this wave
     lsum = xor_sum_rowgroups(lsum);
 
     // ---- merge the waves' states in LDS
@@ -429,7 +562,7 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, const int hkv,
 
 // One workgroup per (KV head, split, sequence): the split's keys of its
 // sequence. An empty split writes an empty record (or, fused, o = 0).
-template <int G, bool PLX>
+template <int G, bool PLX, bool MASK>
 __global__ __launch_bounds__(64 * kDecodeWaves)
 void decode_mfma_bf16_d128(DecodeArgs a) {
     constexpr int D = 128;
@@ -439,7 +572,17 @@ void decode_mfma_bf16_d128(DecodeArgs a) {
     const SeqRange sr = seq_range(a, b);
     const int start = split * a.chunk;
     const int64_t row0 = (int64_t)b * a.Hq + (int64_t)hkv * G;  // first query row of the group
-    if (sr.len <= 0 || start >= sr.len) {
+    // Block mask: the splits share the window's visible blocks equally when its
+    // blocks fit the LDS staging and its bytes 32-bit offsets; otherwise each
+    // split walks the visible blocks of its own key range.
+    bool whole = false;
+    if constexpr (MASK) {
+        const int nblk = ((sr.pos0 + sr.len - 1) >> kMaskShift) - (sr.pos0 >> kMaskShift) + 1;
+        const int64_t tok_bytes = (int64_t)a.Hkv * D * 2;
+        whole = sr.len > 0 && nblk <= kMaxRangeBlocks &&
+                ((int64_t)sr.len + 2 * kMaskBlock + 64) * tok_bytes + 1024 < 0x7fffffffLL;
+    }
+    if (sr.len <= 0 || (!whole && start >= sr.len)) {
         // Nothing to stream: a fused call writes the zero output of an empty
         // sequence, otherwise the records are marked empty for the merge.
         if (a.fused) {
@@ -451,8 +594,13 @@ void decode_mfma_bf16_d128(DecodeArgs a) {
         }
         return;
     }
-    decode_range<G, PLX>(a, hkv, b, sr.tok0, start, min(start + a.chunk, sr.len),
-                         row0 * a.splits + split, a.splits, a.fused);
+    if (whole)
+        decode_range<G, PLX, MASK>(a, hkv, b, sr.tok0, 0, sr.len, sr.pos0, sr.last_blk, split,
+                                   a.splits, row0 * a.splits + split, a.splits, a.fused);
+    else
+        decode_range<G, PLX, MASK>(a, hkv, b, sr.tok0, start, min(start + a.chunk, sr.len),
+                                   sr.pos0, sr.last_blk, 0, 0, row0 * a.splits + split, a.splits,
+                                   a.fused);
 }
 
 // Packed batches (stream-K): the tokens of one KV head, all sequences back to
@@ -462,7 +610,7 @@ void decode_mfma_bf16_d128(DecodeArgs a) {
 // piece (range w, sequence b) goes to record slot w + b of its query head
 // (unique: when range w + k overlaps sequence b - k, sequence b starts after
 // range w ends), [Hq][sk_parts + B - 1] records in all.
-template <int G, bool PLX>
+template <int G, bool PLX, bool MASK>
 __global__ __launch_bounds__(64 * kDecodeWaves)
 void decode_mfma_streamk(DecodeArgs a) {
     const int part = blockIdx.x;
@@ -484,8 +632,8 @@ void decode_mfma_streamk(DecodeArgs a) {
         if (s0 >= t_hi) break;
         const int p0 = max(t_lo, s0), p1 = min(t_hi, s1);
         if (p0 >= p1) continue;  // empty sequence, or one that ends before the range
-        decode_range<G, PLX>(a, hkv, b, s0, p0 - s0, p1 - s0, (int64_t)hkv * G * ns + part + b, ns,
-                             false);
+        decode_range<G, PLX, MASK>(a, hkv, b, s0, p0 - s0, p1 - s0, 0, (s1 - s0 - 1) >> kMaskShift,
+                                   0, 0, (int64_t)hkv * G * ns + part + b, ns, false);
     }
 }
 
@@ -610,9 +758,14 @@ __global__ __launch_bounds__(64) void decode_generic(DecodeArgs a) {
         st.B[e] = 0.f;
     }
 
+    const uint8_t *mrow = mask_row(a, b, hkv);
     for (int j0 = start; j0 < end; j0 += KPI) {
         const int j = j0 + kgrp;
-        const bool valid = j < end;
+        bool valid = j < end;
+        if (mrow && valid) {  // block-sparse: hidden blocks other than the last key's
+            const int blk = (sr.pos0 + j) >> kMaskShift;
+            valid = blk == sr.last_blk || mrow[blk] != 0;
+        }
         const int jj = valid ? j : end - 1;
         float kv[EPL], vv[EPL];
         Elem<T>::load(kseq + (int64_t)jj * tok_stride, kv);
@@ -769,27 +922,27 @@ __global__ __launch_bounds__(256) void decode_reduce(DecodeArgs a) {
         *o = f32_to_bf16(val);
 }
 
-template <bool PLX>
+template <bool PLX, bool MASK>
 hipError_t launch_mfma(const DecodeArgs &a, hipStream_t stream) {
     dim3 block(64 * kDecodeWaves);
     const int G = a.Hq / a.Hkv;
     if (a.sk_parts) {
         dim3 grid(a.sk_parts, a.Hkv);
         switch (G) {
-            case 1: hipLaunchKernelGGL((decode_mfma_streamk<1, PLX>), grid, block, 0, stream, a); break;
-            case 2: hipLaunchKernelGGL((decode_mfma_streamk<2, PLX>), grid, block, 0, stream, a); break;
-            case 4: hipLaunchKernelGGL((decode_mfma_streamk<4, PLX>), grid, block, 0, stream, a); break;
-            case 8: hipLaunchKernelGGL((decode_mfma_streamk<8, PLX>), grid, block, 0, stream, a); break;
+            case 1: hipLaunchKernelGGL((decode_mfma_streamk<1, PLX, MASK>), grid, block, 0, stream, a); break;
+            case 2: hipLaunchKernelGGL((decode_mfma_streamk<2, PLX, MASK>), grid, block, 0, stream, a); break;
+            case 4: hipLaunchKernelGGL((decode_mfma_streamk<4, PLX, MASK>), grid, block, 0, stream, a); break;
+            case 8: hipLaunchKernelGGL((decode_mfma_streamk<8, PLX, MASK>), grid, block, 0, stream, a); break;
             default: return hipErrorInvalidValue;
         }
         return hipGetLastError();
     }
     dim3 grid(a.Hkv, a.splits, a.B);
     switch (G) {
-        case 1: hipLaunchKernelGGL((decode_mfma_bf16_d128<1, PLX>), grid, block, 0, stream, a); break;
-        case 2: hipLaunchKernelGGL((decode_mfma_bf16_d128<2, PLX>), grid, block, 0, stream, a); break;
-        case 4: hipLaunchKernelGGL((decode_mfma_bf16_d128<4, PLX>), grid, block, 0, stream, a); break;
-        case 8: hipLaunchKernelGGL((decode_mfma_bf16_d128<8, PLX>), grid, block, 0, stream, a); break;
+        case 1: hipLaunchKernelGGL((decode_mfma_bf16_d128<1, PLX, MASK>), grid, block, 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((decode_mfma_bf16_d128<2, PLX, MASK>), grid, block, 0, stream, a); break;
+        case 4: hipLaunchKernelGGL((decode_mfma_bf16_d128<4, PLX, MASK>), grid, block, 0, stream, a); break;
+        case 8: hipLaunchKernelGGL((decode_mfma_bf16_d128<8, PLX, MASK>), grid, block, 0, stream, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -819,8 +972,11 @@ hipError_t launch_reduce(const DecodeArgs &a, hipStream_t stream) {
 
 hipError_t launch_decode_split(const DecodeArgs &a, DecodePath path, int dtype, bool parallax,
                                hipStream_t stream) {
-    if (path == DecodePath::Mfma)
-        return parallax ? launch_mfma<true>(a, stream) : launch_mfma<false>(a, stream);
+    if (path == DecodePath::Mfma) {
+        if (a.block_mask)
+            return parallax ? launch_mfma<true, true>(a, stream) : launch_mfma<false, true>(a, stream);
+        return parallax ? launch_mfma<true, false>(a, stream) : launch_mfma<false, false>(a, stream);
+    }
     if (dtype == 1)
         return parallax ? launch_generic<uint16_t, true>(a, stream)
                         : launch_generic<uint16_t, false>(a, stream);

@@ -97,6 +97,26 @@ __device__ __forceinline__ int64_t stat0(const PrefillSeq &s, int b, int h, int 
 }
 __device__ __forceinline__ int stat_stride(const PrefillSeq &s, int H) { return s.packed ? H : 1; }
 
+// Block-sparse tile scan: the first tile u >= t (u < n) with vis(u), or n.
+// Every lane of the wave evaluates vis for one of 64 consecutive tiles at a
+// time; the wave keeps their ballot in (bits, base) between calls (start
+// with base = -64), so a sweep over n tiles reads each mask byte once.
+// Wave-uniform result.
+template <typename Vis>
+__device__ __forceinline__ int next_visible(int t, int n, uint64_t &bits, int &base, const Vis &vis) {
+    while (t < n) {
+        if (t < base || t >= base + 64) {
+            base = t;
+            const int u = t + (int)(threadIdx.x & 63);
+            bits = __builtin_amdgcn_ballot_w64(u < n && vis(u));
+        }
+        const uint64_t rest = bits >> (t - base);
+        if (rest) return t + (int)__builtin_ctzll(rest);
+        t = base + 64;
+    }
+    return n;
+}
+
 // Dynamic work queue of a persistent launch (packed batches, whose grid would
 // otherwise hold a workgroup for every (sequence, tile) slot up to the longest
 // sequence). Workgroup w draws from the share of XCD x = w % 8 (consecutive

@@ -13,6 +13,16 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Block-sparse masks: positions are cut into blocks of kMaskBlock from the
+// start of each sequence; one byte per (sequence, KV head, [query block,]
+// key block), nonzero = visible. A query always sees its own block.
+constexpr int kMaskBlock = 128;
+constexpr int kMaskShift = 7;
+// Keys one decode workgroup streams in one range at most (its blocks'
+// visibility is staged in LDS).
+constexpr int kMaxRangeBlocks = 4096;
+constexpr int kMaxRangeKeys = (kMaxRangeBlocks - 2) * kMaskBlock;
+
 // One decode split's streaming state ("record"), stored in the workspace as
 // A[D], B[D], m, l, S, pi (2D + 4 floats) for every (b, hq, split).
 //   m  : maximum of the logits over the split's keys, in log2 units
@@ -37,6 +47,8 @@ struct DecodeArgs {
     int sk_parts;       // 0, or the stream-K plan's ranges per KV head (packed batches)
     float *ws;          // records [B][Hq][splits] ([Hq][sk_parts + B - 1] stream-K), unless fused
     bool fused;         // one split and no records: write o directly
+    const uint8_t *block_mask;  // nullptr, or [B, Hkv, mask_cols] key-block visibility
+    int mask_cols;      // ceil(kv_len / kMaskBlock)
 };
 
 enum class DecodePath { Mfma, Generic };
@@ -69,6 +81,7 @@ struct PrefillArgs {
     int workers;        // compute units of the device (sizes the persistent grid)
     int B, Hq, Hkv, L, D;  // L: the (maximum) sequence length
     int window;         // query i sees keys i - window + 1 .. i (window = L: causal only)
+    const uint8_t *block_mask;  // nullptr, or [B, Hkv, nb, nb], nb = ceil(L / kMaskBlock)
     float zscale;       // qk_scale * log2(e)
     float rk_scale;
 };
@@ -95,6 +108,7 @@ struct BackwardArgs {
     int workers;                         // workgroups of a persistent launch
     int B, Hq, Hkv, L, D;
     int window;                          // as in PrefillArgs, 1 .. L
+    const uint8_t *block_mask;           // as in PrefillArgs
     float zscale;                        // qk_scale * log2(e)
     float qk_scale, rk_scale;
 };

@@ -8,7 +8,7 @@
 // Optional row statistics for a backward pass: lse_i = ln sum_j exp(z_ij)
 // and sbar_i.
 //
-// prefill_mfma_bf16_d128<HPW>: bf16, head_dim 128, all four contractions
+// prefill_mfma_bf16_d128<HPW, MASK>: bf16, head_dim 128, all four contractions
 // (Q K^T, R K^T, P V, (P o S) V) on v_mfma_f32_16x16x32_bf16 with fp32
 // accumulation. Described at the kernel.
 // prefill_generic<T, D>: any dtype / head_dim; one wave per query row,
@@ -95,9 +95,14 @@ __global__ __launch_bounds__(64) void prefill_generic(PrefillArgs a) {
         Bv[e] = 0.f;
     }
     const int end = i + 1;
+    // block-sparse: this row's query block's mask row (its own block is always visible)
+    const int nb = (a.L + kMaskBlock - 1) >> kMaskShift;
+    const uint8_t *mrow = a.block_mask
+        ? a.block_mask + (((int64_t)b * a.Hkv + hkv) * nb + (i >> kMaskShift)) * nb : nullptr;
     for (int j0 = first; j0 < end; j0 += KPI) {
         const int j = j0 + kgrp;
-        const bool valid = j < end;
+        bool valid = j < end;
+        if (mrow && valid && (j >> kMaskShift) != (i >> kMaskShift)) valid = mrow[j >> kMaskShift] != 0;
         const int jj = valid ? j : end - 1;
         float kv[EPL], vv[EPL];
         Vec16<T>::load(kb + (int64_t)jj * ks, kv);
@@ -189,7 +194,9 @@ __global__ __launch_bounds__(64) void prefill_generic(PrefillArgs a) {
 // Causality: keys j <= i, and with a sliding window W also j > i - W. Tiles
 // entirely outside a wave's visible band are skipped, tiles crossing either
 // edge of the band are masked (and their 32-key sub-tiles holding none of the
-// wave's keys skipped). Work items run heaviest-first
+// wave's keys skipped). A block-sparse mask removes whole tiles (a tile is one
+// 128-key block, a work item's rows lie in one 128-row block): the loop walks
+// the visible tiles only, so hidden ones are neither copied nor computed. Work items run heaviest-first
 // (last q-tile first), and the group index varies fastest so that all
 // q-tiles of one (sequence, KV head) land on one XCD when the number of
 // groups is a multiple of 8 (its L2 then holds that head's K/V).
@@ -203,7 +210,7 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 // One work item; returns before any barrier when the item lies past its
 // sequence's end.
-template <int HPW>
+template <int HPW, bool MASK>
 __device__ __forceinline__ void prefill_item(const PrefillArgs &a, const int item) {
     constexpr int D = 128;
     constexpr int NW = kPrefillWaves;
@@ -213,6 +220,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs &a, const int ite
     constexpr int NSUB = TK / 32;       // sub-tiles per tile
     constexpr int DMA = TK / (4 * NW);  // 1 KB copies (4 keys) of K, and of V, per wave per tile
     static_assert(NW % HPW == 0 && DMA >= 1, "bad workgroup shape");
+    static_assert(TK == kMaskBlock && kMaskBlock % RPH == 0, "a tile is one mask block");
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int n = lane & 15;
@@ -268,7 +276,18 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs &a, const int ite
             __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void *)(lv + kloc * D), 16, off, 0, 0, 0);
         }
     };
-    dma_tile(tile0, lds_k0, lds_v0);
+    // block-sparse: the tiles (key blocks) this item's query block sees
+    const int qb = (qt * RPH) >> kMaskShift;
+    const int nb = (a.L + kMaskBlock - 1) >> kMaskShift;
+    const uint8_t *mrow = MASK ? a.block_mask + (((int64_t)b * a.Hkv + hkv) * nb + qb) * nb : nullptr;
+    uint64_t vbits = 0;
+    int vbase = -64;
+    auto next_tile = [&](int t) {
+        if constexpr (!MASK) return t;
+        return next_visible(t, ntiles, vbits, vbase, [&](int u) { return u == qb || mrow[u] != 0; });
+    };
+    int tile = next_tile(tile0);  // the diagonal tile is always visible
+    dma_tile(tile, lds_k0, lds_v0);
 
     // ---- per-wave query operands (k-step u) and the row's pivot
     bf16x8 qop[4], rop[4];
@@ -438,8 +457,8 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs &a, const int ite
             pv(p, load_vT(lv, 32 * j));
         }
     };
-    auto tile_step = [&](int tile, uint16_t *lk, uint16_t *lv, uint16_t *nk, uint16_t *nv) __attribute__((always_inline)) {
-        if (tile + 1 < ntiles) dma_tile(tile + 1, nk, nv);
+    auto tile_step = [&](int tile, int nxt, uint16_t *lk, uint16_t *lv, uint16_t *nk, uint16_t *nv) __attribute__((always_inline)) {
+        if (nxt < ntiles) dma_tile(nxt, nk, nv);
         const int t0 = tile * TK;
         // wave-uniform: tiles above the wave's rows or left of all their windows are skipped;
         // a tile needs the mask unless every key is visible to all 16 rows
@@ -453,9 +472,22 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs &a, const int ite
     };
 
     __syncthreads();
-    for (int tile = tile0; tile < ntiles; tile += 2) {
-        tile_step(tile, lds_k0, lds_v0, lds_k1, lds_v1);
-        if (tile + 1 < ntiles) tile_step(tile + 1, lds_k1, lds_v1, lds_k0, lds_v0);
+    if constexpr (!MASK) {
+        for (; tile < ntiles; tile += 2) {
+            tile_step(tile, tile + 1, lds_k0, lds_v0, lds_k1, lds_v1);
+            if (tile + 1 < ntiles) tile_step(tile + 1, tile + 2, lds_k1, lds_v1, lds_k0, lds_v0);
+        }
+    } else {
+        while (true) {
+            int nxt = next_tile(tile + 1);
+            tile_step(tile, nxt, lds_k0, lds_v0, lds_k1, lds_v1);
+            if (nxt >= ntiles) break;
+            tile = nxt;
+            nxt = next_tile(tile + 1);
+            tile_step(tile, nxt, lds_k1, lds_v1, lds_k0, lds_v0);
+            if (nxt >= ntiles) break;
+            tile = nxt;
+        }
     }
 
     // ---- epilogue: o = (A + B - (S / l) A) / l per row
@@ -482,7 +514,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs &a, const int ite
                                                                 pack_bf16x2(accA[b][2] * inv_l, accA[b][3] * inv_l)};
         }
         if (g == 0) {
-            if (a.lse) a.lse[ro] = m_run * 0.6931471805599453f + logf(l);
+            if (a.lse) a.lse[ro] = fmaf(m_run, 0.6931471805599453f, logf(l));  // one rounding, whatever the contraction
             if (a.sbar) a.sbar[ro] = S * inv_l + piv;
         }
     }
@@ -493,19 +525,19 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs &a, const int ite
 // order: heaviest first, and with a grid that is a multiple of 8, every item
 // of a (sequence, KV head) group on the group's XCD. Either way each item is
 // computed whole by one workgroup.
-template <int HPW>
+template <int HPW, bool MASK>
 __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_mfma_bf16_d128(PrefillArgs a) {
     const int n_items = a.B * a.Hkv * (a.Hq / a.Hkv / HPW) * ((a.L + 16 * kPrefillWaves / HPW - 1) /
                                                             (16 * kPrefillWaves / HPW));
     if (!a.sched) {
         for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-            prefill_item<HPW>(a, item);
+            prefill_item<HPW, MASK>(a, item);
             __syncthreads();  // the next item's first copy overwrites this one's LDS
         }
         return;
     }
     for (int item = next_item(a.sched, n_items); item >= 0; item = next_item(a.sched, n_items))
-        prefill_item<HPW>(a, item);
+        prefill_item<HPW, MASK>(a, item);
 }
 
 __global__ void zero_counters(int *c, int n) {
@@ -539,10 +571,16 @@ hipError_t launch_prefill(const PrefillArgs &a, int dtype, hipStream_t stream) {
                 if (err != hipSuccess) return err;
             }
             dim3 grid((unsigned)wgs), block(64 * kPrefillWaves);
-            if (hpw == 2)
-                hipLaunchKernelGGL((prefill_mfma_bf16_d128<2>), grid, block, 0, stream, a);
-            else
-                hipLaunchKernelGGL((prefill_mfma_bf16_d128<1>), grid, block, 0, stream, a);
+            if (a.block_mask) {
+                if (hpw == 2)
+                    hipLaunchKernelGGL((prefill_mfma_bf16_d128<2, true>), grid, block, 0, stream, a);
+                else
+                    hipLaunchKernelGGL((prefill_mfma_bf16_d128<1, true>), grid, block, 0, stream, a);
+            } else if (hpw == 2) {
+                hipLaunchKernelGGL((prefill_mfma_bf16_d128<2, false>), grid, block, 0, stream, a);
+            } else {
+                hipLaunchKernelGGL((prefill_mfma_bf16_d128<1, false>), grid, block, 0, stream, a);
+            }
             return hipGetLastError();
         }
     }

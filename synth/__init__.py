@@ -30,6 +30,7 @@ BASE_SEED = 20261203
 # tensor ids inside one seed: one independent stream each
 TID_Q, TID_R, TID_K, TID_V, TID_SHIFT, TID_LENGTHS = 0, 1, 2, 3, 4, 5
 TID_DO = 6  # upstream gradient dLoss/do of the training backward
+TID_MASK = 7  # block-sparse masks
 
 
 def build() -> str:
@@ -88,6 +89,14 @@ def uniform_int(seed: int, tid: int, count: int, lo: int, hi: int) -> np.ndarray
     out = np.empty(count, dtype=np.int64)
     _load().synth_uniform_int(seed, tid, count, lo, hi, out.ctypes.data_as(ctypes.c_void_p))
     return out
+
+
+def block_mask(seed: int, shape, density: float) -> np.ndarray:
+    """A uint8 block mask of the given shape: each entry 1 with probability
+    ``density`` (independent draws of stream (seed, TID_MASK), in units of 1/1e6)."""
+    count = int(np.prod(shape))
+    u = uniform_int(seed, TID_MASK, count, 0, 999999)
+    return (u < int(round(density * 1e6))).astype(np.uint8).reshape(shape)
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = plx.lib()
-    assert L.parallax_abi_version() == 3
+    assert L.parallax_abi_version() == 4
     for s in range(5):
         assert L.parallax_status_string(s).decode() == plx.STATUS[s]
     assert L.parallax_status_string(99) == b"unknown status"
@@ -42,11 +42,11 @@ def test_version_and_status_strings():
 
 def _decode(**kw):
     a = dict(q=FAKE, r=FAKE, k=FAKE, v=FAKE, o=FAKE, cu=None, B=1, Hq=4, Hkv=2, D=128, L=64,
-             W=0, qk=0.1, rk=1.0, dt=1, ns=0, ws=None, wsb=0, stream=None)
+             W=0, mask=None, qk=0.1, rk=1.0, dt=1, ns=0, ws=None, wsb=0, stream=None)
     a.update(kw)
     return plx.lib().parallax_decode(a["q"], a["r"], a["k"], a["v"], a["o"], a["cu"], a["B"],
-                                     a["Hq"], a["Hkv"], a["D"], a["L"], a["W"], a["qk"], a["rk"],
-                                     a["dt"], a["ns"], a["ws"], a["wsb"], a["stream"])
+                                     a["Hq"], a["Hkv"], a["D"], a["L"], a["W"], a["mask"], a["qk"],
+                                     a["rk"], a["dt"], a["ns"], a["ws"], a["wsb"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -65,20 +65,20 @@ def test_decode_rejects_on_host(kw, status):
 
 def test_softmax_decode_and_prefill_reject_on_host():
     L = plx.lib()
-    assert L.softmax_decode(FAKE, FAKE, FAKE, FAKE, None, 1, 4, 3, 128, 10, 0, 0.1, 1, 0, None, 0,
+    assert L.softmax_decode(FAKE, FAKE, FAKE, FAKE, None, 1, 4, 3, 128, 10, 0, None, 0.1, 1, 0, None, 0,
                             None) == 1
-    assert L.softmax_decode(FAKE, FAKE, FAKE, FAKE, None, 1, 4, 2, 80, 10, 0, 0.1, 1, 0, None, 0,
+    assert L.softmax_decode(FAKE, FAKE, FAKE, FAKE, None, 1, 4, 2, 80, 10, 0, None, 0.1, 1, 0, None, 0,
                             None) == 2
-    assert L.softmax_decode(FAKE, FAKE, FAKE, FAKE, None, 1, 4, 2, 128, 10, -3, 0.1, 1, 0, None, 0,
+    assert L.softmax_decode(FAKE, FAKE, FAKE, FAKE, None, 1, 4, 2, 128, 10, -3, None, 0.1, 1, 0, None, 0,
                             None) == 1
     args = [FAKE] * 5 + [None, None, None]
-    assert L.parallax_prefill(*args, 1, 4, 2, 0, 128, 0, 0.1, 1.0, 1, None) == 1
-    assert L.parallax_prefill(*args, 1, 4, 3, 16, 128, 0, 0.1, 1.0, 1, None) == 1
-    assert L.parallax_prefill(*args, 1, 4, 2, 16, 72, 0, 0.1, 1.0, 1, None) == 2
-    assert L.parallax_prefill(*args, 1, 4, 2, 16, 128, 0, 0.1, 1.0, 5, None) == 2
-    assert L.parallax_prefill(*args, 1, 4, 2, 16, 128, -1, 0.1, 1.0, 1, None) == 1
-    assert L.parallax_prefill(*args, 1, 4, 2, 16, 128, 0, -0.1, 1.0, 1, None) == 1
-    assert L.parallax_prefill(None, *args[1:], 1, 4, 2, 16, 128, 0, 0.1, 1.0, 1, None) == 1
+    assert L.parallax_prefill(*args, 1, 4, 2, 0, 128, 0, None, 0.1, 1.0, 1, None) == 1
+    assert L.parallax_prefill(*args, 1, 4, 3, 16, 128, 0, None, 0.1, 1.0, 1, None) == 1
+    assert L.parallax_prefill(*args, 1, 4, 2, 16, 72, 0, None, 0.1, 1.0, 1, None) == 2
+    assert L.parallax_prefill(*args, 1, 4, 2, 16, 128, 0, None, 0.1, 1.0, 5, None) == 2
+    assert L.parallax_prefill(*args, 1, 4, 2, 16, 128, -1, None, 0.1, 1.0, 1, None) == 1
+    assert L.parallax_prefill(*args, 1, 4, 2, 16, 128, 0, None, -0.1, 1.0, 1, None) == 1
+    assert L.parallax_prefill(None, *args[1:], 1, 4, 2, 16, 128, 0, None, 0.1, 1.0, 1, None) == 1
 
 
 def test_workspace_plan():
@@ -112,14 +112,14 @@ def test_workspace_plan():
 
 def _backward(**kw):
     a = dict(q=FAKE, r=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, sbar=FAKE, vbar=None, dq=FAKE,
-             dr=FAKE, dk=FAKE, dv=FAKE, B=1, Hq=4, Hkv=2, L=64, D=128, W=0, qk=0.1, rk=1.0,
-             dt=1, ws=None, wsb=0, stream=None)
+             dr=FAKE, dk=FAKE, dv=FAKE, B=1, Hq=4, Hkv=2, L=64, D=128, W=0, mask=None, qk=0.1,
+             rk=1.0, dt=1, ws=None, wsb=0, stream=None)
     a.update(kw)
     return plx.lib().parallax_prefill_backward(
         a["q"], a["r"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["sbar"], a["vbar"], a["dq"],
         a["dr"],
-        a["dk"], a["dv"], a["B"], a["Hq"], a["Hkv"], a["L"], a["D"], a["W"], a["qk"], a["rk"],
-        a["dt"], a["ws"], a["wsb"], a["stream"])
+        a["dk"], a["dv"], a["B"], a["Hq"], a["Hkv"], a["L"], a["D"], a["W"], a["mask"], a["qk"],
+        a["rk"], a["dt"], a["ws"], a["wsb"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -146,22 +146,22 @@ def test_varlen_prefill_rejects_on_host():
     p8 = [FAKE] * 5 + [None, None, None]
     # cu_seqlens missing, negative total, too long a packed head, empty batch is a no-op
     ws = (FAKE, 256)
-    assert L.parallax_prefill_varlen(*p8, None, 2, 4, 2, 64, 100, 128, 0, 0.1, 1.0, 1, *ws,
+    assert L.parallax_prefill_varlen(*p8, None, 2, 4, 2, 64, 100, 128, 0, None, 0.1, 1.0, 1, *ws,
                                      None) == 1
-    assert L.parallax_prefill_varlen(*p8, FAKE, 2, 4, 2, 64, -1, 128, 0, 0.1, 1.0, 1, *ws,
+    assert L.parallax_prefill_varlen(*p8, FAKE, 2, 4, 2, 64, -1, 128, 0, None, 0.1, 1.0, 1, *ws,
                                      None) == 1
-    assert L.parallax_prefill_varlen(*p8, FAKE, 2, 64, 8, 1 << 21, 100, 128, 0, 0.1, 1.0, 1, *ws,
+    assert L.parallax_prefill_varlen(*p8, FAKE, 2, 64, 8, 1 << 21, 100, 128, 0, None, 0.1, 1.0, 1, *ws,
                                      None) == 2
-    assert L.parallax_prefill_varlen(*p8, FAKE, 2, 4, 2, 64, 100, 128, 0, 0.1, 1.0, 1, FAKE, 255,
+    assert L.parallax_prefill_varlen(*p8, FAKE, 2, 4, 2, 64, 100, 128, 0, None, 0.1, 1.0, 1, FAKE, 255,
                                      None) == 3
-    assert L.parallax_prefill_varlen(*p8, FAKE, 2, 4, 2, 64, 0, 128, 0, 0.1, 1.0, 1, *ws,
+    assert L.parallax_prefill_varlen(*p8, FAKE, 2, 4, 2, 64, 0, 128, 0, None, 0.1, 1.0, 1, *ws,
                                      None) == 0
     assert L.parallax_prefill_varlen_workspace_bytes(4, 100, 0) == 256
     assert L.parallax_prefill_varlen_workspace_bytes(4, 100, 1) == 256 + 4 * 100 * 16
     b13 = [FAKE] * 8 + [None] + [FAKE] + [FAKE] * 4
-    assert L.parallax_prefill_varlen_backward(*b13, 2, 4, 2, 64, 100, 128, 0, 0.1, 1.0, 1, None,
+    assert L.parallax_prefill_varlen_backward(*b13, 2, 4, 2, 64, 100, 128, 0, None, 0.1, 1.0, 1, None,
                                               0, None) == 3
-    assert L.parallax_prefill_varlen_backward(*b13, 2, 4, 2, 64, 100, 128, 0, 0.1, 1.0, 1, FAKE,
+    assert L.parallax_prefill_varlen_backward(*b13, 2, 4, 2, 64, 100, 128, 0, None, 0.1, 1.0, 1, FAKE,
                                               256 + 4 * 100 * 16 - 1, None) == 3
 
 
@@ -178,3 +178,5 @@ def test_split_plan_keeps_read_ahead_inside_32bit_offsets(Hkv, D, code):
             per = -(-kv_len // s)
             chunk = -(-per // 128) * 128
             assert (chunk + 2 * 128 + 32) * tok + 1024 < 2 ** 31, (kv_len, forced, s)
+            # a workgroup stages the block-sparse visibility of at most 4096 blocks
+            assert chunk <= (4096 - 2) * 128, (kv_len, forced, s)
