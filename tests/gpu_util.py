@@ -32,11 +32,12 @@ def max_norm_err(o: np.ndarray, ref: np.ndarray) -> float:
     return float(np.abs(o - ref).max() / np.abs(ref).max())
 
 
-def assert_parity(o: np.ndarray, ref: np.ndarray, dtype: int, what: str = ""):
+def assert_parity(o: np.ndarray, ref: np.ndarray, dtype: int, what: str = "", tol=None):
     assert o.shape == ref.shape, (o.shape, ref.shape)
     assert np.all(np.isfinite(o)), f"{what}: non-finite output"
+    tol = TOL[dtype] if tol is None else tol
     err = max_norm_err(o, ref)
-    assert err <= TOL[dtype], f"{what}: max-norm error {err:.3e} > {TOL[dtype]:.0e}"
+    assert err <= tol, f"{what}: max-norm error {err:.3e} > {tol:.0e}"
     return err
 
 
