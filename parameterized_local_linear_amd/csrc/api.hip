@@ -35,6 +35,12 @@ int device_cu_count() {
 // normalisation into the streaming kernel and needs no workspace.
 constexpr int kTargetWavesPerCU = 4;
 constexpr int kMinKeysPerWave = 32;  // one tile: short sequences split for latency
+// On the MFMA path a sequence of at most this many visible keys (four tiles
+// per wave) runs as one fused split: a second, dependent merge launch costs
+// more than the parallelism buys (B = 1, 8 KV heads: 256 keys 5.2 us fused
+// against 7.7 us split, 512 keys 6.4 against 8.0; from 1024 keys the split
+// plan is faster, 7.8 against 8.6).
+constexpr int kFusedMaxKeys = 512;
 // Most keys one split (or stream-K range) may hold: its keys, plus the keys
 // its streaming loop reads ahead (up to two 128-key strides and one 32-key
 // tile past its end), must span less than 2^31 bytes, since the kernels
@@ -64,7 +70,7 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int kv_len, int window, in
         long s = (target + units - 1) / units;
         const long by_len = (kv_len + (long)kMinKeysPerWave * waves - 1) / ((long)kMinKeysPerWave * waves);
         if (s > by_len) s = by_len;
-        if (s < 1) s = 1;
+        if (s < 1 || (mfma && kv_len <= kFusedMaxKeys)) s = 1;
         splits = (int)s;
     }
     if (splits > max_splits) splits = max_splits;

@@ -107,6 +107,9 @@ def test_workspace_plan():
     s = ns(1, 16, 8, 64, 32768, 1, 0)
     assert 1 < s <= 32768 // 32
     assert ns(1, 8, 8, 128, 1024, 1, 0) == 8       # short sequence: split down to 128 keys
+    # up to 512 visible keys the matrix-core path runs one fused split (no merge launch)
+    assert ns(1, 8, 8, 128, 512, 1, 0) == 1 and ns(1, 8, 8, 128, 513, 1, 0) > 1
+    assert ns(1, 8, 8, 128, 32768, 1, 0, 512) == 1  # a window of 512 keys
     assert ns(2048, 16, 8, 128, 2048, 1, 0) == 1   # large batch: one split
 
 
