@@ -32,9 +32,10 @@
  *    Launch failures return PLX_ERR_HIP. Work is enqueued on `stream`
  *    (a hipStream_t; NULL is the default stream); nothing synchronises.
  *  - Results do not depend on timing: a fixed split plan and no atomic
- *    accumulation (the only atomics, the work-queue counters of packed
- *    prefill and backward batches, decide which workgroup computes an item,
- *    never how), so repeated calls return bit-identical outputs.
+ *    accumulation of values (the work-queue counters of packed prefill and
+ *    backward batches decide which workgroup computes an item, never how;
+ *    masked decode counts visible blocks with integer adds), so repeated
+ *    calls return bit-identical outputs.
  *  - Non-finite inputs propagate; they are not checked.
  *  - qk_scale must be finite and > 0, rk_scale finite (else INVALID_ARG).
  *  - window (sliding-window attention; the PyPI README's overview calls it
