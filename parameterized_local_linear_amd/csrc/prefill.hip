@@ -190,6 +190,13 @@ __global__ __launch_bounds__(64) void prefill_generic(PrefillArgs a) {
 // scores of query n for exactly the keys g + 4t it feeds the readout MFMA
 // (P never leaves registers), and the V^T operand read from the row-major
 // LDS tile with gfx950's transposing LDS read (ds_read_b64_tr_b16).
+// S' is carried unscaled: the probe MFMAs accumulate onto -pivot, so they
+// return r.k - pivot and the vector unit only multiplies by P; the probe
+// scale multiplies B, S and the pivot once per row at the end. On tiles whose
+// keys all rows see, the sub-tiles are software-pipelined (the score MFMAs of
+// the next sub-tile interleave with the softmax of the current one); the
+// vector work per sub-tile (exp, rescale test, the row sums and the bf16
+// packing) costs about as many issue cycles as the products themselves.
 //
 // Causality: keys j <= i, and with a sliding window W also j > i - W. Tiles
 // entirely outside a wave's visible band are skipped, tiles crossing either
@@ -301,7 +308,8 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs &a, const int ite
             qop[u] = load16(qp + 8 * (g + 4 * u));
             rop[u] = load16(rp + 8 * (g + 4 * u));
         }
-        // pivot: probe score of the row's first visible key
+        // pivot: raw probe product r . k of the row's first visible key (the
+        // probe scale multiplies it, S and B once, in the epilogue)
         const uint16_t *k0 = reinterpret_cast<const uint16_t *>(a.k) + kvbase + (int64_t)max(0, row - W + 1) * ks;
         float part = 0.f;
 #pragma unroll
@@ -310,9 +318,12 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs &a, const int ite
 #pragma unroll
             for (int e = 0; e < 8; ++e) part += (float)rop[u][e] * (float)kk[e];
         }
-        piv = xor_sum_rowgroups(part) * a.rk_scale;
+        piv = xor_sum_rowgroups(part);
     }
 
+    // The probe products start from -pivot, so the matrix cores return the
+    // centred r . k - pivot directly.
+    const floatx4 pivq = {-piv, -piv, -piv, -piv};
     // Reference max (log2 units). Finite from the start: with a sliding window
     // a row can meet a sub-tile in which none of its keys is visible before
     // it has seen any key, and exp2(-inf - m) must then be 0, not NaN.
@@ -377,7 +388,8 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs &a, const int ite
     };
     auto scores = [&](const KOp &op) __attribute__((always_inline)) {
         Scores sc;
-        sc.z0 = sc.z1 = sc.s0 = sc.s1 = floatx4{0.f, 0.f, 0.f, 0.f};
+        sc.z0 = sc.z1 = floatx4{0.f, 0.f, 0.f, 0.f};
+        sc.s0 = sc.s1 = pivq;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             sc.z0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.k[0][u], qop[u], sc.z0, 0, 0, 0);
@@ -394,27 +406,23 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs &a, const int ite
             accB[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vo.v[e], p.ps, accB[e], 0, 0, 0);
         }
     };
-    // softmax update of the sub-tile at key k0: rescales the accumulators when
-    // the reference max is raised, returns the bf16 P and P o S' operands
-    auto softmax = [&](Scores sc, int k0, bool diag) __attribute__((always_inline)) {
-        float zr[8], sr[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            zr[i] = sc.z0[i];
-            zr[4 + i] = sc.z1[i];
-            sr[i] = sc.s0[i];
-            sr[4 + i] = sc.s1[i];
-        }
+    // Softmax update of the sub-tile at key k0, in two halves. The first masks
+    // the logits of keys a row cannot see (diag) and rescales the accumulators
+    // when the reference max is raised. Lazy rescale: the lane-local max decides
+    // whether any logit of the column exceeds the reference by more than the
+    // slack; only then is the column max taken across the four rows.
+    auto rescale = [&](Scores &sc, int k0, bool diag) __attribute__((always_inline)) {
         float rmax = -INFINITY;
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
+            float z = t < 4 ? sc.z0[t] : sc.z1[t - 4];
             const int key = k0 + g + 4 * t;
-            if (diag && (key > row || key <= row - W)) zr[t] = -INFINITY;
-            rmax = fmaxf(rmax, zr[t]);
+            if (diag && (key > row || key <= row - W)) {
+                z = -INFINITY;
+                if (t < 4) sc.z0[t] = z; else sc.z1[t - 4] = z;
+            }
+            rmax = fmaxf(rmax, z);
         }
-        // Lazy rescale: the lane-local max decides whether any logit of the
-        // column exceeds the reference by more than the slack; only then is
-        // the column max taken across the four rows.
         const bool raise = rmax * a.zscale > m_run + kRescaleSlack;
         if (__builtin_amdgcn_ballot_w64(raise) != 0) {
             const float tmax = xor_max_rowgroups(rmax) * a.zscale;
@@ -429,13 +437,19 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs &a, const int ite
                 accB[e] *= alpha;
             }
         }
+    };
+    // The second half returns the bf16 operands P and P o S', S' taken in units
+    // of the raw probe product (the scale is applied once, at the end).
+    auto probs = [&](const Scores &sc) __attribute__((always_inline)) {
         const float neg_m = -m_run;
         Probs pr;
         float suma = 0.f, sums = 0.f;
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(zr[t], a.zscale, neg_m));
-            const float q = p * fmaf(sr[t], a.rk_scale, -piv);
+            const float z = t < 4 ? sc.z0[t] : sc.z1[t - 4];
+            const float s = t < 4 ? sc.s0[t] : sc.s1[t - 4];
+            const float p = __builtin_amdgcn_exp2f(fmaf(z, a.zscale, neg_m));
+            const float q = p * s;
             suma += p;
             sums += q;
             pr.pa[t] = (__bf16)p;
@@ -453,8 +467,33 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs &a, const int ite
         for (int j = 0; j < NSUB; ++j) {
             const int k0 = t0 + 32 * j;
             if (diag && (k0 > q_last || k0 + 31 <= q0 - W)) continue;  // wave-uniform
-            const Probs p = softmax(scores(load_k(lk, 32 * j)), k0, diag);
+            Scores sc = scores(load_k(lk, 32 * j));
+            rescale(sc, k0, diag);
+            pv(probs(sc), load_vT(lv, 32 * j));
+        }
+    };
+    // The same on a tile whose keys every row sees, software-pipelined: the
+    // score products of sub-tile j + 1 are issued before the softmax of j and
+    // interleaved with it (one product, then three vector instructions), so the
+    // matrix cores and the vector unit of one wave work side by side.
+    auto tile_body_full = [&](const uint16_t *lk, const uint16_t *lv, int tile) __attribute__((always_inline)) {
+        const int t0 = tile * TK;
+        Scores cur = scores(load_k(lk, 0));
+#pragma unroll
+        for (int j = 0; j < NSUB; ++j) {
+            rescale(cur, t0 + 32 * j, false);
+            Scores nxt{};
+            if (j + 1 < NSUB) nxt = scores(load_k(lk, 32 * (j + 1)));
+            const Probs p = probs(cur);
             pv(p, load_vT(lv, 32 * j));
+            if (j + 1 < NSUB) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // three VALU
+                }
+            }
+            cur = nxt;
         }
     };
     auto tile_step = [&](int tile, int nxt, uint16_t *lk, uint16_t *lv, uint16_t *nk, uint16_t *nv) __attribute__((always_inline)) {
@@ -464,7 +503,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs &a, const int ite
         // a tile needs the mask unless every key is visible to all 16 rows
         if (t0 <= q_last && t0 + TK - 1 > q0 - W) {
             if (t0 + TK - 1 <= q0 && t0 > q_last - W)
-                tile_body(lk, lv, tile, false);
+                tile_body_full(lk, lv, tile);
             else
                 tile_body(lk, lv, tile, true);
         }
@@ -492,7 +531,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs &a, const int ite
 
     // ---- epilogue: o = (A + B - (S / l) A) / l per row
     const float l = xor_sum_rowgroups(lsA);
-    const float S = xor_sum_rowgroups(lsS);
+    const float S = xor_sum_rowgroups(lsS) * a.rk_scale;
     if (row < L) {
         const float inv_l = 1.0f / l;
         const float cA = 1.0f - S * inv_l;
@@ -503,7 +542,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs &a, const int ite
         for (int b = 0; b < 8; ++b) {
             float ov[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) ov[i] = (accA[b][i] * cA + accB[b][i]) * inv_l;
+            for (int i = 0; i < 4; ++i) ov[i] = (accA[b][i] * cA + accB[b][i] * a.rk_scale) * inv_l;
             *reinterpret_cast<uint2 *>(o + 16 * b) = uint2{pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3])};
         }
         if (a.vbar) {  // the softmax readout A / l, for a backward pass
@@ -515,7 +554,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs &a, const int ite
         }
         if (g == 0) {
             if (a.lse) a.lse[ro] = fmaf(m_run, 0.6931471805599453f, logf(l));  // one rounding, whatever the contraction
-            if (a.sbar) a.sbar[ro] = S * inv_l + piv;
+            if (a.sbar) a.sbar[ro] = fmaf(piv, a.rk_scale, S * inv_l);
         }
     }
 }
