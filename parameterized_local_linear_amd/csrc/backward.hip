@@ -450,8 +450,10 @@ __device__ __forceinline__ void bwd_rows_item(const BackwardArgs &a, const int i
             for (int u = 0; u < 4; ++u) f.x[kb][u] = lds_chunk(t, kl + 16 * kb + kperm, g + 4 * u);
         return f;
     };
-    auto contract = [&](const Frags &f, const bf16x8 *bop, floatx4 &c0, floatx4 &c1) __attribute__((always_inline)) {
-        c0 = c1 = floatx4{0.f, 0.f, 0.f, 0.f};
+    // c = rows . bop over the 128 dims, the accumulators starting from init
+    auto contract = [&](const Frags &f, const bf16x8 *bop, floatx4 &c0, floatx4 &c1,
+                        floatx4 init = floatx4{0.f, 0.f, 0.f, 0.f}) __attribute__((always_inline)) {
+        c0 = c1 = init;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.x[0][u], bop[u], c0, 0, 0, 0);
@@ -516,6 +518,10 @@ __device__ __forceinline__ void bwd_rows_item(const BackwardArgs &a, const int i
         }
     });
     const float ubar = a.vbar ? ubar_fwd : xor_sum_rowgroups(ub_part);
+    // sweep 2 takes u - delta straight from the matrix cores (the accumulators
+    // start from -delta); u - ubar is then that plus delta - ubar
+    const floatx4 neg_delta = {-delta, -delta, -delta, -delta};
+    const float delta_ubar = delta - ubar;
 
     // ---- sweep 2: dq, dr
     floatx4 accQ[8], accR[8];
@@ -531,19 +537,20 @@ __device__ __forceinline__ void bwd_rows_item(const BackwardArgs &a, const int i
             contract(kf, rop, s0, s1);
             __builtin_amdgcn_s_setprio(0);
         }
-        contract(load_rows(lv, kl), gop, u0, u1);
+        contract(load_rows(lv, kl), gop, u0, u1, neg_delta);
         bf16x8 pz, ps;
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             const float z = t < 4 ? z0[t] : z1[t - 4];
             const float s = t < 4 ? s0[t] : s1[t - 4];
-            const float u = t < 4 ? u0[t] : u1[t - 4];
+            const float ud = t < 4 ? u0[t] : u1[t - 4];  // u - delta
             float w = __builtin_amdgcn_exp2f(fmaf(z, a.zscale, -lse2));
             const int key = key0 + g + 4 * t;
             if (diag && (key > row || key <= row - W)) w = 0.f;
             const float sc = fmaf(s, a.rk_scale, -sb);
-            pz[t] = (__bf16)(w * (fmaf(sc, u, u) - fmaf(ubar, sc, delta)));
-            ps[t] = (__bf16)(w * (u - ubar));
+            const float uu = ud + delta_ubar;            // u - ubar
+            pz[t] = (__bf16)(w * fmaf(sc, uu, ud));      // w (u - delta + (s - sbar)(u - ubar))
+            ps[t] = (__bf16)(w * uu);
         }
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
