@@ -194,7 +194,7 @@ __global__ __launch_bounds__(64) void prefill_generic(PrefillArgs a) {
 // return r.k - pivot and the vector unit only multiplies by P; the probe
 // scale multiplies B, S and the pivot once per row at the end. On tiles whose
 // keys all rows see, the sub-tiles are software-pipelined (the score MFMAs of
-// the next sub-tile interleave with the softmax of the current one); the
+// the next sub-tile come before the softmax of the current one); the
 // vector work per sub-tile (exp, rescale test, the row sums and the bf16
 // packing) costs about as many issue cycles as the products themselves.
 //
@@ -473,9 +473,10 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs &a, const int ite
         }
     };
     // The same on a tile whose keys every row sees, software-pipelined: the
-    // score products of sub-tile j + 1 are issued before the softmax of j and
-    // interleaved with it (one product, then three vector instructions), so the
-    // matrix cores and the vector unit of one wave work side by side.
+    // score products of sub-tile j + 1 come before the probabilities of j in
+    // program order, and the compiler's scheduler interleaves the two. (Forcing
+    // one MFMA between every two, three or four vector instructions with
+    // sched_group_barrier measured 1-2% slower.)
     auto tile_body_full = [&](const uint16_t *lk, const uint16_t *lv, int tile) __attribute__((always_inline)) {
         const int t0 = tile * TK;
         Scores cur = scores(load_k(lk, 0));
@@ -486,13 +487,6 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs &a, const int ite
             if (j + 1 < NSUB) nxt = scores(load_k(lk, 32 * (j + 1)));
             const Probs p = probs(cur);
             pv(p, load_vT(lv, 32 * j));
-            if (j + 1 < NSUB) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // three VALU
-                }
-            }
             cur = nxt;
         }
     };
