@@ -92,3 +92,23 @@ def test_prefill_workload_sampled_rows():
     ref = oracle.prefill(q, r, k, v, rows=rows)
     got = from_gpu(o[rows[:, 0], rows[:, 1], rows[:, 2]])
     assert_parity(got, ref, spec.dtype, "prefill workload rows")
+
+
+@pytest.mark.parametrize("L", [65, 300])
+def test_prefill_shifted_keys_and_probe_scale(L):
+    """Keys shifted by a constant vector (a large common part in every r.k and
+    q.k) with a probe scale other than 1: the pivot must centre the probe scores
+    and the scale must reach B, S and the pivot alike (bf16, the MFMA path)."""
+    B, Hq, Hkv, D = 1, 4, 2, 128
+    q, r, k, v = inputs(B, Hq, Hkv, L, D, synth.BF16, 1.0, 500 + L)
+    c = 3.0 * synth.key_shift(500 + L, D)
+    ks = np.array([synth.bf16_from_double(x) for x in (synth.bf16_bits_to_f32(k) + c).ravel()],
+                  dtype=np.uint16).reshape(k.shape)
+    t = [to_gpu(x, synth.BF16) for x in (q, r, ks, v)]
+    o, lse, sbar = plx.prefill(*t, 0.05, 0.6, return_stats=True)
+    ref, ref_lse, ref_sbar = oracle.prefill(q, r, ks, v, qk_scale=0.05, rk_scale=0.6, stats=True)
+    assert_parity(from_gpu(o), ref, synth.BF16, f"shifted keys L={L}")
+    lse = lse.cpu().numpy().astype(np.float64)
+    assert np.abs(lse - ref_lse).max() <= 1e-3 * max(1.0, np.abs(ref_lse).max())
+    sbar = sbar.cpu().numpy().astype(np.float64)
+    assert np.abs(sbar - ref_sbar).max() <= 1e-2 * max(1.0, np.abs(ref_sbar).max())
