@@ -113,7 +113,7 @@ const char *parallax_status_string(int status);
  *             to the workspace and merged by a second kernel. A packed
  *             cache (cu_seqlens_k != NULL) with num_splits == 0, no window
  *             and the matrix-core path (bf16, D == 128, Hq / Hkv in
- *             {1, 2, 4, 8}) is instead cut into equal token ranges per KV
+ *             1 to 8) is instead cut into equal token ranges per KV
  *             head across all sequences (one range per workgroup), which
  *             balances a mix of lengths.
  *   workspace, workspace_bytes : device scratch of at least
@@ -159,9 +159,11 @@ int parallax_decode_num_splits(int B, int Hq, int Hkv, int D, int kv_len, int wi
  *   A[D] = sum_j e_j v_j,  B[D] = sum_j e_j (s_j - pi) v_j,
  *   m    = max_j z_j * log2(e)   (z_j = qk_scale q.k_j; -inf: empty record),
  *   l    = sum_j e_j,  S = sum_j e_j (s_j - pi),  pi,
- * with e_j = 2^(z_j log2(e) - m) and pi the probe score of the first key of
- * the range the call saw. Merging re-bases every record onto one pivot
- * (exact in real arithmetic), so records from different calls combine.
+ * with e_j = 2^(z_j log2(e) - m) and pi the pivot the record's probe terms
+ * are taken against (the streaming kernel keeps it near the running weighted
+ * mean of s, which keeps the bf16 rounding of the probe terms small; any
+ * value is valid). Merging re-bases every record onto one pivot (exact in
+ * real arithmetic), so records from different calls combine.
  * ---------------------------------------------------------------------- */
 
 /* Bytes of a records array for (B, Hq, D, num_records); 0 if invalid. */

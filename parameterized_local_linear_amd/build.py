@@ -1,5 +1,6 @@
 """Build the Parallax HIP library (libparallax_hip.so) in-tree for gfx950.
 
+Each source is compiled to an object in parallel (hipcc -c), then linked.
 Usage: python -m parameterized_local_linear_amd.build
 """
 from __future__ import annotations
@@ -7,12 +8,14 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 SOURCES = ["api.hip", "decode.hip", "prefill.hip", "backward.hip"]
 LIB = os.path.join(HERE, "libparallax_hip.so")
+OBJDIR = os.path.join(HERE, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -20,7 +23,6 @@ FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # no packed fp32 instructions: keep plain v_fma/v_mul/v_add
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
@@ -28,18 +30,31 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def _run(cmd):
     res = subprocess.run(cmd, capture_output=True, text=True)
-    errs = "\n".join(line for line in res.stderr.splitlines()
-                     if "packed-fp32-ops" not in line)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{errs}")
-    if errs.strip() and verbose:
-        print(errs, file=sys.stderr)
+    errs = "\n".join(line for line in res.stderr.splitlines() if "packed-fp32-ops" not in line)
+    return res.returncode, errs
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OBJDIR, exist_ok=True)
+    objs = [os.path.join(OBJDIR, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    cmds = [[HIPCC, *FLAGS, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
+    if verbose:
+        for c in cmds:
+            print(" ".join(c), flush=True)
+    with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+        results = list(ex.map(_run, cmds))
+    for (rc, errs), src in zip(results, SOURCES):
+        if rc != 0:
+            raise RuntimeError(f"hipcc failed on {src} ({rc}):\n{errs}")
+        if errs.strip() and verbose:
+            print(errs, file=sys.stderr)
+    tmp = LIB + ".tmp"
+    link = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+    rc, errs = _run(link)
+    if rc != 0:
+        raise RuntimeError(f"link failed ({rc}):\n{errs}")
     os.replace(tmp, LIB)
     return LIB
 

@@ -58,7 +58,7 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int kv_len, int window, in
     DecodePlan p;
     if (window > 0 && window < kv_len) kv_len = window;  // keys a query can see at most
     const int G = Hq / Hkv;
-    const bool mfma = dtype == PLX_BF16 && D == 128 && (G == 1 || G == 2 || G == 4 || G == 8);
+    const bool mfma = dtype == PLX_BF16 && D == 128 && G <= 8;  // 2G MFMA columns <= 16
     p.path = mfma ? DecodePath::Mfma : DecodePath::Generic;
     const int waves = mfma ? 4 : 1;      // waves per workgroup
     const int quantum = 32 * waves;      // keys per split are a multiple of this

@@ -104,14 +104,10 @@ __global__ __launch_bounds__(64) void bwd_rows_generic(BackwardArgs a) {
     const T *kb = reinterpret_cast<const T *>(a.k) + kvoff;
     const T *vb = reinterpret_cast<const T *>(a.v) + kvoff;
 
-    float qv[EPL], rv[EPL], gv[EPL], ov[EPL];
+    float qv[EPL], rv[EPL], gv[EPL];
     Frag<T>::load(reinterpret_cast<const T *>(a.q) + row + c * EPL, qv);
     Frag<T>::load(reinterpret_cast<const T *>(a.r) + row + c * EPL, rv);
     Frag<T>::load(reinterpret_cast<const T *>(a.go) + row + c * EPL, gv);
-    Frag<T>::load(reinterpret_cast<const T *>(a.o) + row + c * EPL, ov);
-    float part = 0.f;
-    for (int e = 0; e < EPL; ++e) part += ov[e] * gv[e];
-    const float delta = row_sum<LPR>(part);
     const float lse2 = a.lse[srow] * kLog2e;
     const float sb = a.sbar[srow];
     const int end = i + 1;
@@ -125,31 +121,36 @@ __global__ __launch_bounds__(64) void bwd_rows_generic(BackwardArgs a) {
         return j < end && (!mrow || (j >> kMaskShift) == qb || mrow[j >> kMaskShift] != 0);
     };
 
-    // sweep 1: ubar = sum_j w_j g.v_j, or g . vbar from the forward's softmax readout
-    float ub = 0.f;
-    if (a.vbar) {
-        float vv[EPL];
-        Frag<T>::load(reinterpret_cast<const T *>(a.vbar) + row + c * EPL, vv);
-        float vp = 0.f;
-        for (int e = 0; e < EPL; ++e) vp += vv[e] * gv[e];
-        ub = row_sum<LPR>(vp);
-    }
-    for (int j0 = first; j0 < end && !a.vbar; j0 += KPI) {
+    // sweep 1: ubar = sum_j w_j u_j and delta = sum_j w_j c_j u_j (= g . o), in
+    // fp32 from the recomputed weights rather than from the forward's outputs
+    // o and vbar: dz is a difference of terms up to |c_j| times larger than
+    // itself, and this keeps delta and ubar consistent with the weights the
+    // gradients are formed from (sum_j dz_j = sum_j ds_j = 0).
+    float ub = 0.f, delta = 0.f;
+    for (int j0 = first; j0 < end; j0 += KPI) {
         const int j = j0 + kgrp;
         const int jj = j < end ? j : end - 1;
         float kv[EPL], vv[EPL];
         Frag<T>::load(kb + (int64_t)jj * ks, kv);
         Frag<T>::load(vb + (int64_t)jj * ks, vv);
-        float zp = 0.f, up = 0.f;
+        float zp = 0.f, sp = 0.f, up = 0.f;
         for (int e = 0; e < EPL; ++e) {
             zp += qv[e] * kv[e];
+            sp += rv[e] * kv[e];
             up += gv[e] * vv[e];
         }
         zp = row_sum<LPR>(zp);
+        sp = row_sum<LPR>(sp);
         up = row_sum<LPR>(up);
-        if (visible(j)) ub += __builtin_amdgcn_exp2f(fmaf(zp, a.zscale, -lse2)) * up;
+        if (visible(j)) {
+            const float w = __builtin_amdgcn_exp2f(fmaf(zp, a.zscale, -lse2));
+            const float sc = fmaf(sp, a.rk_scale, -sb);
+            ub = fmaf(w, up, ub);
+            delta = fmaf(w, fmaf(sc, up, up), delta);
+        }
     }
-    if (!a.vbar) ub = across_rows<LPR>(ub);
+    ub = across_rows<LPR>(ub);
+    delta = across_rows<LPR>(delta);
 
     // sweep 2: dq, dr
     float dqa[EPL], dra[EPL];
@@ -283,6 +284,12 @@ __global__ __launch_bounds__(64) void bwd_keys_generic(BackwardArgs a) {
 // contraction, whose A operand is read transposed at the same rows.
 // -------------------------------------------------------------------------
 constexpr int kBwdWaves = 8;
+// Row pass: the corrections of delta and ubar found by the sweep are applied
+// by a second sweep when together they exceed kDeltaRedo times the sum of the
+// row's |dz'| + |ds'| (the operands they perturb), plus kDeltaFloor times the
+// row's |delta| + |ubar| (below that the sums are fp32 round-off).
+constexpr float kDeltaRedo = 1.0f / 1024.0f;
+constexpr float kDeltaFloor = 1.0f / 16384.0f;
 constexpr int kBwdKeysPerTile = 128;  // row pass: keys per LDS tile
 constexpr int kBwdRowsPerTile = 64;   // key pass: query rows per LDS tile
 
@@ -517,17 +524,33 @@ __device__ __forceinline__ void bwd_rows_item(const BackwardArgs &a, const int i
             ub_part = fmaf(w, u, ub_part);
         }
     });
-    const float ubar = a.vbar ? ubar_fwd : xor_sum_rowgroups(ub_part);
+    float ubar = a.vbar ? ubar_fwd : xor_sum_rowgroups(ub_part);
+
+    // ---- sweep 2: dq, dr
+    // delta = g . o (and ubar = g . vbar) come from the forward's bf16 outputs,
+    // which carry its rounding; dz is a difference of terms up to |1 + s - sbar|
+    // times larger than itself, so that rounding can dominate dz. The sweep
+    // therefore also sums its fp32 dz' and ds': with the recomputed weights
+    // (sum_j w_j = 1, sum_j w_j (s_j - sbar) = 0)
+    //   sum_j dz'_j = delta_true - delta,   sum_j ds'_j = ubar_true - ubar
+    // exactly, so both are corrected after the sweep (and the key pass reads
+    // the corrected values). Where a correction exceeds kDeltaRedo of the sum
+    // of the |dz'| (|ds'|) it touches, which is about the bf16 rounding of
+    // those operands, the work item sweeps again with the corrected values.
+    // (The |dz'| and |ds'| are summed together: one register fewer.)
+    floatx4 accQ[8], accR[8];
+    __shared__ int redo_flag;
+    for (int pass = 0;; ++pass) {
     // sweep 2 takes u - delta straight from the matrix cores (the accumulators
     // start from -delta); u - ubar is then that plus delta - ubar
     const floatx4 neg_delta = {-delta, -delta, -delta, -delta};
     const float delta_ubar = delta - ubar;
-
-    // ---- sweep 2: dq, dr
-    floatx4 accQ[8], accR[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) accQ[e] = accR[e] = floatx4{0.f, 0.f, 0.f, 0.f};
-    if (!a.vbar) dma_tile(first_tile, lds_k0, lds_v0);  // sweep 1 consumed the first copy
+    // sweep 1 or the first pass consumed the first copy
+    if (pass > 0 || !a.vbar) dma_tile(first_tile, lds_k0, lds_v0);
+    if (threadIdx.x == 0) redo_flag = 0;  // ordered by the sweep's first barrier
+    float sz = 0.f, ss = 0.f, am = 0.f;  // sums of dz', ds', |dz'| + |ds'|
     sweep([&](const uint16_t *lk, const uint16_t *lv, int kl, int key0, bool diag) __attribute__((always_inline)) {
         floatx4 z0, z1, s0, s1, u0, u1;
         {
@@ -549,8 +572,13 @@ __device__ __forceinline__ void bwd_rows_item(const BackwardArgs &a, const int i
             if (diag && (key > row || key <= row - W)) w = 0.f;
             const float sc = fmaf(s, a.rk_scale, -sb);
             const float uu = ud + delta_ubar;            // u - ubar
-            pz[t] = (__bf16)(w * fmaf(sc, uu, ud));      // w (u - delta + (s - sbar)(u - ubar))
-            ps[t] = (__bf16)(w * uu);
+            const float dz = w * fmaf(sc, uu, ud);       // w (u - delta + (s - sbar)(u - ubar))
+            const float ds = w * uu;
+            sz += dz;
+            ss += ds;
+            am += fabsf(dz) + fabsf(ds);
+            pz[t] = (__bf16)dz;
+            ps[t] = (__bf16)ds;
         }
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -561,6 +589,16 @@ __device__ __forceinline__ void bwd_rows_item(const BackwardArgs &a, const int i
         }
         __builtin_amdgcn_s_setprio(0);
     });
+    const float ed = xor_sum_rowgroups(sz), eu = xor_sum_rowgroups(ss);
+    delta += ed;
+    ubar += eu;
+    if (pass > 0) break;
+    const float mag = xor_sum_rowgroups(am);
+    const bool redo = row < L && fabsf(ed) + fabsf(eu) > kDeltaRedo * mag + kDeltaFloor * (fabsf(delta) + fabsf(ubar));
+    if (__builtin_amdgcn_ballot_w64(redo) != 0 && lane == 0) redo_flag = 1;
+    __syncthreads();
+    if (!redo_flag) break;
+    }
 
     if (row < L) {
         // block e, accumulator element i holds dim 16 e + 4 g + i
@@ -879,7 +917,8 @@ hipError_t launch_mfma_passes(const BackwardArgs &a, int hpw, long row_items, lo
 
 hipError_t launch_prefill_backward(const BackwardArgs &a, int dtype, hipStream_t stream) {
     const int G = a.Hq / a.Hkv;
-    if (dtype == 1 && a.D == 128 && (G % 2 == 0 || G == 1)) {
+    if (dtype == 1 && a.D == 128) {
+        // as the forward: two query heads per row-pass item for even group sizes
         const int hpw = (G % 2 == 0) ? 2 : 1;
         const int rph = 16 * kBwdWaves / hpw;
         const long row_items = (long)a.B * a.Hkv * (G / hpw) * ((a.L + rph - 1) / rph);

@@ -5,21 +5,22 @@
 // query head h, with every cached key visible,
 //   o = sum_j w_j v_j + sum_j w_j (s_j - sbar) v_j,
 //   w = softmax(qk_scale q.k_j), s_j = rk_scale r.k_j, sbar = sum_j w_j s_j.
-// The summary's "hardware-aware streaming kernel that reuses the same KV
-// tiles as FlashAttention" is the design point kept here: each K tile is
-// read from HBM once and feeds both score sets (q.k and r.k), each V tile
-// once and feeds both readouts (sum e v and sum e s v).
+// The summary describes a streaming decode kernel that keeps FlashAttention's
+// KV tiling; that is the design point kept here: each K tile is read from
+// HBM once and feeds both score sets (q.k and r.k), each V tile once and
+// feeds both readouts (sum e v and sum e s v).
 //
-// Streaming state per (query head, split), with a fixed pivot pi = the
-// probe score of the sequence's first key (exact in real arithmetic, it
-// keeps the fp32/bf16 sums small when all s share an offset):
+// Streaming state per (query head, split), with a pivot pi that follows the
+// running weighted mean of the probe scores (re-based exactly whenever it
+// drifts, see kPivotDrift):
 //   m (log2 units), l = sum e, S = sum e (s - pi), A = sum e v,
 //   B = sum e (s - pi) v,  and  o = (A + B - (S / l) A) / l.
-// Two states merge as (m, l, S, A, B) -> max m and 2^(m_i - M)-weighted sums.
+// Two states merge as (m, l, S, A, B) -> max m and 2^(m_i - M)-weighted sums,
+// after re-basing them onto one pivot (S += (pi_i - pi) l, B += (pi_i - pi) A).
 //
 // Kernels:
 //   decode_mfma_bf16_d128<G, PLX>  bf16, head_dim 128, G query heads per KV
-//       head (1, 2, 4, 8). One workgroup of four waves per (KV head, split,
+//       head (1 to 8). One workgroup of four waves per (KV head, split,
 //       sequence). Both contractions on v_mfma_f32_16x16x32_bf16:
 //         scores   S^T[key, vec] = K_tile . [q_0, r_0, q_1, r_1, ...]^T
 //         readout  O^T[dim, row] = V_tile^T . [p_0, p_0 s'_0, p_1, ...]^T
@@ -255,20 +256,15 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, const int hkv,
         }
     };
 
-    // B operand of the score MFMA (vector n, dims 8(g + 4u) .. +8) and, for
-    // the pivot, the sequence's first key: loaded before the K/V tiles, so
-    // that waiting for them (loads complete in order) leaves the tiles in
-    // flight. Dead columns load head 0's row and are zeroed afterwards.
-    bf16x8 qr[4], kf[4];
+    // B operand of the score MFMA (vector n, dims 8(g + 4u) .. +8): loaded
+    // before the K/V tiles, so that waiting for it (loads complete in order)
+    // leaves the tiles in flight. Dead columns load head 0's row and are
+    // zeroed afterwards.
+    bf16x8 qr[4];
     {
         const uint16_t *src = (kind == 0 ? qh : rh) + ((int64_t)b * a.Hq + hq) * D;
-        const uint16_t *kfirst = kh + seq_tok0 * tok_stride + (int64_t)hkv * D;
 #pragma unroll
         for (int u = 0; u < 4; ++u) qr[u] = load16(src + 8 * (g + 4 * u));
-        if (PLX) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) kf[u] = load16(kfirst + 8 * (g + 4 * u));
-        }
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -323,16 +319,9 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, const int hkv,
         for (int u = 0; u < 4; ++u)
             for (int e = 0; e < 8; ++e) qr[u][e] = (__bf16)0.0f;
     }
-    // Pivot pi = rk_scale * r_h . k_0 on the probe lanes (same for every split).
+    // Probe pivot of the column (probe lanes; probe-scale units): starts at 0
+    // and follows the running weighted mean of the column's probe scores.
     float piv = 0.0f;
-    if (PLX) {
-        float part = 0.0f;
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-            for (int e = 0; e < 8; ++e) part += (float)qr[u][e] * (float)kf[u][e];
-        part = xor_sum_rowgroups(part);
-        piv = part * a.rk_scale;
-    }
 
     // Running reference max of the column's head, in log2 units. It is only
     // raised when a tile's max exceeds it by more than kRescaleSlack (or on
@@ -348,7 +337,7 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, const int hkv,
     // per-lane factor turning p into the column's P-row: 1 on softmax rows,
     // (rk_scale * raw - pi) on probe rows -- one FMA, no select
     const float fa = (PLX && kind) ? a.rk_scale : 0.f;
-    const float fc = (PLX && kind) ? -piv : 1.f;
+    float fc = (PLX && kind) ? -piv : 1.f;
 
     // Consume the tile at t0 (range-relative), then issue this buffer's loads
     // for the tile at tn. masked: some keys of the tile lie outside start ..
@@ -366,7 +355,12 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, const int hkv,
             sc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt[u], qr[u], sc0, 0, 0, 0);
             sc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt[4 + u], qr[u], sc1, 0, 0, 0);
         }
-        // this buffer's next K tile, as soon as the scores hold its operands
+        // this buffer's next K tile, as soon as the scores hold its operands.
+        // The copy overwrites the slot the score operand was just read from:
+        // it must not be issued before those LDS reads have returned, which
+        // the MFMAs' use of them guarantees (the compiler would otherwise
+        // hoist the copy above the wait for the reads).
+        __builtin_amdgcn_sched_barrier(0);
         if constexpr (kDecodeKInLds) dma_k(tn, slot); else load_k(tn, kt);
         float raw[8], zr[8];
 #pragma unroll
@@ -399,15 +393,39 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, const int hkv,
         }
         const float neg_m = -m_run;
         float tsum = 0.0f;
-        bf16x8 pf;
+        float pe[8], pv[8];  // the weight e, and the column's P-row value
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            float p = __builtin_amdgcn_exp2f(fmaf(zr[t], a.zscale, neg_m));
-            p *= fmaf(raw[t], fa, fc);
-            tsum += p;
-            pf[t] = (__bf16)p;
+            pe[t] = __builtin_amdgcn_exp2f(fmaf(zr[t], a.zscale, neg_m));
+            pv[t] = pe[t] * fmaf(raw[t], fa, fc);
+            tsum += pv[t];
         }
         lsum += tsum;
+        if constexpr (PLX) {
+            // pivot drift: a probe lane compares its partial S with the partial
+            // l of its head's softmax lane (same keys); a re-base moves the
+            // column's pivot to its running mean, before this tile's P o S'
+            // is rounded
+            const float lnb = dpp_pair_even(lsum);
+            const bool drift = kind != 0 && fabsf(lsum) > kPivotDrift * lnb;
+            if (__builtin_amdgcn_ballot_w64(drift) != 0) {
+                const float col = xor_sum_rowgroups(lsum);  // l (softmax lanes), S (probe lanes)
+                const float lcol = dpp_pair_even(col);
+                const float d = (kind != 0 && lcol > 0.f) ? col / lcol : 0.f;
+                piv += d;
+                fc -= d;
+                lsum = fmaf(-d, lnb, lsum);
+#pragma unroll
+                for (int t = 0; t < 8; ++t) pv[t] = fmaf(-d, pe[t], pv[t]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[e][i] = fmaf(-d, dpp_pair_even(acc[e][i]), acc[e][i]);
+            }
+        }
+        bf16x8 pf;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) pf[t] = (__bf16)pv[t];
 
         // ---- V^T operand: 8x8 16-bit transpose in registers.
         // vt[t] holds dims 8n..8n+7 of key g + 4t; vT[e] holds keys t = 0..7 of dim 8n + e.
@@ -478,7 +496,7 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, const int hkv,
 
     // ---- merge the waves' states in LDS
     __shared__ float sm_acc[W][NV][D];
-    __shared__ float sm_m[W][NV], sm_l[W][NV], sm_piv[NV];
+    __shared__ float sm_m[W][NV], sm_l[W][NV], sm_piv[W][NV];
     if (live) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -487,10 +505,12 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, const int hkv,
         if (g == 0) {
             sm_m[wave][n] = m_run;
             sm_l[wave][n] = lsum;
-            if (wave == 0) sm_piv[n] = piv;
+            sm_piv[wave][n] = piv;
         }
     }
     __syncthreads();
+    // The waves' probe terms are re-based onto wave 0's pivot:
+    //   B_w + (pi_w - pi_0) A_w,  S_w + (pi_w - pi_0) l_w.
 
     if (!fused) {
         // record element (column n, dim d) for every live column
@@ -503,7 +523,10 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, const int hkv,
 #pragma unroll
             for (int w = 0; w < W; ++w) {
                 const float mw = sm_m[w][cn];
-                if (mw != -INFINITY) val += __builtin_amdgcn_exp2f(mw - M) * sm_acc[w][cn][d];
+                if (mw == -INFINITY) continue;
+                float x = sm_acc[w][cn][d];
+                if (PLX && cn % NR) x = fmaf(sm_piv[w][cn] - sm_piv[0][cn], sm_acc[w][cn - 1][d], x);
+                val += __builtin_amdgcn_exp2f(mw - M) * x;
             }
             float *rec = a.ws + (rbase + (cn / NR) * rstride) * partial_floats(D);
             rec[(cn % NR) * D + d] = val;
@@ -515,7 +538,10 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, const int hkv,
             float sum = 0.f;
             for (int w = 0; w < W; ++w) {
                 const float mw = sm_m[w][cn];
-                if (mw != -INFINITY) sum += __builtin_amdgcn_exp2f(mw - M) * sm_l[w][cn];
+                if (mw == -INFINITY) continue;
+                float x = sm_l[w][cn];
+                if (PLX && cn % NR) x = fmaf(sm_piv[w][cn] - sm_piv[0][cn], sm_l[w][cn - 1], x);
+                sum += __builtin_amdgcn_exp2f(mw - M) * x;
             }
             float *rec = a.ws + (rbase + (cn / NR) * rstride) * partial_floats(D);
             if (cn % NR == 0) {
@@ -527,7 +553,7 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, const int hkv,
                 }
             } else {
                 rec[2 * D + 2] = sum;
-                rec[2 * D + 3] = sm_piv[cn];
+                rec[2 * D + 3] = sm_piv[0][cn];
             }
         }
         __syncthreads();  // the LDS may be reused by the workgroup's next range
@@ -550,8 +576,9 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, const int hkv,
             A += c * sm_acc[w][ca][d];
             l += c * sm_l[w][ca];
             if (PLX) {
-                Bv += c * sm_acc[w][ca + 1][d];
-                S += c * sm_l[w][ca + 1];
+                const float dp = sm_piv[w][ca + 1] - sm_piv[0][ca + 1];
+                Bv += c * fmaf(dp, sm_acc[w][ca][d], sm_acc[w][ca + 1][d]);
+                S += c * fmaf(dp, sm_l[w][ca], sm_l[w][ca + 1]);
             }
         }
         const float inv_l = 1.0f / l;
@@ -936,7 +963,11 @@ hipError_t launch_mfma(const DecodeArgs &a, hipStream_t stream) {
         switch (G) {
             case 1: hipLaunchKernelGGL((decode_mfma_streamk<1, PLX, MASK>), grid, block, 0, stream, a); break;
             case 2: hipLaunchKernelGGL((decode_mfma_streamk<2, PLX, MASK>), grid, block, 0, stream, a); break;
+            case 3: hipLaunchKernelGGL((decode_mfma_streamk<3, PLX, MASK>), grid, block, 0, stream, a); break;
             case 4: hipLaunchKernelGGL((decode_mfma_streamk<4, PLX, MASK>), grid, block, 0, stream, a); break;
+            case 5: hipLaunchKernelGGL((decode_mfma_streamk<5, PLX, MASK>), grid, block, 0, stream, a); break;
+            case 6: hipLaunchKernelGGL((decode_mfma_streamk<6, PLX, MASK>), grid, block, 0, stream, a); break;
+            case 7: hipLaunchKernelGGL((decode_mfma_streamk<7, PLX, MASK>), grid, block, 0, stream, a); break;
             case 8: hipLaunchKernelGGL((decode_mfma_streamk<8, PLX, MASK>), grid, block, 0, stream, a); break;
             default: return hipErrorInvalidValue;
         }
@@ -946,7 +977,11 @@ hipError_t launch_mfma(const DecodeArgs &a, hipStream_t stream) {
     switch (G) {
         case 1: hipLaunchKernelGGL((decode_mfma_bf16_d128<1, PLX, MASK>), grid, block, 0, stream, a); break;
         case 2: hipLaunchKernelGGL((decode_mfma_bf16_d128<2, PLX, MASK>), grid, block, 0, stream, a); break;
+        case 3: hipLaunchKernelGGL((decode_mfma_bf16_d128<3, PLX, MASK>), grid, block, 0, stream, a); break;
         case 4: hipLaunchKernelGGL((decode_mfma_bf16_d128<4, PLX, MASK>), grid, block, 0, stream, a); break;
+        case 5: hipLaunchKernelGGL((decode_mfma_bf16_d128<5, PLX, MASK>), grid, block, 0, stream, a); break;
+        case 6: hipLaunchKernelGGL((decode_mfma_bf16_d128<6, PLX, MASK>), grid, block, 0, stream, a); break;
+        case 7: hipLaunchKernelGGL((decode_mfma_bf16_d128<7, PLX, MASK>), grid, block, 0, stream, a); break;
         case 8: hipLaunchKernelGGL((decode_mfma_bf16_d128<8, PLX, MASK>), grid, block, 0, stream, a); break;
         default: return hipErrorInvalidValue;
     }

@@ -51,6 +51,21 @@ __device__ __forceinline__ bf16x8 load16(const uint16_t *p) {
 // before the accumulators are rescaled.
 constexpr float kRescaleSlack = 8.0f;
 
+// Probe pivot re-basing. The matrix-core kernels accumulate B = sum e (s - pi) v
+// from bf16 operands e (s - pi), and A = sum e v from bf16 e; the output
+// (A (1 - (sbar - pi)) + B) / l then carries the rounding of each key's e
+// multiplied by |sbar - pi| and that of e (s - pi) by |s - pi|. The pivot
+// starts at 0 and follows the running weighted mean of s: after a tile's
+// weights are formed (before they are rounded), a lane whose partial sums have
+// |S| > kPivotDrift * l (S = sum e (s - pi), l = sum e over its keys, s in
+// probe-scale units) triggers a re-base of its row onto the row's running mean
+// d = S_row / l_row:  pi += d,  S -= d l,  B -= d A,  and the tile's
+// e (s - pi) -= d e. Exact in real arithmetic. If the row's mean is off by
+// more than the threshold, at least one lane's partial mean is, so no needed
+// re-base is missed. Inputs whose probe scores stay within the threshold of 0
+// (as with keys and probes of unit total variance) never re-base.
+constexpr float kPivotDrift = 1.0f;
+
 // Word 3 of a raw buffer resource for gfx9-family (CDNA) untyped loads.
 constexpr int kBufferFlags = 0x00020000;
 

@@ -296,9 +296,8 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs &a, const int ite
     int tile = next_tile(tile0);  // the diagonal tile is always visible
     dma_tile(tile, lds_k0, lds_v0);
 
-    // ---- per-wave query operands (k-step u) and the row's pivot
+    // ---- per-wave query operands (k-step u)
     bf16x8 qop[4], rop[4];
-    float piv;
     {
         const int row = min(q0 + n, L - 1);
         const uint16_t *qp = qh + qbase + (int64_t)row * qs;
@@ -308,22 +307,16 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs &a, const int ite
             qop[u] = load16(qp + 8 * (g + 4 * u));
             rop[u] = load16(rp + 8 * (g + 4 * u));
         }
-        // pivot: raw probe product r . k of the row's first visible key (the
-        // probe scale multiplies it, S and B once, in the epilogue)
-        const uint16_t *k0 = reinterpret_cast<const uint16_t *>(a.k) + kvbase + (int64_t)max(0, row - W + 1) * ks;
-        float part = 0.f;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const bf16x8 kk = load16(k0 + 8 * (g + 4 * u));
-#pragma unroll
-            for (int e = 0; e < 8; ++e) part += (float)rop[u][e] * (float)kk[e];
-        }
-        piv = xor_sum_rowgroups(part);
     }
 
-    // The probe products start from -pivot, so the matrix cores return the
-    // centred r . k - pivot directly.
-    const floatx4 pivq = {-piv, -piv, -piv, -piv};
+    // The row's probe pivot, in units of the raw product r . k (the probe
+    // scale multiplies it, S and B once, in the epilogue). It starts at 0 and
+    // follows the row's running weighted mean of r . k (kPivotDrift; the
+    // threshold is taken in probe-scale units). The probe products start from
+    // -pivot, so the matrix cores return the centred r . k - pivot directly.
+    float piv = 0.f;
+    floatx4 pivq = {0.f, 0.f, 0.f, 0.f};
+    const float drift_raw = a.rk_scale != 0.f ? kPivotDrift / fabsf(a.rk_scale) : INFINITY;
     // Reference max (log2 units). Finite from the start: with a sliding window
     // a row can meet a sub-tile in which none of its keys is visible before
     // it has seen any key, and exp2(-inf - m) must then be 0, not NaN.
@@ -439,8 +432,12 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs &a, const int ite
         }
     };
     // The second half returns the bf16 operands P and P o S', S' taken in units
-    // of the raw probe product (the scale is applied once, at the end).
-    auto probs = [&](const Scores &sc) __attribute__((always_inline)) {
+    // of the raw probe product (the scale is applied once, at the end). When a
+    // lane's partial sums show the pivot has drifted from the row's running
+    // mean, the row is re-based before the operands are rounded; `nx` holds
+    // scores already taken against the old pivot (the next sub-tile's, when
+    // the sub-tiles are software-pipelined) and is shifted with it.
+    auto probs = [&](const Scores &sc, Scores &nx) __attribute__((always_inline)) {
         const float neg_m = -m_run;
         Probs pr;
         float suma = 0.f, sums = 0.f;
@@ -457,6 +454,26 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs &a, const int ite
         }
         lsA += suma;
         lsS += sums;
+        if (__builtin_amdgcn_ballot_w64(fabsf(lsS) > drift_raw * lsA) != 0) {
+            // rare: re-base the row and form this sub-tile's P o S' again
+            const float lrow = xor_sum_rowgroups(lsA);
+            const float srow = xor_sum_rowgroups(lsS);
+            const float d = lrow > 0.f ? srow / lrow : 0.f;
+            piv += d;
+            pivq = floatx4{-piv, -piv, -piv, -piv};
+            lsS = fmaf(-d, lsA, lsS);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) accB[e] -= d * accA[e];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const float z = t < 4 ? sc.z0[t] : sc.z1[t - 4];
+                const float s = t < 4 ? sc.s0[t] : sc.s1[t - 4];
+                const float p = __builtin_amdgcn_exp2f(fmaf(z, a.zscale, neg_m));
+                pr.ps[t] = (__bf16)(p * (s - d));
+            }
+            nx.s0 -= d;
+            nx.s1 -= d;
+        }
         return pr;
     };
     // one tile: its sub-tiles in order
@@ -469,7 +486,8 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs &a, const int ite
             if (diag && (k0 > q_last || k0 + 31 <= q0 - W)) continue;  // wave-uniform
             Scores sc = scores(load_k(lk, 32 * j));
             rescale(sc, k0, diag);
-            pv(probs(sc), load_vT(lv, 32 * j));
+            Scores none{};
+            pv(probs(sc, none), load_vT(lv, 32 * j));
         }
     };
     // The same on a tile whose keys every row sees, software-pipelined: the
@@ -485,7 +503,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs &a, const int ite
             rescale(cur, t0 + 32 * j, false);
             Scores nxt{};
             if (j + 1 < NSUB) nxt = scores(load_k(lk, 32 * (j + 1)));
-            const Probs p = probs(cur);
+            const Probs p = probs(cur, nxt);
             pv(p, load_vT(lv, 32 * j));
             cur = nxt;
         }
@@ -588,7 +606,9 @@ bool prefill_supported(int D, int dtype) { return (D == 64 || D == 128) && (dtyp
 
 hipError_t launch_prefill(const PrefillArgs &a, int dtype, hipStream_t stream) {
     const int G = a.Hq / a.Hkv;
-    if (dtype == 1 && a.D == 128 && (G % 2 == 0 || G == 1)) {
+    if (dtype == 1 && a.D == 128) {
+        // two query heads per work item when the group size allows it (they
+        // share every K/V tile), else one (any group size)
         const int hpw = (G % 2 == 0) ? 2 : 1;
         const int rph = 16 * kPrefillWaves / hpw;
         const long items = (long)a.B * a.Hkv * (G / hpw) * ((a.L + rph - 1) / rph);
