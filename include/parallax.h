@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define PARALLAX_ABI_VERSION 4
+#define PARALLAX_ABI_VERSION 5
 
 /* Block size of block_mask, in positions (keys and prefill queries). */
 #define PLX_MASK_BLOCK 128
@@ -139,6 +139,32 @@ int softmax_decode(const void *q, const void *k, const void *v, void *o,
                    const int32_t *cu_seqlens_k, int B, int Hq, int Hkv, int D, int kv_len,
                    int window, const uint8_t *block_mask, float qk_scale, int dtype,
                    int num_splits, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Size of the device workspace that the library itself holds for
+ * parallax_decode_noalloc (one copy per device that runs it). */
+#define PLX_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+
+/* parallax_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same computation, kernels and split plan, with the split records kept
+ * in a file-scope device array of PLX_NOALLOC_SCRATCH_BYTES owned by the
+ * library instead of a caller workspace. The call allocates nothing; the
+ * caller still passes q, r, k, v, o (and cu_seqlens_k, block_mask) as for
+ * parallax_decode. The array's device address is looked up on the first call
+ * on each device (with that device current); HIP errors of that lookup
+ * return PLX_ERR_HIP.
+ * Returns PLX_ERR_WORKSPACE, before touching the device, when the plan needs
+ * more than PLX_NOALLOC_SCRATCH_BYTES, i.e. when
+ * parallax_decode_workspace_bytes(...) for the same arguments exceeds it
+ * (for example B * Hq * splits * (2 D + 4) * 4 bytes with splits > 1); other
+ * errors as parallax_decode. Every call on one device shares that device's
+ * array and keeps the last call's records there, so calls that overlap in
+ * time on one device (other streams, other host threads) race and must be
+ * serialised by the caller. */
+int parallax_decode_noalloc(const void *q, const void *r, const void *k, const void *v, void *o,
+                            const int32_t *cu_seqlens_k, int B, int Hq, int Hkv, int D,
+                            int kv_len, int window, const uint8_t *block_mask, float qk_scale,
+                            float rk_scale, int dtype, int num_splits, void *stream);
 
 /* The split count parallax_decode / softmax_decode use for these
  * arguments (num_splits resolved when it is 0), or 0 when they are invalid. */

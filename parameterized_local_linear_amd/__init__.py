@@ -8,6 +8,7 @@ missing library raises.
 
 Entry points mirror the C ABI (include/parallax.h):
   decode(q, r, k, v, ...)          Parallax decode, q/r [B, Hq, D] or [B, 1, Hq, D]
+  decode_noalloc(q, r, k, v, ...)  the same with the library's own device workspace
   softmax_decode(q, k, v, ...)     the same kernels with the probe path compiled out
   prefill(q, r, k, v, ...)         causal Parallax prefill on [B, H, L, D]
   prefill_backward(...)            its gradients dq, dr, dk, dv
@@ -29,6 +30,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libparallax_hip.so")
 
 PLX_F32, PLX_BF16 = 0, 1
+NOALLOC_SCRATCH_BYTES = 8 << 20  # PLX_NOALLOC_SCRATCH_BYTES
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration",
           3: "workspace missing or too small", 4: "HIP runtime error"}
 
@@ -62,6 +64,9 @@ def lib() -> ctypes.CDLL:
         L.parallax_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp,
                                       f32, f32, i32, i32, vp, sz, vp]
         L.parallax_decode.restype = i32
+        L.parallax_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                              vp, f32, f32, i32, i32, vp]
+        L.parallax_decode_noalloc.restype = i32
         L.softmax_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, f32,
                                      i32, i32, vp, sz, vp]
         L.softmax_decode.restype = i32
@@ -140,7 +145,7 @@ def decode_num_splits(B, Hq, Hkv, D, kv_len, dtype_code, num_splits=0, window=0)
 
 
 def _decode_impl(q, r, k, v, qk_scale, rk_scale, cu_seqlens_k, kv_len, num_splits, out,
-                 workspace, parallax, window, block_mask=None):
+                 workspace, parallax, window, block_mask=None, noalloc=False):
     L_ = lib()
     squeeze = q.dim() == 4
     if squeeze:                       # the pages' (B, 1, H, D)
@@ -184,11 +189,19 @@ def _decode_impl(q, r, k, v, qk_scale, rk_scale, cu_seqlens_k, kv_len, num_split
         _check(out, "out", dt, dev)
         if out.shape != (B, Hq, D):
             raise ValueError("out must be [B, Hq, D]")
+    stream = _stream_handle(dev)
+    if noalloc:
+        st = L_.parallax_decode_noalloc(_ptr(q), _ptr(r), _ptr(k), _ptr(v), _ptr(out),
+                                        _ptr(cu_seqlens_k), B, Hq, Hkv, D, int(kv_len), int(window),
+                                        _ptr(block_mask), float(qk_scale), float(rk_scale), code,
+                                        int(num_splits), stream)
+        if st != 0:
+            raise ParallaxError(st, "parallax_decode_noalloc")
+        return out[:, None] if squeeze else out
     need = decode_workspace_bytes(B, Hq, Hkv, D, int(kv_len), code, num_splits, window)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    stream = _stream_handle(dev)
     if parallax:
         st = L_.parallax_decode(_ptr(q), _ptr(r), _ptr(k), _ptr(v), _ptr(out), _ptr(cu_seqlens_k),
                                 B, Hq, Hkv, D, int(kv_len), int(window), _ptr(block_mask),
@@ -214,6 +227,15 @@ def decode(q, r, k, v, qk_scale=None, rk_scale=1.0, *, cu_seqlens_k=None, kv_len
     sequence's last key is always visible)."""
     return _decode_impl(q, r, k, v, qk_scale, rk_scale, cu_seqlens_k, kv_len, num_splits, out,
                         workspace, True, window, block_mask)
+
+
+def decode_noalloc(q, r, k, v, qk_scale=None, rk_scale=1.0, *, cu_seqlens_k=None, kv_len=None,
+                   num_splits=0, out=None, window=0, block_mask=None):
+    """decode() through parallax_decode_noalloc: the split records live in the
+    library's own device array (NOALLOC_SCRATCH_BYTES per device), so the call
+    needs no workspace. Calls on one device must not overlap in time."""
+    return _decode_impl(q, r, k, v, qk_scale, rk_scale, cu_seqlens_k, kv_len, num_splits, out,
+                        None, True, window, block_mask, noalloc=True)
 
 
 def softmax_decode(q, k, v, qk_scale=None, *, cu_seqlens_k=None, kv_len=None, num_splits=0,

@@ -6,6 +6,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 namespace plx {
 
 namespace {
@@ -26,7 +28,7 @@ int device_cu_count() {
 
 }  // namespace
 
-// Decode plan. The MFMA path (bf16, head_dim 128, group size 1/2/4/8) runs
+// Decode plan. The MFMA path (bf16, head_dim 128, group size 1 to 8) runs
 // one four-wave workgroup per (KV head, split, sequence) over a multiple of
 // 128 keys; the generic path one wave per (query head, split, sequence) over
 // a multiple of 32 keys. Without a forced count, the sequence is cut into
@@ -232,6 +234,65 @@ int softmax_decode(const void *q, const void *k, const void *v, void *o, const i
     return decode_common(q, nullptr, k, v, o, cu_seqlens_k, B, Hq, Hkv, D, kv_len, window,
                          block_mask, qk_scale, 1.0f, dtype, num_splits, workspace, workspace_bytes,
                          stream, false);
+}
+
+}  // extern "C"
+
+// ---- decode with the library's own device workspace ---------------------
+// For callers that cannot allocate device memory (code under graph capture,
+// tight serving loops): the split records of parallax_decode_noalloc live in
+// this file-scope device array. Each device that runs the call holds its own
+// copy until the process ends. In host code `scratch` names a host-side
+// stand-in, not device memory: its device address is looked up once per
+// device (hipGetSymbolAddress, with that device current) and only that
+// address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[PLX_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+void *g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// The current device's copy of `scratch` (looked up on its first use).
+int current_scratch(void **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return PLX_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return PLX_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return PLX_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return PLX_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int parallax_decode_noalloc(const void *q, const void *r, const void *k, const void *v, void *o,
+                            const int32_t *cu_seqlens_k, int B, int Hq, int Hkv, int D,
+                            int kv_len, int window, const uint8_t *block_mask, float qk_scale,
+                            float rk_scale, int dtype, int num_splits, void *stream) {
+    // host-only checks first: invalid arguments, and a plan whose records
+    // exceed the static workspace, are refused before anything touches the device
+    plx::DecodeArgs a;
+    DecodePlan p;
+    int st = fill_decode_args(a, q, r, k, v, o, cu_seqlens_k, B, Hq, Hkv, D, kv_len, window,
+                              block_mask, qk_scale, rk_scale, dtype, num_splits, true, p);
+    if (st != PLX_OK) return st;
+    const size_t need = parallax_decode_workspace_bytes(B, Hq, Hkv, D, kv_len, window, dtype,
+                                                        num_splits);
+    if (need > PLX_NOALLOC_SCRATCH_BYTES) return PLX_ERR_WORKSPACE;
+    void *ws = nullptr;
+    st = current_scratch(&ws);
+    if (st != PLX_OK) return st;
+    // no kernel of the decode path needs its workspace cleared: every record
+    // the merge reads is written by the streaming kernel of the same call
+    return decode_common(q, r, k, v, o, cu_seqlens_k, B, Hq, Hkv, D, kv_len, window, block_mask,
+                         qk_scale, rk_scale, dtype, num_splits, ws, PLX_NOALLOC_SCRATCH_BYTES,
+                         stream, true);
 }
 
 size_t parallax_decode_record_bytes(int B, int Hq, int D, int num_records) {

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = plx.lib()
-    assert L.parallax_abi_version() == 4
+    assert L.parallax_abi_version() == 5
     for s in range(5):
         assert L.parallax_status_string(s).decode() == plx.STATUS[s]
     assert L.parallax_status_string(99) == b"unknown status"
@@ -183,3 +183,16 @@ def test_split_plan_keeps_read_ahead_inside_32bit_offsets(Hkv, D, code):
             assert (chunk + 2 * 128 + 32) * tok + 1024 < 2 ** 31, (kv_len, forced, s)
             # a workgroup stages the block-sparse visibility of at most 4096 blocks
             assert chunk <= (4096 - 2) * 128, (kv_len, forced, s)
+
+
+def test_noalloc_decode_refuses_plans_beyond_its_array_on_host():
+    # 64 sequences x 64 query heads x 64 forced splits of records: 272 MB > 8 MiB
+    L = plx.lib()
+    need = L.parallax_decode_workspace_bytes(64, 64, 8, 128, 32768, 0, 1, 64)
+    assert need > plx.NOALLOC_SCRATCH_BYTES
+    st = L.parallax_decode_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, None, 64, 64, 8, 128, 32768, 0,
+                                   None, 0.1, 1.0, 1, 64, None)
+    assert st == 3
+    # invalid sizes are reported as by parallax_decode, also before any device call
+    assert L.parallax_decode_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 4, 2, 128, 64, 0,
+                                     None, 0.1, 1.0, 1, 0, None) == 1
