@@ -1,23 +1,30 @@
 #!/usr/bin/env python
 """Benchmark of the Parallax attention hot path on one MI355X.
 
-Default workload: long-context decode, bf16, B=1, Hq=16, Hkv=8, D=128,
-32768 cached keys (contiguous cache), q/r/K/V ~ N(0,1)/sqrt(128), seeded.
-A step is one parallax_decode call over the batch (streaming kernel + split
-merge). Inputs are resident in HBM before timing; the KV cache is replicated
-into enough copies that consecutive steps never find their keys in the
-256 MB Infinity Cache, and steps rotate through the copies. Warmup and
-timed steps are each captured into one HIP graph and replayed, bracketed
-by device synchronisation and HIP events on the launch stream.
+Default (--workload metric): the headline is large-batch decode, bf16,
+B=2048, Hq=16, Hkv=8, D=128, 2048 cached keys per sequence (17.2 GB of K/V),
+q/r/K/V ~ N(0,1)/sqrt(128), seeded: the largest single-GPU decode
+configuration of the metric. A step is one parallax_decode call over the
+batch. Inputs are resident in HBM before timing; a cache smaller than four
+times the 256 MB Infinity Cache is replicated into enough copies that
+consecutive steps never find their keys there, and steps rotate through the
+copies. The warmup steps and the timed steps are captured into HIP graphs and
+replayed; the timed steps run as ten equal replays, each between HIP events
+on the replay stream, bracketed by device synchronisation: value is the mean
+over all timed steps, us_per_step the q05 / q50 / q95 over the replays.
 
-Also measured in the same run:
-  * the streaming kernel alone (a graph of parallax_decode_partial calls),
-    against the HBM roofline (8 TB/s), from algorithmic bytes K + V + q + r;
+Also measured in the same run, for each workload:
+  * the dominant streaming kernel against the HBM roofline (8 TB/s), from
+    algorithmic bytes K + V + q + r (+ o when the kernel writes o itself);
   * softmax_decode on the same inputs (the cost of the correction branch);
-  * the CPU oracle on the same inputs (cpu_baseline), on the host's cores.
+  * the CPU oracle on the same inputs (cpu_baseline: bounded sample, every core).
+The default line carries sub-records for the tiny fp32 decode and the
+long-context decode (each with the oracle's full step on one thread and on
+every core), the varlen decode batch, and the causal prefill (TFLOP/s against
+the bf16 dense MFMA peak).
 
-Other workloads (--workload varlen | large | prefill | backward | grid |
-prefill-varlen) print their own line; prefill-varlen times the packed
+Other workloads (--workload tiny | long | varlen | large | prefill | backward |
+grid | prefill-varlen) print their own line; prefill-varlen times the packed
 forward and backward of 16 sequences of U{256..4096} tokens; backward times parallax_prefill_backward (row pass + key
 pass) on the causal-prefill shapes; grid runs the pages' own decode shapes
 (multi-head H = 8, B in {1, 32}, L in {512 .. 16384}) and reports a table.
@@ -49,9 +56,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="long",
-                    choices=["long", "varlen", "large", "prefill", "backward", "grid",
-                             "prefill-varlen"])
+    ap.add_argument("--workload", default="metric",
+                    choices=["metric", "tiny", "long", "varlen", "large", "prefill", "backward",
+                             "grid", "prefill-varlen"])
     ap.add_argument("--num-splits", type=int, default=0, help="0: library plan")
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window (keys a query sees); 0: none")
@@ -62,6 +69,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the CPU oracle sample")
+    ap.add_argument("--cpu-seconds-one", type=float, default=3.0,
+                    help="target wall time of each one-thread / all-core oracle figure of the "
+                         "small decode workloads in the default run")
     ap.add_argument("--eager", action="store_true",
                     help="launch steps one by one instead of replaying a HIP graph (for profilers)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -121,49 +131,86 @@ def masked_pairs(m, L):
     return total
 
 
-def graph_time(torch, fn, steps, warmup):
-    """Capture `warmup` and `steps` calls of fn(i) into two graphs; replay the
-    warmup graph, then time the steps graph with events. Returns seconds/step.
-    With --eager the same calls are launched one by one instead."""
+def timed_steps(torch, fn, steps, warmup, trials=10):
+    """Exactly `steps` timed calls of fn(i), after `warmup` untimed ones.
+
+    Graph mode (default): the warmup calls are captured into one graph and the
+    timed calls into graphs of n = steps // trials calls (plus one graph of the
+    remainder). After the warmup replay, each timed replay runs between HIP
+    events recorded on the replay stream; the timed region is bracketed by
+    device synchronisation. Returns seconds per step: the mean over all timed
+    steps, and q05 / q50 / q95 over the equal-size replays (the pages' replay
+    sweep reports q50 with q05 / q95). With --eager every call is launched and
+    timed on its own."""
     stream = torch.cuda.Stream()
+    trials = max(1, min(trials, steps))
     if EAGER:
         with torch.cuda.stream(stream):
             for i in range(warmup):
                 fn(i)
-            torch.cuda.synchronize()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for i in range(steps):
-                fn(i)
-            e1.record(stream)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e-3 / steps
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        with torch.cuda.stream(stream):
+            for i, (e0, e1) in enumerate(ev):
+                e0.record(stream)
+                fn(warmup + i)
+                e1.record(stream)
+        torch.cuda.synchronize()
+        per = np.array([e0.elapsed_time(e1) * 1e-3 for e0, e1 in ev])
+        q = np.quantile(per, [0.05, 0.5, 0.95])
+        return {"mean": float(per.mean()), "q05": q[0], "q50": q[1], "q95": q[2]}
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
         for i in range(2):  # eager warm calls before capture
             fn(i)
     torch.cuda.synchronize()
+    n = steps // trials
+    rem = steps - n * trials
     gw = torch.cuda.CUDAGraph()
     with torch.cuda.graph(gw, stream=stream):
         for i in range(max(warmup, 1)):
             fn(i)
     gs = torch.cuda.CUDAGraph()
     with torch.cuda.graph(gs, stream=stream):
-        for i in range(steps):
+        for i in range(n):
             fn(i)
+    gr = None
+    if rem:
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=stream):
+            for i in range(rem):
+                fn(n + i)
     torch.cuda.synchronize()
     if warmup > 0:
         gw.replay()
     torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(trials + (1 if rem else 0))]
     with torch.cuda.stream(stream):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        gs.replay()
-        e1.record(stream)
+        for t in range(trials):
+            ev[t][0].record(stream)
+            gs.replay()
+            ev[t][1].record(stream)
+        if rem:
+            ev[-1][0].record(stream)
+            gr.replay()
+            ev[-1][1].record(stream)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e-3 / steps
+    per = np.array([ev[t][0].elapsed_time(ev[t][1]) * 1e-3 / n for t in range(trials)])
+    total = per.sum() * n + (ev[-1][0].elapsed_time(ev[-1][1]) * 1e-3 if rem else 0.0)
+    q = np.quantile(per, [0.05, 0.5, 0.95])
+    return {"mean": float(total / steps), "q05": q[0], "q50": q[1], "q95": q[2]}
+
+
+def graph_time(torch, fn, steps, warmup):
+    """Mean seconds per step of timed_steps."""
+    return timed_steps(torch, fn, steps, warmup)["mean"]
+
+
+def us_quantiles(t):
+    return {"q05": round(t["q05"] * 1e6, 3), "q50": round(t["q50"] * 1e6, 3),
+            "q95": round(t["q95"] * 1e6, 3)}
 
 
 def measured_traffic(workload_name, splits):
@@ -186,22 +233,6 @@ def measured_traffic(workload_name, splits):
     return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["source_sha256"] else None
 
 
-def cpu_baseline_decode(oracle, q, r, kv_rows, spec, seconds, window=0):
-    """Time the oracle on the full step (all heads, all keys), repeated to fill
-    about `seconds` of wall time. Returns (us_per_step, repeats, threads)."""
-    k, v = kv_rows
-    t = time.perf_counter()
-    oracle.decode(q, r, k, v, window=window)
-    one = time.perf_counter() - t
-    reps = max(1, int(seconds / max(one, 1e-6)))
-    t = time.perf_counter()
-    for _ in range(reps):
-        oracle.decode(q, r, k, v, window=window)
-    per = (time.perf_counter() - t) / reps
-    threads = min(omp_threads(), spec.B * spec.Hq)
-    return per * 1e6, reps + 1, threads
-
-
 def omp_threads():
     env = os.environ.get("OMP_NUM_THREADS")
     n = len(os.sched_getaffinity(0))
@@ -210,18 +241,33 @@ def omp_threads():
     return n
 
 
-def run_decode_workload(args, torch, plx, synth, oracle):
-    idx = {"long": 2, "varlen": 3, "large": 4}[args.workload]
+def upload_any(torch, spec, synth, tid, tokens):
+    if spec.dtype == synth.BF16:
+        return upload_cache(torch, spec, synth, tid, tokens)
+    a = synth.normal(spec.seed, tid, (tokens, spec.Hkv, spec.D), spec.scale, spec.dtype)
+    return torch.from_numpy(a).cuda()
+
+
+def to_device(torch, a, synth, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    return (t.view(torch.bfloat16) if dtype == synth.BF16 else t).cuda()
+
+
+def decode_record(args, torch, plx, synth, oracle, idx, steps, warmup, cpu="cores"):
+    """One decode workload (BASELINE configuration idx 1..4), timed as a step of
+    parallax_decode over the batch. cpu: "cores" (the oracle on a bounded sample
+    with every core), "one" (the oracle's full step on one thread), "none"."""
     spec = synth.decode_spec(idx)
     lens = spec.seq_lengths()
     T = int(lens.sum())
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
     q_np, r_np = synth.decode_qr(spec)
-    q = torch.from_numpy(q_np).view(torch.bfloat16).cuda()
-    r = torch.from_numpy(r_np).view(torch.bfloat16).cuda()
-    k0 = upload_cache(torch, spec, synth, synth.TID_K, T)
-    v0 = upload_cache(torch, spec, synth, synth.TID_V, T)
-    kv_bytes = 2 * k0.numel() * 2
+    q = to_device(torch, q_np, synth, spec.dtype)
+    r = to_device(torch, r_np, synth, spec.dtype)
+    k0 = upload_any(torch, spec, synth, synth.TID_K, T)
+    v0 = upload_any(torch, spec, synth, synth.TID_V, T)
+    esize = k0.element_size()
+    kv_bytes = 2 * k0.numel() * esize
     copies = max(1, min(4, math.ceil(3 * MALL_BYTES / kv_bytes) + 1)) if kv_bytes < 4 * MALL_BYTES \
         else 1
     ks = [k0] + [k0.clone() for _ in range(copies - 1)]
@@ -231,13 +277,13 @@ def run_decode_workload(args, torch, plx, synth, oracle):
     if not varlen:
         ks = [k.view(spec.B, spec.L, spec.Hkv, spec.D) for k in ks]
         vs = [v.view(spec.B, spec.L, spec.Hkv, spec.D) for v in vs]
-    code = plx.PLX_BF16
+    code = plx.PLX_BF16 if spec.dtype == synth.BF16 else plx.PLX_F32
     ns = args.num_splits
     W = args.window
     splits = plx.decode_num_splits(spec.B, spec.Hq, spec.Hkv, spec.D, spec.L, code, ns, W)
     ws_bytes = plx.decode_workspace_bytes(spec.B, spec.Hq, spec.Hkv, spec.D, spec.L, code, ns, W)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
-    out = torch.empty((spec.B, spec.Hq, spec.D), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((spec.B, spec.Hq, spec.D), dtype=q.dtype, device="cuda")
     out_s = torch.empty_like(out)
     recs = torch.empty((spec.B, spec.Hq, splits, 2 * spec.D + 4), dtype=torch.float32,
                        device="cuda")
@@ -261,14 +307,25 @@ def run_decode_workload(args, torch, plx, synth, oracle):
         c = i % copies
         plx.decode_partial(q, r, ks[c], vs[c], records=recs, **kw)
 
-    t_step = graph_time(torch, step, args.steps, args.warmup)
-    t_soft = graph_time(torch, step_softmax, args.steps, args.warmup)
-    # A packed cache with the automatic plan runs the stream-K kernel, which has
-    # no separate streaming-only entry point: its roofline is taken over the
-    # whole step (streaming kernel + merge). Otherwise the streaming kernel is
-    # timed alone through parallax_decode_partial (the same kernel and plan).
-    stream_k = varlen and ns == 0 and W == 0
-    t_kern = t_step if stream_k else graph_time(torch, step_stream_only, args.steps, args.warmup)
+    tt = timed_steps(torch, step, steps, warmup)
+    t_step = tt["mean"]
+    t_soft = timed_steps(torch, step_softmax, steps, warmup)
+    # The roofline kernel: with one split per sequence the step is a single fused
+    # streaming kernel; a packed cache with the automatic plan runs the stream-K
+    # kernel, which has no streaming-only entry point (its roofline is taken over
+    # the whole step); otherwise the streaming kernel is timed alone through
+    # parallax_decode_partial (the same kernel and plan, records instead of o).
+    mfma = code == plx.PLX_BF16 and spec.D == 128 and spec.Hq // spec.Hkv <= 8
+    stream_k = varlen and ns == 0 and W == 0 and mfma
+    fused = splits == 1 and not stream_k
+    if stream_k or fused:
+        t_kern = t_step
+    else:
+        t_kern = timed_steps(torch, step_stream_only, steps, warmup)["mean"]
+    kname = ("decode_mfma_streamk + decode_reduce (whole step)" if stream_k else
+             ("decode_mfma_bf16_d128" if mfma else "decode_generic")
+             + (" (fused: one split, o written directly)" if fused else
+                " (streaming, split records)"))
 
     # algorithmic bytes: K + V over the visible keys, plus q, r and o
     T_vis = int(np.minimum(lens, W).sum()) if W > 0 else T
@@ -284,24 +341,24 @@ def run_decode_workload(args, torch, plx, synth, oracle):
             last = n - (nb_b - 1) * MASK_BLOCK
             head_keys += spec.Hkv * last + int(mask[b, :, :nb_b - 1].sum()) * MASK_BLOCK
         T_vis = head_keys / spec.Hkv  # key rows of all heads, in units of tokens
-        kv_vis = int(head_keys * 2 * spec.D * 2)
-    qr_bytes = 2 * q.numel() * 2
-    o_bytes = out.numel() * 2
+        kv_vis = int(head_keys * 2 * spec.D * esize)
+    qr_bytes = 2 * q.numel() * esize
+    o_bytes = out.numel() * esize
     step_bytes = kv_vis + qr_bytes + o_bytes
-    kern_bytes = kv_vis + qr_bytes
+    kern_bytes = kv_vis + qr_bytes + (o_bytes if (stream_k or fused) else 0)
     flops = 8 * spec.D * spec.Hq * T_vis
     res = {
         "metric": METRIC,
         "value": round(t_step * 1e6, 3),
         "unit": "us/step",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(t_step * 1e3, 6),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if spec.dtype == synth.BF16 else "f32",
         "data": "synthetic",
         "config": {"workload": spec.name + (f" window{W}" if W > 0 else "")
                    + (f" block-density{args.block_density}" if mask is not None else ""),
@@ -309,14 +366,14 @@ def run_decode_workload(args, torch, plx, synth, oracle):
                    "kv_len": spec.L, "total_kv_tokens": T, "visible_kv_tokens": T_vis,
                    "window": W, "block_density": args.block_density,
                    "kv_cache_copies": copies, "splits": splits},
+        "us_per_step": us_quantiles(tt),
         "hbm_tb_s": round(step_bytes / t_step / 1e12, 4),
         "hbm_frac_of_8tbs": round(step_bytes / t_step / 1e9 / HBM_PEAK_GBS, 4),
         "tflops": round(flops / t_step / 1e12, 3),
-        "softmax_decode_us": round(t_soft * 1e6, 3),
-        "parallax_over_softmax": round(t_step / t_soft, 4),
-        "roofline": {"bound": "hbm",
-                     "kernel": "decode_mfma_streamk + decode_reduce (whole step)" if stream_k else
-                     "decode_mfma_bf16_d128 (streaming, split records)",
+        "softmax_decode_us": round(t_soft["mean"] * 1e6, 3),
+        "softmax_decode_us_q50": round(t_soft["q50"] * 1e6, 3),
+        "parallax_over_softmax": round(t_step / t_soft["mean"], 4),
+        "roofline": {"bound": "hbm", "kernel": kname,
                      "achieved": round(kern_bytes / t_kern / 1e9, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(kern_bytes / t_kern / 1e9 / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(spec.name, splits)
@@ -324,7 +381,10 @@ def run_decode_workload(args, torch, plx, synth, oracle):
                      "avg_us": round(t_kern * 1e6, 3),
                      "bytes_per_launch": kern_bytes},
     }
-    if not args.no_cpu_baseline and mask is None:
+    if idx == 1:  # 256 keys: latency-bound, no roofline claim
+        res["roofline"]["bound"] = "latency"
+    if cpu == "cores" and mask is None:
+        oracle.set_num_threads(omp_threads())
         if varlen or spec.B > 64:
             # bounded sample: the first sequences, regenerated from the same streams
             nb = 4 if spec.B > 64 else 8
@@ -348,18 +408,27 @@ def run_decode_workload(args, torch, plx, synth, oracle):
                      f"{reps} repeats, scaled to the full step by key count"
             threads = min(omp_threads(), nb * spec.Hq)
         else:
-            k_h = synth.decode_kv_rows(spec, synth.TID_K, 0, T).reshape(spec.B, spec.L, spec.Hkv,
-                                                                         spec.D)
-            v_h = synth.decode_kv_rows(spec, synth.TID_V, 0, T).reshape(spec.B, spec.L, spec.Hkv,
-                                                                         spec.D)
-            us, reps, threads = cpu_baseline_decode(oracle, q_np, r_np, (k_h, v_h), spec,
-                                                    args.cpu_seconds, W)
+            k_h, v_h = dense_kv_host(synth, spec, T)
+            us, reps = time_oracle_decode(oracle, q_np, r_np, k_h, v_h, args.cpu_seconds, W)
             sample = f"the full step (all {spec.Hq} heads x {T_vis} keys), {reps} repeats"
+            threads = min(omp_threads(), spec.B * spec.Hq)
         res["cpu_baseline"] = {"value": round(us, 1), "unit": "us/step", "cores": threads,
                                "kind": "oracle", "sample": sample}
+    elif cpu == "one" and mask is None and not varlen:
+        # the full step on one core (per-core figure), and on every core
+        k_h, v_h = dense_kv_host(synth, spec, T)
+        oracle.set_num_threads(1)
+        us1, reps1 = time_oracle_decode(oracle, q_np, r_np, k_h, v_h, args.cpu_seconds_one, W)
+        oracle.set_num_threads(omp_threads())
+        usn, repsn = time_oracle_decode(oracle, q_np, r_np, k_h, v_h, args.cpu_seconds_one, W)
+        res["cpu_oracle_1thread"] = {"value": round(us1, 2), "unit": "us/step", "cores": 1,
+                                     "kind": "oracle", "sample": f"the full step, {reps1} repeats"}
+        res["cpu_oracle_all_cores"] = {"value": round(usn, 2), "unit": "us/step",
+                                       "cores": min(omp_threads(), spec.B * spec.Hq),
+                                       "kind": "oracle", "sample": f"the full step, {repsn} repeats"}
     # parity of the timed configuration on a few rows (the full check lives in the tests)
     o_full = out.float().cpu().numpy().astype(np.float64)
-    rows = [(0, 0), (spec.B - 1, spec.Hq - 1), (spec.B // 2, 3)]
+    rows = [(0, 0), (spec.B - 1, spec.Hq - 1), (spec.B // 2, min(3, spec.Hq - 1))]
     errs = []
     for b, h in rows:
         toks = int(lens[b])
@@ -371,10 +440,70 @@ def run_decode_workload(args, torch, plx, synth, oracle):
                                                                       :-(-toks // MASK_BLOCK)])[0, h]
         errs.append(float(np.abs(o_full[b, h] - ref).max() / np.abs(ref).max()))
     res["sampled_parity_max_norm_err"] = max(errs)
+    del ks, vs, k0, v0
+    torch.cuda.empty_cache()
     return res
 
 
+def dense_kv_host(synth, spec, T):
+    k_h = synth.decode_kv_rows(spec, synth.TID_K, 0, T).reshape(spec.B, spec.L, spec.Hkv, spec.D)
+    v_h = synth.decode_kv_rows(spec, synth.TID_V, 0, T).reshape(spec.B, spec.L, spec.Hkv, spec.D)
+    return k_h, v_h
+
+
+def time_oracle_decode(oracle, q, r, k, v, seconds, window=0):
+    """The oracle's full decode step, repeated to fill about `seconds` of wall
+    time. Returns (us_per_step, repeats)."""
+    t = time.perf_counter()
+    oracle.decode(q, r, k, v, window=window)
+    one = time.perf_counter() - t
+    reps = max(1, int(seconds / max(one, 1e-6)))
+    t = time.perf_counter()
+    for _ in range(reps):
+        oracle.decode(q, r, k, v, window=window)
+    return (time.perf_counter() - t) / reps * 1e6, reps + 1
+
+
+def run_decode_workload(args, torch, plx, synth, oracle):
+    idx = {"tiny": 1, "long": 2, "varlen": 3, "large": 4}[args.workload]
+    return decode_record(args, torch, plx, synth, oracle, idx, args.steps, args.warmup,
+                         "none" if args.no_cpu_baseline else "cores")
+
+
+SUB_KEYS = ("value", "unit", "steps", "warmup", "ms_per_step", "dtype", "config", "us_per_step",
+            "hbm_tb_s", "hbm_frac_of_8tbs", "tflops", "tflops_q50", "softmax_decode_us",
+            "softmax_decode_us_q50", "parallax_over_softmax", "roofline", "cpu_baseline",
+            "cpu_oracle_1thread", "cpu_oracle_all_cores", "sampled_parity_max_norm_err")
+
+
+def run_metric_workload(args, torch, plx, synth, oracle):
+    """The default line. The metric's decode half is headlined on the largest
+    single-GPU decode configuration (large-batch decode, B = 2048, 2048 keys
+    each: 17.2 GB of K/V per step), with its roofline and the oracle's CPU
+    baseline; the other configurations ride along as sub-records, each with
+    its own timing (q05 / q50 / q95 over graph replays) and roofline fraction:
+    tiny fp32 decode and long-context decode (with one-thread and all-core
+    oracle figures), the varlen batch, and the causal prefill (the metric's
+    TFLOP/s half, against the bf16 dense MFMA peak)."""
+    cpu = "none" if args.no_cpu_baseline else "cores"
+    one = "none" if args.no_cpu_baseline else "one"
+    head = decode_record(args, torch, plx, synth, oracle, 4, args.steps, args.warmup, cpu)
+    subs = []
+    for idx, mode in ((1, one), (2, one), (3, "none")):
+        rec = decode_record(args, torch, plx, synth, oracle, idx, 200, 20, mode)
+        subs.append({k: rec[k] for k in SUB_KEYS if k in rec})
+    rec = prefill_record(args, torch, plx, synth, oracle, 20, 3, False)
+    subs.append({k: rec[k] for k in SUB_KEYS if k in rec})
+    head["configs"] = subs
+    return head
+
+
 def run_prefill_workload(args, torch, plx, synth, oracle):
+    return prefill_record(args, torch, plx, synth, oracle, max(1, min(args.steps, 20)),
+                          max(1, min(args.warmup, 3)), not args.no_cpu_baseline)
+
+
+def prefill_record(args, torch, plx, synth, oracle, steps, warm, cpu):
     spec = synth.prefill_spec(5)
     B, Hq, Hkv, L, D = spec.B, spec.Hq, spec.Hkv, spec.L, spec.D
     arrs = {}
@@ -393,9 +522,8 @@ def run_prefill_workload(args, torch, plx, synth, oracle):
     def step(i):
         plx.prefill(t["q"], t["r"], t["k"], t["v"], out=out, window=W, block_mask=mask_t)
 
-    steps = max(1, min(args.steps, 20))
-    warm = max(1, min(args.warmup, 3))
-    ts = graph_time(torch, step, steps, warm)
+    tt = timed_steps(torch, step, steps, warm)
+    ts = tt["mean"]
     pairs = B * visible_pairs(L, W) if mask is None else masked_pairs(mask, L)
     flops = 8 * D * Hq * pairs if mask is None else 8 * D * (Hq // Hkv) * pairs
     res = {
@@ -411,6 +539,8 @@ def run_prefill_workload(args, torch, plx, synth, oracle):
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(flops / ts / 1e12 / BF16_PEAK_TFLOPS, 4), "traffic": None,
                      "avg_us": round(ts * 1e6, 1), "flops_per_launch": flops},
+        "us_per_step": us_quantiles(tt),
+        "tflops_q50": round(flops / tt["q50"] / 1e12, 2),
     }
     rows = np.array([[0, 0, 0], [B - 1, Hq - 1, L - 1], [3, 5, 1000], [7, 8, 2047]])
     o = out.float().cpu().numpy()
@@ -419,8 +549,9 @@ def run_prefill_workload(args, torch, plx, synth, oracle):
     got = o[rows[:, 0], rows[:, 1], rows[:, 2]]
     res["sampled_parity_max_norm_err"] = float(
         (np.abs(got - ref).max(axis=1) / np.abs(ref).max(axis=1)).max())  # worst row
-    if not args.no_cpu_baseline and mask is None:
+    if cpu and mask is None:
         # bounded sample: rows spread over the causal range, scaled by visible keys
+        oracle.set_num_threads(omp_threads())
         g = np.random.default_rng(0)
         n = 512
         sample_rows = np.stack([g.integers(0, B, n), g.integers(0, Hq, n),
@@ -703,7 +834,9 @@ def main():
     plx.lib()
     if args.calibrate_copy:
         calibrate_copy(torch)
-    if args.workload == "prefill":
+    if args.workload == "metric":
+        res = run_metric_workload(args, torch, plx, synth, oracle)
+    elif args.workload == "prefill":
         res = run_prefill_workload(args, torch, plx, synth, oracle)
     elif args.workload == "backward":
         res = run_backward_workload(args, torch, plx, synth, oracle)

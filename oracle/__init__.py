@@ -55,6 +55,10 @@ def _bind(path: str):
     lib.oracle_prefill_backward.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                             dbl, dbl, i64, vp, i64, i64, vp, vp, vp, vp, vp]
     lib.oracle_prefill_backward.restype = i32
+    lib.oracle_set_num_threads.argtypes = [i32]
+    lib.oracle_set_num_threads.restype = None
+    lib.oracle_max_threads.argtypes = []
+    lib.oracle_max_threads.restype = i32
     return lib
 
 
@@ -88,6 +92,15 @@ class _Using:
 
 def using_library(path: str) -> _Using:
     return _Using(path)
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's OpenMP regions (for timing on a given core count)."""
+    _load().oracle_set_num_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
 
 
 def _dtype_of(a: np.ndarray) -> int:

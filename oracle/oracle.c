@@ -144,6 +144,16 @@ static void one_row(const void *q, size_t q_off, const void *r, size_t r_off,
  * block_mask: NULL, or bytes [B, Hkv, mask_cols]; byte kb (nonzero: visible)
  * covers key positions kb * block .. kb * block + block - 1 of the sequence.
  */
+/* Thread count of the OpenMP regions below (for timing the oracle on a given
+ * number of cores; the forward's results do not depend on it). */
+void oracle_set_num_threads(int n)
+{
+    if (n > 0)
+        omp_set_num_threads(n);
+}
+
+int oracle_max_threads(void) { return omp_get_max_threads(); }
+
 int oracle_decode(const void *q, const void *r, const void *k, const void *v, int dtype,
                   const int64_t *seq_start, const int64_t *seq_len, int B, int Hq, int Hkv, int D,
                   double tau, double rho, int64_t window, const uint8_t *block_mask,
