@@ -278,6 +278,45 @@ def test_prefill_stats():
             assert abs(sbar[0, h, i] - softmax(z) @ s) < 1e-13
 
 
+def test_prefill_stats_through_other_paths():
+    """lse and sbar pinned without their own formula:
+    - d lse / d q = qk_scale * kbar, where kbar = sum_j w_j k_j is the oracle's
+      softmax readout (r = 0) with the keys as values (central differences);
+    - sbar = rk_scale * r . kbar (the same readout), and also
+      sbar = rk_scale * d/dt lse(q + (t / qk_scale) r) at t = 0 (the probe score
+      is the slope of the log-partition along r: central differences);
+    - shifting every key by c adds qk_scale * q . c to lse (logits all move by it);
+    - one visible key: lse = its logit; two: numpy's logaddexp of the two."""
+    g = rng(25)
+    B, Hq, Hkv, L, D = 1, 2, 1, 9, 4
+    Q, R = rand(g, B, Hq, L, D), rand(g, B, Hq, L, D)
+    K, V = rand(g, B, Hkv, L, D), rand(g, B, Hkv, L, D)
+    tau, rho = 0.7, 1.3
+    _, lse, sbar = oracle.prefill(Q, R, K, V, qk_scale=tau, rk_scale=rho, stats=True)
+    kbar = oracle.prefill(Q, None, K, K, qk_scale=tau)  # sum_j w_j k_j per row
+    np.testing.assert_allclose(sbar, rho * np.einsum("bhld,bhld->bhl", R, kbar), rtol=0,
+                               atol=1e-12)
+    eps = 1e-5
+    for d in range(D):
+        e = np.zeros(D)
+        e[d] = eps
+        _, lp, _ = oracle.prefill(Q + e, R, K, V, qk_scale=tau, stats=True)
+        _, lm, _ = oracle.prefill(Q - e, R, K, V, qk_scale=tau, stats=True)
+        np.testing.assert_allclose((lp - lm) / (2 * eps), tau * kbar[..., d], rtol=0, atol=1e-8)
+    t = 1e-5
+    _, lp, _ = oracle.prefill(Q + (t / tau) * R, R, K, V, qk_scale=tau, stats=True)
+    _, lm, _ = oracle.prefill(Q - (t / tau) * R, R, K, V, qk_scale=tau, stats=True)
+    np.testing.assert_allclose(rho * (lp - lm) / (2 * t), sbar, rtol=0, atol=1e-8)
+    c = rand(g, D)
+    _, ls, _ = oracle.prefill(Q, R, K + c, V, qk_scale=tau, stats=True)
+    np.testing.assert_allclose(ls, lse + tau * (Q @ c), rtol=0, atol=1e-12)
+    z0 = tau * (Q[0, :, 0] @ K[0, 0, 0])
+    np.testing.assert_allclose(lse[0, :, 0], z0, rtol=0, atol=1e-14)
+    z1 = tau * (Q[0, :, 1] @ K[0, 0, 1])
+    zz = tau * (Q[0, :, 1] @ K[0, 0, 0])
+    np.testing.assert_allclose(lse[0, :, 1], np.logaddexp(zz, z1), rtol=0, atol=1e-14)
+
+
 # ---------------------------------------------------------------- varlen
 def test_packed_varlen_equals_per_sequence_and_empty_sequence_is_zero():
     g = rng(16)

@@ -63,8 +63,9 @@ def test_prefill_row_matches_decode_on_prefix():
 @pytest.mark.parametrize("Hq,Hkv", [(4, 2), (2, 2), (8, 2), (6, 2), (3, 1)])
 @pytest.mark.parametrize("L", [1, 31, 64, 100, 257])
 def test_prefill_mfma_shapes(Hq, Hkv, L):
-    """bf16, head_dim 128: the MFMA kernel (group sizes 1 and even) across q-tile,
-    KV-tile and diagonal boundaries; other group sizes take the generic kernel."""
+    """bf16, head_dim 128: the MFMA kernel across q-tile, KV-tile and diagonal
+    boundaries, for group sizes 1, even (two query heads per work item) and odd
+    (one)."""
     B, D = 2, 128
     q, r, k, v = inputs(B, Hq, Hkv, L, D, synth.BF16, 1.0, 300 + L + Hq)
     t = [to_gpu(x, synth.BF16) for x in (q, r, k, v)]
@@ -92,6 +93,21 @@ def test_prefill_workload_sampled_rows():
     ref = oracle.prefill(q, r, k, v, rows=rows)
     got = from_gpu(o[rows[:, 0], rows[:, 1], rows[:, 2]])
     assert_parity(got, ref, spec.dtype, "prefill workload rows")
+
+
+def test_prefill_workload_full_output():
+    """B=8, L=4096, Hq=16, Hkv=8, D=128, bf16, N(0,1)/sqrt(128): every output row of
+    every (sequence, query head), with lse and sbar, against the oracle."""
+    spec = synth.prefill_spec(5)
+    B, Hq, Hkv, L, D = spec.B, spec.Hq, spec.Hkv, spec.L, spec.D
+    q, r, k, v = inputs(B, Hq, Hkv, L, D, spec.dtype, spec.scale, spec.seed)
+    t = [to_gpu(x, spec.dtype) for x in (q, r, k, v)]
+    o, lse, sbar = plx.prefill(*t, return_stats=True)
+    o, lse, sbar = from_gpu(o), lse.cpu().numpy(), sbar.cpu().numpy()
+    ref, ref_lse, ref_sbar = oracle.prefill(q, r, k, v, stats=True)
+    assert_parity(o, ref, spec.dtype, "causal prefill workload")
+    assert np.abs(lse - ref_lse).max() <= 1e-4 * max(1.0, np.abs(ref_lse).max())
+    assert np.abs(sbar - ref_sbar).max() <= 1e-2 * max(1.0, np.abs(ref_sbar).max())
 
 
 @pytest.mark.parametrize("L", [65, 300])
