@@ -856,28 +856,47 @@ __global__ __launch_bounds__(64) void decode_generic(DecodeArgs a) {
 }
 
 // -------------------------------------------------------------------------
-// Record merge. One workgroup of 256 threads per (query head, sequence,
-// half of the dims). Wave w owns records w, w+4, w+8, ...; it issues the
-// loads of a whole batch of kBatch records before touching any of them (the
-// merge is latency-bound: a handful of dependent round trips would cost more
-// than the bytes), then folds the batch with the online rescaling. The four
-// wave states meet in LDS.
+// Record merge. One wave per (query head, sequence, slice of kMergeDims
+// dims): the merge is latency-bound (a few hundred kilobytes written by the
+// previous kernel), so it is spread over as many compute units as there are
+// slices and every record load is issued before any is used. Lane
+// (group rg, dim dd) folds records rg, rg + RG, rg + 2 RG, ... of the slice's
+// dim dd with the online rescaling; the RG groups then combine through
+// cross-lane exchanges. No LDS, no barrier.
 // Empty records (m = -inf) are skipped (their A, B are never written); a row
 // with no record gets o = 0. Records may carry different pivots: each is
-// re-based onto record 0's pivot pi_0 with
+// re-based onto the first record's pivot pi_0 with
 //   S' = S + (pi_i - pi_0) l,   B' = B + (pi_i - pi_0) A
-// (exact algebra; no change when the pivots agree, as in one call).
+// (exact algebra).
 // -------------------------------------------------------------------------
-constexpr int kBatch = 16;
+constexpr int kMergeDims = 16;     // dims per wave
+constexpr int kMergeBatch = 8;     // records per lane whose loads are in flight together
+
+struct MergeState {
+    float m, l, S, A, B;
+};
+
+__device__ __forceinline__ void merge_into(MergeState &x, float mi, float li, float Si, float Ai, float Bi) {
+    const float M = fmaxf(x.m, mi);
+    if (M == -INFINITY) return;
+    const float ax = __builtin_amdgcn_exp2f(x.m - M);
+    const float ay = __builtin_amdgcn_exp2f(mi - M);
+    x.m = M;
+    x.l = x.l * ax + li * ay;
+    x.S = x.S * ax + Si * ay;
+    x.A = x.A * ax + Ai * ay;
+    x.B = x.B * ax + Bi * ay;
+}
 
 template <typename TO, int D, bool PLX>
-__global__ __launch_bounds__(256) void decode_reduce(DecodeArgs a) {
-    constexpr int DS = D / 2;  // dims per workgroup
-    const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
+__global__ __launch_bounds__(64) void decode_reduce(DecodeArgs a) {
+    constexpr int DW = kMergeDims;
+    constexpr int RG = 64 / DW;  // record groups per wave
+    const int lane = threadIdx.x;
+    const int rg = lane / DW;
+    const int d = blockIdx.z * DW + lane % DW;
     const int hq = blockIdx.x;
     const int b = blockIdx.y;
-    const int d = blockIdx.z * DS + (lane < DS ? lane : 0);
     // this (sequence, head)'s records: a.splits of them, or, for a stream-K
     // plan, the slots b + w of the ranges w that overlap the sequence
     int ns = a.splits;
@@ -893,59 +912,36 @@ __global__ __launch_bounds__(256) void decode_reduce(DecodeArgs a) {
     const float *base = a.ws + first * partial_floats(D);
     const float piv0 = PLX && ns > 0 ? base[2 * D + 3] : 0.f;
 
-    float m = -INFINITY, l = 0.f, S = 0.f, A = 0.f, Bv = 0.f;
-    for (int i0 = w; i0 < ns; i0 += 4 * kBatch) {
-        float4 tail[kBatch];
-        float Ai[kBatch], Bi[kBatch];
+    MergeState st = {-INFINITY, 0.f, 0.f, 0.f, 0.f};
+    for (int i0 = rg; i0 < ns; i0 += RG * kMergeBatch) {
+        float4 tail[kMergeBatch];
+        float Ai[kMergeBatch], Bi[kMergeBatch];
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-            const int i = min(i0 + 4 * j, ns - 1);
+        for (int j = 0; j < kMergeBatch; ++j) {
+            const int i = min(i0 + RG * j, ns - 1);
             const float *rec = base + (int64_t)i * partial_floats(D);
             tail[j] = reinterpret_cast<const float4 *>(rec + 2 * D)[0];
             Ai[j] = rec[d];
             Bi[j] = PLX ? rec[D + d] : 0.f;
         }
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-            const float mi = tail[j].x;
-            if (i0 + 4 * j >= ns || mi == -INFINITY) continue;
+        for (int j = 0; j < kMergeBatch; ++j) {
+            if (i0 + RG * j >= ns || tail[j].x == -INFINITY) continue;
             const float dp = PLX ? tail[j].w - piv0 : 0.f;
-            const float M = fmaxf(m, mi);
-            const float ax = __builtin_amdgcn_exp2f(m - M);
-            const float ay = __builtin_amdgcn_exp2f(mi - M);
-            m = M;
-            l = l * ax + tail[j].y * ay;
-            A = A * ax + Ai[j] * ay;
-            if (PLX) {
-                S = S * ax + (tail[j].z + dp * tail[j].y) * ay;
-                Bv = Bv * ax + (Bi[j] + dp * Ai[j]) * ay;
-            }
+            merge_into(st, tail[j].x, tail[j].y, PLX ? fmaf(dp, tail[j].y, tail[j].z) : 0.f, Ai[j],
+                       PLX ? fmaf(dp, Ai[j], Bi[j]) : 0.f);
         }
     }
-    __shared__ float part[4][5][64];
-    part[w][0][lane] = m;
-    part[w][1][lane] = l;
-    part[w][2][lane] = S;
-    part[w][3][lane] = A;
-    part[w][4][lane] = Bv;
-    __syncthreads();
-    if (w != 0 || lane >= DS) return;
-    float M = -INFINITY;
-    for (int x = 0; x < 4; ++x) M = fmaxf(M, part[x][0][lane]);
+    // combine the record groups (lanes dd, dd + DW, dd + 2 DW, ...)
+#pragma unroll
+    for (int off = DW; off < 64; off <<= 1)
+        merge_into(st, __shfl_xor(st.m, off), __shfl_xor(st.l, off), __shfl_xor(st.S, off),
+                   __shfl_xor(st.A, off), __shfl_xor(st.B, off));
+    if (rg != 0) return;
     float val = 0.f;
-    if (M != -INFINITY) {
-        l = S = A = Bv = 0.f;
-        for (int x = 0; x < 4; ++x) {
-            const float mx = part[x][0][lane];
-            if (mx == -INFINITY) continue;
-            const float c = __builtin_amdgcn_exp2f(mx - M);
-            l += part[x][1][lane] * c;
-            S += part[x][2][lane] * c;
-            A += part[x][3][lane] * c;
-            Bv += part[x][4][lane] * c;
-        }
-        const float inv_l = 1.0f / l;
-        val = PLX ? (A * (1.0f - S * inv_l) + Bv) * inv_l : A * inv_l;
+    if (st.m != -INFINITY) {
+        const float inv_l = 1.0f / st.l;
+        val = PLX ? (st.A * (1.0f - st.S * inv_l) + st.B) * inv_l : st.A * inv_l;
     }
     TO *o = reinterpret_cast<TO *>(a.o) + ((int64_t)b * a.Hq + hq) * D + d;
     if constexpr (sizeof(TO) == 4)
@@ -1000,11 +996,11 @@ hipError_t launch_generic(const DecodeArgs &a, hipStream_t stream) {
 
 template <typename TO, bool PLX>
 hipError_t launch_reduce(const DecodeArgs &a, hipStream_t stream) {
-    dim3 grid(a.Hq, a.B, 2);
+    dim3 grid(a.Hq, a.B, a.D / kMergeDims);
     if (a.D == 64)
-        hipLaunchKernelGGL((decode_reduce<TO, 64, PLX>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((decode_reduce<TO, 64, PLX>), grid, dim3(64), 0, stream, a);
     else
-        hipLaunchKernelGGL((decode_reduce<TO, 128, PLX>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((decode_reduce<TO, 128, PLX>), grid, dim3(64), 0, stream, a);
     return hipGetLastError();
 }
 
