@@ -28,19 +28,28 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# PLX_SANITIZED_HOST_LIBS=1 selects the AddressSanitizer + UBSan build
+# (liboracle_san.so, from build(sanitize=True)); the process must then preload
+# gcc's libasan and libubsan.
+_SANITIZED = os.environ.get("PLX_SANITIZED_HOST_LIBS") == "1"
+_LIB_PATH = os.path.join(_HERE, "liboracle_san.so" if _SANITIZED else "liboracle.so")
 _lib = None
 
 F32, BF16, F64 = 0, 1, 2
 
 
-def build() -> str:
-    """Compile ``liboracle.so`` (plain C, double, OpenMP; no fast-math)."""
-    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-ffp-contract=off",
-           os.path.join(_HERE, "oracle.c"), "-o", _LIB_PATH + ".tmp", "-lm"]
+def build(sanitize: bool = False) -> str:
+    """Compile ``liboracle.so`` (plain C, double, OpenMP; no fast-math).
+    sanitize=True builds liboracle_san.so with AddressSanitizer and UBSan
+    instead (host test tier)."""
+    out = os.path.join(_HERE, "liboracle_san.so" if sanitize else "liboracle.so")
+    opt = (["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+            "-fno-sanitize-recover=undefined"] if sanitize else ["-O2"])
+    cmd = ["gcc", *opt, "-fopenmp", "-fPIC", "-shared", "-std=c11", "-ffp-contract=off",
+           os.path.join(_HERE, "oracle.c"), "-o", out + ".tmp", "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
-    return _LIB_PATH
+    os.replace(out + ".tmp", out)
+    return out
 
 
 def _bind(path: str):

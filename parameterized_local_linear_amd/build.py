@@ -59,5 +59,40 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+CLANG_RT = "/opt/rocm/llvm/lib/clang"
+
+
+def asan_runtime() -> str:
+    """The ROCm clang's shared AddressSanitizer runtime (to preload)."""
+    for ver in sorted(os.listdir(CLANG_RT), reverse=True):
+        p = os.path.join(CLANG_RT, ver, "lib", "linux", "libclang_rt.asan-x86_64.so")
+        if os.path.exists(p):
+            return p
+    raise RuntimeError("no libclang_rt.asan-x86_64.so under " + CLANG_RT)
+
+
+def build_host_sanitized() -> str:
+    """The library with its host code (the C ABI's argument checks, the decode
+    split planner, the launch wrappers of api.hip) built with AddressSanitizer
+    and UBSan, for the host test tier: _build/libparallax_hip_san.so. Device
+    code is built as usual; the kernels' objects are those of build(). A process
+    that loads it must preload asan_runtime()."""
+    objs = [os.path.join(OBJDIR, os.path.splitext(s)[0] + ".o") for s in SOURCES[1:]]
+    if not all(os.path.exists(o) for o in objs):
+        build()
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-omit-frame-pointer"]
+    api_o = os.path.join(OBJDIR, "api_san.o")
+    rc, errs = _run([HIPCC, *FLAGS, "-g", *san, "-c", os.path.join(CSRC, SOURCES[0]), "-o", api_o])
+    if rc != 0:
+        raise RuntimeError(f"hipcc failed on {SOURCES[0]} ({rc}):\n{errs}")
+    out = os.path.join(OBJDIR, "libparallax_hip_san.so")
+    rc, errs = _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *san, "-shared-libsan",
+                     api_o, *objs, "-o", out])
+    if rc != 0:
+        raise RuntimeError(f"link failed ({rc}):\n{errs}")
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

@@ -21,7 +21,11 @@ from dataclasses import dataclass, field
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libsynth.so")
+# PLX_SANITIZED_HOST_LIBS=1 selects the AddressSanitizer + UBSan build
+# (libsynth_san.so, from build(sanitize=True)); the process must then preload
+# gcc's libasan and libubsan.
+_SANITIZED = os.environ.get("PLX_SANITIZED_HOST_LIBS") == "1"
+_LIB_PATH = os.path.join(_HERE, "libsynth_san.so" if _SANITIZED else "libsynth.so")
 _lib = None
 
 F32 = 0
@@ -33,13 +37,18 @@ TID_DO = 6  # upstream gradient dLoss/do of the training backward
 TID_MASK = 7  # block-sparse masks
 
 
-def build() -> str:
-    """Compile ``libsynth.so`` next to this file (gcc, OpenMP)."""
-    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
-           os.path.join(_HERE, "synth.c"), "-o", _LIB_PATH + ".tmp", "-lm"]
+def build(sanitize: bool = False) -> str:
+    """Compile ``libsynth.so`` next to this file (gcc, OpenMP).
+    sanitize=True builds libsynth_san.so with AddressSanitizer and UBSan
+    instead (host test tier)."""
+    out = os.path.join(_HERE, "libsynth_san.so" if sanitize else "libsynth.so")
+    opt = (["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+            "-fno-sanitize-recover=undefined"] if sanitize else ["-O2"])
+    cmd = ["gcc", *opt, "-fopenmp", "-fPIC", "-shared", "-std=c11",
+           os.path.join(_HERE, "synth.c"), "-o", out + ".tmp", "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
-    return _LIB_PATH
+    os.replace(out + ".tmp", out)
+    return out
 
 
 def _load():
