@@ -83,12 +83,21 @@ typedef enum {
     PLX_ERR_HIP = 4          /* the HIP runtime reported an error */
 } plx_status;
 
-typedef enum { PLX_F32 = 0, PLX_BF16 = 1 } plx_dtype;
+typedef enum {
+    PLX_F32 = 0,
+    PLX_BF16 = 1,
+    /* Not element types: these two make every 32-bit int a value of
+     * plx_dtype, so that any code a caller passes is a valid argument and an
+     * unknown one is rejected with PLX_ERR_UNSUPPORTED. */
+    PLX_DTYPE_RANGE_MIN_ = -0x7fffffff - 1,
+    PLX_DTYPE_RANGE_MAX_ = 0x7fffffff
+} plx_dtype;
 
 /* PARALLAX_ABI_VERSION of the built library. */
 int parallax_abi_version(void);
 
-/* Static, never-NULL description of a status code. */
+/* Static, never-NULL description of a status code (any int: values that are
+ * no plx_status give "unknown status"). */
 const char *parallax_status_string(int status);
 
 /* ------------------------------------------------------------------------
@@ -123,21 +132,21 @@ const char *parallax_status_string(int status);
  * Returns PLX_OK or an error status.
  * ---------------------------------------------------------------------- */
 size_t parallax_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int kv_len, int window,
-                                       int dtype, int num_splits);
+                                       plx_dtype dtype, int num_splits);
 
-int parallax_decode(const void *q, const void *r, const void *k, const void *v, void *o,
+plx_status parallax_decode(const void *q, const void *r, const void *k, const void *v, void *o,
                     const int32_t *cu_seqlens_k, int B, int Hq, int Hkv, int D, int kv_len,
                     int window, const uint8_t *block_mask, float qk_scale, float rk_scale,
-                    int dtype, int num_splits, void *workspace, size_t workspace_bytes,
+                    plx_dtype dtype, int num_splits, void *workspace, size_t workspace_bytes,
                     void *stream);
 
 /* Plain softmax-attention decode on the same kernels and loader with the
  * probe path compiled out: o = sum_j w_j v_j. The baseline against which the
  * cost of the Parallax correction is measured; same layouts and rules as
  * parallax_decode without r and rk_scale. Uses the same workspace size. */
-int softmax_decode(const void *q, const void *k, const void *v, void *o,
+plx_status softmax_decode(const void *q, const void *k, const void *v, void *o,
                    const int32_t *cu_seqlens_k, int B, int Hq, int Hkv, int D, int kv_len,
-                   int window, const uint8_t *block_mask, float qk_scale, int dtype,
+                   int window, const uint8_t *block_mask, float qk_scale, plx_dtype dtype,
                    int num_splits, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Size of the device workspace that the library itself holds for
@@ -161,14 +170,14 @@ int softmax_decode(const void *q, const void *k, const void *v, void *o,
  * array and keeps the last call's records there, so calls that overlap in
  * time on one device (other streams, other host threads) race and must be
  * serialised by the caller. */
-int parallax_decode_noalloc(const void *q, const void *r, const void *k, const void *v, void *o,
+plx_status parallax_decode_noalloc(const void *q, const void *r, const void *k, const void *v, void *o,
                             const int32_t *cu_seqlens_k, int B, int Hq, int Hkv, int D,
                             int kv_len, int window, const uint8_t *block_mask, float qk_scale,
-                            float rk_scale, int dtype, int num_splits, void *stream);
+                            float rk_scale, plx_dtype dtype, int num_splits, void *stream);
 
 /* The split count parallax_decode / softmax_decode use for these
  * arguments (num_splits resolved when it is 0), or 0 when they are invalid. */
-int parallax_decode_num_splits(int B, int Hq, int Hkv, int D, int kv_len, int window, int dtype,
+int parallax_decode_num_splits(int B, int Hq, int Hkv, int D, int kv_len, int window, plx_dtype dtype,
                                int num_splits);
 
 /* ------------------------------------------------------------------------
@@ -201,18 +210,18 @@ size_t parallax_decode_record_bytes(int B, int Hq, int D, int num_records);
  * bytes) instead of o. r == NULL selects the softmax baseline (the probe
  * terms of the records are then zero). Returns PLX_ERR_WORKSPACE when
  * `records` is NULL or too small. */
-int parallax_decode_partial(const void *q, const void *r, const void *k, const void *v,
+plx_status parallax_decode_partial(const void *q, const void *r, const void *k, const void *v,
                             const int32_t *cu_seqlens_k, int B, int Hq, int Hkv, int D, int kv_len,
                             int window, const uint8_t *block_mask, float qk_scale,
-                            float rk_scale, int dtype, int num_splits, void *records,
+                            float rk_scale, plx_dtype dtype, int num_splits, void *records,
                             size_t records_bytes, void *stream);
 
 /* Merge records[B][Hq][num_records] (DEVICE) into o [B, Hq, D] (DEVICE,
  * dtype): o = (A + B - (S / l) A) / l over the combined state, or A / l
  * when with_probe == 0. Empty records are skipped; a row with none gets
  * o = 0. D in {64, 128}. */
-int parallax_decode_merge(const void *records, void *o, int B, int Hq, int D, int num_records,
-                          int dtype, int with_probe, void *stream);
+plx_status parallax_decode_merge(const void *records, void *o, int B, int Hq, int D, int num_records,
+                          plx_dtype dtype, int with_probe, void *stream);
 
 /* ------------------------------------------------------------------------
  * Causal prefill / training forward (PyPI README, "Training (Triton)":
@@ -231,10 +240,10 @@ int parallax_decode_merge(const void *records, void *o, int B, int Hq, int D, in
  *   D == 128 and dtype == PLX_BF16 run on bf16 MFMA with fp32 accumulation;
  *   other D in {64, 128} and PLX_F32 run on a plain fp32 kernel. L <= 2^22.
  * ---------------------------------------------------------------------- */
-int parallax_prefill(const void *q, const void *r, const void *k, const void *v, void *o,
+plx_status parallax_prefill(const void *q, const void *r, const void *k, const void *v, void *o,
                      float *lse, float *sbar, void *vbar, int B, int Hq, int Hkv, int L, int D,
                      int window, const uint8_t *block_mask, float qk_scale, float rk_scale,
-                     int dtype, void *stream);
+                     plx_dtype dtype, void *stream);
 
 /* ------------------------------------------------------------------------
  * Backward of the causal prefill (PyPI README, "Training (Triton)": the
@@ -260,12 +269,12 @@ int parallax_prefill(const void *q, const void *r, const void *k, const void *v,
  * ---------------------------------------------------------------------- */
 size_t parallax_prefill_backward_workspace_bytes(int B, int Hq, int L);
 
-int parallax_prefill_backward(const void *q, const void *r, const void *k, const void *v,
+plx_status parallax_prefill_backward(const void *q, const void *r, const void *k, const void *v,
                               const void *o, const void *d_o, const float *lse,
                               const float *sbar, const void *vbar, void *dq, void *dr, void *dk,
                               void *dv, int B, int Hq, int Hkv, int L, int D, int window,
                               const uint8_t *block_mask, float qk_scale, float rk_scale,
-                              int dtype, void *workspace, size_t workspace_bytes, void *stream);
+                              plx_dtype dtype, void *workspace, size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * Packed-sequence (varlen) prefill and its backward (the pages name
@@ -293,20 +302,20 @@ int parallax_prefill_backward(const void *q, const void *r, const void *k, const
  * ---------------------------------------------------------------------- */
 size_t parallax_prefill_varlen_workspace_bytes(int Hq, int total_tokens, int backward);
 
-int parallax_prefill_varlen(const void *q, const void *r, const void *k, const void *v, void *o,
+plx_status parallax_prefill_varlen(const void *q, const void *r, const void *k, const void *v, void *o,
                             float *lse, float *sbar, void *vbar, const int32_t *cu_seqlens, int B,
                             int Hq, int Hkv, int max_len, int total_tokens, int D, int window,
-                            const uint8_t *block_mask, float qk_scale, float rk_scale, int dtype,
+                            const uint8_t *block_mask, float qk_scale, float rk_scale, plx_dtype dtype,
                             void *workspace, size_t workspace_bytes, void *stream);
 
-int parallax_prefill_varlen_backward(const void *q, const void *r, const void *k, const void *v,
+plx_status parallax_prefill_varlen_backward(const void *q, const void *r, const void *k, const void *v,
                                      const void *o, const void *d_o, const float *lse,
                                      const float *sbar, const void *vbar,
                                      const int32_t *cu_seqlens, void *dq, void *dr, void *dk,
                                      void *dv, int B, int Hq, int Hkv,
                                      int max_len, int total_tokens, int D, int window,
                                      const uint8_t *block_mask, float qk_scale, float rk_scale,
-                                     int dtype, void *workspace, size_t workspace_bytes,
+                                     plx_dtype dtype, void *workspace, size_t workspace_bytes,
                                      void *stream);
 
 #ifdef __cplusplus

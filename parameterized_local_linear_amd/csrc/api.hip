@@ -107,6 +107,8 @@ static int check_decode_sizes(int B, int Hq, int Hkv, int D, int kv_len, int win
     return PLX_OK;
 }
 
+static inline plx_status as_status(int s) { return static_cast<plx_status>(s); }
+
 extern "C" {
 
 int parallax_abi_version(void) { return PARALLAX_ABI_VERSION; }
@@ -142,7 +144,7 @@ static size_t streamk_bytes(int B, int Hq, int D, int parts) {
 }
 
 size_t parallax_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int kv_len, int window,
-                                       int dtype, int num_splits) {
+                                       plx_dtype dtype, int num_splits) {
     if (check_decode_sizes(B, Hq, Hkv, D, kv_len, window, dtype) != PLX_OK) return 0;
     const DecodePlan p = plx::plan_decode(B, Hq, Hkv, D, kv_len, window, dtype, num_splits);
     // the same size must also cover a packed cache's stream-K plan
@@ -151,7 +153,7 @@ size_t parallax_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int kv_len
     return p.ws_bytes > sk ? p.ws_bytes : sk;
 }
 
-int parallax_decode_num_splits(int B, int Hq, int Hkv, int D, int kv_len, int window, int dtype,
+int parallax_decode_num_splits(int B, int Hq, int Hkv, int D, int kv_len, int window, plx_dtype dtype,
                                int num_splits) {
     if (check_decode_sizes(B, Hq, Hkv, D, kv_len, window, dtype) != PLX_OK) return 0;
     return plx::plan_decode(B, Hq, Hkv, D, kv_len, window, dtype, num_splits).splits;
@@ -217,23 +219,23 @@ static int decode_common(const void *q, const void *r, const void *k, const void
     return err == hipSuccess ? PLX_OK : PLX_ERR_HIP;
 }
 
-int parallax_decode(const void *q, const void *r, const void *k, const void *v, void *o,
+plx_status parallax_decode(const void *q, const void *r, const void *k, const void *v, void *o,
                     const int32_t *cu_seqlens_k, int B, int Hq, int Hkv, int D, int kv_len,
                     int window, const uint8_t *block_mask, float qk_scale, float rk_scale,
-                    int dtype, int num_splits, void *workspace, size_t workspace_bytes,
+                    plx_dtype dtype, int num_splits, void *workspace, size_t workspace_bytes,
                     void *stream) {
-    return decode_common(q, r, k, v, o, cu_seqlens_k, B, Hq, Hkv, D, kv_len, window, block_mask,
+    return as_status(decode_common(q, r, k, v, o, cu_seqlens_k, B, Hq, Hkv, D, kv_len, window, block_mask,
                          qk_scale, rk_scale, dtype, num_splits, workspace, workspace_bytes, stream,
-                         true);
+                         true));
 }
 
-int softmax_decode(const void *q, const void *k, const void *v, void *o, const int32_t *cu_seqlens_k,
+plx_status softmax_decode(const void *q, const void *k, const void *v, void *o, const int32_t *cu_seqlens_k,
                    int B, int Hq, int Hkv, int D, int kv_len, int window,
-                   const uint8_t *block_mask, float qk_scale, int dtype, int num_splits,
+                   const uint8_t *block_mask, float qk_scale, plx_dtype dtype, int num_splits,
                    void *workspace, size_t workspace_bytes, void *stream) {
-    return decode_common(q, nullptr, k, v, o, cu_seqlens_k, B, Hq, Hkv, D, kv_len, window,
+    return as_status(decode_common(q, nullptr, k, v, o, cu_seqlens_k, B, Hq, Hkv, D, kv_len, window,
                          block_mask, qk_scale, 1.0f, dtype, num_splits, workspace, workspace_bytes,
-                         stream, false);
+                         stream, false));
 }
 
 }  // extern "C"
@@ -271,28 +273,28 @@ int current_scratch(void **out) {
 
 extern "C" {
 
-int parallax_decode_noalloc(const void *q, const void *r, const void *k, const void *v, void *o,
+plx_status parallax_decode_noalloc(const void *q, const void *r, const void *k, const void *v, void *o,
                             const int32_t *cu_seqlens_k, int B, int Hq, int Hkv, int D,
                             int kv_len, int window, const uint8_t *block_mask, float qk_scale,
-                            float rk_scale, int dtype, int num_splits, void *stream) {
+                            float rk_scale, plx_dtype dtype, int num_splits, void *stream) {
     // host-only checks first: invalid arguments, and a plan whose records
     // exceed the static workspace, are refused before anything touches the device
     plx::DecodeArgs a;
     DecodePlan p;
     int st = fill_decode_args(a, q, r, k, v, o, cu_seqlens_k, B, Hq, Hkv, D, kv_len, window,
                               block_mask, qk_scale, rk_scale, dtype, num_splits, true, p);
-    if (st != PLX_OK) return st;
+    if (st != PLX_OK) return as_status(st);
     const size_t need = parallax_decode_workspace_bytes(B, Hq, Hkv, D, kv_len, window, dtype,
                                                         num_splits);
-    if (need > PLX_NOALLOC_SCRATCH_BYTES) return PLX_ERR_WORKSPACE;
+    if (need > PLX_NOALLOC_SCRATCH_BYTES) return as_status(PLX_ERR_WORKSPACE);
     void *ws = nullptr;
     st = current_scratch(&ws);
-    if (st != PLX_OK) return st;
+    if (st != PLX_OK) return as_status(st);
     // no kernel of the decode path needs its workspace cleared: every record
     // the merge reads is written by the streaming kernel of the same call
-    return decode_common(q, r, k, v, o, cu_seqlens_k, B, Hq, Hkv, D, kv_len, window, block_mask,
+    return as_status(decode_common(q, r, k, v, o, cu_seqlens_k, B, Hq, Hkv, D, kv_len, window, block_mask,
                          qk_scale, rk_scale, dtype, num_splits, ws, PLX_NOALLOC_SCRATCH_BYTES,
-                         stream, true);
+                         stream, true));
 }
 
 size_t parallax_decode_record_bytes(int B, int Hq, int D, int num_records) {
@@ -300,10 +302,10 @@ size_t parallax_decode_record_bytes(int B, int Hq, int D, int num_records) {
     return (size_t)B * Hq * num_records * plx::partial_floats(D) * sizeof(float);
 }
 
-int parallax_decode_partial(const void *q, const void *r, const void *k, const void *v,
+plx_status parallax_decode_partial(const void *q, const void *r, const void *k, const void *v,
                             const int32_t *cu_seqlens_k, int B, int Hq, int Hkv, int D, int kv_len,
                             int window, const uint8_t *block_mask, float qk_scale, float rk_scale,
-                            int dtype, int num_splits, void *records, size_t records_bytes,
+                            plx_dtype dtype, int num_splits, void *records, size_t records_bytes,
                             void *stream) {
     plx::DecodeArgs a;
     DecodePlan p;
@@ -311,22 +313,22 @@ int parallax_decode_partial(const void *q, const void *r, const void *k, const v
     // o is not written in this mode; any non-null value passes the checks
     int st = fill_decode_args(a, q, r, k, v, records, cu_seqlens_k, B, Hq, Hkv, D, kv_len, window,
                               block_mask, qk_scale, rk_scale, dtype, num_splits, parallax, p);
-    if (st != PLX_OK) return st;
+    if (st != PLX_OK) return as_status(st);
     if (!records || records_bytes < parallax_decode_record_bytes(B, Hq, D, p.splits))
-        return PLX_ERR_WORKSPACE;
+        return as_status(PLX_ERR_WORKSPACE);
     a.o = nullptr;
     a.ws = reinterpret_cast<float *>(records);
     a.fused = false;
     hipError_t err = plx::launch_decode_split(a, p.path, dtype, parallax, reinterpret_cast<hipStream_t>(stream));
-    return err == hipSuccess ? PLX_OK : PLX_ERR_HIP;
+    return as_status(err == hipSuccess ? PLX_OK : PLX_ERR_HIP);
 }
 
-int parallax_decode_merge(const void *records, void *o, int B, int Hq, int D, int num_records, int dtype,
+plx_status parallax_decode_merge(const void *records, void *o, int B, int Hq, int D, int num_records, plx_dtype dtype,
                           int with_probe, void *stream) {
-    if (B < 1 || Hq < 1 || num_records < 1 || !records || !o) return PLX_ERR_INVALID_ARG;
-    if (B > 65535 || Hq > 65535) return PLX_ERR_UNSUPPORTED;
-    if (D != 64 && D != 128) return PLX_ERR_UNSUPPORTED;
-    if (dtype != PLX_F32 && dtype != PLX_BF16) return PLX_ERR_UNSUPPORTED;
+    if (B < 1 || Hq < 1 || num_records < 1 || !records || !o) return as_status(PLX_ERR_INVALID_ARG);
+    if (B > 65535 || Hq > 65535) return as_status(PLX_ERR_UNSUPPORTED);
+    if (D != 64 && D != 128) return as_status(PLX_ERR_UNSUPPORTED);
+    if (dtype != PLX_F32 && dtype != PLX_BF16) return as_status(PLX_ERR_UNSUPPORTED);
     plx::DecodeArgs a = {};
     a.o = o;
     a.B = B;
@@ -336,7 +338,7 @@ int parallax_decode_merge(const void *records, void *o, int B, int Hq, int D, in
     a.splits = num_records;
     a.ws = const_cast<float *>(reinterpret_cast<const float *>(records));
     hipError_t err = plx::launch_decode_merge(a, dtype, with_probe != 0, reinterpret_cast<hipStream_t>(stream));
-    return err == hipSuccess ? PLX_OK : PLX_ERR_HIP;
+    return as_status(err == hipSuccess ? PLX_OK : PLX_ERR_HIP);
 }
 
 }  // extern "C"
@@ -444,12 +446,12 @@ static int backward_common(const void *q, const void *r, const void *k, const vo
 
 extern "C" {
 
-int parallax_prefill(const void *q, const void *r, const void *k, const void *v, void *o, float *lse,
+plx_status parallax_prefill(const void *q, const void *r, const void *k, const void *v, void *o, float *lse,
                      float *sbar, void *vbar, int B, int Hq, int Hkv, int L, int D, int window,
-                     const uint8_t *block_mask, float qk_scale, float rk_scale, int dtype,
+                     const uint8_t *block_mask, float qk_scale, float rk_scale, plx_dtype dtype,
                      void *stream) {
-    return prefill_common(q, r, k, v, o, lse, sbar, vbar, nullptr, B, Hq, Hkv, L, 0, D, window,
-                          block_mask, qk_scale, rk_scale, dtype, nullptr, 0, stream);
+    return as_status(prefill_common(q, r, k, v, o, lse, sbar, vbar, nullptr, B, Hq, Hkv, L, 0, D, window,
+                          block_mask, qk_scale, rk_scale, dtype, nullptr, 0, stream));
 }
 
 size_t parallax_prefill_varlen_workspace_bytes(int Hq, int total_tokens, int backward) {
@@ -457,15 +459,15 @@ size_t parallax_prefill_varlen_workspace_bytes(int Hq, int total_tokens, int bac
     return kQueueBytes + (backward ? (size_t)Hq * total_tokens * sizeof(plx::RowStat) : 0);
 }
 
-int parallax_prefill_varlen(const void *q, const void *r, const void *k, const void *v, void *o,
+plx_status parallax_prefill_varlen(const void *q, const void *r, const void *k, const void *v, void *o,
                             float *lse, float *sbar, void *vbar, const int32_t *cu_seqlens, int B, int Hq, int Hkv,
                             int max_len, int total_tokens, int D, int window,
-                            const uint8_t *block_mask, float qk_scale, float rk_scale, int dtype,
+                            const uint8_t *block_mask, float qk_scale, float rk_scale, plx_dtype dtype,
                             void *workspace, size_t workspace_bytes, void *stream) {
-    if (!cu_seqlens) return PLX_ERR_INVALID_ARG;
-    return prefill_common(q, r, k, v, o, lse, sbar, vbar, cu_seqlens, B, Hq, Hkv, max_len, total_tokens, D,
+    if (!cu_seqlens) return as_status(PLX_ERR_INVALID_ARG);
+    return as_status(prefill_common(q, r, k, v, o, lse, sbar, vbar, cu_seqlens, B, Hq, Hkv, max_len, total_tokens, D,
                           window, block_mask, qk_scale, rk_scale, dtype, workspace, workspace_bytes,
-                          stream);
+                          stream));
 }
 
 size_t parallax_prefill_backward_workspace_bytes(int B, int Hq, int L) {
@@ -473,28 +475,28 @@ size_t parallax_prefill_backward_workspace_bytes(int B, int Hq, int L) {
     return (size_t)B * Hq * L * sizeof(plx::RowStat);
 }
 
-int parallax_prefill_backward(const void *q, const void *r, const void *k, const void *v, const void *o,
+plx_status parallax_prefill_backward(const void *q, const void *r, const void *k, const void *v, const void *o,
                               const void *d_o, const float *lse, const float *sbar, const void *vbar,
                               void *dq, void *dr,
                               void *dk, void *dv, int B, int Hq, int Hkv, int L, int D, int window,
-                              const uint8_t *block_mask, float qk_scale, float rk_scale, int dtype,
+                              const uint8_t *block_mask, float qk_scale, float rk_scale, plx_dtype dtype,
                               void *workspace, size_t workspace_bytes, void *stream) {
-    return backward_common(q, r, k, v, o, d_o, lse, sbar, vbar, nullptr, dq, dr, dk, dv, B, Hq, Hkv, L, 0, D,
+    return as_status(backward_common(q, r, k, v, o, d_o, lse, sbar, vbar, nullptr, dq, dr, dk, dv, B, Hq, Hkv, L, 0, D,
                            window, block_mask, qk_scale, rk_scale, dtype, workspace,
-                           workspace_bytes, stream);
+                           workspace_bytes, stream));
 }
 
-int parallax_prefill_varlen_backward(const void *q, const void *r, const void *k, const void *v,
+plx_status parallax_prefill_varlen_backward(const void *q, const void *r, const void *k, const void *v,
                                      const void *o, const void *d_o, const float *lse, const float *sbar,
                                      const void *vbar, const int32_t *cu_seqlens, void *dq, void *dr, void *dk, void *dv,
                                      int B, int Hq, int Hkv, int max_len, int total_tokens, int D,
                                      int window, const uint8_t *block_mask, float qk_scale,
-                                     float rk_scale, int dtype, void *workspace,
+                                     float rk_scale, plx_dtype dtype, void *workspace,
                                      size_t workspace_bytes, void *stream) {
-    if (!cu_seqlens) return PLX_ERR_INVALID_ARG;
-    return backward_common(q, r, k, v, o, d_o, lse, sbar, vbar, cu_seqlens, dq, dr, dk, dv, B, Hq, Hkv, max_len,
+    if (!cu_seqlens) return as_status(PLX_ERR_INVALID_ARG);
+    return as_status(backward_common(q, r, k, v, o, d_o, lse, sbar, vbar, cu_seqlens, dq, dr, dk, dv, B, Hq, Hkv, max_len,
                            total_tokens, D, window, block_mask, qk_scale, rk_scale, dtype,
-                           workspace, workspace_bytes, stream);
+                           workspace, workspace_bytes, stream));
 }
 
 }  // extern "C"
