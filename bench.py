@@ -214,23 +214,23 @@ def us_quantiles(t):
 
 
 def measured_traffic(workload_name, splits):
-    """HBM bytes per launch of the streaming kernel from the committed counter
-    summary, or None when the kernel sources changed since it was taken (or
-    it covers another workload / split plan)."""
+    """HBM bytes per launch of the roofline kernel from the committed counter
+    summaries (profiles/*_hbm_traffic.json), or None when none covers this
+    workload and split plan, or when the kernel sources changed since the
+    counters were taken."""
+    import glob
     import hashlib
-    path = os.path.join(ROOT, "profiles", "decode_long_bf16_hbm_traffic.json")
-    if not os.path.exists(path):
-        return None
-    with open(path) as f:
-        rec = json.load(f)
-    if not rec["workload"].startswith(workload_name) or not rec["workload"].endswith(
-            f"{splits} splits"):
-        return None
-    h = hashlib.sha256()
-    for src in rec["sources"]:
-        with open(os.path.join(ROOT, src), "rb") as f:
-            h.update(f.read())
-    return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["source_sha256"] else None
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_hbm_traffic.json"))):
+        with open(path) as f:
+            rec = json.load(f)
+        if rec["workload"] != f"{workload_name}, {splits} splits":
+            continue
+        h = hashlib.sha256()
+        for src in rec["sources"]:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+        return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["source_sha256"] else None
+    return None
 
 
 def omp_threads():
