@@ -233,6 +233,21 @@ def measured_traffic(workload_name, splits):
     return None
 
 
+# Elements whose reference magnitude is below this fraction of the row's largest are left
+# out of the per-element relative error (an elementwise ratio is unbounded where the
+# reference crosses zero).
+REL_FLOOR = 1e-2
+
+
+def elementwise_rel_err(o, ref):
+    """Worst per-element relative error |o - ref| / |ref| over the elements with
+    |ref| >= REL_FLOOR x the largest |ref| of their row (last axis): the pages'
+    accuracy figure, beside the max-norm error used for the parity bar."""
+    o, ref = np.asarray(o, dtype=np.float64), np.asarray(ref, dtype=np.float64)
+    big = np.abs(ref) >= REL_FLOOR * np.abs(ref).max(axis=-1, keepdims=True)
+    return float((np.abs(o - ref)[big] / np.abs(ref)[big]).max())
+
+
 def omp_threads():
     env = os.environ.get("OMP_NUM_THREADS")
     n = len(os.sched_getaffinity(0))
@@ -429,7 +444,7 @@ def decode_record(args, torch, plx, synth, oracle, idx, steps, warmup, cpu="core
     # parity of the timed configuration on a few rows (the full check lives in the tests)
     o_full = out.float().cpu().numpy().astype(np.float64)
     rows = [(0, 0), (spec.B - 1, spec.Hq - 1), (spec.B // 2, min(3, spec.Hq - 1))]
-    errs = []
+    errs, rel = [], []
     for b, h in rows:
         toks = int(lens[b])
         k_h = synth.decode_kv_rows(spec, synth.TID_K, int(cu[b]), toks)[None]
@@ -439,7 +454,9 @@ def decode_record(args, torch, plx, synth, oracle, idx, steps, warmup, cpu="core
                             block_mask=None if mask is None else mask[b:b + 1, :,
                                                                       :-(-toks // MASK_BLOCK)])[0, h]
         errs.append(float(np.abs(o_full[b, h] - ref).max() / np.abs(ref).max()))
+        rel.append(elementwise_rel_err(o_full[b, h], ref))
     res["sampled_parity_max_norm_err"] = max(errs)
+    res["sampled_elementwise_rel_err"] = max(rel)
     del ks, vs, k0, v0
     torch.cuda.empty_cache()
     return res
@@ -473,7 +490,8 @@ def run_decode_workload(args, torch, plx, synth, oracle):
 SUB_KEYS = ("value", "unit", "steps", "warmup", "ms_per_step", "dtype", "config", "us_per_step",
             "hbm_tb_s", "hbm_frac_of_8tbs", "tflops", "tflops_q50", "softmax_decode_us",
             "softmax_decode_us_q50", "parallax_over_softmax", "roofline", "cpu_baseline",
-            "cpu_oracle_1thread", "cpu_oracle_all_cores", "sampled_parity_max_norm_err")
+            "cpu_oracle_1thread", "cpu_oracle_all_cores", "sampled_parity_max_norm_err",
+            "sampled_elementwise_rel_err")
 
 
 def run_metric_workload(args, torch, plx, synth, oracle):
@@ -549,6 +567,7 @@ def prefill_record(args, torch, plx, synth, oracle, steps, warm, cpu):
     got = o[rows[:, 0], rows[:, 1], rows[:, 2]]
     res["sampled_parity_max_norm_err"] = float(
         (np.abs(got - ref).max(axis=1) / np.abs(ref).max(axis=1)).max())  # worst row
+    res["sampled_elementwise_rel_err"] = elementwise_rel_err(got, ref)
     if cpu and mask is None:
         # bounded sample: rows spread over the causal range, scaled by visible keys
         oracle.set_num_threads(omp_threads())
@@ -789,6 +808,7 @@ def run_grid_workload(args, torch, plx, synth, oracle):
                      "kv_gb_s": round(kv_bytes / tq[1] / 1e9, 1),
                      "softmax_decode_us_q50": round(ts[1] * 1e6, 2),
                      "max_norm_err": float(np.abs(got - ref).max() / np.abs(ref).max()),
+                     "elementwise_rel_err": elementwise_rel_err(got, ref),
                      "splits": plx.decode_num_splits(spec.B, spec.Hq, spec.Hkv, spec.D, spec.L,
                                                      plx.PLX_BF16),
                      "pages_h200_parallax_us": PAGES_H200_PARALLAX_US[(spec.B, spec.L)]})

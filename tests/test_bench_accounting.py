@@ -39,3 +39,11 @@ def test_masked_pairs_counts_the_expanded_mask(L, density, seed):
             vis = (j <= i) & ((qb == kb) | (m[b, h][qb, kb] != 0))
             total += int(vis.sum())
     assert bench.masked_pairs(m, L) == total
+
+
+def test_elementwise_relative_error_skips_near_zero_references():
+    import bench
+    ref = np.array([[1.0, -0.5, 1e-9, 0.25]])
+    o = ref * np.array([[1.002, 0.997, 50.0, 1.001]])  # the 1e-9 element is far off
+    # the near-zero element is below 1% of the row's largest and is left out
+    assert abs(bench.elementwise_rel_err(o, ref) - 0.003) < 1e-12
