@@ -70,8 +70,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the CPU oracle sample")
     ap.add_argument("--cpu-seconds-one", type=float, default=3.0,
-                    help="target wall time of each one-thread / all-core oracle figure of the "
-                         "small decode workloads in the default run")
+                    help="target wall time of each oracle figure of the sub-records in the "
+                         "default run (one-thread and all-core full steps of the small decodes, "
+                         "bounded samples of the varlen decode and the prefill)")
     ap.add_argument("--eager", action="store_true",
                     help="launch steps one by one instead of replaying a HIP graph (for profilers)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -268,10 +269,13 @@ def to_device(torch, a, synth, dtype):
     return (t.view(torch.bfloat16) if dtype == synth.BF16 else t).cuda()
 
 
-def decode_record(args, torch, plx, synth, oracle, idx, steps, warmup, cpu="cores"):
-    """One decode workload (BASELINE configuration idx 1..4), timed as a step of
-    parallax_decode over the batch. cpu: "cores" (the oracle on a bounded sample
-    with every core), "one" (the oracle's full step on one thread), "none"."""
+def decode_record(args, torch, plx, synth, oracle, idx, steps, warmup, cpu="cores", cpu_seconds=None):
+    """One decode workload (idx 1..4: tiny fp32, long-context, varlen batch,
+    large batch), timed as a step of parallax_decode over the batch. cpu:
+    "cores" (the oracle on a bounded sample with every core, for cpu_seconds,
+    default --cpu-seconds), "one" (the oracle's full step on one thread), "none"."""
+    if cpu_seconds is None:
+        cpu_seconds = args.cpu_seconds
     spec = synth.decode_spec(idx)
     lens = spec.seq_lengths()
     T = int(lens.sum())
@@ -413,7 +417,7 @@ def decode_record(args, torch, plx, synth, oracle, idx, steps, warmup, cpu="core
             while True:
                 oracle.decode(qs, rs, k_h, v_h, seq_start=cu[:nb], seq_len=lens[:nb], window=W)
                 reps += 1
-                if time.perf_counter() - t > args.cpu_seconds:
+                if time.perf_counter() - t > cpu_seconds:
                     break
             per_seq = (time.perf_counter() - t) / reps / nb
             # scale by tokens: the oracle's cost is linear in the visible keys
@@ -424,7 +428,7 @@ def decode_record(args, torch, plx, synth, oracle, idx, steps, warmup, cpu="core
             threads = min(omp_threads(), nb * spec.Hq)
         else:
             k_h, v_h = dense_kv_host(synth, spec, T)
-            us, reps = time_oracle_decode(oracle, q_np, r_np, k_h, v_h, args.cpu_seconds, W)
+            us, reps = time_oracle_decode(oracle, q_np, r_np, k_h, v_h, cpu_seconds, W)
             sample = f"the full step (all {spec.Hq} heads x {T_vis} keys), {reps} repeats"
             threads = min(omp_threads(), spec.B * spec.Hq)
         res["cpu_baseline"] = {"value": round(us, 1), "unit": "us/step", "cores": threads,
@@ -501,16 +505,19 @@ def run_metric_workload(args, torch, plx, synth, oracle):
     baseline; the other configurations ride along as sub-records, each with
     its own timing (q05 / q50 / q95 over graph replays) and roofline fraction:
     tiny fp32 decode and long-context decode (with one-thread and all-core
-    oracle figures), the varlen batch, and the causal prefill (the metric's
-    TFLOP/s half, against the bf16 dense MFMA peak)."""
+    oracle figures of the full step), the varlen batch and the causal prefill
+    (the metric's TFLOP/s half, against the bf16 dense MFMA peak), these two
+    with the oracle timed on a bounded sample."""
     cpu = "none" if args.no_cpu_baseline else "cores"
     one = "none" if args.no_cpu_baseline else "one"
     head = decode_record(args, torch, plx, synth, oracle, 4, args.steps, args.warmup, cpu)
     subs = []
-    for idx, mode in ((1, one), (2, one), (3, "none")):
-        rec = decode_record(args, torch, plx, synth, oracle, idx, 200, 20, mode)
+    for idx, mode in ((1, one), (2, one), (3, cpu)):
+        rec = decode_record(args, torch, plx, synth, oracle, idx, 200, 20, mode,
+                            cpu_seconds=args.cpu_seconds_one)
         subs.append({k: rec[k] for k in SUB_KEYS if k in rec})
-    rec = prefill_record(args, torch, plx, synth, oracle, 100, COMPUTE_WARMUP, False)
+    rec = prefill_record(args, torch, plx, synth, oracle, 100, COMPUTE_WARMUP, cpu == "cores",
+                         cpu_seconds=args.cpu_seconds_one)
     subs.append({k: rec[k] for k in SUB_KEYS if k in rec})
     head["configs"] = subs
     return head
@@ -529,7 +536,9 @@ def run_prefill_workload(args, torch, plx, synth, oracle):
                           max(args.warmup, COMPUTE_WARMUP), not args.no_cpu_baseline)
 
 
-def prefill_record(args, torch, plx, synth, oracle, steps, warm, cpu):
+def prefill_record(args, torch, plx, synth, oracle, steps, warm, cpu, cpu_seconds=None):
+    if cpu_seconds is None:
+        cpu_seconds = args.cpu_seconds
     spec = synth.prefill_spec(5)
     B, Hq, Hkv, L, D = spec.B, spec.Hq, spec.Hkv, spec.L, spec.D
     arrs = {}
@@ -588,7 +597,7 @@ def prefill_record(args, torch, plx, synth, oracle, steps, warm, cpu):
         while True:
             oracle.prefill(arrs["q"], arrs["r"], arrs["k"], arrs["v"], rows=sample_rows, window=W)
             reps += 1
-            if time.perf_counter() - tt > args.cpu_seconds:
+            if time.perf_counter() - tt > cpu_seconds:
                 break
         per = (time.perf_counter() - tt) / reps
         vis = sample_rows[:, 2] + 1
