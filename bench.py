@@ -772,6 +772,9 @@ PAGES_H200_PARALLAX_US = {(1, 512): 5.79, (1, 1024): 6.48, (1, 4096): 8.61, (1, 
                           (32, 16384): 1094.37}
 
 
+ROTATE_BYTES = 1 << 30  # K/V bytes a cache-defeating rotation cycles through
+
+
 def graph_trials(torch, fn, iters, trials, warmup):
     """Per-step seconds of `trials` replays of one graph of `iters` calls (after
     `warmup` eager calls): the pages' q05 / q50 / q95 replay sweep."""
@@ -819,12 +822,27 @@ def run_grid_workload(args, torch, plx, synth, oracle):
                           trials, max(1, min(args.warmup, 100)))
         ts = graph_trials(torch, lambda i: plx.softmax_decode(q, k, v, out=out_s, workspace=ws),
                           50, trials, max(1, min(args.warmup, 100)))
+        kv_bytes = 2 * k.numel() * 2
+        # the same step with the Infinity Cache defeated: a graph of n steps over n
+        # copies of K and V, n * kv_bytes >= 1 GiB (four times the cache), so no
+        # replay finds its keys there
+        n_rot = 1 if kv_bytes >= ROTATE_BYTES else min(512, -(-ROTATE_BYTES // kv_bytes))
+        if n_rot > 1:
+            ks, vs = [k] + [k.clone() for _ in range(n_rot - 1)], [v] + [v.clone() for _ in range(n_rot - 1)]
+            tr = graph_trials(torch, lambda i: plx.decode(q, r, ks[i % n_rot], vs[i % n_rot], out=out,
+                                                          workspace=ws),
+                              n_rot, trials, max(1, min(args.warmup, 100)))
+            del ks, vs
+        else:
+            tr = tq
+        plx.decode(q, r, k, v, out=out, workspace=ws)
         ref = oracle.decode(q_np, r_np, k_np, v_np)
         got = out.float().cpu().numpy().astype(np.float64)
-        kv_bytes = 2 * k.numel() * 2
         rows.append({"B": spec.B, "L": spec.L, "us_q05": round(tq[0] * 1e6, 2),
                      "us_q50": round(tq[1] * 1e6, 2), "us_q95": round(tq[2] * 1e6, 2),
                      "kv_gb_s": round(kv_bytes / tq[1] / 1e9, 1),
+                     "us_q50_cache_defeated": round(tr[1] * 1e6, 2),
+                     "kv_copies_cache_defeated": n_rot,
                      "softmax_decode_us_q50": round(ts[1] * 1e6, 2),
                      "max_norm_err": float(np.abs(got - ref).max() / np.abs(ref).max()),
                      "elementwise_rel_err": elementwise_rel_err(got, ref),
@@ -839,7 +857,8 @@ def run_grid_workload(args, torch, plx, synth, oracle):
         "data": "synthetic",
         "config": {"workload": "pages-grid-decode-bf16 H8 D128 B{1,32} L{512..16384}",
                    "value_row": "B32 L16384", "timing": "q50 of graph replays of 50 steps, "
-                   "inputs not rotated (the pages' replay sweep)"},
+                   "inputs not rotated (the pages' replay sweep); us_q50_cache_defeated: "
+                   "q50 of replays of one step per K/V copy over >= 1 GiB of copies"},
         "table": rows,
     }
 
