@@ -21,7 +21,9 @@
  * Conventions shared by every entry point:
  *  - Every tensor pointer is a DEVICE pointer; buffers are dense row-major
  *    in the layouts stated below. The caller owns every buffer, including
- *    the decode workspace; the library never allocates or frees memory.
+ *    the decode workspace; the library never allocates or frees memory
+ *    (the scratch of parallax_decode_noalloc is a static device array that
+ *    comes with the loaded library).
  *  - dtype: PLX_F32 (float) or PLX_BF16 (bfloat16 bits). q, r, k, v and o
  *    share it. Arithmetic is fp32 (bf16 inputs are contracted on matrix
  *    cores with fp32 accumulation); bf16 outputs are rounded to nearest-even.
