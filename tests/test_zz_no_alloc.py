@@ -80,3 +80,31 @@ def test_noalloc_decode_python_binding_and_fused_plan():
     t = [to_gpu(x, synth.BF16) for x in (q, r, k, v)]
     assert torch.equal(plx.decode_noalloc(*t), plx.decode(*t))
     assert torch.equal(plx.decode_noalloc(*t, num_splits=2), plx.decode(*t, num_splits=2))
+
+
+def test_noalloc_decode_generic_kernel_window_and_block_mask():
+    # fp32 at D = 64 runs the generic kernel; a window moves every split's range
+    B, Hq, Hkv, D, L = 2, 4, 2, 64, 700
+    q, r = (synth.normal(904, tid, (B, Hq, D), 1.0, synth.F32) for tid in (0, 1))
+    k, v = (synth.normal(904, tid, (B, L, Hkv, D), 1.0, synth.F32) for tid in (2, 3))
+    t = [to_gpu(x, synth.F32) for x in (q, r, k, v)]
+    for splits in (3, 0):
+        a = plx.decode_noalloc(*t, num_splits=splits, window=100)
+        assert torch.equal(a, plx.decode(*t, num_splits=splits, window=100))
+    assert_parity(from_gpu(a), oracle.decode(q, r, k, v, window=100), synth.F32, "noalloc, fp32 window")
+
+    # bf16 with a seeded block mask over 128-key blocks, then a smaller unmasked call
+    B, Hq, Hkv, D, L = 2, 16, 8, 128, 1500
+    s = 1.0 / math.sqrt(D)
+    q, r = (synth.normal(905, tid, (B, Hq, D), s, synth.BF16) for tid in (0, 1))
+    k, v = (synth.normal(905, tid, (B, L, Hkv, D), s, synth.BF16) for tid in (2, 3))
+    t = [to_gpu(x, synth.BF16) for x in (q, r, k, v)]
+    nb = -(-L // plx.MASK_BLOCK)
+    mask = (np.random.default_rng(905).random((B, Hkv, nb)) < 0.5).astype(np.uint8)
+    mask_t = torch.from_numpy(mask).cuda()
+    a = plx.decode_noalloc(*t, num_splits=4, block_mask=mask_t)
+    assert torch.equal(a, plx.decode(*t, num_splits=4, block_mask=mask_t))
+    assert_parity(from_gpu(a), oracle.decode(q, r, k, v, block_mask=mask), synth.BF16,
+                  "noalloc, block mask")
+    t_small = [(x[:1] if x.dim() == 3 else x[:1, :700]).contiguous() for x in t]
+    assert torch.equal(plx.decode_noalloc(*t_small, num_splits=2), plx.decode(*t_small, num_splits=2))
