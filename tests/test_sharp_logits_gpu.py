@@ -1,0 +1,54 @@
+"""Sharp softmax: unscaled N(0,1) inputs with qk_scale = 1, so the logits z = q.k have a
+standard deviation of sqrt(D) (about 11 at D = 128) and the weights are close to
+one-hot. This drives the online softmax through large jumps of the running maximum
+(its lazy rescale), exp2 underflow of most weights, and probe scores far from their
+weighted mean, in decode (one split and several), the causal prefill and its
+backward, against the double-precision oracle at the same bars as every other case
+(max-norm 1e-2 for bf16 outputs and gradients, 1e-5 / 1e-4 for fp32)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parameterized_local_linear_amd as plx
+import synth
+from gpu_util import assert_parity, from_gpu, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+GTOL = {synth.F32: 1e-4, synth.BF16: 1e-2}
+
+
+@pytest.mark.parametrize("splits", [1, 7, 0])
+def test_sharp_logits_decode(splits):
+    B, Hq, Hkv, D, L = 2, 8, 4, 128, 3000
+    q, r = (synth.normal(960, tid, (B, Hq, D), 1.0, synth.BF16) for tid in (0, 1))
+    k, v = (synth.normal(960, tid, (B, L, Hkv, D), 1.0, synth.BF16) for tid in (2, 3))
+    t = [to_gpu(x, synth.BF16) for x in (q, r, k, v)]
+    o = from_gpu(plx.decode(*t, 1.0, 1.0, num_splits=splits))
+    assert_parity(o, oracle.decode(q, r, k, v, qk_scale=1.0, rk_scale=1.0), synth.BF16,
+                  f"sharp decode, splits={splits}")
+
+
+@pytest.mark.parametrize("dtype,D", [(synth.BF16, 128), (synth.F32, 64)])
+def test_sharp_logits_prefill_and_backward(dtype, D):
+    B, Hq, Hkv, L = 1, 4, 2, 300
+    q, r = (synth.normal(961, tid, (B, Hq, L, D), 1.0, dtype) for tid in (synth.TID_Q, synth.TID_R))
+    k, v = (synth.normal(961, tid, (B, Hkv, L, D), 1.0, dtype) for tid in (synth.TID_K, synth.TID_V))
+    do = synth.normal(961, synth.TID_DO, (B, Hq, L, D), 1.0, dtype)
+    t = [to_gpu(x, dtype) for x in (q, r, k, v, do)]
+    vbar = torch.empty_like(t[0])
+    o, lse, sbar = plx.prefill(*t[:4], 1.0, 1.0, return_stats=True, vbar_out=vbar)
+    ref, ref_lse, _ = oracle.prefill(q, r, k, v, qk_scale=1.0, rk_scale=1.0, stats=True)
+    assert_parity(from_gpu(o), ref, dtype, f"sharp prefill D={D}")
+    lse_h = lse.cpu().numpy().astype(np.float64)
+    assert np.abs(lse_h - ref_lse).max() <= 1e-4 * max(1.0, np.abs(ref_lse).max())
+    grads = plx.prefill_backward(*t[:4], o, t[4], lse, sbar, 1.0, 1.0, vbar=vbar)
+    ref_g = oracle.prefill_backward(q, r, k, v, do, qk_scale=1.0, rk_scale=1.0)
+    for name, a, b in zip(("dq", "dr", "dk", "dv"), grads, ref_g):
+        a = from_gpu(a)
+        assert np.all(np.isfinite(a)), name
+        err = np.abs(a - b).max() / np.abs(b).max()
+        assert err <= GTOL[dtype], f"sharp backward D={D} {name}: max-norm error {err:.3e}"
