@@ -52,3 +52,31 @@ def test_sharp_logits_prefill_and_backward(dtype, D):
         assert np.all(np.isfinite(a)), name
         err = np.abs(a - b).max() / np.abs(b).max()
         assert err <= GTOL[dtype], f"sharp backward D={D} {name}: max-norm error {err:.3e}"
+
+
+def test_zero_probe_scale_is_softmax_attention():
+    # r != 0 with rk_scale = 0: every probe score is 0, so the output is softmax
+    # attention; the prefill's pivot drift is switched off at this scale
+    B, Hq, Hkv, D, L = 1, 4, 2, 128, 700
+    q, r = (synth.normal(962, tid, (B, Hq, D), 1.0, synth.BF16) for tid in (0, 1))
+    k, v = (synth.normal(962, tid, (B, L, Hkv, D), 1.0, synth.BF16) for tid in (2, 3))
+    t = [to_gpu(x, synth.BF16) for x in (q, r, k, v)]
+    ref0 = oracle.decode(q, None, k, v, qk_scale=0.3)
+    for splits in (1, 5):
+        assert_parity(from_gpu(plx.decode(*t, 0.3, 0.0, num_splits=splits)), ref0, synth.BF16,
+                      f"decode rk_scale 0, splits={splits}")
+    L = 260
+    q, r = (synth.normal(963, tid, (B, Hq, L, D), 1.0, synth.BF16) for tid in (synth.TID_Q, synth.TID_R))
+    k, v = (synth.normal(963, tid, (B, Hkv, L, D), 1.0, synth.BF16) for tid in (synth.TID_K, synth.TID_V))
+    do = synth.normal(963, synth.TID_DO, (B, Hq, L, D), 1.0, synth.BF16)
+    t = [to_gpu(x, synth.BF16) for x in (q, r, k, v, do)]
+    o, lse, sbar = plx.prefill(*t[:4], 0.3, 0.0, return_stats=True)
+    assert_parity(from_gpu(o), oracle.prefill(q, None, k, v, qk_scale=0.3), synth.BF16,
+                  "prefill rk_scale 0")
+    assert np.abs(sbar.cpu().numpy()).max() == 0.0
+    grads = [from_gpu(x) for x in plx.prefill_backward(*t[:4], o, t[4], lse, sbar, 0.3, 0.0)]
+    ref_g = oracle.prefill_backward(q, r, k, v, do, qk_scale=0.3, rk_scale=0.0)
+    assert np.abs(grads[1]).max() == 0.0  # dr = rk_scale sum ds k
+    for name, a, b in zip(("dq", "dk", "dv"), (grads[0], grads[2], grads[3]), (ref_g[0], ref_g[2], ref_g[3])):
+        err = np.abs(a - b).max() / np.abs(b).max()
+        assert err <= GTOL[synth.BF16], f"backward rk_scale 0 {name}: max-norm error {err:.3e}"
