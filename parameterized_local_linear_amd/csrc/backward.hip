@@ -17,8 +17,10 @@
 //
 // Two kernels, no atomics (results are bit-identical from call to call):
 //  - row pass, one query row per output row: a first sweep over the row's
-//    keys gives ubar, a second accumulates dq and dr; it also stores the
-//    row's {lse log2 e, sbar, delta, ubar} for the key pass.
+//    keys gives ubar (skipped when the forward stored vbar: ubar = g.vbar),
+//    a second accumulates dq and dr together with fp32 sums that correct
+//    delta and ubar (sweeping again when the correction is large); it stores
+//    the row's {lse log2 e, sbar, delta, ubar} for the key pass.
 //  - key pass, one key per output row: sweeps every query row that sees the
 //    key, over all query heads of its KV head, and accumulates dk and dv.
 #include "plx_internal.h"
