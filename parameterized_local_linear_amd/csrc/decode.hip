@@ -28,9 +28,14 @@
 //       MFMA's output lands in exactly the lanes and register order the
 //       readout MFMA wants for its B operand (see the lane map below), and
 //       V's natural [key][dim] layout becomes the readout's A operand by an
-//       8x8 16-bit transpose inside each lane's registers. K and V stream
-//       with 128-bit non-temporal buffer loads straight into registers; the
-//       four waves' states meet in LDS only once, at the end of the split.
+//       8x8 16-bit transpose inside each lane's registers. K tiles are
+//       copied into LDS by the buffer unit (whole 256-byte rows) and read
+//       back in the score MFMA's layout; V streams with 128-bit non-temporal
+//       buffer loads straight into registers. The four waves' states meet in
+//       LDS only once, at the end of the split.
+//   decode_mfma_streamk<G, PLX>  the same streaming for a packed batch: each
+//       KV head's tokens, all sequences back to back, cut into equal ranges,
+//       one workgroup per range and one record per sequence piece.
 //   decode_generic<T, D, PLX>  fp32 or bf16, head_dim 64/128, any group size.
 //       One wave per (query head, split, sequence), fp32 VALU.
 //   decode_reduce<TO, D, PLX>  merges split records into o.
@@ -116,8 +121,8 @@ __device__ __forceinline__ const uint8_t *mask_row(const DecodeArgs &a, int b, i
 // Keys start .. end - 1 (range-relative, non-empty) of sequence b, whose
 // range starts at token seq_tok0 and sequence position pos0, for KV head
 // hkv: writes the G heads' records at record index rbase + h * rstride, or o
-// when `fused`. Ends with a workgroup barrier, so a workgroup may stream
-// several ranges in a row.
+// when `fused`. The record path ends with a workgroup barrier, so a workgroup
+// may stream several ranges in a row; the fused path runs once per workgroup.
 //
 // MASK (a block mask is given): the waves walk the visible 128-key blocks of
 // the range only -- wave w takes keys 32w .. 32w + 31 of each -- so every
