@@ -20,14 +20,15 @@ Also measured in the same run, for each workload:
   * the CPU oracle on the same inputs (cpu_baseline: bounded sample, every core).
 The default line carries sub-records for the tiny fp32 decode and the
 long-context decode (each with the oracle's full step on one thread and on
-every core), the varlen decode batch, and the causal prefill (TFLOP/s against
-the bf16 dense MFMA peak).
+every core), the varlen decode batch and the causal prefill (TFLOP/s against
+the bf16 dense MFMA peak), these two with the oracle on a bounded sample.
 
 Other workloads (--workload tiny | long | varlen | large | prefill | backward |
 grid | prefill-varlen) print their own line; prefill-varlen times the packed
 forward and backward of 16 sequences of U{256..4096} tokens; backward times parallax_prefill_backward (row pass + key
 pass) on the causal-prefill shapes; grid runs the pages' own decode shapes
-(multi-head H = 8, B in {1, 32}, L in {512 .. 16384}) and reports a table.
+(multi-head H = 8, B in {1, 32}, L in {512 .. 16384}) and reports a table, each
+row also timed with the Infinity Cache defeated.
 Prints one JSON line on stdout.
 """
 from __future__ import annotations
