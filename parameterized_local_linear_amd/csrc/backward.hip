@@ -70,8 +70,7 @@ __device__ __forceinline__ int64_t rowstat0(const PrefillSeq &s, int b, int h, i
 // Sum over the LPR lanes that share one row of a wave.
 template <int LPR>
 __device__ __forceinline__ float row_sum(float x) {
-    for (int off = 1; off < LPR; off <<= 1) x += __shfl_xor(x, off, LPR);
-    return x;
+    return group_sum<LPR>(x);
 }
 // Sum over the 64 / LPR rows of a wave (lanes c, c + LPR, ...).
 template <int LPR>
@@ -128,13 +127,37 @@ __global__ __launch_bounds__(64) void bwd_rows_generic(BackwardArgs a) {
     // o and vbar: dz is a difference of terms up to |c_j| times larger than
     // itself, and this keeps delta and ubar consistent with the weights the
     // gradients are formed from (sum_j dz_j = sum_j ds_j = 0).
+    // Both sweeps take the key rows a batch of U steps at a time, loaded while
+    // the batch before is used (step t: keys first + KPI t .. + KPI - 1).
+    constexpr int U = EPL == 4 ? 8 : 4;
+    const int nit = (end - first + KPI - 1) / KPI;
+    auto sweep = [&](auto &&body) __attribute__((always_inline)) {
+        auto load_step = [&](int t, float *kv, float *vv) __attribute__((always_inline)) {
+            const int jj = min(first + t * KPI + kgrp, end - 1);  // past the end: a valid row, unused
+            Frag<T>::load(kb + (int64_t)jj * ks, kv);
+            Frag<T>::load(vb + (int64_t)jj * ks, vv);
+        };
+        float kcur[U][EPL], vcur[U][EPL];
+#pragma unroll
+        for (int u = 0; u < U; ++u) load_step(u, kcur[u], vcur[u]);
+        for (int t0 = 0; t0 < nit; t0 += U) {
+            float knext[U][EPL], vnext[U][EPL];
+#pragma unroll
+            for (int u = 0; u < U; ++u) load_step(t0 + U + u, knext[u], vnext[u]);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (t0 + u < nit) body(first + (t0 + u) * KPI + kgrp, kcur[u], vcur[u]);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) {
+                    kcur[u][e] = knext[u][e];
+                    vcur[u][e] = vnext[u][e];
+                }
+        }
+    };
     float ub = 0.f, delta = 0.f;
-    for (int j0 = first; j0 < end; j0 += KPI) {
-        const int j = j0 + kgrp;
-        const int jj = j < end ? j : end - 1;
-        float kv[EPL], vv[EPL];
-        Frag<T>::load(kb + (int64_t)jj * ks, kv);
-        Frag<T>::load(vb + (int64_t)jj * ks, vv);
+    sweep([&](int j, const float *kv, const float *vv) __attribute__((always_inline)) {
         float zp = 0.f, sp = 0.f, up = 0.f;
         for (int e = 0; e < EPL; ++e) {
             zp += qv[e] * kv[e];
@@ -150,19 +173,14 @@ __global__ __launch_bounds__(64) void bwd_rows_generic(BackwardArgs a) {
             ub = fmaf(w, up, ub);
             delta = fmaf(w, fmaf(sc, up, up), delta);
         }
-    }
+    });
     ub = across_rows<LPR>(ub);
     delta = across_rows<LPR>(delta);
 
     // sweep 2: dq, dr
     float dqa[EPL], dra[EPL];
     for (int e = 0; e < EPL; ++e) dqa[e] = dra[e] = 0.f;
-    for (int j0 = first; j0 < end; j0 += KPI) {
-        const int j = j0 + kgrp;
-        const int jj = j < end ? j : end - 1;
-        float kv[EPL], vv[EPL];
-        Frag<T>::load(kb + (int64_t)jj * ks, kv);
-        Frag<T>::load(vb + (int64_t)jj * ks, vv);
+    sweep([&](int j, const float *kv, const float *vv) __attribute__((always_inline)) {
         float zp = 0.f, sp = 0.f, up = 0.f;
         for (int e = 0; e < EPL; ++e) {
             zp += qv[e] * kv[e];
@@ -180,7 +198,7 @@ __global__ __launch_bounds__(64) void bwd_rows_generic(BackwardArgs a) {
             dqa[e] = fmaf(dz, kv[e], dqa[e]);
             dra[e] = fmaf(ds, kv[e], dra[e]);
         }
-    }
+    });
     for (int e = 0; e < EPL; ++e) {
         dqa[e] = across_rows<LPR>(dqa[e]) * a.qk_scale;
         dra[e] = across_rows<LPR>(dra[e]) * a.rk_scale;
@@ -212,6 +230,7 @@ __global__ __launch_bounds__(64) void bwd_keys_generic(BackwardArgs a) {
     Frag<T>::load(reinterpret_cast<const T *>(a.k) + kvrow + c * EPL, kv);
     Frag<T>::load(reinterpret_cast<const T *>(a.v) + kvrow + c * EPL, vv);
     for (int e = 0; e < EPL; ++e) dka[e] = dva[e] = 0.f;
+    constexpr int UK = EPL == 4 ? 4 : 2;
     // block-sparse: row i sees key j iff j's block is i's own or the mask shows it
     const int nb = (a.L + kMaskBlock - 1) >> kMaskShift;
     const int kb = j >> kMaskShift;
@@ -222,15 +241,18 @@ __global__ __launch_bounds__(64) void bwd_keys_generic(BackwardArgs a) {
         const int64_t rbase = row0_elem(sq, b, hq, a.Hq, a.L, D);
         const int64_t sbase = rowstat0(sq, b, hq, a.Hq, a.L, a.total);
         const int rend = min(sq.len, j + a.window);  // rows that see key j
-        for (int i0 = j; i0 < rend; i0 += RPI) {
-            const int i = i0 + rgrp;
-            const int ii = i < rend ? i : rend - 1;
+        // rows j + RPI t .. + RPI - 1 at step t, a batch of UK steps loaded while
+        // the batch before is used
+        const int nit = (rend - j + RPI - 1) / RPI;
+        auto load_step = [&](int t, float *qv, float *rv, float *gv, RowStat &st) __attribute__((always_inline)) {
+            const int ii = min(j + t * RPI + rgrp, rend - 1);  // past the end: a valid row, unused
             const int64_t row = rbase + (int64_t)ii * qs;
-            float qv[EPL], rv[EPL], gv[EPL];
             Frag<T>::load(reinterpret_cast<const T *>(a.q) + row + c * EPL, qv);
             Frag<T>::load(reinterpret_cast<const T *>(a.r) + row + c * EPL, rv);
             Frag<T>::load(reinterpret_cast<const T *>(a.go) + row + c * EPL, gv);
-            const RowStat st = a.rowstat[sbase + ii];
+            st = a.rowstat[sbase + ii];
+        };
+        auto body = [&](int i, const float *qv, const float *rv, const float *gv, const RowStat &st) __attribute__((always_inline)) {
             float zp = 0.f, sp = 0.f, up = 0.f;
             for (int e = 0; e < EPL; ++e) {
                 zp += qv[e] * kv[e];
@@ -250,6 +272,29 @@ __global__ __launch_bounds__(64) void bwd_keys_generic(BackwardArgs a) {
             for (int e = 0; e < EPL; ++e) {
                 dva[e] = fmaf(pv, gv[e], dva[e]);
                 dka[e] = fmaf(dz, qv[e], fmaf(ds, rv[e], dka[e]));
+            }
+        };
+        float qc[UK][EPL], rc[UK][EPL], gc[UK][EPL];
+        RowStat sc_[UK];
+#pragma unroll
+        for (int u = 0; u < UK; ++u) load_step(u, qc[u], rc[u], gc[u], sc_[u]);
+        for (int t0 = 0; t0 < nit; t0 += UK) {
+            float qn[UK][EPL], rn[UK][EPL], gn[UK][EPL];
+            RowStat sn[UK];
+#pragma unroll
+            for (int u = 0; u < UK; ++u) load_step(t0 + UK + u, qn[u], rn[u], gn[u], sn[u]);
+#pragma unroll
+            for (int u = 0; u < UK; ++u)
+                if (t0 + u < nit) body(j + (t0 + u) * RPI + rgrp, qc[u], rc[u], gc[u], sc_[u]);
+#pragma unroll
+            for (int u = 0; u < UK; ++u) {
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) {
+                    qc[u][e] = qn[u][e];
+                    rc[u][e] = rn[u][e];
+                    gc[u][e] = gn[u][e];
+                }
+                sc_[u] = sn[u];
             }
         }
     }

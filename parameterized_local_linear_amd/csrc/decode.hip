@@ -737,29 +737,6 @@ __device__ __forceinline__ void merge_state(State<EPL> &x, const State<EPL> &y) 
     }
 }
 
-// Sum over each group of LPR consecutive lanes (LPR = 8, 16 or 32), every lane
-// of the group receiving it: DPP exchanges within rows of 16 lanes (partners
-// lane ^ 1, lane ^ 2, then the mirrored half-row and row, which hold the same
-// partial sums as lane ^ 4 and lane ^ 8), then gfx950's permlane16 swap for
-// the partner row. All VALU; the pairing is that of an xor butterfly.
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
-}
-template <int LPR>
-__device__ __forceinline__ float group_sum(float x) {
-    static_assert(LPR == 8 || LPR == 16 || LPR == 32, "group of 8, 16 or 32 lanes");
-    x += dpp_f32<0xb1>(x);   // quad_perm [1, 0, 3, 2]
-    x += dpp_f32<0x4e>(x);   // quad_perm [2, 3, 0, 1]
-    x += dpp_f32<0x141>(x);  // row_half_mirror
-    if constexpr (LPR >= 16) x += dpp_f32<0x140>(x);  // row_mirror
-    if constexpr (LPR >= 32) {
-        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-        x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-    }
-    return x;
-}
-
 template <typename T, int D, bool PLX>
 __global__ __launch_bounds__(64) void decode_generic(DecodeArgs a) {
     constexpr int EPL = Elem<T>::per16;

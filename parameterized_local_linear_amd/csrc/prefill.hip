@@ -12,7 +12,8 @@
 // (Q K^T, R K^T, P V, (P o S) V) on v_mfma_f32_16x16x32_bf16 with fp32
 // accumulation. Described at the kernel.
 // prefill_generic<T, D>: any dtype / head_dim; one wave per query row,
-// the streaming state of the decode kernels (pivot = probe score of key 0).
+// the streaming state of the decode kernels (pivot = probe score of key 0),
+// with the key rows of a batch of steps in flight at once.
 #include "plx_internal.h"
 #include "plx_device.h"
 
@@ -99,36 +100,77 @@ __global__ __launch_bounds__(64) void prefill_generic(PrefillArgs a) {
     const int nb = (a.L + kMaskBlock - 1) >> kMaskShift;
     const uint8_t *mrow = a.block_mask
         ? a.block_mask + (((int64_t)b * a.Hkv + hkv) * nb + (i >> kMaskShift)) * nb : nullptr;
-    for (int j0 = first; j0 < end; j0 += KPI) {
-        const int j = j0 + kgrp;
-        bool valid = j < end;
-        if (mrow && valid && (j >> kMaskShift) != (i >> kMaskShift)) valid = mrow[j >> kMaskShift] != 0;
-        const int jj = valid ? j : end - 1;
-        float kv[EPL], vv[EPL];
+    // Step t covers keys first + KPI t .. + KPI - 1 (key group kgrp takes one).
+    // The key rows of a batch of U steps are loaded while the batch before is
+    // folded in; a batch's dot products reduce with DPP lane exchanges, and
+    // its max rescales the state once.
+    constexpr int U = EPL == 4 ? 8 : 4;
+    const int nit = (end - first + KPI - 1) / KPI;
+    auto load_step = [&](int t, float *kv, float *vv) __attribute__((always_inline)) {
+        const int jj = min(first + t * KPI + kgrp, end - 1);  // past the end: a valid row, unused
         Vec16<T>::load(kb + (int64_t)jj * ks, kv);
         Vec16<T>::load(vb + (int64_t)jj * ks, vv);
-        float zp = 0.f, sp = 0.f;
-        for (int e = 0; e < EPL; ++e) {
-            zp += qv[e] * kv[e];
-            sp += rv[e] * kv[e];
-        }
-        for (int off = 1; off < LPR; off <<= 1) {
-            zp += __shfl_xor(zp, off, LPR);
-            sp += __shfl_xor(sp, off, LPR);
-        }
-        if (valid) {
-            const float m_new = fmaxf(m, zp);
-            const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-            const float p = __builtin_amdgcn_exp2f(zp - m_new);
-            const float sd = sp - piv;
-            m = m_new;
-            l = l * alpha + p;
-            S = S * alpha + p * sd;
+    };
+    auto fold_batch = [&](int t0, float (*kv)[EPL], float (*vv)[EPL]) __attribute__((always_inline)) {
+        float zs[U], ss[U];
+        bool val[U];
+        float mb = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = first + (t0 + u) * KPI + kgrp;
+            bool valid = t0 + u < nit && j < end;
+            if (mrow && valid && (j >> kMaskShift) != (i >> kMaskShift)) valid = mrow[j >> kMaskShift] != 0;
+            float zp = 0.f, sp = 0.f;
+#pragma unroll
             for (int e = 0; e < EPL; ++e) {
-                A[e] = A[e] * alpha + p * vv[e];
-                Bv[e] = Bv[e] * alpha + (p * sd) * vv[e];
+                zp += qv[e] * kv[u][e];
+                sp += rv[e] * kv[u][e];
+            }
+            zs[u] = group_sum<LPR>(zp);
+            ss[u] = group_sum<LPR>(sp);
+            val[u] = valid;
+            if (valid) mb = fmaxf(mb, zs[u]);
+        }
+        if (mb == -INFINITY) return;  // nothing visible in this batch for this key group
+        const float m_new = fmaxf(m, mb);
+        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+        m = m_new;
+        l *= alpha;
+        S *= alpha;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            A[e] *= alpha;
+            Bv[e] *= alpha;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (!val[u]) continue;
+            const float p = __builtin_amdgcn_exp2f(zs[u] - m_new);
+            const float sd = ss[u] - piv;
+            l += p;
+            S += p * sd;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                A[e] += p * vv[u][e];
+                Bv[e] += (p * sd) * vv[u][e];
             }
         }
+    };
+    float kcur[U][EPL], vcur[U][EPL];
+#pragma unroll
+    for (int u = 0; u < U; ++u) load_step(u, kcur[u], vcur[u]);
+    for (int t0 = 0; t0 < nit; t0 += U) {
+        float knext[U][EPL], vnext[U][EPL];
+#pragma unroll
+        for (int u = 0; u < U; ++u) load_step(t0 + U + u, knext[u], vnext[u]);
+        fold_batch(t0, kcur, vcur);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                kcur[u][e] = knext[u][e];
+                vcur[u][e] = vnext[u][e];
+            }
     }
     for (int off = LPR; off < 64; off <<= 1) {
         const float mo = __shfl_xor(m, off);
