@@ -215,17 +215,17 @@ def us_quantiles(t):
             "q95": round(t["q95"] * 1e6, 3)}
 
 
-def measured_traffic(workload_name, splits):
+def measured_traffic(workload):
     """HBM bytes per launch of the roofline kernel from the committed counter
     summaries (profiles/*_hbm_traffic.json), or None when none covers this
-    workload and split plan, or when the kernel sources changed since the
-    counters were taken."""
+    workload (for decode: the workload name and its split plan), or when the
+    kernel sources changed since the counters were taken."""
     import glob
     import hashlib
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_hbm_traffic.json"))):
         with open(path) as f:
             rec = json.load(f)
-        if rec["workload"] != f"{workload_name}, {splits} splits":
+        if rec["workload"] != workload:
             continue
         h = hashlib.sha256()
         for src in rec["sources"]:
@@ -396,7 +396,7 @@ def decode_record(args, torch, plx, synth, oracle, idx, steps, warmup, cpu="core
         "roofline": {"bound": "hbm", "kernel": kname,
                      "achieved": round(kern_bytes / t_kern / 1e9, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(kern_bytes / t_kern / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(spec.name, splits)
+                     "traffic": measured_traffic(f"{spec.name}, {splits} splits")
                      if W == 0 and mask is None else None,
                      "avg_us": round(t_kern * 1e6, 3),
                      "bytes_per_launch": kern_bytes},
@@ -573,7 +573,8 @@ def prefill_record(args, torch, plx, synth, oracle, steps, warm, cpu, cpu_second
                    "block_density": args.block_density},
         "roofline": {"bound": "mfma", "kernel": "prefill", "achieved": round(flops / ts / 1e12, 2),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(flops / ts / 1e12 / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(flops / ts / 1e12 / BF16_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic(spec.name) if W == 0 and mask is None else None,
                      "avg_us": round(ts * 1e6, 1), "flops_per_launch": flops},
         "us_per_step": us_quantiles(tt),
         "tflops_q50": round(flops / tt["q50"] / 1e12, 2),
