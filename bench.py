@@ -335,8 +335,8 @@ def decode_record(args, torch, plx, synth, oracle, idx, steps, warmup, cpu="core
     # kernel, which has no streaming-only entry point (its roofline is taken over
     # the whole step); otherwise the streaming kernel is timed alone through
     # parallax_decode_partial (the same kernel and plan, records instead of o).
-    mfma = code == plx.PLX_BF16 and spec.D == 128 and spec.Hq // spec.Hkv <= 8
-    stream_k = varlen and ns == 0 and W == 0 and mfma
+    mfma = code == plx.PLX_BF16 and spec.D == 128
+    stream_k = varlen and ns == 0 and W == 0 and mfma and spec.Hq // spec.Hkv <= 8
     fused = splits == 1 and not stream_k
     if stream_k or fused:
         t_kern = t_step

@@ -60,11 +60,13 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int kv_len, int window, in
     DecodePlan p;
     if (window > 0 && window < kv_len) kv_len = window;  // keys a query can see at most
     const int G = Hq / Hkv;
-    const bool mfma = dtype == PLX_BF16 && D == 128 && G <= 8;  // 2G MFMA columns <= 16
+    // matrix cores for bf16 at D = 128: 2G MFMA columns <= 16, so larger groups run in
+    // chunks of 8 query heads, one workgroup per (KV head, chunk)
+    const bool mfma = dtype == PLX_BF16 && D == 128;
     p.path = mfma ? DecodePath::Mfma : DecodePath::Generic;
     const int waves = mfma ? 4 : 1;      // waves per workgroup
     const int quantum = 32 * waves;      // keys per split are a multiple of this
-    const long units = (long)B * (mfma ? Hkv : Hq);
+    const long units = (long)B * (mfma ? (long)Hkv * ((G + 7) / 8) : Hq);
     const int max_splits = (kv_len + quantum - 1) / quantum;
     int splits = num_splits;
     if (splits <= 0) {
@@ -130,9 +132,9 @@ const char *parallax_status_string(int status) {
 // 1 per CU 238 us, 2 per CU 229 us, 3 per CU 239 us). Returns the range
 // count per KV head, or 0 where it does not apply (the per-sequence split
 // plan then runs).
-static int streamk_parts(const DecodePlan &p, int B, int Hkv, int D, int kv_len, int dtype,
+static int streamk_parts(const DecodePlan &p, int B, int Hq, int Hkv, int D, int kv_len, int dtype,
                          int window, int num_splits) {
-    if (p.path != plx::DecodePath::Mfma || window != 0 || num_splits != 0) return 0;
+    if (p.path != plx::DecodePath::Mfma || window != 0 || num_splits != 0 || Hq / Hkv > 8) return 0;
     int parts = 2 * plx::device_cu_count() / Hkv;
     parts = parts < 1 ? 1 : (parts > 65535 ? 65535 : parts);
     // the cache holds at most B * kv_len tokens; a range must fit 32-bit offsets
@@ -148,7 +150,7 @@ size_t parallax_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int kv_len
     if (check_decode_sizes(B, Hq, Hkv, D, kv_len, window, dtype) != PLX_OK) return 0;
     const DecodePlan p = plx::plan_decode(B, Hq, Hkv, D, kv_len, window, dtype, num_splits);
     // the same size must also cover a packed cache's stream-K plan
-    const int parts = streamk_parts(p, B, Hkv, D, kv_len, dtype, window, num_splits);
+    const int parts = streamk_parts(p, B, Hq, Hkv, D, kv_len, dtype, window, num_splits);
     const size_t sk = parts ? streamk_bytes(B, Hq, D, parts) : 0;
     return p.ws_bytes > sk ? p.ws_bytes : sk;
 }
@@ -205,7 +207,7 @@ static int decode_common(const void *q, const void *r, const void *k, const void
                               qk_scale, rk_scale, dtype, num_splits, parallax, p);
     if (st != PLX_OK) return st;
     if (cu) {
-        a.sk_parts = streamk_parts(p, B, Hkv, D, kv_len, dtype, window, num_splits);
+        a.sk_parts = streamk_parts(p, B, Hq, Hkv, D, kv_len, dtype, window, num_splits);
         if (a.sk_parts) {
             a.fused = false;
             p.ws_bytes = streamk_bytes(B, Hq, D, a.sk_parts);

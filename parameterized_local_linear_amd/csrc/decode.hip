@@ -20,7 +20,8 @@
 //
 // Kernels:
 //   decode_mfma_bf16_d128<G, PLX>  bf16, head_dim 128, G query heads per KV
-//       head (1 to 8). One workgroup of four waves per (KV head, split,
+//       head (1 to 8; larger groups in chunks of 8). One workgroup of four
+//       waves per (KV head, split, sequence), or per (KV head, chunk, split,
 //       sequence). Both contractions on v_mfma_f32_16x16x32_bf16:
 //         scores   S^T[key, vec] = K_tile . [q_0, r_0, q_1, r_1, ...]^T
 //         readout  O^T[dim, row] = V_tile^T . [p_0, p_0 s'_0, p_1, ...]^T
@@ -137,7 +138,7 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, const int hkv,
                                              const int pos0, const int last_blk,
                                              const int vsplit, const int nvsplit,
                                              const int64_t rbase, const int64_t rstride,
-                                             const bool fused) {
+                                             const bool fused, const int hq0, const int ngl) {
     constexpr int D = 128;
     constexpr int NR = PLX ? 2 : 1;
     constexpr int NV = NR * G;
@@ -147,11 +148,12 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, const int hkv,
     const int wave = threadIdx.x >> 6;
     const int n = lane & 15;
     const int g = lane >> 4;
-    const bool live = n < NV;
+    const int nv = NR * ngl;  // live columns (NV unless a chunk of a larger group ends early)
+    const bool live = n < nv;
     const int h = live ? n / NR : 0;  // head within the group
     const int kind = live ? n % NR : 0;
-    const int hq = hkv * G + h;
-    const int64_t row0 = (int64_t)b * a.Hq + (int64_t)hkv * G;  // first query row of the group
+    const int hq = hq0 + h;
+    const int64_t row0 = (int64_t)b * a.Hq + hq0;  // first query row of the group
 
     const uint16_t *qh = reinterpret_cast<const uint16_t *>(a.q);
     const uint16_t *rh = reinterpret_cast<const uint16_t *>(a.r);
@@ -519,7 +521,7 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, const int hkv,
 
     if (!fused) {
         // record element (column n, dim d) for every live column
-        for (int idx = threadIdx.x; idx < NV * D; idx += 64 * W) {
+        for (int idx = threadIdx.x; idx < nv * D; idx += 64 * W) {
             const int cn = idx / D, d = idx % D;
             float M = -INFINITY;
 #pragma unroll
@@ -536,7 +538,7 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, const int hkv,
             float *rec = a.ws + (rbase + (cn / NR) * rstride) * partial_floats(D);
             rec[(cn % NR) * D + d] = val;
         }
-        if (threadIdx.x < NV) {
+        if (threadIdx.x < nv) {
             const int cn = threadIdx.x;
             float M = -INFINITY;
             for (int w = 0; w < W; ++w) M = fmaxf(M, sm_m[w][cn]);
@@ -566,7 +568,7 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, const int hkv,
     }
 
     // One split: finalise here, o = (A + B - (S / l) A) / l per (head, dim).
-    for (int idx = threadIdx.x; idx < G * D; idx += 64 * W) {
+    for (int idx = threadIdx.x; idx < ngl * D; idx += 64 * W) {
         const int hh = idx / D, d = idx % D;
         const int ca = NR * hh;
         float M = -INFINITY;
@@ -599,16 +601,23 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, const int hkv,
 // AGPRs (no copies before the transpose), and two workgroups share a CU when
 // the grid has more than one per CU (measured: kernel 24.7 -> 24.4 us at
 // B = 1 with 32 splits, 2.60 -> 2.58 ms per step at B = 2048).
-template <int G, bool PLX, bool MASK>
+// CHUNK: more than G query heads per KV head (G = 8 then), taken G at a time:
+// workgroup x = (KV head, chunk) streams the KV head's keys for heads
+// 8 chunk .. 8 chunk + 7 of its group (fewer in a last, partial chunk).
+template <int G, bool PLX, bool MASK, bool CHUNK = false>
 __global__ __launch_bounds__(64 * kDecodeWaves, G <= 2 ? 2 : 1)
 void decode_mfma_bf16_d128(DecodeArgs a) {
     constexpr int D = 128;
-    const int hkv = blockIdx.x;
+    const int gq = a.Hq / a.Hkv;                          // query heads per KV head
+    const int nch = CHUNK ? (gq + G - 1) / G : 1;
+    const int hkv = CHUNK ? blockIdx.x / nch : blockIdx.x;
+    const int hq0 = CHUNK ? hkv * gq + G * (blockIdx.x % nch) : hkv * G;  // first query head
+    const int ngl = CHUNK ? min(G, gq - G * (int)(blockIdx.x % nch)) : G;  // its heads
     const int split = blockIdx.y;
     const int b = blockIdx.z;
     const SeqRange sr = seq_range(a, b);
     const int start = split * a.chunk;
-    const int64_t row0 = (int64_t)b * a.Hq + (int64_t)hkv * G;  // first query row of the group
+    const int64_t row0 = (int64_t)b * a.Hq + hq0;  // first query row of the workgroup
     // Block mask: the splits share the window's visible blocks equally when its
     // blocks fit the LDS staging and its bytes 32-bit offsets; otherwise each
     // split walks the visible blocks of its own key range.
@@ -624,8 +633,8 @@ void decode_mfma_bf16_d128(DecodeArgs a) {
         // sequence, otherwise the records are marked empty for the merge.
         if (a.fused) {
             uint16_t *o = reinterpret_cast<uint16_t *>(a.o) + row0 * D;
-            for (int i = threadIdx.x; i < G * D; i += 64 * kDecodeWaves) o[i] = 0;
-        } else if (threadIdx.x < G) {
+            for (int i = threadIdx.x; i < ngl * D; i += 64 * kDecodeWaves) o[i] = 0;
+        } else if (threadIdx.x < ngl) {
             float *rec = a.ws + ((row0 + threadIdx.x) * a.splits + split) * partial_floats(D);
             reinterpret_cast<float4 *>(rec + 2 * D)[0] = float4{-INFINITY, 0.f, 0.f, 0.f};
         }
@@ -633,11 +642,11 @@ void decode_mfma_bf16_d128(DecodeArgs a) {
     }
     if (whole)
         decode_range<G, PLX, MASK>(a, hkv, b, sr.tok0, 0, sr.len, sr.pos0, sr.last_blk, split,
-                                   a.splits, row0 * a.splits + split, a.splits, a.fused);
+                                   a.splits, row0 * a.splits + split, a.splits, a.fused, hq0, ngl);
     else
         decode_range<G, PLX, MASK>(a, hkv, b, sr.tok0, start, min(start + a.chunk, sr.len),
                                    sr.pos0, sr.last_blk, 0, 0, row0 * a.splits + split, a.splits,
-                                   a.fused);
+                                   a.fused, hq0, ngl);
 }
 
 // Packed batches (stream-K): the tokens of one KV head, all sequences back to
@@ -670,7 +679,7 @@ void decode_mfma_streamk(DecodeArgs a) {
         const int p0 = max(t_lo, s0), p1 = min(t_hi, s1);
         if (p0 >= p1) continue;  // empty sequence, or one that ends before the range
         decode_range<G, PLX, MASK>(a, hkv, b, s0, p0 - s0, p1 - s0, 0, (s1 - s0 - 1) >> kMaskShift,
-                                   0, 0, (int64_t)hkv * G * ns + part + b, ns, false);
+                                   0, 0, (int64_t)hkv * G * ns + part + b, ns, false, hkv * G, G);
     }
 }
 
@@ -1018,6 +1027,11 @@ hipError_t launch_mfma(const DecodeArgs &a, hipStream_t stream) {
             case 8: hipLaunchKernelGGL((decode_mfma_streamk<8, PLX, MASK>), grid, block, 0, stream, a); break;
             default: return hipErrorInvalidValue;
         }
+        return hipGetLastError();
+    }
+    if (G > 8) {  // groups of more than 8 query heads: chunks of 8
+        dim3 grid(a.Hkv * ((G + 7) / 8), a.splits, a.B);
+        hipLaunchKernelGGL((decode_mfma_bf16_d128<8, PLX, MASK, true>), grid, block, 0, stream, a);
         return hipGetLastError();
     }
     dim3 grid(a.Hkv, a.splits, a.B);

@@ -82,14 +82,53 @@ def test_bf16_group_sizes_and_unscaled_inputs(G, scale):
 
 @pytest.mark.parametrize("dtype,D,Hq,Hkv", [
     (synth.BF16, 64, 4, 2), (synth.F32, 128, 4, 2), (synth.F32, 64, 6, 2),
-    (synth.BF16, 128, 18, 2), (synth.F32, 128, 3, 3)])
+    (synth.F32, 128, 18, 2), (synth.F32, 128, 3, 3)])
 @pytest.mark.parametrize("L,splits", [(1, 0), (77, 1), (300, 4), (2000, 0)])
 def test_generic_path(dtype, D, Hq, Hkv, L, splits):
-    """fp32 inputs, head_dim 64 and group sizes above 8 use the generic kernel."""
+    """fp32 inputs and head_dim 64 use the generic kernel."""
     B = 2
     q, r, k, v = decode_inputs(B, Hq, Hkv, D, [L] * B, dtype, 1.0, 31 + L + D)
     o = run_decode(q, r, k, v, dtype, num_splits=splits)
     assert_parity(o, oracle_dense(q, r, k, v), dtype, f"{dtype} D={D} G={Hq // Hkv} L={L}")
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(18, 2), (12, 1), (16, 1), (34, 2), (64, 2)])
+@pytest.mark.parametrize("L,splits,W", [(1, 0, 0), (300, 0, 0), (777, 1, 0), (3001, 5, 0),
+                                        (5000, 0, 0), (2000, 3, 250)])
+def test_large_groups_on_matrix_cores(Hq, Hkv, L, splits, W):
+    """Groups of more than 8 query heads per KV head (9, 12, 16, 17, 32) run the bf16 MFMA
+    kernel in chunks of 8 heads, the last chunk partial where 8 does not divide the group."""
+    B = 2
+    q, r, k, v = decode_inputs(B, Hq, Hkv, 128, [L] * B, synth.BF16, S128, 640 + L + Hq)
+    o = run_decode(q, r, k, v, synth.BF16, num_splits=splits, window=W)
+    what = f"G={Hq // Hkv} L={L} splits={splits} W={W}"
+    assert_parity(o, oracle_dense(q, r, k, v, window=W), synth.BF16, what)
+    t = [to_gpu(x, synth.BF16) for x in (q, k, v)]
+    o0 = from_gpu(plx.softmax_decode(*t, num_splits=splits, window=W))
+    assert_parity(o0, oracle_dense(q, None, k, v, window=W), synth.BF16, what + " softmax")
+
+
+def test_large_group_packed_and_block_mask():
+    """G = 12 over a packed cache (the per-sequence split plan; stream-K takes G <= 8 only)
+    and with a block mask."""
+    Hq, Hkv, D = 24, 2, 128
+    lens = np.array([0, 1, 700, 129, 2500], dtype=np.int64)
+    B = len(lens)
+    q, r, k, v = decode_inputs(B, Hq, Hkv, D, lens, synth.BF16, S128, 77, packed=True)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    tq, tr, tk, tv = (to_gpu(x, synth.BF16) for x in (q, r, k, v))
+    cu_t = torch.from_numpy(cu).cuda()
+    o = from_gpu(plx.decode(tq, tr, tk, tv, cu_seqlens_k=cu_t, kv_len=int(lens.max())))
+    assert np.all(o[lens == 0] == 0.0)
+    ref = oracle.decode(q, r, k, v, seq_start=cu[:-1].astype(np.int64), seq_len=lens)
+    assert_parity(o, ref, synth.BF16, "G=12 packed")
+    L = 3000
+    q, r, k, v = decode_inputs(2, Hq, Hkv, D, [L, L], synth.BF16, S128, 78)
+    nb = -(-L // plx.MASK_BLOCK)
+    mask = (np.random.default_rng(78).random((2, Hkv, nb)) < 0.4).astype(np.uint8)
+    t = [to_gpu(x, synth.BF16) for x in (q, r, k, v)]
+    o = from_gpu(plx.decode(*t, block_mask=torch.from_numpy(mask).cuda()))
+    assert_parity(o, oracle_dense(q, r, k, v, block_mask=mask), synth.BF16, "G=12 block mask")
 
 
 # ------------------------------------------------------------------ varlen
