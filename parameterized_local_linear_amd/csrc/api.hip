@@ -28,8 +28,9 @@ int device_cu_count() {
 
 }  // namespace
 
-// Decode plan. The MFMA path (bf16, head_dim 128, group size 1 to 8) runs
-// one four-wave workgroup per (KV head, split, sequence) over a multiple of
+// Decode plan. The MFMA path (bf16, head_dim 128, any group size; groups of
+// more than 8 query heads in chunks of 8) runs one four-wave workgroup per
+// (KV head, chunk, split, sequence) over a multiple of
 // 128 keys; the generic path one wave per (query head, split, sequence) over
 // a multiple of 32 keys. Without a forced count, the sequence is cut into
 // enough splits for about kTargetWavesPerCU resident waves per compute unit,
