@@ -502,7 +502,7 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, const int hkv,
     lsum = xor_sum_rowgroups(lsum);
 
     // ---- merge the waves' states in LDS
-    __shared__ float sm_acc[W][NV][D];
+    __shared__ __attribute__((aligned(16))) float sm_acc[W][NV][D];
     __shared__ float sm_m[W][NV], sm_l[W][NV], sm_piv[W][NV];
     if (live) {
 #pragma unroll
@@ -518,49 +518,56 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, const int hkv,
     __syncthreads();
     // The waves' probe terms are re-based onto wave 0's pivot:
     //   B_w + (pi_w - pi_0) A_w,  S_w + (pi_w - pi_0) l_w.
+    // Each thread below issues all its LDS reads before it uses any of them:
+    // the weight of a wave that saw no key is selected to 0, not branched
+    // around, so the merge is one round of LDS reads after the barrier.
+    // Weights of the waves' states for a column whose wave maxima are mw.
+    auto wave_weights = [](const float (&mw)[W], float (&c)[W]) __attribute__((always_inline)) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < W; ++w) M = fmaxf(M, mw[w]);
+#pragma unroll
+        for (int w = 0; w < W; ++w) c[w] = mw[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[w] - M);
+        return M;
+    };
 
     if (!fused) {
-        // record element (column n, dim d) for every live column
-        for (int idx = threadIdx.x; idx < nv * D; idx += 64 * W) {
-            const int cn = idx / D, d = idx % D;
-            float M = -INFINITY;
-#pragma unroll
-            for (int w = 0; w < W; ++w) M = fmaxf(M, sm_m[w][cn]);
-            float val = 0.f;
+        // thread: dims d, d + 1 of record column cn (a wave covers one column);
+        // the column's first thread also writes its scalars
+        for (int idx = threadIdx.x; idx < nv * (D / 2); idx += 64 * W) {
+            const int cn = idx / (D / 2), d = 2 * (idx % (D / 2));
+            const bool probe = PLX && cn % NR != 0;
+            const int cb = probe ? cn - 1 : cn;  // the probe column's softmax neighbour
+            float mw[W], c[W], dp[W], lw[W], lb[W];
+            float2 x[W], y[W];
 #pragma unroll
             for (int w = 0; w < W; ++w) {
-                const float mw = sm_m[w][cn];
-                if (mw == -INFINITY) continue;
-                float x = sm_acc[w][cn][d];
-                if (PLX && cn % NR) x = fmaf(sm_piv[w][cn] - sm_piv[0][cn], sm_acc[w][cn - 1][d], x);
-                val += __builtin_amdgcn_exp2f(mw - M) * x;
+                mw[w] = sm_m[w][cn];
+                x[w] = *reinterpret_cast<const float2 *>(&sm_acc[w][cn][d]);
+                y[w] = *reinterpret_cast<const float2 *>(&sm_acc[w][cb][d]);
+                dp[w] = sm_piv[w][cn] - sm_piv[0][cn];
+                lw[w] = sm_l[w][cn];
+                lb[w] = sm_l[w][cb];
             }
-            float *rec = a.ws + (rbase + (cn / NR) * rstride) * partial_floats(D);
-            rec[(cn % NR) * D + d] = val;
-        }
-        if (threadIdx.x < nv) {
-            const int cn = threadIdx.x;
-            float M = -INFINITY;
-            for (int w = 0; w < W; ++w) M = fmaxf(M, sm_m[w][cn]);
+            const float M = wave_weights(mw, c);
+            float2 val = {0.f, 0.f};
             float sum = 0.f;
+#pragma unroll
             for (int w = 0; w < W; ++w) {
-                const float mw = sm_m[w][cn];
-                if (mw == -INFINITY) continue;
-                float x = sm_l[w][cn];
-                if (PLX && cn % NR) x = fmaf(sm_piv[w][cn] - sm_piv[0][cn], sm_l[w][cn - 1], x);
-                sum += __builtin_amdgcn_exp2f(mw - M) * x;
+                const float e = probe ? dp[w] : 0.f;
+                val.x = fmaf(c[w], fmaf(e, y[w].x, x[w].x), val.x);
+                val.y = fmaf(c[w], fmaf(e, y[w].y, x[w].y), val.y);
+                sum = fmaf(c[w], fmaf(e, lb[w], lw[w]), sum);
             }
             float *rec = a.ws + (rbase + (cn / NR) * rstride) * partial_floats(D);
-            if (cn % NR == 0) {
-                rec[2 * D + 0] = M;
-                rec[2 * D + 1] = sum;
-                if (!PLX) {
-                    rec[2 * D + 2] = 0.f;
-                    rec[2 * D + 3] = 0.f;
-                }
-            } else {
-                rec[2 * D + 2] = sum;
-                rec[2 * D + 3] = sm_piv[0][cn];
+            *reinterpret_cast<float2 *>(rec + (cn % NR) * D + d) = val;
+            if (d == 0) {
+                if (!probe)
+                    *reinterpret_cast<float2 *>(rec + 2 * D) = float2{M, sum};
+                if (!PLX)
+                    *reinterpret_cast<float2 *>(rec + 2 * D + 2) = float2{0.f, 0.f};
+                else if (probe)
+                    *reinterpret_cast<float2 *>(rec + 2 * D + 2) = float2{sum, sm_piv[0][cn]};
             }
         }
         __syncthreads();  // the LDS may be reused by the workgroup's next range
@@ -571,21 +578,26 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, const int hkv,
     for (int idx = threadIdx.x; idx < ngl * D; idx += 64 * W) {
         const int hh = idx / D, d = idx % D;
         const int ca = NR * hh;
-        float M = -INFINITY;
+        const int cp = PLX ? ca + 1 : ca;  // the head's probe column
+        float mw[W], c[W], xa[W], xb[W], la[W], lp[W], dp[W];
 #pragma unroll
-        for (int w = 0; w < W; ++w) M = fmaxf(M, sm_m[w][ca]);
+        for (int w = 0; w < W; ++w) {
+            mw[w] = sm_m[w][ca];
+            xa[w] = sm_acc[w][ca][d];
+            la[w] = sm_l[w][ca];
+            xb[w] = sm_acc[w][cp][d];
+            lp[w] = sm_l[w][cp];
+            dp[w] = sm_piv[w][cp] - sm_piv[0][cp];
+        }
+        wave_weights(mw, c);
         float A = 0.f, Bv = 0.f, l = 0.f, S = 0.f;
 #pragma unroll
         for (int w = 0; w < W; ++w) {
-            const float mw = sm_m[w][ca];
-            if (mw == -INFINITY) continue;
-            const float c = __builtin_amdgcn_exp2f(mw - M);
-            A += c * sm_acc[w][ca][d];
-            l += c * sm_l[w][ca];
+            A = fmaf(c[w], xa[w], A);
+            l = fmaf(c[w], la[w], l);
             if (PLX) {
-                const float dp = sm_piv[w][ca + 1] - sm_piv[0][ca + 1];
-                Bv += c * fmaf(dp, sm_acc[w][ca][d], sm_acc[w][ca + 1][d]);
-                S += c * fmaf(dp, sm_l[w][ca], sm_l[w][ca + 1]);
+                Bv = fmaf(c[w], fmaf(dp[w], xa[w], xb[w]), Bv);
+                S = fmaf(c[w], fmaf(dp[w], la[w], lp[w]), S);
             }
         }
         const float inv_l = 1.0f / l;
