@@ -122,8 +122,9 @@ __device__ __forceinline__ const uint8_t *mask_row(const DecodeArgs &a, int b, i
 // Keys start .. end - 1 (range-relative, non-empty) of sequence b, whose
 // range starts at token seq_tok0 and sequence position pos0, for KV head
 // hkv: writes the G heads' records at record index rbase + h * rstride, or o
-// when `fused`. The record path ends with a workgroup barrier, so a workgroup
-// may stream several ranges in a row; the fused path runs once per workgroup.
+// when `fused`. With `more` (the workgroup streams another range after this
+// one) the record path ends with a workgroup barrier, so that the next range
+// may reuse the LDS; the fused path runs once per workgroup.
 //
 // MASK (a block mask is given): the waves walk the visible 128-key blocks of
 // the range only -- wave w takes keys 32w .. 32w + 31 of each -- so every
@@ -138,7 +139,8 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, const int hkv,
                                              const int pos0, const int last_blk,
                                              const int vsplit, const int nvsplit,
                                              const int64_t rbase, const int64_t rstride,
-                                             const bool fused, const int hq0, const int ngl) {
+                                             const bool fused, const int hq0, const int ngl,
+                                             const bool more) {
     constexpr int D = 128;
     constexpr int NR = PLX ? 2 : 1;
     constexpr int NV = NR * G;
@@ -495,8 +497,10 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, const int hkv,
             nx1 = nx2;
         }
     }
-    // the read-ahead copies land in LDS before the workgroup moves on (or ends)
-    if constexpr (kDecodeKInLds) __syncthreads();
+    // the wave's read-ahead copies land in its LDS slots before the workgroup
+    // moves on or ends (the slots are the wave's own; the barrier after the
+    // state writes below then holds every wave until all copies have landed)
+    if constexpr (kDecodeKInLds) __builtin_amdgcn_s_waitcnt(0);
 
     if (MASK && m_run < -1e29f) m_run = -INFINITY;  // no visible key in this wave
     lsum = xor_sum_rowgroups(lsum);
@@ -570,7 +574,7 @@ __device__ __forceinline__ void decode_range(const DecodeArgs &a, const int hkv,
                     *reinterpret_cast<float2 *>(rec + 2 * D + 2) = float2{sum, sm_piv[0][cn]};
             }
         }
-        __syncthreads();  // the LDS may be reused by the workgroup's next range
+        if (more) __syncthreads();  // the workgroup's next range reuses the LDS
         return;
     }
 
@@ -654,11 +658,12 @@ void decode_mfma_bf16_d128(DecodeArgs a) {
     }
     if (whole)
         decode_range<G, PLX, MASK>(a, hkv, b, sr.tok0, 0, sr.len, sr.pos0, sr.last_blk, split,
-                                   a.splits, row0 * a.splits + split, a.splits, a.fused, hq0, ngl);
+                                   a.splits, row0 * a.splits + split, a.splits, a.fused, hq0, ngl,
+                                   false);
     else
         decode_range<G, PLX, MASK>(a, hkv, b, sr.tok0, start, min(start + a.chunk, sr.len),
                                    sr.pos0, sr.last_blk, 0, 0, row0 * a.splits + split, a.splits,
-                                   a.fused, hq0, ngl);
+                                   a.fused, hq0, ngl, false);
 }
 
 // Packed batches (stream-K): the tokens of one KV head, all sequences back to
@@ -691,7 +696,8 @@ void decode_mfma_streamk(DecodeArgs a) {
         const int p0 = max(t_lo, s0), p1 = min(t_hi, s1);
         if (p0 >= p1) continue;  // empty sequence, or one that ends before the range
         decode_range<G, PLX, MASK>(a, hkv, b, s0, p0 - s0, p1 - s0, 0, (s1 - s0 - 1) >> kMaskShift,
-                                   0, 0, (int64_t)hkv * G * ns + part + b, ns, false, hkv * G, G);
+                                   0, 0, (int64_t)hkv * G * ns + part + b, ns, false, hkv * G, G,
+                                   true);
     }
 }
 
