@@ -1002,12 +1002,38 @@ __global__ __launch_bounds__(64) void decode_reduce(DecodeArgs a) {
             Ai[j] = rec[d];
             Bi[j] = PLX ? rec[D + d] : 0.f;
         }
+        // The batch's max first, then every record's weight at once: no
+        // dependent chain of rescales through the records. A record past the
+        // end or empty (its A, B never written) gets weight 0 and zeroed terms.
+        bool ok[kMergeBatch];
+        float M = st.m;
 #pragma unroll
         for (int j = 0; j < kMergeBatch; ++j) {
-            if (i0 + RG * j >= ns || tail[j].x == -INFINITY) continue;
-            const float dp = PLX ? tail[j].w - piv0 : 0.f;
-            merge_into(st, tail[j].x, tail[j].y, PLX ? fmaf(dp, tail[j].y, tail[j].z) : 0.f, Ai[j],
-                       PLX ? fmaf(dp, Ai[j], Bi[j]) : 0.f);
+            ok[j] = i0 + RG * j < ns && tail[j].x != -INFINITY;
+            M = fmaxf(M, ok[j] ? tail[j].x : -INFINITY);
+        }
+        if (M != -INFINITY) {
+            const float a0 = __builtin_amdgcn_exp2f(st.m - M);  // 0 while the state is empty
+            st.l *= a0;
+            st.S *= a0;
+            st.A *= a0;
+            st.B *= a0;
+#pragma unroll
+            for (int j = 0; j < kMergeBatch; ++j) {
+                const float c = ok[j] ? __builtin_amdgcn_exp2f(tail[j].x - M) : 0.f;
+                const float lj = ok[j] ? tail[j].y : 0.f;
+                const float aj = ok[j] ? Ai[j] : 0.f;
+                st.l = fmaf(c, lj, st.l);
+                st.A = fmaf(c, aj, st.A);
+                if (PLX) {
+                    const float dp = tail[j].w - piv0;
+                    const float sj = ok[j] ? fmaf(dp, lj, tail[j].z) : 0.f;
+                    const float bj = ok[j] ? fmaf(dp, aj, Bi[j]) : 0.f;
+                    st.S = fmaf(c, sj, st.S);
+                    st.B = fmaf(c, bj, st.B);
+                }
+            }
+            st.m = M;
         }
     }
     // combine the record groups (lanes dd, dd + DW, dd + 2 DW, ...)
