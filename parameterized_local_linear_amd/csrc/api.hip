@@ -129,11 +129,11 @@ const char *parallax_status_string(int status) {
 
 // Packed caches with an automatic plan and no window run the stream-K kernel:
 // each KV head's tokens in equal ranges, one workgroup per range and four
-// workgroups per CU in all (measured on the 64-sequence mixed-length batch,
-// one box: 1 per CU 214-216 us, 2 per CU 205-209 us, 3 per CU 212 us, 4 per
-// CU 203-206 us, 6 per CU 209 us, 8 per CU 215 us). Returns the range count
-// per KV head, or 0 where it does not apply (the per-sequence split plan
-// then runs).
+// workgroups per CU in all (measured side by side on the 64-sequence
+// mixed-length batch: 1 per CU 214-216 us, 2 per CU 205-209 us, 3 per CU
+// 212 us, 4 per CU 203-206 us, 6 per CU 209 us, 8 per CU 215 us). Returns
+// the range count per KV head, or 0 where it does not apply (the
+// per-sequence split plan then runs).
 static int streamk_parts(const DecodePlan &p, int B, int Hq, int Hkv, int D, int kv_len, int dtype,
                          int window, int num_splits) {
     if (p.path != plx::DecodePath::Mfma || window != 0 || num_splits != 0 || Hq / Hkv > 8) return 0;
