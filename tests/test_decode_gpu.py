@@ -315,9 +315,20 @@ def test_packed_stream_k_plan(G, lens):
     """Packed caches with the automatic plan stream each KV head's tokens in equal ranges
     (records per sequence piece, merged per sequence): every length pattern and group size
     against the oracle, softmax baseline included."""
+    check_stream_k(G, 2, lens, 500 + G)
+
+
+@pytest.mark.parametrize("Hkv", [1, 3])
+@pytest.mark.parametrize("G", [1, 2])
+def test_packed_stream_k_plan_kv_heads(G, Hkv):
+    """The stream-K range count follows the KV head count (four ranges per CU in all: 1024
+    ranges for one KV head, 341 for three); ranges crossing many sequence boundaries."""
+    check_stream_k(G, Hkv, [3, 0, 700, 1, 1, 0, 2500, 31, 32, 33, 0], 530 + 10 * Hkv + G)
+
+
+def check_stream_k(G, Hkv, lens, seed):
     lens = np.array(lens, dtype=np.int64)
-    Hkv = 2
-    q, r, k, v = decode_inputs(len(lens), G * Hkv, Hkv, 128, lens, synth.BF16, 1.0, 500 + G,
+    q, r, k, v = decode_inputs(len(lens), G * Hkv, Hkv, 128, lens, synth.BF16, 1.0, seed,
                                packed=True)
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     t = [to_gpu(x, synth.BF16) for x in (q, r, k, v)]
@@ -330,8 +341,8 @@ def test_packed_stream_k_plan(G, lens):
     if live.any():
         ref = oracle.decode(q, r, k, v, seq_start=cu[:-1].astype(np.int64), seq_len=lens)
         ref0 = oracle.decode(q, None, k, v, seq_start=cu[:-1].astype(np.int64), seq_len=lens)
-        assert_parity(o[live], ref[live], synth.BF16, "stream-K")
-        assert_parity(o0[live], ref0[live], synth.BF16, "stream-K softmax")
+        assert_parity(o[live], ref[live], synth.BF16, f"stream-K Hkv={Hkv}")
+        assert_parity(o0[live], ref0[live], synth.BF16, f"stream-K softmax Hkv={Hkv}")
     # repeated calls are bit-identical
     assert np.array_equal(from_gpu(plx.decode(*t, **kw)), o)
 
