@@ -113,6 +113,24 @@ def test_workspace_plan():
     assert ns(2048, 16, 8, 128, 2048, 1, 0) == 1   # large batch: one split
 
 
+def test_workspace_covers_stream_k_plan():
+    """The decode workspace size also covers a packed cache's stream-K plan: four ranges per
+    CU in all (4 CUs / Hkv per KV head; with no device the CU count falls back to 256), and
+    one record per sequence piece, (ranges + B - 1) per query head. Windows, forced split
+    counts and the generic path do not take that plan."""
+    ws = plx.decode_workspace_bytes
+    rec = (2 * 128 + 4) * 4
+    for B, Hq, Hkv in ((64, 16, 8), (3, 2, 1), (5, 6, 3), (1, 8, 8)):
+        parts = 4 * 256 // Hkv
+        assert ws(B, Hq, Hkv, 128, 8192, 1, 0) >= Hq * (parts + B - 1) * rec
+        # the split plan's records where stream-K does not apply (none for one fused split)
+        s = plx.decode_num_splits(B, Hq, Hkv, 128, 8192, 1, 0, 1000)
+        assert ws(B, Hq, Hkv, 128, 8192, 1, 0, 1000) == (B * Hq * s * rec if s > 1 else 0)
+        assert ws(B, Hq, Hkv, 128, 8192, 1, 7) == B * Hq * 7 * rec
+    # workload 3's plan: 16 x (128 + 63) records
+    assert ws(64, 16, 8, 128, 8192, 1, 0) == 16 * (128 + 63) * rec
+
+
 def _backward(**kw):
     a = dict(q=FAKE, r=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, sbar=FAKE, vbar=None, dq=FAKE,
              dr=FAKE, dk=FAKE, dv=FAKE, B=1, Hq=4, Hkv=2, L=64, D=128, W=0, mask=None, qk=0.1,
