@@ -164,10 +164,11 @@ plx_status softmax_decode(const void *q, const void *k, const void *v, void *o,
  * parallax_decode. The array's device address is looked up on the first call
  * on each device (with that device current); HIP errors of that lookup
  * return PLX_ERR_HIP.
- * Returns PLX_ERR_WORKSPACE, before touching the device, when the plan needs
- * more than PLX_NOALLOC_SCRATCH_BYTES, i.e. when
- * parallax_decode_workspace_bytes(...) for the same arguments exceeds it
- * (for example B * Hq * splits * (2 D + 4) * 4 bytes with splits > 1); other
+ * Returns PLX_ERR_WORKSPACE, before touching the device, when the records of
+ * the plan the call runs need more than PLX_NOALLOC_SCRATCH_BYTES: B * Hq *
+ * splits * (2 D + 4) * 4 bytes for the per-sequence split plan (none with one
+ * split), Hq * (ranges + B - 1) * (2 D + 4) * 4 bytes for a packed cache's
+ * stream-K plan (parallax_decode_workspace_bytes(...) bounds both); other
  * errors as parallax_decode. Every call on one device shares that device's
  * array and keeps the last call's records there, so calls that overlap in
  * time on one device (other streams, other host threads) race and must be

@@ -288,8 +288,13 @@ plx_status parallax_decode_noalloc(const void *q, const void *r, const void *k, 
     int st = fill_decode_args(a, q, r, k, v, o, cu_seqlens_k, B, Hq, Hkv, D, kv_len, window,
                               block_mask, qk_scale, rk_scale, dtype, num_splits, true, p);
     if (st != PLX_OK) return as_status(st);
-    const size_t need = parallax_decode_workspace_bytes(B, Hq, Hkv, D, kv_len, window, dtype,
-                                                        num_splits);
+    // the records of the plan this call runs: the per-sequence splits, or a packed
+    // cache's stream-K ranges (parallax_decode_workspace_bytes bounds both)
+    size_t need = p.ws_bytes;
+    if (cu_seqlens_k) {
+        const int parts = streamk_parts(p, B, Hq, Hkv, D, kv_len, dtype, window, num_splits);
+        if (parts) need = streamk_bytes(B, Hq, D, parts);
+    }
     if (need > PLX_NOALLOC_SCRATCH_BYTES) return as_status(PLX_ERR_WORKSPACE);
     void *ws = nullptr;
     st = current_scratch(&ws);

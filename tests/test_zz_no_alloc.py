@@ -46,7 +46,7 @@ def _both(q, r, k, v, cu, B, Hq, Hkv, D, kv_len, splits):
 def test_noalloc_decode_matches_workspace_decode_on_two_calls():
     Hq, Hkv, D = 16, 8, 128
     # call 1: a packed batch of 32 mixed lengths (the stream-K plan; its records fill
-    # ~1.6 MB of the library's array)
+    # ~2.6 MB of the library's array)
     g = np.random.default_rng(900)
     lens = g.integers(100, 3001, size=32)
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
@@ -108,3 +108,27 @@ def test_noalloc_decode_generic_kernel_window_and_block_mask():
                   "noalloc, block mask")
     t_small = [(x[:1] if x.dim() == 3 else x[:1, :700]).contiguous() for x in t]
     assert torch.equal(plx.decode_noalloc(*t_small, num_splits=2), plx.decode(*t_small, num_splits=2))
+
+
+def test_noalloc_refuses_by_the_plan_it_runs():
+    """The array must hold the records of the plan the call runs, not the bound over both
+    plans that parallax_decode_workspace_bytes gives: a dense batch whose own split records
+    fit runs, though a packed cache of the same sizes would take the stream-K plan, whose
+    records (Hq (4 CUs / Hkv + B - 1) of them) do not fit and are refused before anything
+    runs."""
+    B, Hq, Hkv, D, L = 64, 16, 2, 128, 600
+    assert plx.decode_workspace_bytes(B, Hq, Hkv, D, L, plx.PLX_BF16) > plx.NOALLOC_SCRATCH_BYTES
+    s = 1.0 / math.sqrt(D)
+    q, r = (synth.normal(906, tid, (B, Hq, D), s, synth.BF16) for tid in (0, 1))
+    k, v = (synth.normal(906, tid, (B, L, Hkv, D), s, synth.BF16) for tid in (2, 3))
+    t = [to_gpu(x, synth.BF16) for x in (q, r, k, v)]
+    splits = plx.decode_num_splits(B, Hq, Hkv, D, L, plx.PLX_BF16)
+    assert B * Hq * splits * (2 * D + 4) * 4 <= plx.NOALLOC_SCRATCH_BYTES
+    a = plx.decode_noalloc(*t)
+    assert torch.equal(a, plx.decode(*t))
+    assert_parity(from_gpu(a), oracle.decode(q, r, k, v), synth.BF16, "noalloc, dense G=8")
+    cu = torch.arange(0, (B + 1) * L, L, dtype=torch.int32, device="cuda")
+    kp, vp = (x.reshape(B * L, Hkv, D) for x in t[2:])
+    with pytest.raises(plx.ParallaxError) as e:
+        plx.decode_noalloc(t[0], t[1], kp, vp, cu_seqlens_k=cu, kv_len=L)
+    assert e.value.status == 3
